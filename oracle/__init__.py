@@ -1,0 +1,62 @@
+"""CPU oracle for one tensor-parallel rank's share of a Llama-style MLP.
+
+TEST INFRASTRUCTURE ONLY.  This package is the independent, slow and
+obviously-correct reference that the HIP library is checked against.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import it.  The product path (``tensor_transformer_mlp_tp_amd``)
+never imports, calls or links anything here, and nothing here imports the
+product path: the two share no code.  The only module both sides use is
+``workloads`` (seeded synthetic inputs), which holds none of the MLP's
+arithmetic.
+
+Everything is computed in float64 with numpy from the exact bytes the GPU
+receives (bf16 bit patterns, fp32 values, OCP e4m3fn codes plus fp32 scales).
+
+Sources (the web pages this build follows):
+
+* "Build a model sharding system for serving 70B+ parameter models"
+  (scalablesystem.dev), section "The Tensor-Parallel Shard Group": the
+  column-parallel gate/up projections, the row-parallel down projection whose
+  per-rank output is a partial sum, and the all-reduce that adds the partials.
+* "Tensor, Pipeline and Expert Parallelism: One Model, Many GPUs" (vidyal.ai),
+  section "Step 1: tensor parallelism slices every layer": the first matrix is
+  split by columns and the activation applied locally; Llama adds a second
+  input matrix split the same way; the second matrix is split by rows.
+* "Chapter 12 Parallelism Strategies" (arunshar.com), section 12.2.1
+  "Tensor Parallelism (Megatron-Style)": A = [A_1 | ... | A_t],
+  B = [B_1; ...; B_t], Z = sum_k Z_k.
+* "Model, Tensor & Pipeline Parallelism" (engineer-atlas.dev), sections
+  "What must remain true about the layout" and "What must stay true after
+  deployment": the split must compute the same function as the unsplit
+  model, checked split-against-unsplit on a small configuration.
+
+Parity status: every function here is pinned by ``tests/test_oracle_*.py``
+(brute force, closed forms, a library special case, the Megatron invariant,
+format tables).  No function is "parity unpinned".
+"""
+
+from .formats import bf16_bits_to_f64, e4m3fn_to_f64, E4M3FN_MAX
+from .mlp import (
+    silu,
+    mlp_full,
+    mlp_partial,
+    shard_slice,
+    shard_of_full,
+    fold_fp32,
+    rank_partial_from_storage,
+    rms_normalised_max_error,
+)
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "e4m3fn_to_f64",
+    "E4M3FN_MAX",
+    "silu",
+    "mlp_full",
+    "mlp_partial",
+    "shard_slice",
+    "shard_of_full",
+    "fold_fp32",
+    "rank_partial_from_storage",
+    "rms_normalised_max_error",
+]

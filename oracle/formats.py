@@ -1,0 +1,59 @@
+"""Exact decoding of the storage formats the library consumes (oracle side).
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+* bfloat16: the upper 16 bits of an IEEE-754 binary32.  Decoding places the 16
+  bits in the high half of a 32-bit word and reads it as binary32, which is
+  exact, then widens to float64 (also exact).
+* OCP FP8 E4M3 ("e4m3fn"): 1 sign bit, 4 exponent bits with bias 7, 3 mantissa
+  bits.  Exponent field 0 encodes subnormals (-1)^s * 2^-6 * m/8; other
+  exponent fields encode (-1)^s * 2^(e-7) * (1 + m/8).  There are no
+  infinities; the two codes S.1111.111 (0x7F, 0xFF) are NaN, so the largest
+  finite magnitude is 1.75 * 2^8 = 448.  The pages only say "fp8" at one byte
+  per parameter (shard planner, "The Shard Planner" section of the
+  scalablesystem.dev page); the OCP E4M3 variant is the reading used here.
+
+The e4m3 table is built from that definition with a direct loop over the 256
+codes; it does not use any library fp8 type.
+"""
+
+import numpy as np
+
+E4M3FN_MAX = 448.0
+
+
+def bf16_bits_to_f64(bits):
+    """Decode an array of bf16 bit patterns (uint16) to float64, exactly."""
+    b = np.asarray(bits)
+    if b.dtype != np.uint16:
+        raise TypeError("bf16 storage must be uint16 bit patterns")
+    u32 = b.astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):   # NaN payloads widen to NaN
+        return u32.view(np.float32).astype(np.float64)
+
+
+def _e4m3fn_value(code):
+    sign = -1.0 if (code >> 7) & 1 else 1.0
+    exp_field = (code >> 3) & 0xF
+    mant = code & 0x7
+    if exp_field == 0xF and mant == 0x7:
+        return float("nan")
+    if exp_field == 0:
+        return sign * (2.0 ** -6) * (mant / 8.0)
+    return sign * (2.0 ** (exp_field - 7)) * (1.0 + mant / 8.0)
+
+
+_E4M3FN_TABLE = np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float64)
+
+
+def e4m3fn_table():
+    """The 256 code values, index = code (a copy)."""
+    return _E4M3FN_TABLE.copy()
+
+
+def e4m3fn_to_f64(codes):
+    """Decode an array of e4m3fn codes (uint8) to float64, exactly."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise TypeError("e4m3fn storage must be uint8 codes")
+    return _E4M3FN_TABLE[c]
