@@ -1,0 +1,188 @@
+/*
+ * tp_mlp.h -- C ABI of the MI355X (gfx950) tensor-parallel MLP shard library.
+ *
+ * One tensor-parallel rank's share of a Llama-style MLP under the Megatron
+ * split, and the local sum of the t ranks' partial outputs.
+ *
+ * The operation (sources are web pages; section names given so a reader can
+ * find the passage):
+ *
+ *   - "Build a model sharding system for serving 70B+ parameter models"
+ *     (scalablesystem.dev), section "The Tensor-Parallel Shard Group":
+ *     gate_proj and up_proj are column-parallel (each rank holds a slice of
+ *     the intermediate dimension, weight layout (local_out, in)); down_proj is
+ *     row-parallel (weight layout (out, local_in)); each rank's down output is
+ *     a partial that an all-reduce sums; out/in features must divide by the
+ *     group size.
+ *   - "Tensor, Pipeline and Expert Parallelism: One Model, Many GPUs"
+ *     (vidyal.ai), section "Step 1: tensor parallelism slices every layer":
+ *     the activation is applied locally after the column split; Llama's MLP
+ *     adds a second input matrix split the same way.
+ *   - "Chapter 12 Parallelism Strategies" (arunshar.com), section 12.2.1:
+ *     A = [A_1 | ... | A_t] by columns, B by rows, Z = sum_k Z_k.
+ *
+ * With S_k = [k*I_s, (k+1)*I_s), I_s = I_full / t, rank k computes
+ *
+ *     G = X * W_gate_k^T,  U = X * W_up_k^T          (M x I_s, fp32 accumulate)
+ *     A = SiLU(G) (.) U,   SiLU(z) = z / (1 + e^-z)   (elementwise)
+ *     P_k = A * W_down_k^T                            (M x h, fp32)
+ *
+ * and tp_partial_reduce computes Y = (((P_0 + P_1) + P_2) + ...) + P_{t-1}
+ * elementwise in fp32, always in that order (the pages note that the
+ * all-reduce's summation order changes the bits: scalablesystem.dev,
+ * "Quality, Evaluation, and Guardrails").
+ *
+ * Conventions for every entry point:
+ *   - All matrices are row-major.  Leading dimensions are in elements.
+ *   - Device pointers are HIP device addresses on the current device; the
+ *     caller owns every buffer.  The library never allocates, frees or
+ *     synchronises device memory on these paths; work is enqueued on `stream`
+ *     (a hipStream_t, NULL = the null stream) and the call returns at once.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is launched and a status other than TP_OK is
+ *     returned.  tp_last_error() then gives a message (thread-local).
+ *   - Nothing is thrown across the ABI.
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_F32 = 0,         /* IEEE binary32                                       */
+  TP_BF16 = 1,        /* bfloat16 (upper half of binary32)                   */
+  TP_FP8_E4M3FN = 2   /* OCP FP8 E4M3 (bias 7, max 448, no inf); weights only */
+} tp_dtype;
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1,  /* shapes, indices, pointers inconsistent        */
+  TP_ERR_UNSUPPORTED = 2,  /* valid but not implemented (dtype pair, shape
+                              alignment, pointer alignment)                 */
+  TP_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required    */
+  TP_ERR_HIP = 4           /* a HIP runtime call failed (launch, device)    */
+} tp_status;
+
+/*
+ * Workspace bytes tp_mlp_shard_forward needs for these arguments (0 if the
+ * arguments are invalid).  The workspace holds the intermediate activation A
+ * (M x I_s, in the activation dtype) plus alignment padding.
+ */
+size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
+                              int32_t act_dtype, int32_t w_dtype);
+
+/*
+ * Rank k's partial P_k (definition above).
+ *
+ *   M        tokens (rows of X and P), M >= 1.
+ *   h        hidden size, h >= 1.
+ *   I_full   full (unsharded) intermediate size; I_full % t == 0.
+ *   t, k     TP degree (1..64) and this rank's index (0..t-1).  k selects no
+ *            data: the caller passes rank k's shard pointers.  It is
+ *            validated, and the result for given shard bytes does not depend
+ *            on it.
+ *   act_dtype  dtype of X and of the intermediate A: TP_BF16 or TP_F32.
+ *   w_dtype    dtype of the three weight shards.  Supported pairs:
+ *              (TP_BF16, TP_BF16), (TP_BF16, TP_FP8_E4M3FN), (TP_F32, TP_F32).
+ *   x        M x h, leading dimension ldx >= h.
+ *   w_gate, w_up   I_s x h each ((out, in) layout: row j is intermediate
+ *            channel k*I_s + j of the full matrix), leading dimension
+ *            ldw_gu >= h.  A caller holding the full matrix passes the
+ *            pointer to row k*I_s.
+ *   w_down   h x I_s ((out, in) layout, the rank's column block of the full
+ *            W_down), leading dimension ldw_down >= I_s.  A caller holding
+ *            the full h x I_full matrix passes the pointer to column k*I_s
+ *            and ldw_down = I_full.
+ *   s_gate, s_up, s_down   fp32 per-output-channel scales, required for
+ *            TP_FP8_E4M3FN weights (lengths I_s, I_s, h; the dequantised
+ *            weight is code value * scale of its row) and must be NULL
+ *            otherwise.
+ *   partial  M x h fp32 output, leading dimension ldp >= h; overwritten.
+ *            Must not overlap any input or the workspace.
+ *   workspace, workspace_bytes   device scratch of at least
+ *            tp_mlp_workspace_bytes(...) bytes, 256-byte aligned; its
+ *            contents on entry are ignored.  Concurrent calls must not share
+ *            a workspace.
+ *   stream   hipStream_t or NULL.
+ *
+ * Requirements beyond validity (else TP_ERR_UNSUPPORTED): with bf16
+ * activations (bf16 or fp8 weights) h % 64 == 0 and I_s % 64 == 0, all tensor
+ * pointers 16-byte aligned and every row 16-byte aligned (leading dimension
+ * times element size a multiple of 16 bytes), scales 4-byte aligned; with
+ * fp32 activations and weights any h and I_s, 4-byte alignment.  The
+ * workspace is 256-byte aligned in both cases.
+ *
+ * Numerics: fp32 accumulation; SiLU and the gate/up product in fp32; A is
+ * rounded to the activation dtype (bf16, round-to-nearest-even) before the
+ * down projection.  Results are deterministic (no atomics in the sums).
+ */
+tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full,
+                               int32_t t, int32_t k,
+                               int32_t act_dtype, int32_t w_dtype,
+                               const void* x, int64_t ldx,
+                               const void* w_gate, const void* w_up, int64_t ldw_gu,
+                               const void* w_down, int64_t ldw_down,
+                               const float* s_gate, const float* s_up,
+                               const float* s_down,
+                               float* partial, int64_t ldp,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * out[i] = (((partials[0][i] + partials[1][i]) + partials[2][i]) + ...)
+ *          + partials[t-1][i]   for 0 <= i < n, fp32 round-to-nearest-even,
+ * no fused operations and no flush of subnormals: bit-exact against that
+ * left fold.  This is the sum the all-reduce after the row-parallel
+ * projection computes, run locally over t buffers on one device.
+ *
+ *   n          elements per buffer (n >= 0; n == 0 is a no-op that reads no
+ *              pointer, so any of them may then be NULL).
+ *   t          number of partials, 1..64.
+ *   partials   HOST array of t device pointers, each 16-byte aligned (the
+ *              array itself is read during the call only).
+ *   out        n fp32, 16-byte aligned.  May be equal to partials[0] (in
+ *              place); must not otherwise overlap a partial.
+ */
+tp_status tp_partial_reduce(int64_t n, int32_t t, const float* const* partials,
+                            float* out, void* stream);
+
+/* Static text for a status code. */
+const char* tp_status_string(int32_t status);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* tp_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (for benchmarks).  While enabled, every kernel the library
+ * launches records its own start and end timestamps on the stream it runs on
+ * (HIP extended launch with a start and a stop event).  tp_profile_collect
+ * waits for those events, adds the durations per kernel kind and clears the
+ * record.  Not thread-safe; intended for a single benchmarking thread.
+ * ---------------------------------------------------------------------- */
+
+/* Number of kernel kinds (indices 0 .. n-1 for the calls below). */
+int32_t tp_kernel_kind_count(void);
+
+/* Static name of a kernel kind (NULL if out of range). */
+const char* tp_kernel_kind_name(int32_t kind);
+
+/* Turn per-kernel timing on (1) or off (0). */
+tp_status tp_profile_enable(int32_t on);
+
+/*
+ * Synchronise the recorded events and add, for each kind i < n_kinds,
+ * the summed duration in milliseconds to total_ms[i] and the number of
+ * launches to counts[i].  Clears the record.  Both arrays are host memory.
+ */
+tp_status tp_profile_collect(double* total_ms, int64_t* counts, int32_t n_kinds);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

@@ -1,0 +1,167 @@
+"""MI355X-native tensor-parallel MLP shard (Python binding of libtp_mlp.so).
+
+One TP rank's share of a Llama-style MLP under the Megatron split and the
+local fixed-order sum of the ranks' partials.  The functions below only
+marshal torch tensors (device memory) and the current HIP stream into the C
+ABI declared in ``include/tp_mlp.h``; the computation is entirely in the
+library's HIP kernels.
+
+    P_k = (SiLU(X W_gate_k^T) * (X W_up_k^T)) W_down_k^T      (shard_forward)
+    Y   = (((P_0 + P_1) + P_2) + ...) + P_{t-1}              (partial_reduce)
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, EXPORTED_SYMBOLS,  # noqa: F401
+                   LIB_PATH, load)
+
+__all__ = ["shard_forward", "partial_reduce", "workspace_bytes", "profile_enable",
+           "profile_collect", "kernel_kinds", "TPError", "load"]
+
+
+def _act_code(dt):
+    if dt == torch.bfloat16:
+        return TP_BF16
+    if dt == torch.float32:
+        return TP_F32
+    raise TypeError("activations must be bfloat16 or float32, got %s" % dt)
+
+
+def _w_code(dt):
+    if dt == torch.bfloat16:
+        return TP_BF16
+    if dt == torch.float32:
+        return TP_F32
+    if dt in (torch.float8_e4m3fn, torch.uint8):
+        return TP_FP8_E4M3FN
+    raise TypeError("weights must be bfloat16, float32 or float8_e4m3fn (uint8 codes), got %s" % dt)
+
+
+def _check_matrix(name, t, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("%s must be a 2-D tensor with unit stride along its rows" % name)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream_of(device, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def workspace_bytes(M, h, I_full, t, act_dtype=torch.bfloat16, w_dtype=torch.bfloat16):
+    """Bytes of device workspace ``shard_forward`` needs (0 for invalid arguments)."""
+    return int(_lib.load().tp_mlp_workspace_bytes(int(M), int(h), int(I_full), int(t),
+                                                  _act_code(act_dtype), _w_code(w_dtype)))
+
+
+def alloc_workspace(nbytes, device):
+    """A 256-byte aligned uint8 view of at least ``nbytes`` device bytes."""
+    raw = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
+    off = (-raw.data_ptr()) % 256
+    return raw[off:off + int(nbytes)]
+
+
+def shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,
+                  partial=None, workspace=None, stream=None):
+    """Rank k's fp32 partial P_k (M x h) of the TP-MLP; see ``include/tp_mlp.h``.
+
+    x: (M, h) bf16 or fp32.  w_gate, w_up: (I_s, h); w_down: (h, I_s), in the
+    (out, in) layout, bf16 / fp32 / float8_e4m3fn (or uint8 codes).  For fp8
+    weights s_gate, s_up (I_s) and s_down (h) are the fp32 per-row scales.
+    ``partial`` (M, h) fp32 and ``workspace`` (uint8, >= workspace_bytes) may be
+    passed to avoid allocation.  Work is enqueued on ``stream`` (default: the
+    current stream) and the call returns without waiting.
+    """
+    device = x.device
+    for name, m in (("x", x), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_matrix(name, m, device)
+    M, h = x.shape
+    I_s = w_gate.shape[0]
+    I_full = I_s * int(t)
+    act, wc = _act_code(x.dtype), _w_code(w_gate.dtype)
+    if _w_code(w_up.dtype) != wc or _w_code(w_down.dtype) != wc:
+        raise TypeError("w_gate, w_up and w_down must share a dtype")
+    if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
+        raise ValueError("shard shapes must be w_gate/w_up (I_s, h) and w_down (h, I_s); got %s %s %s"
+                         % (tuple(w_gate.shape), tuple(w_up.shape), tuple(w_down.shape)))
+    scales = (s_gate, s_up, s_down)
+    for s in scales:
+        if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
+            raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+    if partial is None:
+        partial = torch.empty((M, h), dtype=torch.float32, device=device)
+    else:
+        _check_matrix("partial", partial, device)
+        if partial.dtype != torch.float32 or tuple(partial.shape) != (M, h):
+            raise ValueError("partial must be float32 of shape (%d, %d)" % (M, h))
+    if w_gate.stride(0) != w_up.stride(0):
+        raise ValueError("w_gate and w_up must share a leading dimension")
+    lib = _lib.load()
+    need = int(lib.tp_mlp_workspace_bytes(M, h, I_full, int(t), act, wc))
+    if workspace is None:
+        workspace = alloc_workspace(max(need, 1), device)
+    elif workspace.device != device:
+        raise ValueError("workspace must be on %s" % device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _lib.check(lib.tp_mlp_shard_forward(
+        M, h, I_full, int(t), int(k), act, wc,
+        _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+        _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
+        _ptr(partial), partial.stride(0), _ptr(workspace), ws_bytes, _stream_of(device, stream)))
+    return partial
+
+
+def partial_reduce(partials, out=None, stream=None):
+    """out = (((P_0 + P_1) + P_2) + ...) elementwise in fp32, fixed order.
+
+    ``partials``: sequence of t same-shaped contiguous float32 device tensors.
+    ``out`` may be ``partials[0]`` (in place); default: a new tensor.
+    """
+    if len(partials) < 1:
+        raise ValueError("need at least one partial")
+    p0 = partials[0]
+    device = p0.device
+    for i, p in enumerate(partials):
+        if p.dtype != torch.float32 or p.device != device or not p.is_contiguous() or p.shape != p0.shape:
+            raise ValueError("partials[%d] must be a contiguous float32 tensor shaped like partials[0]" % i)
+    if out is None:
+        out = torch.empty_like(p0)
+    elif out.dtype != torch.float32 or out.device != device or not out.is_contiguous() or out.shape != p0.shape:
+        raise ValueError("out must be a contiguous float32 tensor shaped like the partials")
+    arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
+    lib = _lib.load()
+    _lib.check(lib.tp_partial_reduce(p0.numel(), len(partials), arr, _ptr(out), _stream_of(device, stream)))
+    return out
+
+
+def kernel_kinds():
+    lib = _lib.load()
+    return [lib.tp_kernel_kind_name(i).decode() for i in range(lib.tp_kernel_kind_count())]
+
+
+def profile_enable(on=True):
+    _lib.check(_lib.load().tp_profile_enable(1 if on else 0))
+
+
+def profile_collect():
+    """{kernel kind: (total milliseconds, launches)} since the last collect."""
+    lib = _lib.load()
+    n = lib.tp_kernel_kind_count()
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int64 * n)()
+    _lib.check(lib.tp_profile_collect(ms, cnt, n))
+    names = kernel_kinds()
+    return {names[i]: (ms[i], cnt[i]) for i in range(n) if cnt[i]}

@@ -1,0 +1,298 @@
+// C ABI of the TP-MLP shard library: argument validation, dispatch, status
+// strings and the kernel timing record.  The operation and the calling
+// conventions are documented in include/tp_mlp.h.
+//
+// Validation follows the pages' statement of the layers: out_features and
+// in_features must divide by the group size (ColumnParallelLinear /
+// RowParallelLinear in "The Tensor-Parallel Shard Group", scalablesystem.dev),
+// a rank holds only its own shard, and its forward returns a partial that the
+// all-reduce sums.  Everything is checked on the host before any HIP call.
+#include "tp_mlp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "common.h"
+#include "internal.h"
+
+#define TP_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "no error";
+
+tp_status fail(tp_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+tp_status from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TP_OK;
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int elem_bytes(int32_t dt) {
+  switch (dt) {
+    case TP_F32: return 4;
+    case TP_BF16: return 2;
+    case TP_FP8_E4M3FN: return 1;
+    default: return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte extent of a rows x cols matrix with leading dimension ld.
+struct Extent {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Extent extent(const void* p, int64_t rows, int64_t cols, int64_t ld, int eb) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  const uintptr_t len = (uintptr_t)(((rows - 1) * ld + cols) * eb);
+  return Extent{lo, lo + len};
+}
+
+bool overlap(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// Shape checks shared by the workspace query and the forward.
+tp_status check_shapes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k, int32_t act,
+                       int32_t w) {
+  if (M < 1 || h < 1 || I_full < 1)
+    return fail(TP_ERR_INVALID_ARG, "M, h and I_full must be >= 1 (got %lld, %lld, %lld)",
+                (long long)M, (long long)h, (long long)I_full);
+  if (t < 1 || t > tpmlp::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "t must be in [1, %d] (got %d)", tpmlp::kMaxPartials, t);
+  if (k < 0 || k >= t) return fail(TP_ERR_INVALID_ARG, "k must be in [0, t) (got k=%d, t=%d)", k, t);
+  if (I_full % t != 0)
+    return fail(TP_ERR_INVALID_ARG, "I_full (%lld) must be divisible by t (%d)", (long long)I_full, t);
+  if (elem_bytes(act) == 0 || elem_bytes(w) == 0)
+    return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act, w);
+  if (act == TP_FP8_E4M3FN) return fail(TP_ERR_UNSUPPORTED, "fp8 activations are not supported");
+  const bool ok_pair = (act == TP_BF16 && (w == TP_BF16 || w == TP_FP8_E4M3FN)) ||
+                       (act == TP_F32 && w == TP_F32);
+  if (!ok_pair) return fail(TP_ERR_UNSUPPORTED, "unsupported dtype pair (act=%d, w=%d)", act, w);
+  const int64_t I_s = I_full / t;
+  if (M > kMaxDim || h > kMaxDim || I_s > kMaxDim)
+    return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
+  if (act == TP_BF16 && (h % 64 != 0 || I_s % 64 != 0))
+    return fail(TP_ERR_UNSUPPORTED, "bf16/fp8 paths need h %% 64 == 0 and I_s %% 64 == 0 (h=%lld, I_s=%lld)",
+                (long long)h, (long long)I_s);
+  return TP_OK;
+}
+
+int64_t workspace_need(int64_t M, int64_t I_s, int32_t act) {
+  return round_up(M * I_s * elem_bytes(act), 256);
+}
+
+// ------------------------------------------------------------------ timing
+
+struct ProfRec {
+  hipEvent_t start, stop;
+  int kind;
+};
+
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_pool;
+size_t g_prof_used = 0;
+
+const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
+    "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
+    "partial_reduce", "gateup_f32", "down_f32"};
+
+}  // namespace
+
+namespace tpmlp {
+
+void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop) {
+  *start = nullptr;
+  *stop = nullptr;
+  if (!g_prof_on) return;
+  if (g_prof_used == g_prof_pool.size()) {
+    ProfRec r{};
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+      (void)hipEventDestroy(r.start);
+      return;
+    }
+    g_prof_pool.push_back(r);
+  }
+  ProfRec& r = g_prof_pool[g_prof_used++];
+  r.kind = kind;
+  *start = r.start;
+  *stop = r.stop;
+}
+
+}  // namespace tpmlp
+
+TP_API size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
+                                     int32_t act_dtype, int32_t w_dtype) {
+  if (check_shapes(M, h, I_full, t, 0, act_dtype, w_dtype) != TP_OK) return 0;
+  return (size_t)workspace_need(M, I_full / t, act_dtype);
+}
+
+TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                      int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
+                                      const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                      const void* w_down, int64_t ldw_down, const float* s_gate,
+                                      const float* s_up, const float* s_down, float* partial,
+                                      int64_t ldp, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  tp_status st = check_shapes(M, h, I_full, t, k, act_dtype, w_dtype);
+  if (st != TP_OK) return st;
+  const int64_t I_s = I_full / t;
+  if (!x || !w_gate || !w_up || !w_down || !partial)
+    return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  const bool fp8 = w_dtype == TP_FP8_E4M3FN;
+  if (fp8 && (!s_gate || !s_up || !s_down))
+    return fail(TP_ERR_INVALID_ARG, "fp8 weights need s_gate, s_up and s_down");
+  if (!fp8 && (s_gate || s_up || s_down))
+    return fail(TP_ERR_INVALID_ARG, "scales are only accepted with fp8 weights");
+  if (ldx < h || ldw_gu < h || ldw_down < I_s || ldp < h)
+    return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length "
+                "(ldx=%lld ldw_gu=%lld ldw_down=%lld ldp=%lld)", (long long)ldx, (long long)ldw_gu,
+                (long long)ldw_down, (long long)ldp);
+  const int64_t need = workspace_need(M, I_s, act_dtype);
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
+                (unsigned long long)workspace_bytes);
+  const int ea = elem_bytes(act_dtype), ew = elem_bytes(w_dtype);
+  if (act_dtype == TP_BF16) {
+    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
+        !aligned(partial, 16))
+      return fail(TP_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+    if ((ldx * ea) % 16 || (ldw_gu * ew) % 16 || (ldw_down * ew) % 16 || (ldp * 4) % 16)
+      return fail(TP_ERR_UNSUPPORTED, "rows must start 16-byte aligned (leading dimensions)");
+    if (fp8 && (!aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4)))
+      return fail(TP_ERR_UNSUPPORTED, "scale pointers must be 4-byte aligned");
+  } else {
+    if (!aligned(x, 4) || !aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) ||
+        !aligned(partial, 4))
+      return fail(TP_ERR_UNSUPPORTED, "fp32 pointers must be 4-byte aligned");
+  }
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+
+  const Extent ep = extent(partial, M, h, ldp, 4);
+  const Extent ins[5] = {extent(x, M, h, ldx, ea), extent(w_gate, I_s, h, ldw_gu, ew),
+                         extent(w_up, I_s, h, ldw_gu, ew), extent(w_down, h, I_s, ldw_down, ew),
+                         Extent{reinterpret_cast<uintptr_t>(workspace),
+                                reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need}};
+  for (const Extent& e : ins)
+    if (overlap(ep, e)) return fail(TP_ERR_INVALID_ARG, "partial overlaps an input or the workspace");
+  const Extent ew_ = ins[4];
+  for (int i = 0; i < 4; ++i)
+    if (overlap(ew_, ins[i])) return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input");
+
+  tpmlp::ShardArgs a;
+  a.M = (int)M;
+  a.h = (int)h;
+  a.I_s = (int)I_s;
+  a.x = x;
+  a.ldx = ldx;
+  a.wg = w_gate;
+  a.wu = w_up;
+  a.ldw_gu = ldw_gu;
+  a.wd = w_down;
+  a.ldw_down = ldw_down;
+  a.sg = s_gate;
+  a.su = s_up;
+  a.sd = s_down;
+  a.p = partial;
+  a.ldp = ldp;
+  a.a = workspace;
+  a.lda = I_s;
+  a.fp8 = fp8;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (act_dtype == TP_F32)
+    e = tpmlp::launch_forward_f32(a, s);
+  else if (M <= tpmlp::kDecodeMaxM)
+    e = tpmlp::launch_forward_decode(a, s);
+  else
+    e = tpmlp::launch_forward_prefill(a, s);
+  return from_hip(e, "kernel launch");
+}
+
+TP_API tp_status tp_partial_reduce(int64_t n, int32_t t, const float* const* partials, float* out,
+                                   void* stream) {
+  if (n < 0) return fail(TP_ERR_INVALID_ARG, "n must be >= 0");
+  if (t < 1 || t > tpmlp::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "t must be in [1, %d] (got %d)", tpmlp::kMaxPartials, t);
+  if (n == 0) return TP_OK;  // nothing is read or written; pointers may be null
+  if (!partials || !out) return fail(TP_ERR_INVALID_ARG, "null pointer");
+  if (n > ((int64_t)1 << 40)) return fail(TP_ERR_UNSUPPORTED, "n above 2^40");
+  tpmlp::PartialPtrs ptrs{};
+  const Extent eo = extent(out, 1, n > 0 ? n : 1, n, 4);
+  for (int j = 0; j < t; ++j) {
+    if (!partials[j]) return fail(TP_ERR_INVALID_ARG, "partials[%d] is null", j);
+    if (!aligned(partials[j], 16)) return fail(TP_ERR_UNSUPPORTED, "partials[%d] not 16-byte aligned", j);
+    const Extent ej = extent(partials[j], 1, n > 0 ? n : 1, n, 4);
+    const bool in_place = (j == 0 && partials[0] == out);
+    if (!in_place && overlap(eo, ej))
+      return fail(TP_ERR_INVALID_ARG, "out overlaps partials[%d] (only out == partials[0] is allowed)", j);
+    ptrs.p[j] = partials[j];
+  }
+  if (!aligned(out, 16)) return fail(TP_ERR_UNSUPPORTED, "out not 16-byte aligned");
+  return from_hip(tpmlp::launch_partial_reduce(ptrs, t, out, n, reinterpret_cast<hipStream_t>(stream)),
+                  "kernel launch");
+}
+
+TP_API const char* tp_status_string(int32_t status) {
+  switch (status) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID_ARG: return "TP_ERR_INVALID_ARG: invalid argument";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED: valid but unsupported argument";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_HIP: return "TP_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+TP_API const char* tp_last_error(void) { return g_last_error; }
+
+TP_API int32_t tp_kernel_kind_count(void) { return tpmlp::K_NUM_KINDS; }
+
+TP_API const char* tp_kernel_kind_name(int32_t kind) {
+  if (kind < 0 || kind >= tpmlp::K_NUM_KINDS) return nullptr;
+  return kKindNames[kind];
+}
+
+TP_API tp_status tp_profile_enable(int32_t on) {
+  g_prof_on = on != 0;
+  return TP_OK;
+}
+
+TP_API tp_status tp_profile_collect(double* total_ms, int64_t* counts, int32_t n_kinds) {
+  if (!total_ms || !counts || n_kinds < 0) return fail(TP_ERR_INVALID_ARG, "bad output arrays");
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    ProfRec& r = g_prof_pool[i];
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) {
+      g_prof_used = 0;
+      return from_hip(e, "hipEventSynchronize");
+    }
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) {
+      g_prof_used = 0;
+      return from_hip(e, "hipEventElapsedTime");
+    }
+    if (r.kind < n_kinds) {
+      total_ms[r.kind] += ms;
+      counts[r.kind] += 1;
+    }
+  }
+  g_prof_used = 0;
+  return TP_OK;
+}

@@ -1,0 +1,84 @@
+// Shared device helpers and the launch wrapper for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Kernel kinds for the timing record (kept in sync with kKindNames in abi.cpp).
+enum KernelKind : int {
+  K_GATEUP_DECODE = 0,
+  K_DOWN_DECODE = 1,
+  K_GATEUP_PREFILL = 2,
+  K_DOWN_PREFILL = 3,
+  K_PARTIAL_REDUCE = 4,
+  K_GATEUP_F32 = 5,
+  K_DOWN_F32 = 6,
+  K_NUM_KINDS = 7
+};
+
+// Implemented in abi.cpp: returns the start/stop events to attach to the next
+// launch of `kind` when timing is on, or null events.
+void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop);
+
+// Every kernel of the library is launched through here so that, when timing
+// is on, the dispatch itself carries the start and stop timestamps (no extra
+// marker packets in the stream).
+template <typename... Params, typename... Args>
+inline hipError_t launch(int kind, void (*kernel)(Params...), dim3 grid, dim3 block,
+                         uint32_t lds_bytes, hipStream_t stream, Args... args) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  profile_events_for_launch(kind, &e0, &e1);
+  hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, e0, e1, 0,
+                        static_cast<Params>(args)...);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- numerics
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// SiLU(z) = z / (1 + e^-z).  For z below about -88 the exponential is +inf and
+// the quotient is -0, the limit of the function.
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// Eight OCP e4m3fn codes (two dwords) -> eight bf16 (exact: every e4m3 value
+// is a bf16 value).  Hardware conversion, unit scale.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  bf16x8 r;
+  r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+  r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16x16x32 bf16 MFMA: D(16x16) += A(16x32) * B(32x16).  Lane l supplies row
+// (l % 16) of A and column (l % 16) of B, each with the eight k values of
+// group (l / 16); it receives D rows 4*(l/16) .. 4*(l/16)+3 of column l % 16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace tpmlp

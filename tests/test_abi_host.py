@@ -1,0 +1,148 @@
+"""Host-only checks of the C ABI: the library loads, exports every declared
+symbol, and rejects invalid arguments before enqueuing anything.
+
+Every forward / reduce call in this file is invalid by construction (the
+pointer values are never dereferenced because validation fails first), so it
+is safe on a machine with or without a GPU.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import tensor_transformer_mlp_tp_amd as tp
+from tensor_transformer_mlp_tp_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    txt = open(os.path.join(ROOT, "include", "tp_mlp.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_expected_api():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTED_SYMBOLS), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # and the dynamic symbol table has nothing else public from us
+    out = os.popen("nm -D --defined-only %s" % _lib.LIB_PATH).read()
+    ours = sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\b", out)))
+    assert ours == declared_functions()
+
+
+def test_status_strings_and_kinds():
+    lib = _lib.load()
+    for s in range(5):
+        assert lib.tp_status_string(s).startswith(b"TP_")
+    assert lib.tp_status_string(99) == b"unknown status"
+    kinds = tp.kernel_kinds()
+    assert "gateup_decode" in kinds and "partial_reduce" in kinds
+    assert lib.tp_kernel_kind_name(-1) is None
+    assert lib.tp_kernel_kind_name(len(kinds)) is None
+
+
+BF16, F32, FP8 = _lib.TP_BF16, _lib.TP_F32, _lib.TP_FP8_E4M3FN
+
+
+def test_workspace_bytes():
+    lib = _lib.load()
+    # A = M x I_s bf16, rounded up to 256 bytes
+    assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 8, BF16, BF16) == 3584 * 2
+    assert lib.tp_mlp_workspace_bytes(3, 64, 128, 2, BF16, FP8) == 512          # 3*64*2 = 384 -> 512
+    assert lib.tp_mlp_workspace_bytes(5, 64, 128, 2, BF16, BF16) == 768         # 5*64*2 = 640 -> 768
+    assert lib.tp_mlp_workspace_bytes(16, 256, 1024, 4, F32, F32) == 16 * 256 * 4
+    # invalid arguments give 0
+    assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 5, BF16, BF16) == 0       # I % t
+    assert lib.tp_mlp_workspace_bytes(0, 8192, 28672, 8, BF16, BF16) == 0
+    assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 8, F32, BF16) == 0        # unsupported pair
+    assert lib.tp_mlp_workspace_bytes(1, 100, 28672, 8, BF16, BF16) == 0        # h % 64
+
+
+P = 0x10000  # a 256-byte aligned fake address; never dereferenced (every call fails validation)
+
+
+def fwd(M=1, h=128, I=256, t=2, k=0, act=BF16, w=BF16, x=P, wg=P * 2, wu=P * 3, wd=P * 4,
+        ldx=None, ldgu=None, ldd=None, sg=None, su=None, sd=None, p=P * 8, ldp=None, ws=P * 16,
+        wsb=1 << 20):
+    lib = _lib.load()
+    I_s = I // t if t else 1
+    return lib.tp_mlp_shard_forward(M, h, I, t, k, act, w, x, ldx if ldx is not None else h,
+                                    wg, wu, ldgu if ldgu is not None else h, wd,
+                                    ldd if ldd is not None else I_s, sg, su, sd, p,
+                                    ldp if ldp is not None else h, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(I=255), _lib.TP_ERR_INVALID_ARG),                 # I_full % t != 0
+    (dict(k=2), _lib.TP_ERR_INVALID_ARG),                   # k >= t
+    (dict(k=-1), _lib.TP_ERR_INVALID_ARG),
+    (dict(t=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(t=65, I=65 * 64), _lib.TP_ERR_INVALID_ARG),
+    (dict(M=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(h=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(x=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(wd=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(p=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(act=7), _lib.TP_ERR_INVALID_ARG),
+    (dict(act=F32, w=BF16), _lib.TP_ERR_UNSUPPORTED),
+    (dict(act=FP8, w=FP8), _lib.TP_ERR_UNSUPPORTED),
+    (dict(w=FP8), _lib.TP_ERR_INVALID_ARG),                 # fp8 without scales
+    (dict(sg=P, su=P, sd=P), _lib.TP_ERR_INVALID_ARG),      # scales with bf16 weights
+    (dict(ldx=64), _lib.TP_ERR_INVALID_ARG),                # ld < row length
+    (dict(ldd=64), _lib.TP_ERR_INVALID_ARG),
+    (dict(ldp=100), _lib.TP_ERR_INVALID_ARG),
+    (dict(h=96), _lib.TP_ERR_UNSUPPORTED),                  # h % 64
+    (dict(I=2 * 96), _lib.TP_ERR_UNSUPPORTED),              # I_s % 64
+    (dict(wsb=10), _lib.TP_ERR_WORKSPACE),
+    (dict(ws=None), _lib.TP_ERR_WORKSPACE),
+    (dict(x=P + 2), _lib.TP_ERR_UNSUPPORTED),               # misaligned
+    (dict(ldx=132), _lib.TP_ERR_UNSUPPORTED),               # rows not 16-byte aligned
+    (dict(ws=P * 16 + 16), _lib.TP_ERR_UNSUPPORTED),        # workspace not 256-aligned
+    (dict(p=P * 2), _lib.TP_ERR_INVALID_ARG),               # partial aliases w_gate
+    (dict(ws=P * 8), _lib.TP_ERR_INVALID_ARG),              # workspace aliases partial
+    (dict(ws=P), _lib.TP_ERR_INVALID_ARG),                  # workspace aliases x
+])
+def test_forward_rejects(kw, status):
+    lib = _lib.load()
+    assert fwd(**kw) == status
+    assert lib.tp_last_error() not in (b"", None)
+
+
+def reduce_call(n, t, ptrs, out):
+    lib = _lib.load()
+    arr = None if ptrs is None else (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return lib.tp_partial_reduce(n, t, arr, out, None)
+
+
+@pytest.mark.parametrize("n,t,ptrs,out,status", [
+    (-1, 2, [P, P * 2], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (16, 0, [P], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (16, 65, [P] * 65, P * 4, _lib.TP_ERR_INVALID_ARG),
+    (16, 2, None, P * 4, _lib.TP_ERR_INVALID_ARG),
+    (16, 2, [P, P * 2], None, _lib.TP_ERR_INVALID_ARG),
+    (16, 2, [P, None], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (16, 2, [P + 4, P * 2], P * 4, _lib.TP_ERR_UNSUPPORTED),
+    (16, 2, [P, P * 2], P * 4 + 4, _lib.TP_ERR_UNSUPPORTED),
+    (16, 2, [P, P * 2], P * 2, _lib.TP_ERR_INVALID_ARG),        # out aliases partials[1]
+    (16, 2, [P, P * 2], P + 16, _lib.TP_ERR_INVALID_ARG),       # partial overlap with partials[0]
+])
+def test_reduce_rejects(n, t, ptrs, out, status):
+    assert reduce_call(n, t, ptrs, out) == status
+
+
+def test_reduce_empty_is_noop():
+    # n == 0 passes validation and launches nothing
+    assert reduce_call(0, 2, [P, P * 2], P * 4) == _lib.TP_OK
+    assert reduce_call(0, 1, [P], P) == _lib.TP_OK
+    assert reduce_call(0, 3, None, None) == _lib.TP_OK
+    # t is still validated
+    assert reduce_call(0, 0, None, None) == _lib.TP_ERR_INVALID_ARG

@@ -29,6 +29,8 @@ arunshar.com chapter) and the 405B hidden size (case studies of the same
 chapter).  No trained weights are involved: values are Gaussian stand-ins.
 """
 
+import concurrent.futures
+
 import numpy as np
 
 # ---------------------------------------------------------------------------
@@ -165,6 +167,14 @@ def to_storage(w32, dtype):
     raise ValueError("unknown dtype %r" % (dtype,))
 
 
+def _parallel(fn, items):
+    """Map fn over items on a few threads (numpy releases the GIL in the draws)."""
+    if len(items) <= 1:
+        return [fn(i) for i in items]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(items), 8)) as ex:
+        return list(ex.map(fn, items))
+
+
 # ---------------------------------------------------------------------------
 # tensors of a configuration
 # ---------------------------------------------------------------------------
@@ -181,9 +191,10 @@ def make_shard_weights(config_id, h, I_s, k, dtype, std_gu, std_down, weight_set
     Returns a dict with storage arrays ``w_gate``, ``w_up``, ``w_down`` and,
     for e4m3fn, the scales ``s_gate`` (I_s), ``s_up`` (I_s), ``s_down`` (h).
     """
-    g = to_storage(draw_f32(seed_of(config_id, tensor_id_gate(k), weight_set), (I_s, h), std_gu), dtype)
-    u = to_storage(draw_f32(seed_of(config_id, tensor_id_up(k), weight_set), (I_s, h), std_gu), dtype)
-    d = to_storage(draw_f32(seed_of(config_id, tensor_id_down(k), weight_set), (h, I_s), std_down), dtype)
+    jobs = [(tensor_id_gate(k), (I_s, h), std_gu), (tensor_id_up(k), (I_s, h), std_gu),
+            (tensor_id_down(k), (h, I_s), std_down)]
+    g, u, d = _parallel(lambda j: to_storage(draw_f32(seed_of(config_id, j[0], weight_set), j[1], j[2]), dtype),
+                        jobs)
     return dict(w_gate=g["data"], w_up=u["data"], w_down=d["data"],
                 s_gate=g["scale"], s_up=u["scale"], s_down=d["scale"])
 
@@ -195,8 +206,8 @@ def make_full_weights(config_id, h, I, dtype, std_gu, std_down, weight_set=0):
 
 def make_partials(config_id, t, n, weight_set=0):
     """t float32 partial buffers of n elements, each N(0, 1)."""
-    return [draw_f32(seed_of(config_id, TENSOR_PARTIAL_BASE + j, weight_set), (n,), 1.0)
-            for j in range(t)]
+    return _parallel(lambda j: draw_f32(seed_of(config_id, TENSOR_PARTIAL_BASE + j, weight_set), (n,), 1.0),
+                     list(range(t)))
 
 
 # ---------------------------------------------------------------------------
