@@ -1,0 +1,400 @@
+"""Benchmark of the TP-MLP shard library on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  The default workload is the 70B-shaped TP=8 rank at
+decode: one step runs, for each of M = 1, 8 and 64 tokens, the rank's forward
+(gate/up with fused SwiGLU, down to an fp32 partial) and the 8-way fp32
+partial reduce over that partial and seven resident stand-ins.  Inputs are
+seeded synthetic tensors (``workloads``), resident in HBM before timing.
+Successive steps walk through several distinct weight sets (like successive
+layers), so the weights come from HBM and not from the 256 MB last-level
+cache.  ``value`` is algorithmic bytes per second over the timed steps.
+
+Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
+(TP=4 fp8 weights: decode M=32 and prefill M=2048), prefill405b (8192 tokens),
+reduce70b / reduce405b (the 8-way reduces alone).
+
+The ``roofline`` object is for the step's dominant kernel: algorithmic bytes
+(or FLOP) of its launches divided by their summed durations, taken from HIP
+events that the library attaches to each of its own kernel dispatches during
+the timed steps.  ``cpu_baseline`` times the float64 CPU oracle on a bounded
+sample of the same workload (rank 0, one GPU only).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "decode-shard HBM GB/s (% peak) & prefill-shard TFLOP/s (% MFMA peak)"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+N_WEIGHT_SETS = 8
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode70b",
+                    choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def to_dev(arr, dt):
+    import torch
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
+    if dt == "e4m3fn":
+        return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).cuda()
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
+
+
+def device_weights(cfg_id, h, I_s, w, std_gu, std_down, n_sets):
+    import torch
+    sets = []
+    for s in range(n_sets):
+        ws = workloads.make_shard_weights(cfg_id, h, I_s, 0, w, std_gu, std_down, weight_set=s)
+        d = dict(w_gate=to_dev(ws["w_gate"], w), w_up=to_dev(ws["w_up"], w), w_down=to_dev(ws["w_down"], w))
+        for k in ("s_gate", "s_up", "s_down"):
+            d[k] = None if ws[k] is None else torch.from_numpy(ws[k]).cuda()
+        sets.append(d)
+        if s == 0:
+            host0 = ws
+    return sets, host0
+
+
+class Phase:
+    """One forward (+ optional reduce) of a rank at M tokens, buffers preallocated."""
+
+    def __init__(self, tp, cfg_id, M, h, I_s, t, act, w, with_reduce):
+        import torch
+        self.tp, self.M, self.h, self.I_s, self.t, self.w = tp, M, h, I_s, t, w
+        self.x_host = workloads.make_x(cfg_id, M, h, act)
+        self.x = to_dev(self.x_host, act)
+        self.partial = torch.empty((M, h), dtype=torch.float32, device="cuda")
+        nbytes = tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16,
+                                    torch.float8_e4m3fn if w == "e4m3fn" else torch.bfloat16)
+        self.ws = tp.alloc_workspace(nbytes, "cuda")
+        self.with_reduce = with_reduce
+        if with_reduce:
+            others = workloads.make_partials(cfg_id, t - 1, M * h, weight_set=M)
+            self.others = [torch.from_numpy(o).cuda() for o in others]
+            self.reduced = torch.empty(M * h, dtype=torch.float32, device="cuda")
+
+        self.calls = {}
+
+    def run(self, wset):
+        # arguments are marshalled once per weight set; the loop only re-issues the C calls
+        key = id(wset)
+        if key not in self.calls:
+            fwd = self.tp.prepare_shard_forward(self.x, wset["w_gate"], wset["w_up"], wset["w_down"], t=self.t,
+                                                k=0, s_gate=wset["s_gate"], s_up=wset["s_up"],
+                                                s_down=wset["s_down"], partial=self.partial, workspace=self.ws)
+            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others, out=self.reduced) \
+                if self.with_reduce else None
+            self.calls[key] = (fwd, red)
+        fwd, red = self.calls[key]
+        fwd()
+        if red is not None:
+            red()
+
+    def bytes(self, act="bf16"):
+        b = workloads.forward_bytes(self.M, self.h, self.I_s, act, self.w)
+        if self.with_reduce:
+            b += workloads.reduce_bytes(self.M * self.h, self.t)
+        return b
+
+    def flops(self):
+        return workloads.forward_flops(self.M, self.h, self.I_s)
+
+
+# ----------------------------------------------------------------------------- timing
+
+def timed(tp, step_fn, steps, warmup):
+    import torch
+    for i in range(warmup):
+        step_fn(i)
+    torch.cuda.synchronize()
+    tp.profile_collect()          # drop anything recorded before the timed region
+    tp.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step_fn(warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    tp.profile_enable(False)
+    prof = tp.profile_collect()
+    return elapsed, prof
+
+
+def cpu_info():
+    info = {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+    blas_threads = None
+    try:
+        import threadpoolctl
+        for p in threadpoolctl.threadpool_info():
+            if p.get("user_api") == "blas":
+                blas_threads = max(blas_threads or 0, int(p.get("num_threads", 0)))
+                info["blas"] = "%s %s" % (p.get("internal_api"), p.get("version"))
+    except Exception:
+        pass
+    info["blas_threads"] = blas_threads
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return info
+
+
+def cpu_baseline(fn_once, unit_amount, unit, sample, min_seconds=10.0, max_reps=1000):
+    """Time the oracle: repeat fn_once until min_seconds have passed."""
+    info = cpu_info()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn_once()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    cores = info.get("blas_threads") or info["affinity"]
+    return {"value": unit_amount * reps / el, "unit": unit, "cores": cores, "kind": "oracle",
+            "sample": "%s; %d repetitions in %.1f s" % (sample, reps, el), "host": info}
+
+
+# ----------------------------------------------------------------------------- workloads
+
+def bench_decode70b(tp, args):
+    import oracle
+    c = workloads.CONFIGS[2]
+    h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
+    log("generating %d weight sets of the 70B TP=8 shard" % args.weight_sets)
+    sets, host0 = device_weights(2, h, I_s, "bf16", c["std_gu"], c["std_down"], args.weight_sets)
+    phases = [Phase(tp, 2, M, h, I_s, t, "bf16", "bf16", True) for M in c["M"]]
+
+    def step(i):
+        wset = sets[i % len(sets)]
+        for ph in phases:
+            ph.run(wset)
+
+    steps, warmup = args.steps or 400, args.warmup if args.warmup is not None else 40
+    elapsed, prof = timed(tp, step, steps, warmup)
+    step_bytes = sum(ph.bytes() for ph in phases)
+    value = step_bytes * steps / elapsed / 1e9
+    gu_bytes = steps * sum(workloads.gateup_bytes(ph.M, h, I_s) for ph in phases)
+    dn_bytes = steps * sum(workloads.down_bytes(ph.M, h, I_s) for ph in phases)
+    red_bytes = steps * sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)
+    kern = {}
+    for name, b in (("gateup_decode", gu_bytes), ("down_decode", dn_bytes), ("partial_reduce", red_bytes)):
+        ms, cnt = prof.get(name, (0.0, 0))
+        kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
+                      "GBps": b / (ms * 1e-3) / 1e9 if ms > 0 else None}
+    ms, cnt = prof["gateup_decode"]
+    achieved = gu_bytes / (ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gateup_decode",
+            "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases}}
+    fwd_time_ms = sum(prof[k][0] for k in ("gateup_decode", "down_decode")) / steps
+    fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
+    # parity sample at full size, outside the timed region: the last step used set (warmup+steps-1)
+    parity = None
+    if not args.no_cpu_baseline:
+        ph = phases[0]
+        step(0)  # set 0
+        import torch
+        torch.cuda.synchronize()
+        ref = oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
+                                               host0["w_down"], "bf16")
+        parity = oracle.rms_normalised_max_error(ph.partial.cpu().numpy(), ref)
+
+    out = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 5), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic",
+               config={"workload": "70B-shaped TP=8 rank decode (h=8192, I_s=3584, bf16 weights) at "
+                                   "M=1, 8 and 64 tokens, each forward followed by the 8-way fp32 "
+                                   "partial reduce",
+                       "M": list(c["M"]), "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
+               roofline=roof,
+               frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
+               forward_only={"GBps": round(fwd_bytes / (fwd_time_ms * 1e-3) / 1e9, 1),
+                             "us_per_step": round(fwd_time_ms * 1e3, 2)},
+               kernels=kern, parity_err_M1=parity)
+    if not args.no_cpu_baseline:
+        host_parts = [np.zeros(ph.M * h, np.float32) for ph in phases]
+
+        def once():
+            for ph, hp in zip(phases, host_parts):
+                p = oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
+                                                     host0["w_down"], "bf16")
+                oracle.fold_fp32([p.astype(np.float32).reshape(-1)] + [hp] * (t - 1))
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(once, step_bytes / 1e9, "GB/s",
+                                           "one full step (M=1, 8, 64 rank partials from the bf16 "
+                                           "weight bytes + 8-way fp32 folds), repeated >= 10 s")
+    return out
+
+
+def bench_prefill(tp, args, cfg_id, M, label):
+    import oracle
+    import torch
+    c = workloads.CONFIGS[cfg_id]
+    h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
+    n_sets = 1   # compute-bound: weight reuse across tokens dwarfs any cache effect
+    sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
+    ph = Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, c["reduce_n"] is not None)
+
+    def step(i):
+        ph.run(sets[0])
+
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    elapsed, prof = timed(tp, step, steps, warmup)
+    flops = ph.flops()
+    value = flops * steps / elapsed / 1e12
+    gu_ms, gu_n = prof["gateup_prefill"]
+    dn_ms, dn_n = prof["down_prefill"]
+    gu_tf = (4 * M * h * I_s) * gu_n / (gu_ms * 1e-3) / 1e12
+    dn_tf = (2 * M * h * I_s) * dn_n / (dn_ms * 1e-3) / 1e12
+    fwd_tf = flops * steps / ((gu_ms + dn_ms) * 1e-3) / 1e12
+    kern = {"gateup_prefill": {"launches": gu_n, "avg_us": 1e3 * gu_ms / gu_n, "TFLOPs": round(gu_tf, 1)},
+            "down_prefill": {"launches": dn_n, "avg_us": 1e3 * dn_ms / dn_n, "TFLOPs": round(dn_tf, 1)}}
+    if "partial_reduce" in prof:
+        ms, n = prof["partial_reduce"]
+        kern["partial_reduce"] = {"launches": n, "avg_us": 1e3 * ms / n,
+                                  "GBps": round(workloads.reduce_bytes(M * h, t) * n / (ms * 1e-3) / 1e9, 1)}
+    roof = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gateup_prefill",
+            "per_launch_flop": 4 * M * h * I_s}
+    out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic",
+               config={"workload": label, "M": M, "h": h, "I_s": I_s, "t": t, "weights": w,
+                       "step_includes_reduce": ph.with_reduce},
+               roofline=roof, forward_only_TFLOPs=round(fwd_tf, 1),
+               forward_frac_of_bf16_peak=round(fwd_tf / BF16_PEAK_TFLOPS, 4), kernels=kern)
+    if not args.no_cpu_baseline:
+        rows = np.arange(0, M, max(1, M // 16))[:16]
+
+        def once():
+            oracle.rank_partial_from_storage(ph.x_host[rows], "bf16", host0["w_gate"], host0["w_up"],
+                                             host0["w_down"], w, host0["s_gate"], host0["s_up"], host0["s_down"])
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(once, workloads.forward_flops(len(rows), h, I_s) / 1e12, "TFLOP/s",
+                                           "rank partial for %d of the %d token rows (decoding the weight "
+                                           "bytes each time), repeated >= 10 s" % (len(rows), M))
+    return out
+
+
+def bench_fp8(tp, args):
+    import torch
+    c = workloads.CONFIGS[4]
+    h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
+    sets, host0 = device_weights(4, h, I_s, "e4m3fn", c["std_gu"], c["std_down"], args.weight_sets)
+    dec = Phase(tp, 4, 32, h, I_s, t, "bf16", "e4m3fn", False)
+    pre = Phase(tp, 4, 2048, h, I_s, t, "bf16", "e4m3fn", False)
+    steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
+    el_d, prof_d = timed(tp, lambda i: dec.run(sets[i % len(sets)]), steps, warmup)
+    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), max(10, steps // 10), 3)
+    dec_bytes = dec.bytes()
+    dec_gbs = dec_bytes * steps / el_d / 1e9
+    pre_tf = pre.flops() * max(10, steps // 10) / el_p / 1e12
+    gu_ms, gu_n = prof_d["gateup_decode"]
+    gu_gbs = workloads.gateup_bytes(32, h, I_s, "bf16", "e4m3fn") * gu_n / (gu_ms * 1e-3) / 1e9
+    pgu_ms, pgu_n = prof_p["gateup_prefill"]
+    pgu_tf = 4 * 2048 * h * I_s * pgu_n / (pgu_ms * 1e-3) / 1e12
+    return dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
+                ms_per_step=round(1e3 * el_d / steps, 5), higher_is_better=True, scaling="weak",
+                vs_baseline=None, dtype="bf16 (fp8 e4m3fn weights)", data="synthetic",
+                config={"workload": "70B-shaped TP=4 rank, fp8 e4m3fn weights + fp32 row scales: decode M=32 "
+                                    "(value) and prefill M=2048", "h": h, "I_s": I_s, "t": t,
+                        "weight_sets": len(sets)},
+                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gateup_decode"},
+                prefill={"M": 2048, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
+                         "gateup_TFLOPs": round(pgu_tf, 1), "kernels": {k: {"avg_us": 1e3 * v[0] / v[1]}
+                                                                       for k, v in prof_p.items()}},
+                kernels={k: {"avg_us": 1e3 * v[0] / v[1]} for k, v in prof_d.items()})
+
+
+def bench_reduce(tp, args, cfg_id):
+    import torch
+    import oracle
+    c = workloads.CONFIGS[cfg_id]
+    n, t = c["reduce_n"], c["t"]
+    parts_host = workloads.make_partials(cfg_id, t, n)
+    parts = [torch.from_numpy(p).cuda() for p in parts_host]
+    out = torch.empty_like(parts[0])
+    steps, warmup = args.steps or 50, args.warmup if args.warmup is not None else 5
+    elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup)
+    b = workloads.reduce_bytes(n, t)
+    ms, cnt = prof["partial_reduce"]
+    achieved = b * cnt / (ms * 1e-3) / 1e9
+    value = b * steps / elapsed / 1e9
+    res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="f32", data="synthetic",
+               config={"workload": "%d-way fp32 partial reduce of %d elements" % (t, n), "t": t, "n": n},
+               roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "partial_reduce"})
+    if not args.no_cpu_baseline:
+        sub = max(1, n // 16)
+        hp = [p[:sub] for p in parts_host]
+        res["cpu_baseline"] = cpu_baseline(lambda: oracle.fold_fp32(hp), workloads.reduce_bytes(sub, t) / 1e9,
+                                           "GB/s", "fold of the first %d elements of each buffer" % sub)
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the TP exchange "
+              "across GPUs is design-only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import tensor_transformer_mlp_tp_amd as tp
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    tp.load()
+    if args.workload == "decode70b":
+        out = bench_decode70b(tp, args)
+    elif args.workload == "prefill70b":
+        out = bench_prefill(tp, args, 3, 4096, "70B-shaped TP=8 rank prefill, M=4096, h=8192, I_s=3584, "
+                                               "bf16, forward + 8-way fp32 partial reduce of 4096x8192")
+    elif args.workload == "prefill405b":
+        out = bench_prefill(tp, args, 5, 8192, "405B-shaped TP=8 rank prefill, M=8192, h=16384, I_s=6656, "
+                                               "bf16, forward + 8-way fp32 partial reduce of 8192x16384")
+    elif args.workload == "fp8_70b":
+        out = bench_fp8(tp, args)
+    elif args.workload == "reduce70b":
+        out = bench_reduce(tp, args, 3)
+    else:
+        out = bench_reduce(tp, args, 5)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,9 @@ from . import _lib
 from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, EXPORTED_SYMBOLS,  # noqa: F401
                    LIB_PATH, load)
 
-__all__ = ["shard_forward", "partial_reduce", "workspace_bytes", "profile_enable",
-           "profile_collect", "kernel_kinds", "TPError", "load"]
+__all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
+           "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "kernel_kinds",
+           "TPError", "load"]
 
 
 def _act_code(dt):
@@ -74,6 +75,22 @@ def alloc_workspace(nbytes, device):
     return raw[off:off + int(nbytes)]
 
 
+class PreparedCall:
+    """A library call with its arguments marshalled once (for tight loops).
+
+    Holds references to the tensors it points at; calling it re-issues the
+    same C call on the same stream.
+    """
+
+    def __init__(self, fn, args, keep):
+        self._fn, self._args, self._keep = fn, args, keep
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            _lib.check(status)
+
+
 def shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,
                   partial=None, workspace=None, stream=None):
     """Rank k's fp32 partial P_k (M x h) of the TP-MLP; see ``include/tp_mlp.h``.
@@ -85,6 +102,16 @@ def shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_do
     passed to avoid allocation.  Work is enqueued on ``stream`` (default: the
     current stream) and the call returns without waiting.
     """
+    call = prepare_shard_forward(x, w_gate, w_up, w_down, t=t, k=k, s_gate=s_gate, s_up=s_up,
+                                 s_down=s_down, partial=partial, workspace=workspace, stream=stream)
+    call()
+    return call.partial
+
+
+def prepare_shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,
+                          partial=None, workspace=None, stream=None):
+    """Validate and marshal a shard_forward once; returns a PreparedCall
+    (attribute ``partial`` is the output tensor)."""
     device = x.device
     for name, m in (("x", x), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _check_matrix(name, m, device)
@@ -116,12 +143,14 @@ def shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_do
     elif workspace.device != device:
         raise ValueError("workspace must be on %s" % device)
     ws_bytes = workspace.numel() * workspace.element_size()
-    _lib.check(lib.tp_mlp_shard_forward(
-        M, h, I_full, int(t), int(k), act, wc,
-        _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
-        _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
-        _ptr(partial), partial.stride(0), _ptr(workspace), ws_bytes, _stream_of(device, stream)))
-    return partial
+    args = (M, h, I_full, int(t), int(k), act, wc,
+            _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+            _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
+            _ptr(partial), partial.stride(0), _ptr(workspace), ws_bytes, _stream_of(device, stream))
+    call = PreparedCall(lib.tp_mlp_shard_forward, args,
+                        (x, w_gate, w_up, w_down, s_gate, s_up, s_down, partial, workspace))
+    call.partial = partial
+    return call
 
 
 def partial_reduce(partials, out=None, stream=None):
@@ -130,6 +159,14 @@ def partial_reduce(partials, out=None, stream=None):
     ``partials``: sequence of t same-shaped contiguous float32 device tensors.
     ``out`` may be ``partials[0]`` (in place); default: a new tensor.
     """
+    call = prepare_partial_reduce(partials, out=out, stream=stream)
+    call()
+    return call.out
+
+
+def prepare_partial_reduce(partials, out=None, stream=None):
+    """Validate and marshal a partial_reduce once; returns a PreparedCall
+    (attribute ``out`` is the output tensor)."""
     if len(partials) < 1:
         raise ValueError("need at least one partial")
     p0 = partials[0]
@@ -143,8 +180,11 @@ def partial_reduce(partials, out=None, stream=None):
         raise ValueError("out must be a contiguous float32 tensor shaped like the partials")
     arr = (ctypes.c_void_p * len(partials))(*[p.data_ptr() for p in partials])
     lib = _lib.load()
-    _lib.check(lib.tp_partial_reduce(p0.numel(), len(partials), arr, _ptr(out), _stream_of(device, stream)))
-    return out
+    call = PreparedCall(lib.tp_partial_reduce,
+                        (p0.numel(), len(partials), arr, _ptr(out), _stream_of(device, stream)),
+                        (list(partials), out))
+    call.out = out
+    return call
 
 
 def kernel_kinds():

@@ -11,7 +11,9 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libtp_mlp.so")
+# The in-tree library; TP_MLP_LIB may name another build of the same sources
+# (used when comparing launch-shape variants).
+LIB_PATH = os.environ.get("TP_MLP_LIB") or os.path.join(PKG, "libtp_mlp.so")
 
 TP_F32, TP_BF16, TP_FP8_E4M3FN = 0, 1, 2
 TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_WORKSPACE, TP_ERR_HIP = 0, 1, 2, 3, 4

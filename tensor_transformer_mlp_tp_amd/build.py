@@ -40,9 +40,10 @@ def hipcc():
     raise RuntimeError("hipcc not found (ROCm toolchain is required to build the library)")
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-x", "hip", "--offload-arch=" + ARCH] + COMMON_FLAGS + ["-c", src, "-o", obj]
+def _compile(src, verbose, defines=(), build_dir=BUILD_DIR):
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-x", "hip", "--offload-arch=" + ARCH] + COMMON_FLAGS + ["-D" + d for d in defines] + \
+        ["-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -54,22 +55,27 @@ def _compile(src, verbose):
     return obj
 
 
-def build(verbose=False, jobs=None):
-    """Compile every source and link libtp_mlp.so next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose=False, jobs=None, defines=(), out=LIB_PATH):
+    """Compile every source and link libtp_mlp.so (next to this file by default).
+
+    ``defines`` are extra preprocessor definitions (launch-shape variants);
+    ``out`` is the library path to write.
+    """
+    build_dir = BUILD_DIR if not defines else os.path.join(BUILD_DIR, "v_" + "_".join(defines).replace("=", ""))
+    os.makedirs(build_dir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 2)))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, defines, build_dir), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed\n%s\n%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

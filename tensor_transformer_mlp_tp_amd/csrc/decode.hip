@@ -39,59 +39,98 @@ namespace {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// U consecutive k-steps starting at step s.  A step is 32 k (bf16 weights) or
-// 64 k (fp8 weights): one 16-byte weight load per lane per row block.
+// Weights are read exactly once per call: non-temporal loads keep them from
+// displacing the activations, which every workgroup re-reads from L2.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+// A batch of U consecutive k-steps held in registers.  A step is 32 k (bf16
+// weights) or 64 k (fp8 weights): one 16-byte weight load per lane per row
+// block, plus the matching activation fragments.
 template <int NT, int RB, int U, bool FP8>
-__device__ __forceinline__ void mac_steps(f32x4 (&acc)[RB][NT], const uint8_t* const (&wrow)[RB],
-                                          const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
-                                          int s, int grp) {
+struct Batch {
+  static constexpr int XJ = FP8 ? 2 : 1;
+  u32x4 wf[U][RB];
+  u32x4 xf[U][NT][XJ];
+};
+
+// Issue the loads of the batch starting at step s.  Steps at or past s_end
+// (only in the last, partial batch) re-read step s_end - 1, which is valid
+// memory; their products are skipped in mac_batch.
+template <int NT, int RB, int U, bool FP8>
+__device__ __forceinline__ void load_batch(Batch<NT, RB, U, FP8>& bt, const uint8_t* const (&wrow)[RB],
+                                           const uint16_t* const (&xrow)[NT], int s, int s_end, int grp) {
   constexpr int KSTEP = FP8 ? 64 : 32;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int XJ = FP8 ? 2 : 1;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 wf[U][RB];
-  u32x4 xf[U][NT][XJ];
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    const int64_t st = min(s + u, s_end - 1);
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-      wf[u][r] = ld16(wrow[r] + (int64_t)(s + u) * KSTEP * EB + grp * 16);
-#pragma unroll
-  for (int u = 0; u < U; ++u)
+    for (int r = 0; r < RB; ++r) bt.wf[u][r] = ld16_stream(wrow[r] + st * KSTEP * EB + grp * 16);
 #pragma unroll
     for (int b = 0; b < NT; ++b)
 #pragma unroll
-      for (int j = 0; j < XJ; ++j) {
-        const u32x4 v = ld16(xrow[b] + (int64_t)(s + u) * KSTEP + grp * (8 * XJ) + j * 8);
-        xf[u][b][j] = xok[b] ? v : zero;
-      }
+      for (int j = 0; j < XJ; ++j) bt.xf[u][b][j] = ld16(xrow[b] + st * KSTEP + grp * (8 * XJ) + j * 8);
+  }
+}
+
+// MFMAs of the first n (<= U) steps of a loaded batch.  Token rows past M
+// were loaded from a clamped row and are zeroed here.
+template <int NT, int RB, int U, bool FP8>
+__device__ __forceinline__ void mac_batch(f32x4 (&acc)[RB][NT], const Batch<NT, RB, U, FP8>& bt,
+                                          const bool (&xok)[NT], int n) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int u = 0; u < U; ++u) {
+    if (u >= n) break;  // wave-uniform
+    bf16x8 xv[NT][FP8 ? 2 : 1];
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int j = 0; j < (FP8 ? 2 : 1); ++j) xv[b][j] = as_bf16x8(xok[b] ? bt.xf[u][b][j] : zero);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       if constexpr (FP8) {
-        const bf16x8 lo = fp8x8_to_bf16x8(wf[u][r][0], wf[u][r][1]);
-        const bf16x8 hi = fp8x8_to_bf16x8(wf[u][r][2], wf[u][r][3]);
+        const bf16x8 lo = fp8x8_to_bf16x8(bt.wf[u][r][0], bt.wf[u][r][1]);
+        const bf16x8 hi = fp8x8_to_bf16x8(bt.wf[u][r][2], bt.wf[u][r][3]);
 #pragma unroll
         for (int b = 0; b < NT; ++b) {
-          acc[r][b] = mfma16(lo, as_bf16x8(xf[u][b][0]), acc[r][b]);
-          acc[r][b] = mfma16(hi, as_bf16x8(xf[u][b][1]), acc[r][b]);
+          acc[r][b] = mfma16(lo, xv[b][0], acc[r][b]);
+          acc[r][b] = mfma16(hi, xv[b][1], acc[r][b]);
         }
       } else {
-        const bf16x8 w = as_bf16x8(wf[u][r]);
+        const bf16x8 w = as_bf16x8(bt.wf[u][r]);
 #pragma unroll
-        for (int b = 0; b < NT; ++b) acc[r][b] = mfma16(w, as_bf16x8(xf[u][b][0]), acc[r][b]);
+        for (int b = 0; b < NT; ++b) acc[r][b] = mfma16(w, xv[b][0], acc[r][b]);
       }
     }
+  }
 }
 
-template <int NT, int RB, int UNROLL, bool FP8>
+// Steps [s_beg, s_end) with two register batches in flight: the loads of
+// batch i+1 are issued before the MFMAs of batch i.
+template <int NT, int RB, int U, bool FP8>
 __device__ __forceinline__ void mac_range(f32x4 (&acc)[RB][NT], const uint8_t* const (&wrow)[RB],
                                           const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
                                           int s_beg, int s_end, int grp) {
+  if (s_beg >= s_end) return;
+  Batch<NT, RB, U, FP8> b0, b1;
   int s = s_beg;
-  for (; s + UNROLL <= s_end; s += UNROLL) mac_steps<NT, RB, UNROLL, FP8>(acc, wrow, xrow, xok, s, grp);
-  for (; s < s_end; ++s) mac_steps<NT, RB, 1, FP8>(acc, wrow, xrow, xok, s, grp);
+  load_batch(b0, wrow, xrow, s, s_end, grp);
+  while (true) {
+    int nxt = s + U;
+    if (nxt < s_end) load_batch(b1, wrow, xrow, nxt, s_end, grp);
+    mac_batch(acc, b0, xok, s_end - s);
+    if (nxt >= s_end) break;
+    s = nxt;
+    nxt = s + U;
+    if (nxt < s_end) load_batch(b0, wrow, xrow, nxt, s_end, grp);
+    mac_batch(acc, b1, xok, s_end - s);
+    if (nxt >= s_end) break;
+    s = nxt;
+  }
 }
 
 // Sum the WAVES partial accumulators of (row block r, token block b) pairs in
@@ -129,7 +168,7 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 64 : 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row16 = lane & 15;
   const int grp = lane >> 4;
   const int c0 = blockIdx.x * (8 * RB);
@@ -192,7 +231,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 64 : 32;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row16 = lane & 15;
   const int grp = lane >> 4;
   const int n0 = blockIdx.x * (16 * RB);
@@ -235,16 +274,24 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   });
 }
 
-constexpr int kWaves = 4;
+// Launch shape (waves per workgroup splitting K; steps per register batch).
+#ifndef TPMLP_DECODE_WAVES
+#define TPMLP_DECODE_WAVES 4
+#endif
+#ifndef TPMLP_DECODE_UNROLL
+#define TPMLP_DECODE_UNROLL 8
+#endif
+constexpr int kWaves = TPMLP_DECODE_WAVES;
+constexpr int kUnroll = TPMLP_DECODE_UNROLL;
 
 template <int NT, bool FP8>
 hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
   // Row blocks per workgroup: with more token blocks, two weight blocks share
-  // each activation fragment load.
+  // each activation fragment load.  Batches shrink as fragments per step grow.
   constexpr int RB_GU = NT >= 3 ? 2 : 1;
-  constexpr int UN_GU = FP8 ? (NT >= 3 ? 2 : 4) : (NT >= 3 ? 4 : 8);
+  constexpr int UN_GU = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
   constexpr int RB_DN = 1;
-  constexpr int UN_DN = FP8 ? (NT >= 3 ? 2 : 4) : (NT >= 3 ? 4 : 8);
+  constexpr int UN_DN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
   const dim3 block(kWaves * 64);
   const dim3 grid_gu((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU));
   hipError_t e = launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB_GU, kWaves, UN_GU, FP8>, grid_gu,
