@@ -30,6 +30,7 @@
 // the per-output-channel fp32 scale is applied to the fp32 sums.  The
 // activations are read with the same k order, so the dot products are exact
 // reorderings of the definition.
+
 #include "common.h"
 #include "internal.h"
 
@@ -274,6 +275,230 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   });
 }
 
+// ---------------------------------------------------------------------------
+// Streaming variant: weights go HBM -> LDS with direct-to-LDS loads into a
+// ring private to each wave, then LDS -> MFMA fragments.  Each direct load
+// instruction reads 4 weight rows x 256 contiguous bytes (instead of the 16
+// rows x 64 bytes a lane-per-row MFMA fragment load touches), which streams
+// HBM measurably better, and the ring keeps S-1 slots of 4 KB per wave in
+// flight without spending VGPRs.  A slot is 16 rows x 256 bytes (128 bf16 or
+// 256 fp8 k-values); its 16-byte chunks are stored XOR-swizzled by row so
+// the 16 rows of a fragment read sit in 16 different bank slots.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gsrc,
+                                   (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(N), lgkmcnt/expcnt not waited on.  The counter holds at
+// most 63 loads, so a larger N is clamped (which only waits longer).
+template <int N0>
+__device__ __forceinline__ void wait_vm() {
+  constexpr int N = N0 > 63 ? 63 : N0;
+  static_assert(N >= 0, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Wait until slot j's 4 direct loads have landed.  Per iteration the wave
+// issues XL activation loads and then the 4 direct loads of a slot S-1
+// ahead; the first S-1 slots were issued up front without activation loads.
+template <int S, int XL, int J>
+__device__ __forceinline__ void wait_slot_peeled(int j) {
+  if constexpr (J >= S - 2) {
+    wait_vm<(S - 2) * (XL + 4)>();
+  } else {
+    if (j == J) wait_vm<4 * (S - 2 - J) + J * (XL + 4)>();
+    else wait_slot_peeled<S, XL, J + 1>(j);
+  }
+}
+
+// Stream slots [j_beg, j_end) of this wave's 16-row block through its ring
+// and accumulate the MFMAs.  dsrc[i]: this lane's source for direct-load
+// instruction i of slot 0 (row 4i + lane/16, pre-swizzled chunk); slot j
+// adds j*256 bytes.  xrow/xok: activation rows of the NT token blocks.
+template <int NT, bool FP8, int S>
+__device__ __forceinline__ void stream_rows(f32x4 (&acc)[NT], uint8_t* ring,
+                                            const uint8_t* const (&dsrc)[4],
+                                            const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
+                                            int j_beg, int j_end, int lane) {
+  constexpr int STEPS = FP8 ? 8 : 4;          // MFMA k-steps (32 k) per slot
+  constexpr int KS = FP8 ? 256 : 128;         // k per slot
+  constexpr int XL = STEPS * NT;              // activation loads per slot
+  const int r = lane & 15, g = lane >> 4;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  const int nsl = j_end - j_beg;
+  if (nsl <= 0) return;
+  auto issue = [&](int j, int pos) {
+    uint8_t* dst = ring + pos * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(dsrc[i] + (int64_t)j * 256, dst + i * 1024);
+  };
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(j_beg + min(p, nsl - 1), p);
+  int pos = 0;
+  for (int jj = 0; jj < nsl; ++jj) {
+    wait_slot_peeled<S, XL, 0>(jj);
+    const int j = j_beg + jj;
+    // activation fragments of this slot (from L2; same k order as the weights)
+    u32x4 xf[STEPS][NT];
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+      for (int b = 0; b < NT; ++b) {
+        const int ko = FP8 ? (64 * (st >> 1) + 16 * g + 8 * (st & 1)) : (32 * st + 8 * g);
+        xf[st][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (int64_t)j * KS + ko);
+      }
+    const int npos = pos == 0 ? S - 1 : pos - 1;   // ring slot of j+S-1 (held j-1)
+    issue(j_beg + min(jj + S - 1, nsl - 1), npos);
+    const uint8_t* sl = ring + pos * 4096 + r * 256;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      bf16x8 w;
+      if constexpr (FP8) {
+        if ((st & 1) == 0) {
+          const int q = 4 * (st >> 1) + g;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sl + ((q ^ r) * 16));
+          w = fp8x8_to_bf16x8(v[0], v[1]);
+#pragma unroll
+          for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[b]);
+          w = fp8x8_to_bf16x8(v[2], v[3]);
+#pragma unroll
+          for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st + 1][b] : zero), acc[b]);
+        }
+      } else {
+        const int q = 4 * st + g;
+        w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + ((q ^ r) * 16)));
+#pragma unroll
+        for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[b]);
+      }
+    }
+    pos = pos == S - 1 ? 0 : pos + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the ring's last (duplicate) loads are done before LDS is reused
+}
+
+// Direct-load sources of this lane for the 4 instructions of slot 0: rows
+// 4i + lane/16 of the block, logical chunk (lane%16) ^ row.
+template <typename RowPtr>
+__device__ __forceinline__ void stream_sources(const uint8_t* (&dsrc)[4], int lane, int k_byte0, RowPtr row_ptr) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ row;
+    dsrc[i] = row_ptr(row) + k_byte0 + c * 16;
+  }
+}
+
+#ifndef TPMLP_DECODE_SLOTS
+#define TPMLP_DECODE_SLOTS 2
+#endif
+constexpr int kSlots = TPMLP_DECODE_SLOTS;
+constexpr int kSWaves = 4;
+
+template <int NT, bool FP8>
+__global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
+    int M, int h, int I_s, const uint16_t* __restrict__ x, int64_t ldx,
+    const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
+    const float* __restrict__ sg, const float* __restrict__ su,
+    uint16_t* __restrict__ a_out, int64_t lda) {
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int KS = FP8 ? 256 : 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * 4096];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row16 = lane & 15, grp = lane >> 4;
+  const int c0 = blockIdx.x * 8;
+  // 16-row block: rows 0-7 gate channels c0..c0+7, rows 8-15 the same channels' up rows
+  auto row_ptr = [&](int row) {
+    const int ch = min(c0 + (row & 7), I_s - 1);
+    return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
+  };
+  const int nslots = h / KS;
+  const int j_beg = (wave * nslots) / kSWaves, j_end = ((wave + 1) * nslots) / kSWaves;
+  const uint8_t* dsrc[4];
+  stream_sources(dsrc, lane, 0, row_ptr);
+  const uint16_t* xrow[NT];
+  bool xok[NT];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    const int tok = b * 16 + row16;
+    xok[b] = tok < M;
+    xrow[b] = x + (int64_t)min(tok, M - 1) * ldx;
+  }
+  f32x4 acc[1][NT];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_rows<NT, FP8, kSlots>(acc[0], ring_all + wave * kSlots * 4096, dsrc, xrow, xok, j_beg, j_end, lane);
+
+  reduce_waves<NT, 1, kSWaves>(acc, wave, lane, [&](int, int b, f32x4 v) {
+    f32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
+    if (grp < 2) {
+      const int ch = c0 + 4 * grp;
+      const int tok = b * 16 + row16;
+      if (tok < M && ch < I_s) {
+        float a[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float gv = v[i], uv = o[i];
+          if constexpr (FP8) {
+            gv *= sg[ch + i];
+            uv *= su[ch + i];
+          }
+          a[i] = silu(gv) * uv;
+        }
+        u32x2 packed = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+        *reinterpret_cast<u32x2*>(a_out + (int64_t)tok * lda + ch) = packed;
+      }
+    }
+  });
+}
+
+template <int NT, bool FP8>
+__global__ __launch_bounds__(kSWaves * 64) void down_stream_kernel(
+    int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
+    const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
+    float* __restrict__ p, int64_t ldp) {
+  constexpr int EB = FP8 ? 1 : 2;
+  constexpr int KS = FP8 ? 256 : 128;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * 4096];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row16 = lane & 15, grp = lane >> 4;
+  const int n0 = blockIdx.x * 16;
+  auto row_ptr = [&](int row) { return wd + (int64_t)min(n0 + row, h - 1) * ldw * EB; };
+  const int nslots = I_s / KS;
+  const int j_beg = (wave * nslots) / kSWaves, j_end = ((wave + 1) * nslots) / kSWaves;
+  const uint8_t* dsrc[4];
+  stream_sources(dsrc, lane, 0, row_ptr);
+  const uint16_t* xrow[NT];
+  bool xok[NT];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) {
+    const int tok = b * 16 + row16;
+    xok[b] = tok < M;
+    xrow[b] = a_in + (int64_t)min(tok, M - 1) * lda;
+  }
+  f32x4 acc[1][NT];
+#pragma unroll
+  for (int b = 0; b < NT; ++b) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_rows<NT, FP8, kSlots>(acc[0], ring_all + wave * kSlots * 4096, dsrc, xrow, xok, j_beg, j_end, lane);
+
+  reduce_waves<NT, 1, kSWaves>(acc, wave, lane, [&](int, int b, f32x4 v) {
+    const int f = n0 + 4 * grp;
+    const int tok = b * 16 + row16;
+    if (tok < M && f < h) {
+      if constexpr (FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
+      }
+      *reinterpret_cast<f32x4*>(p + (int64_t)tok * ldp + f) = v;
+    }
+  });
+}
+
 // Launch shape (waves per workgroup splitting K; steps per register batch).
 #ifndef TPMLP_DECODE_WAVES
 #define TPMLP_DECODE_WAVES 4
@@ -305,8 +530,35 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
                 a.ldw_down, a.sd, a.p, a.ldp);
 }
 
+template <int NT, bool FP8>
+hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
+  const dim3 block(kSWaves * 64);
+  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, FP8>, dim3((a.I_s + 7) / 8), block, 0,
+                        stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
+                        (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+  if (e != hipSuccess) return e;
+  return launch(K_DOWN_DECODE, down_stream_kernel<NT, FP8>, dim3((a.h + 15) / 16), block, 0, stream, a.M,
+                a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd, a.p, a.ldp);
+}
+
+#ifndef TPMLP_DECODE_V2
+#define TPMLP_DECODE_V2 1
+#endif
 template <bool FP8>
 hipError_t run_decode_nt(const ShardArgs& a, hipStream_t stream) {
+  // The streaming kernels move whole 16-row x 256-byte slots: they need h and
+  // I_s to be multiples of 128 (bf16) / 256 (fp8) k-values; other shapes use
+  // the register-batch kernels, which step 32 / 64 k-values at a time.
+  constexpr int KS = FP8 ? 256 : 128;
+  if (TPMLP_DECODE_V2 && a.h % KS == 0 && a.I_s % KS == 0) {
+    switch ((a.M + 15) / 16) {
+      case 1: return run_stream<1, FP8>(a, stream);
+      case 2: return run_stream<2, FP8>(a, stream);
+      case 3: return run_stream<3, FP8>(a, stream);
+      case 4: return run_stream<4, FP8>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch ((a.M + 15) / 16) {
     case 1: return run_decode<1, FP8>(a, stream);
     case 2: return run_decode<2, FP8>(a, stream);

@@ -12,26 +12,26 @@
 //             partial).
 //
 // Both compute C^T = W * act^T with K-contiguous operands (the (out, in)
-// weight layout and row-major activations): 256 x 256 output tiles, BK = 64,
-// four waves in a 2 x 2 grid with a 128 x 128 sub-tile each, built from
-// 32x32x16 bf16 MFMAs (the full-rate bf16 matrix instruction on gfx950;
-// 4 x 4 blocks = 256 fp32 accumulators per lane, held in AGPRs).
+// weight layout and row-major activations): 256 x 256 output tiles, four
+// waves in a 2 x 2 grid with a 128 x 128 sub-tile each, built from 32x32x16
+// bf16 MFMAs (the full-rate bf16 matrix instruction on gfx950; 4 x 4 blocks =
+// 256 fp32 accumulators per lane, held in AGPRs).
 //
-// Global -> LDS: direct-to-LDS 16-byte loads (global_load_lds_dwordx4), two
-// stages.  The loads of k-tile kt+1 are issued right after the barrier that
-// opens k-tile kt and land while its MFMAs run; nothing is staged in VGPRs.
-// Rows past M (tokens) or N (channels) are loaded from the last valid row: a
-// row of the output depends only on its own activation row and its own weight
-// row, so those rows only feed outputs that are never stored.
+// Global -> LDS: direct-to-LDS 16-byte loads (global_load_lds_dwordx4) into a
+// ring of NS stages of BK k-values; a stage's loads are issued NS-1 k-tiles
+// before it is used and nothing is staged in VGPRs.  bf16 weights run two
+// stages of 64 (128 KB); fp8 weights, with smaller stages, three.  Rows past M
+// (tokens) or N (channels) are loaded from the last valid row: a row of the
+// output depends only on its own activation row and its own weight row, so
+// those rows only feed outputs that are never stored.
 //
-// LDS rows are BK elements (128 B bf16, 64 B fp8) split in 16-byte chunks
-// stored XOR-swizzled by row.  gfx950's LDS has 64 four-byte banks and serves
-// a 16-byte-per-lane read 16 lanes per cycle, so the 16 rows those lanes read
-// (same logical chunk) must land in 16 different 16-byte bank slots: physical
-// chunk = logical ^ ((row >> 1) & 7) for 128-byte rows (rows of equal parity
-// then differ in chunk) and logical ^ ((row >> 2) & 3) for 64-byte rows.  A
-// direct-to-LDS load writes 64 consecutive 16-byte slots, so the swizzle is
-// applied by choosing which global chunk each lane fetches.
+// LDS rows are BK elements split in 16-byte chunks stored XOR-swizzled by
+// row.  gfx950's LDS has 64 four-byte banks and serves a 16-byte-per-lane
+// read 16 lanes per cycle, so the 16 rows those lanes read (same logical
+// chunk) must land in 16 different 16-byte bank slots (swz below; measured
+// SQ_LDS_BANK_CONFLICT = 0).  A direct-to-LDS load writes 64 consecutive
+// 16-byte slots, so the swizzle is applied by choosing which global chunk each
+// lane fetches.
 //
 // A gate/up tile holds 128 channels: LDS weight rows 0-127 are their gate
 // rows and 128-255 their up rows; a wave's four 32-row blocks are two gate
@@ -40,9 +40,9 @@
 //
 // fp8 (e4m3fn) weights are staged in LDS as bytes (half the traffic) and
 // widened to bf16 (exact) when the fragments are read; one 16-byte LDS read
-// gives a lane the k values of two MFMA steps, and the activation fragments
-// are read in the same k order.  Per-channel scales multiply the fp32
-// accumulators in the epilogue.
+// gives a lane the k values of both MFMA steps of a stage, and the activation
+// fragments are read in the same k order.  Per-channel scales multiply the
+// fp32 accumulators in the epilogue.
 //
 // Workgroup-to-tile mapping: consecutive workgroup ids are dispatched
 // round-robin to the eight XCDs, each with its own L2, so the id is first
@@ -58,7 +58,6 @@ namespace {
 
 constexpr int BM = 256;      // tokens per tile
 constexpr int BN = 256;      // weight rows per tile
-constexpr int BK = 64;       // k per stage
 constexpr int THREADS = 256; // 4 waves
 constexpr int GROUP_M = 4;
 
@@ -78,9 +77,35 @@ __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_dst) {
 
 __device__ __forceinline__ u32x4 lds_read16(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Physical 16-byte chunk of a logical chunk: 128-byte and 64-byte LDS rows.
-__device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
-__device__ __forceinline__ int swz64(int row) { return (row >> 2) & 3; }
+// Physical 16-byte chunk of a logical chunk in an LDS row of ROWB bytes:
+// the 16 rows read by one 16-lane LDS cycle land in 16 different 16-byte
+// bank slots (64 banks x 4 bytes).
+template <int ROWB>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (ROWB == 128) return (row >> 1) & 7;
+  else if constexpr (ROWB == 64) return (row >> 2) & 3;
+  else return (row >> 3) & 1;  // 32-byte rows
+}
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() would also
+// wait for every outstanding global load (vmcnt(0)), which would drain the
+// direct-load ring at each k-tile; the ring's completion is tracked with
+// explicit vmcnt waits instead.
+// Before it, this wave's LDS reads are complete (lgkmcnt(0)); the acquire
+// fence after it keeps later LDS reads below the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt that waits until at most n vector-memory loads of this wave are
+// outstanding (expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 // Scheduling groups for one sub-step: its 16 MFMAs with NDS fragment reads
 // of the next sub-step threaded one after each of the first NDS MFMAs.
@@ -111,22 +136,30 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   return TileCoord{first_m + i % gsize, i / gsize};
 }
 
-template <bool SWIGLU, bool FP8>
+template <bool SWIGLU, bool FP8, int BK, int NS, bool REG>
 __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
     int M, int N, int K, const uint16_t* __restrict__ act, int64_t ld_act,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
     const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
     int64_t ld_out, int tiles_m, int tiles_n) {
+  static_assert(BK == 32 || BK == 64, "stage depth");
   constexpr int EB = FP8 ? 1 : 2;              // weight bytes per element
+  constexpr int KSUB = BK / 16;                // MFMA sub-steps per stage
+  constexpr int XROWB = BK * 2;                // bytes per LDS activation row
   constexpr int WROWB = BK * EB;               // bytes per LDS weight row
-  constexpr int XBYTES = BM * BK * 2;          // activation stage (32 KB)
-  constexpr int WBYTES = BN * WROWB;           // weight stage (32 KB / 16 KB)
+  constexpr int XBYTES = BM * XROWB;
+  constexpr int WBYTES = BN * WROWB;
   constexpr int SBYTES = XBYTES + WBYTES;
   constexpr int XINST = XBYTES / 1024 / 4;     // 1 KB direct loads per wave per stage
   constexpr int WINST = WBYTES / 1024 / 4;
+  constexpr int LPS = XINST + WINST;           // loads per wave per stage
   constexpr int TILE_N = SWIGLU ? BN / 2 : BN; // output columns per tile
+  constexpr int XRPI = 1024 / XROWB;           // rows per 1 KB load
+  constexpr int WRPI = 1024 / WROWB;
+  constexpr int XCH = XROWB / 16;              // 16-byte chunks per row
+  constexpr int WCH = WROWB / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * SBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + 4 * 512];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -139,26 +172,20 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   const int n0 = tc.tn * TILE_N;
 
   // ---- direct-to-LDS sources: instruction i of this wave fills LDS bytes
-  // [(wave*INST + i) KB, +1 KB) of the stage; lane l fills 16 bytes of it.
+  // [(wave*INST + i) KB, +1 KB) of a stage; lane l fills 16 bytes of it.
   const uint8_t* xsrc[XINST];
 #pragma unroll
   for (int i = 0; i < XINST; ++i) {
-    const int row = (wave * XINST + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz128(row);
+    const int row = (wave * XINST + i) * XRPI + lane / XCH;
+    const int c = (lane % XCH) ^ swz<XROWB>(row);
     const int tok = min(m0 + row, M - 1);
     xsrc[i] = reinterpret_cast<const uint8_t*>(act + (int64_t)tok * ld_act) + c * 16;
   }
   const uint8_t* wsrc[WINST];
 #pragma unroll
   for (int i = 0; i < WINST; ++i) {
-    int row, c;
-    if constexpr (FP8) {
-      row = (wave * WINST + i) * 16 + (lane >> 2);
-      c = (lane & 3) ^ swz64(row);
-    } else {
-      row = (wave * WINST + i) * 8 + (lane >> 3);
-      c = (lane & 7) ^ swz128(row);
-    }
+    const int row = (wave * WINST + i) * WRPI + lane / WCH;
+    const int c = (lane % WCH) ^ swz<WROWB>(row);
     int ch;
     const uint8_t* base;
     if constexpr (SWIGLU) {
@@ -170,6 +197,24 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
     }
     wsrc[i] = base + (int64_t)min(ch, N - 1) * ldw * EB + c * 16;
   }
+  // L2 warm-up one k-tile ahead of the direct loads: each thread touches the
+  // 128-byte line of one activation row and one weight row of k-tile kt with a
+  // 4-byte direct-to-LDS load into a scratch area nobody reads (no VGPR is
+  // written, so nothing waits on it).  The misses of a k-tile are then in
+  // flight one k-tile before its own loads, which find the lines in L2.
+  const uint8_t* tx = reinterpret_cast<const uint8_t*>(act + (int64_t)min(m0 + tid, M - 1) * ld_act);
+  const uint8_t* tw;
+  if constexpr (SWIGLU)
+    tw = (tid < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (tid & (BN / 2 - 1)), N - 1) * ldw * EB;
+  else
+    tw = w0 + (int64_t)min(n0 + tid, N - 1) * ldw * EB;
+  uint8_t* tdst = lds + NS * SBYTES + wave * 512;
+  auto touch_stage = [&](int kt) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tx + (int64_t)kt * BK * 2),
+                                     (__attribute__((address_space(3))) void*)tdst, 4, 0, 0);
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tw + (int64_t)kt * BK * EB),
+                                     (__attribute__((address_space(3))) void*)(tdst + 256), 4, 0, 0);
+  };
   auto issue_stage = [&](int kt, int buf) {
     uint8_t* xdst = lds + buf * SBYTES + wave * XINST * 1024;
     uint8_t* wdst = lds + buf * SBYTES + XBYTES + wave * WINST * 1024;
@@ -177,6 +222,23 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
     for (int i = 0; i < XINST; ++i) load_lds16(xsrc[i] + (int64_t)kt * BK * 2, xdst + i * 1024);
 #pragma unroll
     for (int i = 0; i < WINST; ++i) load_lds16(wsrc[i] + (int64_t)kt * BK * EB, wdst + i * 1024);
+  };
+  // Register-staged alternative: the same 16-byte pieces go global -> VGPR
+  // -> LDS (same LDS slots as the direct loads would fill).
+  u32x4 rx[REG ? XINST : 1], rw[REG ? WINST : 1];
+  auto load_regs = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < XINST; ++i) rx[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (int64_t)kt * BK * 2);
+#pragma unroll
+    for (int i = 0; i < WINST; ++i) rw[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + (int64_t)kt * BK * EB);
+  };
+  auto store_regs = [&](int buf) {
+    uint8_t* xdst = lds + buf * SBYTES + wave * XINST * 1024 + lane * 16;
+    uint8_t* wdst = lds + buf * SBYTES + XBYTES + wave * WINST * 1024 + lane * 16;
+#pragma unroll
+    for (int i = 0; i < XINST; ++i) *reinterpret_cast<u32x4*>(xdst + i * 1024) = rx[i];
+#pragma unroll
+    for (int i = 0; i < WINST; ++i) *reinterpret_cast<u32x4*>(wdst + i * 1024) = rw[i];
   };
 
   // ---- fragment rows of this lane inside a stage
@@ -199,11 +261,11 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
 
-  // Fragments of sub-step kk (16 k).  bf16: lane group g holds chunk 2kk+g of
-  // both operands.  fp8: at even kk the weight lane reads 16-byte chunk kk+g
-  // (16 codes) once; its low 8 codes serve sub-step kk and its high 8 codes
-  // sub-step kk+1, so the activation chunk of 8 elements is 4*(kk/2) + 2g +
-  // kk%2.
+  // Fragments of sub-step kk (16 k) of a stage.  bf16: lane group g holds
+  // chunk 2kk+g of both operands.  fp8: at even kk the weight lane reads
+  // 16-byte chunk kk+g (16 codes) once; its low 8 codes serve sub-step kk and
+  // its high 8 codes sub-step kk+1, so the activation chunk of 8 elements is
+  // 4*(kk/2) + 2g + kk%2.
   u32x4 wq[4];
   auto read_frags = [&](const uint8_t* sx, const uint8_t* sw, int kk, bf16x8 (&wf)[4], bf16x8 (&xf)[4]) {
 #pragma unroll
@@ -211,60 +273,106 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       const int r = wrow[cb];
       if constexpr (FP8) {
         if ((kk & 1) == 0) {
-          const int q = kk + g;
-          wq[cb] = lds_read16(sw + r * WROWB + ((q ^ swz64(r)) * 16));
+          wq[cb] = lds_read16(sw + r * WROWB + (((kk + g) ^ swz<WROWB>(r)) * 16));
           wf[cb] = fp8x8_to_bf16x8(wq[cb][0], wq[cb][1]);
         } else {
           wf[cb] = fp8x8_to_bf16x8(wq[cb][2], wq[cb][3]);
         }
       } else {
         const int ch = 2 * kk + g;
-        wf[cb] = as_bf16x8(lds_read16(sw + r * WROWB + ((ch ^ swz128(r)) * 16)));
+        wf[cb] = as_bf16x8(lds_read16(sw + r * WROWB + ((ch ^ swz<WROWB>(r)) * 16)));
       }
     }
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
       const int r = xrow[tb];
       const int ch = FP8 ? (4 * (kk >> 1) + 2 * g + (kk & 1)) : (2 * kk + g);
-      xf[tb] = as_bf16x8(lds_read16(sx + r * 128 + ((ch ^ swz128(r)) * 16)));
+      xf[tb] = as_bf16x8(lds_read16(sx + r * XROWB + ((ch ^ swz<XROWB>(r)) * 16)));
     }
   };
 
-  // Main loop, one barrier per k-tile.  The body is a single basic block (the
-  // last iteration re-loads its own k-tile into the idle buffer rather than
-  // branching), so the scheduling groups below order the whole of it: the
-  // direct loads of the next k-tile first, then the fragments of sub-step 0,
-  // then each sub-step's 16 MFMAs with the 8 fragment reads of the following
-  // sub-step threaded between them, so the matrix core never waits on LDS
-  // inside a k-tile.
+  // Main loop, one barrier per k-tile.  Stages 0 .. NS-2 are issued up front;
+  // iteration kt waits for stage kt (allowing the NS-2 younger stages to stay
+  // in flight), meets the other waves at the barrier (after which stage kt-1's
+  // buffer is free), issues stage kt+NS-1 into it and runs its MFMAs.  Past
+  // the last k-tile the issue re-loads the last k-tile into the free buffer,
+  // so the body stays one basic block with a fixed load count; the
+  // scheduling groups thread the fragment reads of sub-step 1 between the
+  // MFMAs of sub-step 0.
   const int KT = K / BK;
-  issue_stage(0, 0);
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of stage kt have landed
-    __syncthreads();                // ... and every wave's; stage kt-1 is no longer read
-    issue_stage(min(kt + 1, KT - 1), cur ^ 1);
-    const uint8_t* sx = lds + cur * SBYTES;
-    const uint8_t* sw = sx + XBYTES;
-    bf16x8 wf[2][4], xf[2][4];
-    read_frags(sx, sw, 0, wf[0], xf[0]);
+  if constexpr (REG) {
+    static_assert(NS == 2, "register staging uses two LDS stages");
+    load_regs(0);
+    store_regs(0);
+    int buf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      lds_barrier();  // every wave's writes of stage kt are done; stage kt-1 is no longer read
+      load_regs(min(kt + 1, KT - 1));
+      const uint8_t* sx = lds + buf * SBYTES;
+      const uint8_t* sw = sx + XBYTES;
+      bf16x8 wf[2][4], xf[2][4];
+      read_frags(sx, sw, 0, wf[0], xf[0]);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      if (kk + 1 < 4) read_frags(sx, sw, kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+      for (int kk = 0; kk < KSUB; ++kk) {
+        if (kk + 1 < KSUB) read_frags(sx, sw, kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+          for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+      }
+      store_regs(buf ^ 1);
+      __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      sched_substep<FP8 ? 4 : 8>();
+      if constexpr (KSUB == 4) {
+        sched_substep<8>();
+        sched_substep<FP8 ? 4 : 8>();
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, LPS, 0);
+      buf ^= 1;
     }
-    // fragment reads per sub-step: 8 (bf16); fp8: 8 at even sub-steps
-    // (4 weight + 4 activation), 4 at odd ones (activations only)
-    __builtin_amdgcn_sched_group_barrier(0x020, XINST + WINST, 0);  // direct loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);              // fragments of sub-step 0
-    sched_substep<FP8 ? 4 : 8>();
-    sched_substep<8>();
-    sched_substep<FP8 ? 4 : 8>();
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-  }
+  } else {
+  #pragma unroll
+    for (int s = 0; s < NS - 1; ++s) {
+      issue_stage(min(s, KT - 1), s);
+      touch_stage(min(s + 1, KT - 1));
+    }
+    int buf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      // this wave's loads of stage kt have landed (younger: the touch issued
+      // with them and NS-2 later iterations' loads + touches)
+      wait_vmcnt<2 + (NS - 2) * (LPS + 2)>();
+      lds_barrier();                  // ... and every wave's; stage kt-1 is no longer read
+      const int nbuf = buf == 0 ? NS - 1 : buf - 1;   // (kt + NS - 1) % NS
+      issue_stage(min(kt + NS - 1, KT - 1), nbuf);
+      touch_stage(min(kt + NS, KT - 1));
+      const uint8_t* sx = lds + buf * SBYTES;
+      const uint8_t* sw = sx + XBYTES;
+      bf16x8 wf[2][4], xf[2][4];
+      read_frags(sx, sw, 0, wf[0], xf[0]);
+  #pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) {
+        if (kk + 1 < KSUB) read_frags(sx, sw, kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+  #pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+  #pragma unroll
+          for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+      }
+      // scheduling: direct loads of stage kt+NS-1, fragments of sub-step 0,
+      // then each sub-step's MFMAs with the next sub-step's reads threaded in
+      // (fp8 odd sub-steps read activations only)
+      __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      sched_substep<FP8 ? 4 : 8>();
+      if constexpr (KSUB == 4) {
+        sched_substep<8>();
+        sched_substep<FP8 ? 4 : 8>();
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      buf = buf == NS - 1 ? 0 : buf + 1;
+    }
+}
   __builtin_amdgcn_s_waitcnt(0);  // no direct load is left in flight at exit
 
   // ---- epilogue.  Lane holds, per block, rows 8j + 4g + (0..3) (j = 0..3)
@@ -331,21 +439,39 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   }
 }
 
+// Stage shape: bf16 weights use two stages of BK = 64 (128 KB of LDS); fp8
+// weights, with 48 KB stages, fit three.
+#ifndef TPMLP_PREFILL_BK
+#define TPMLP_PREFILL_BK 64
+#endif
+#ifndef TPMLP_PREFILL_NS_BF16
+#define TPMLP_PREFILL_NS_BF16 2
+#endif
+#ifndef TPMLP_PREFILL_NS_FP8
+#define TPMLP_PREFILL_NS_FP8 3
+#endif
+#ifndef TPMLP_PREFILL_REG
+#define TPMLP_PREFILL_REG 0
+#endif
+
 template <bool FP8>
 hipError_t run_prefill(const ShardArgs& a, hipStream_t stream) {
+  constexpr int BK = TPMLP_PREFILL_BK;
+  constexpr int NS = FP8 ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
+  constexpr bool REG = TPMLP_PREFILL_REG != 0;
   const int tiles_m = (a.M + BM - 1) / BM;
   const dim3 block(THREADS);
   {
     const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
-    hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8>, grid, block, 0, stream, a.M, a.I_s,
+    hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, BK, NS, REG>, grid, block, 0, stream, a.M, a.I_s,
                           a.h, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
                           (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m, tiles_n);
     if (e != hipSuccess) return e;
   }
   const int tiles_n = (a.h + BN - 1) / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8>, grid, block, 0, stream, a.M, a.h, a.I_s,
+  return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8, BK, NS, REG>, grid, block, 0, stream, a.M, a.h, a.I_s,
                 (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
                 a.ldw_down, a.sd, (const float*)nullptr, (void*)a.p, a.ldp, tiles_m, tiles_n);
 }

@@ -205,3 +205,55 @@ def test_config4_fp8_prefill_full():
 
 def test_config5_prefill_full():
     _full_prefill(5, 8192)
+
+
+# ------------------------------------------------------------ streaming decode path, several slots per wave
+
+@pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("w", ["bf16", "e4m3fn"])
+def test_stream_decode_shapes(M, w):
+    # h and I_s multiples of the slot width (128 bf16 / 256 fp8 k-values) take
+    # the streaming kernels; uneven slot counts per wave, ragged token blocks
+    h, I_s = (512, 640) if w == "bf16" else (1024, 1280)
+    print("stream decode M=%d w=%s" % (M, w), flush=True)
+    x, ws = make_case(45, M, h, I_s, "bf16", w, 0.05, 0.05, weight_set=M)
+    d = upload_case(x, ws, "bf16", w)
+    ref = oracle_partial(x, ws, "bf16", w)
+    outs = []
+    for rep in range(3):   # repeated calls give identical bits
+        outs.append(run_forward(d, 4, 1).cpu().numpy())
+    check(outs[0], ref, TOL_FP8 if w == "e4m3fn" else TOL_BF16, "stream M=%d %s" % (M, w))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+
+
+def test_decode_many_calls_and_graph():
+    # many calls on two streams in turn, then a captured graph replayed
+    M, h, I_s = 8, 512, 512
+    x, ws = make_case(46, M, h, I_s, "bf16", "bf16", 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", "bf16")
+    ref = run_forward(d, 2, 0).clone()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty_like(ref) for _ in range(2)]
+    for i in range(150):
+        s = streams[i % 2]
+        with torch.cuda.stream(s):
+            tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=2, k=0, partial=outs[i % 2])
+        s.synchronize()
+        assert torch.equal(outs[i % 2].view(torch.int32), ref.view(torch.int32)), i
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        # a prepared call is bound to the stream current when it is prepared
+        call = tp.prepare_shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=2, k=0)
+        call()   # warm-up outside capture
+        s.synchronize()
+        call.partial.zero_()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    for i in range(5):
+        call.partial.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.partial.view(torch.int32), ref.view(torch.int32)), i
