@@ -13,16 +13,23 @@ cache.  ``value`` is algorithmic bytes per second over the timed steps.
 
 Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
 (TP=4 fp8 weights: decode M=32 and prefill M=2048), prefill405b (8192 tokens),
-reduce70b / reduce405b (the 8-way reduces alone).
+reduce70b / reduce405b (the 8-way reduces alone), copy (the reduce with one
+buffer over 1 GiB: a plain copy of known size, the calibration run for the
+HBM byte counters).
 
 The ``roofline`` object is for the step's dominant kernel: algorithmic bytes
 (or FLOP) of its launches divided by their summed durations, taken from HIP
 events that the library attaches to each of its own kernel dispatches during
-the timed steps.  ``cpu_baseline`` times the float64 CPU oracle on a bounded
+the timed steps.  Its ``traffic`` is the HBM bytes per launch that
+rocprofv3's FETCH_SIZE and WRITE_SIZE counters recorded for that kernel
+(scaled by what they read for the copy), kept as text under profiles/ with
+the hash of the kernel's sources at the time; it is null when no record
+exists or the sources have changed since.  ``cpu_baseline`` times the float64 CPU oracle on a bounded
 sample of the same workload (rank 0, one GPU only).
 """
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,10 +55,46 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode70b",
-                    choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b"])
+                    choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     return ap.parse_args()
+
+
+KERNEL_SOURCES = {
+    "gateup_decode": ("decode.hip", "common.h"),
+    "gateup_prefill": ("prefill.hip", "common.h"),
+    "partial_reduce": ("reduce.hip", "common.h"),
+}
+
+
+def sources_sha256(kernel):
+    hsh = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "tensor_transformer_mlp_tp_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in `workload` from profiles/traffic_<kernel>_<workload>.txt,
+    or None when there is no record or the kernel's sources differ from the recorded hash."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("kernel_sources_sha256") != sources_sha256(kernel):
+        return None
+    try:
+        return float(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -216,7 +259,8 @@ def bench_decode70b(tp, args):
     ms, cnt = prof["gateup_decode"]
     achieved = gu_bytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gateup_decode",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
             "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases}}
     fwd_time_ms = sum(prof[k][0] for k in ("gateup_decode", "down_decode")) / steps
     fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
@@ -286,7 +330,8 @@ def bench_prefill(tp, args, cfg_id, M, label):
         kern["partial_reduce"] = {"launches": n, "avg_us": 1e3 * ms / n,
                                   "GBps": round(workloads.reduce_bytes(M * h, t) * n / (ms * 1e-3) / 1e9, 1)}
     roof = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4), "traffic": None, "kernel": "gateup_prefill",
+            "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
+            "traffic": recorded_traffic("gateup_prefill", args.workload), "kernel": "gateup_prefill",
             "per_launch_flop": 4 * M * h * I_s}
     out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
@@ -358,13 +403,35 @@ def bench_reduce(tp, args, cfg_id):
                vs_baseline=None, dtype="f32", data="synthetic",
                config={"workload": "%d-way fp32 partial reduce of %d elements" % (t, n), "t": t, "n": n},
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "partial_reduce"})
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("partial_reduce", args.workload), "kernel": "partial_reduce"})
     if not args.no_cpu_baseline:
         sub = max(1, n // 16)
         hp = [p[:sub] for p in parts_host]
         res["cpu_baseline"] = cpu_baseline(lambda: oracle.fold_fp32(hp), workloads.reduce_bytes(sub, t) / 1e9,
                                            "GB/s", "fold of the first %d elements of each buffer" % sub)
     return res
+
+
+def bench_copy(tp, args):
+    """One-buffer reduce over 1 GiB: reads n*4 bytes and writes n*4 bytes, nothing else."""
+    import torch
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(src)
+    steps, warmup = args.steps or 20, args.warmup if args.warmup is not None else 3
+    elapsed, prof = timed(tp, lambda i: tp.partial_reduce([src], out=out), steps, warmup)
+    b = workloads.reduce_bytes(n, 1)
+    ms, cnt = prof["partial_reduce"]
+    achieved = b * cnt / (ms * 1e-3) / 1e9
+    return dict(metric="copy GB/s (HBM counter calibration)", value=round(b * steps / elapsed / 1e9, 1),
+                unit="GB/s", n_gpus=1, steps=steps, warmup=warmup, ms_per_step=round(1e3 * elapsed / steps, 4),
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32", data="synthetic",
+                config={"workload": "copy of %d fp32 (one-buffer partial reduce)" % n, "n": n,
+                        "bytes_read": 4 * n, "bytes_written": 4 * n},
+                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                          "kernel": "partial_reduce"})
 
 
 def main():
@@ -391,6 +458,8 @@ def main():
         out = bench_fp8(tp, args)
     elif args.workload == "reduce70b":
         out = bench_reduce(tp, args, 3)
+    elif args.workload == "copy":
+        out = bench_copy(tp, args)
     else:
         out = bench_reduce(tp, args, 5)
     print(json.dumps(out), flush=True)
