@@ -280,10 +280,19 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
 // ring private to each wave, then LDS -> MFMA fragments.  Each direct load
 // instruction reads 4 weight rows x 256 contiguous bytes (instead of the 16
 // rows x 64 bytes a lane-per-row MFMA fragment load touches), which streams
-// HBM measurably better, and the ring keeps S-1 slots of 4 KB per wave in
-// flight without spending VGPRs.  A slot is 16 rows x 256 bytes (128 bf16 or
-// 256 fp8 k-values); its 16-byte chunks are stored XOR-swizzled by row so
-// the 16 rows of a fragment read sit in 16 different bank slots.
+// HBM measurably better, and the ring keeps S-1 slots per wave in flight
+// without spending VGPRs.  A slot is RB blocks of 16 rows x 256 bytes (128
+// bf16 or 256 fp8 k-values each); its 16-byte chunks are stored XOR-swizzled
+// by row so the 16 rows of a fragment read sit in 16 different bank slots.
+//
+// The activation fragments of a slot come from L2 in registers and serve all
+// RB row blocks.  With more than 16 tokens those fragment reads, not the
+// weight stream, bound the kernel (every workgroup re-reads the whole
+// activation from L2), so the launch gives each wave RB = 2 row blocks there:
+// half the activation traffic per weight byte, at half the workgroup count.
+//
+// The four waves of a workgroup take interleaved slots (wave q: q, q+4, ...),
+// so at any moment the workgroup reads a contiguous kilobyte of each row.
 // ---------------------------------------------------------------------------
 
 __device__ __forceinline__ void dma16(const void* gsrc, void* lds_dst) {
@@ -300,103 +309,167 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Wait until slot j's 4 direct loads have landed.  Per iteration the wave
-// issues XL activation loads and then the 4 direct loads of a slot S-1
+#ifndef TPMLP_DECODE_SLOTS
+#define TPMLP_DECODE_SLOTS 2
+#endif
+#ifndef TPMLP_DECODE_XPF
+#define TPMLP_DECODE_XPF 1
+#endif
+
+// Wait until slot j's D direct loads have landed.  Per iteration the wave
+// issues XL activation loads and then the D direct loads of a slot S-1
 // ahead; the first S-1 slots were issued up front without activation loads.
-template <int S, int XL, int J>
+template <int S, int XL, int D, int J>
 __device__ __forceinline__ void wait_slot_peeled(int j) {
   if constexpr (J >= S - 2) {
-    wait_vm<(S - 2) * (XL + 4)>();
+    wait_vm<(S - 2) * (XL + D)>();
   } else {
-    if (j == J) wait_vm<4 * (S - 2 - J) + J * (XL + 4)>();
-    else wait_slot_peeled<S, XL, J + 1>(j);
+    if (j == J) wait_vm<D * (S - 2 - J) + J * (XL + D)>();
+    else wait_slot_peeled<S, XL, D, J + 1>(j);
   }
 }
 
-// Stream slots [j_beg, j_end) of this wave's 16-row block through its ring
-// and accumulate the MFMAs.  dsrc[i]: this lane's source for direct-load
-// instruction i of slot 0 (row 4i + lane/16, pre-swizzled chunk); slot j
-// adds j*256 bytes.  xrow/xok: activation rows of the NT token blocks.
-template <int NT, bool FP8, int S>
-__device__ __forceinline__ void stream_rows(f32x4 (&acc)[NT], uint8_t* ring,
-                                            const uint8_t* const (&dsrc)[4],
+// Stream slots j_beg, j_beg + jstep, ... (nsl of them) of this wave's RB
+// row blocks through its ring and accumulate the MFMAs.  dsrc[rb][i]: this
+// lane's source for direct-load instruction i of block rb in slot 0 (row
+// 4i + lane/16, pre-swizzled chunk); slot j adds j*256 bytes.  xrow/xok:
+// activation rows of the NT token blocks.
+template <int NT, int RB, bool FP8, int S>
+__device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
+                                            const uint8_t* const (&dsrc)[RB][4],
                                             const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
-                                            int j_beg, int j_end, int lane) {
+                                            int j_beg, int nsl, int jstep, int lane) {
   constexpr int STEPS = FP8 ? 8 : 4;          // MFMA k-steps (32 k) per slot
   constexpr int KS = FP8 ? 256 : 128;         // k per slot
   constexpr int XL = STEPS * NT;              // activation loads per slot
+  constexpr int D = 4 * RB;                   // direct loads per slot
+  constexpr int SLOT = RB * 4096;             // bytes per slot
   const int r = lane & 15, g = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  const int nsl = j_end - j_beg;
   if (nsl <= 0) return;
   auto issue = [&](int j, int pos) {
-    uint8_t* dst = ring + pos * 4096;
+    uint8_t* dst = ring + pos * SLOT;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(dsrc[i] + (int64_t)j * 256, dst + i * 1024);
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * 256, dst + rb * 4096 + i * 1024);
   };
+  auto load_x = [&](int j, u32x4 (&xf)[STEPS][NT]) {
 #pragma unroll
-  for (int p = 0; p < S - 1; ++p) issue(j_beg + min(p, nsl - 1), p);
-  int pos = 0;
-  for (int jj = 0; jj < nsl; ++jj) {
-    wait_slot_peeled<S, XL, 0>(jj);
-    const int j = j_beg + jj;
-    // activation fragments of this slot (from L2; same k order as the weights)
-    u32x4 xf[STEPS][NT];
+    for (int b = 0; b < NT; ++b)
 #pragma unroll
-    for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-      for (int b = 0; b < NT; ++b) {
+      for (int st = 0; st < STEPS; ++st) {
         const int ko = FP8 ? (64 * (st >> 1) + 16 * g + 8 * (st & 1)) : (32 * st + 8 * g);
         xf[st][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (int64_t)j * KS + ko);
       }
-    const int npos = pos == 0 ? S - 1 : pos - 1;   // ring slot of j+S-1 (held j-1)
-    issue(j_beg + min(jj + S - 1, nsl - 1), npos);
-    const uint8_t* sl = ring + pos * 4096 + r * 256;
+  };
+  auto compute = [&](int pos, const u32x4 (&xf)[STEPS][NT]) {
+    const uint8_t* sl = ring + pos * SLOT + r * 256;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-      bf16x8 w;
-      if constexpr (FP8) {
-        if ((st & 1) == 0) {
-          const int q = 4 * (st >> 1) + g;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sl + ((q ^ r) * 16));
-          w = fp8x8_to_bf16x8(v[0], v[1]);
 #pragma unroll
-          for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[b]);
-          w = fp8x8_to_bf16x8(v[2], v[3]);
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (FP8) {
+          if ((st & 1) == 0) {
+            const int q = 4 * (st >> 1) + g;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
+            const bf16x8 w0 = fp8x8_to_bf16x8(v[0], v[1]);
+            const bf16x8 w1 = fp8x8_to_bf16x8(v[2], v[3]);
 #pragma unroll
-          for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st + 1][b] : zero), acc[b]);
+            for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w0, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[rb][b]);
+#pragma unroll
+            for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w1, as_bf16x8(xok[b] ? xf[st + 1][b] : zero), acc[rb][b]);
+          }
+        } else {
+          const int q = 4 * st + g;
+          const bf16x8 w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16)));
+#pragma unroll
+          for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[rb][b]);
         }
-      } else {
-        const int q = 4 * st + g;
-        w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + ((q ^ r) * 16)));
-#pragma unroll
-        for (int b = 0; b < NT; ++b) acc[b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[b]);
       }
     }
+  };
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(j_beg + min(p, nsl - 1) * jstep, p);
+#if TPMLP_DECODE_XPF
+  // Activation fragments one slot ahead in a second register set: the loads
+  // of slot jj+1 (activations and weights) fly while slot jj is computed.
+  // Issue order per step: activations of jj+1, then the direct loads of
+  // jj+S-1, so the wait before slot jj covers both of its groups.
+  static_assert(S == 2, "activation prefetch assumes a two-slot ring");
+  u32x4 xa[STEPS][NT], xb[STEPS][NT];
+  load_x(j_beg, xa);
+  auto step = [&](int jj, u32x4 (&cur)[STEPS][NT], u32x4 (&nxt)[STEPS][NT]) {
+    wait_vm<0>();
+    load_x(j_beg + min(jj + 1, nsl - 1) * jstep, nxt);
+    issue(j_beg + min(jj + 1, nsl - 1) * jstep, (jj + 1) & 1);
+    compute(jj & 1, cur);
+  };
+  int jj = 0;
+  for (; jj + 1 < nsl; jj += 2) {
+    step(jj, xa, xb);
+    step(jj + 1, xb, xa);
+  }
+  if (jj < nsl) step(jj, xa, xb);
+#else
+  int pos = 0;
+  for (int jj = 0; jj < nsl; ++jj) {
+    wait_slot_peeled<S, XL, D, 0>(jj);
+    const int j = j_beg + jj * jstep;
+    // activation fragments of this slot (from L2; same k order as the weights)
+    u32x4 xf[STEPS][NT];
+    load_x(j, xf);
+    const int npos = pos == 0 ? S - 1 : pos - 1;   // ring slot of j+S-1 (held j-1)
+    issue(j_beg + min(jj + S - 1, nsl - 1) * jstep, npos);
+    compute(pos, xf);
     pos = pos == S - 1 ? 0 : pos + 1;
   }
+#endif
   __builtin_amdgcn_s_waitcnt(0);  // the ring's last (duplicate) loads are done before LDS is reused
 }
 
-// Direct-load sources of this lane for the 4 instructions of slot 0: rows
-// 4i + lane/16 of the block, logical chunk (lane%16) ^ row.
+// Direct-load sources of this lane for the 4 instructions of a block in slot
+// 0: rows 4i + lane/16 of the block, logical chunk (lane%16) ^ row.
 template <typename RowPtr>
-__device__ __forceinline__ void stream_sources(const uint8_t* (&dsrc)[4], int lane, int k_byte0, RowPtr row_ptr) {
+__device__ __forceinline__ void stream_sources(const uint8_t* (&dsrc)[4], int lane, RowPtr row_ptr) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = 4 * i + (lane >> 4);
     const int c = (lane & 15) ^ row;
-    dsrc[i] = row_ptr(row) + k_byte0 + c * 16;
+    dsrc[i] = row_ptr(row) + c * 16;
   }
 }
 
-#ifndef TPMLP_DECODE_SLOTS
-#define TPMLP_DECODE_SLOTS 2
-#endif
+// Cross-wave sum for the streaming kernels: like reduce_waves, but through
+// the (no longer needed) ring memory instead of a separate LDS array.
+template <int NT, int RB, int WAVES, typename Epi>
+__device__ __forceinline__ void reduce_waves_ring(f32x4 (&acc)[RB][NT], f32x4* buf, int wave, int lane,
+                                                  Epi epi) {
+  __syncthreads();  // every wave is done with its ring
+#pragma unroll
+  for (int r = 0; r < RB; ++r)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) buf[(wave * RB * NT + r * NT + b) * 64 + lane] = acc[r][b];
+  __syncthreads();
+  for (int q = wave; q < RB * NT; q += WAVES) {
+    f32x4 s = buf[q * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) s = s + buf[(w * RB * NT + q) * 64 + lane];
+    epi(q / NT, q % NT, s);
+  }
+}
+
 constexpr int kSlots = TPMLP_DECODE_SLOTS;
 constexpr int kSWaves = 4;
 
-template <int NT, bool FP8>
+// Slots of this wave: interleaved over the workgroup's waves.
+__device__ __forceinline__ void wave_slots(int nslots, int wave, int& j_beg, int& nsl, int& jstep) {
+  j_beg = wave;
+  jstep = kSWaves;
+  nsl = (nslots - wave + kSWaves - 1) / kSWaves;
+}
+
+template <int NT, int RB, bool FP8>
 __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ x, int64_t ldx,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
@@ -404,20 +477,22 @@ __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
     uint16_t* __restrict__ a_out, int64_t lda) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * 4096];
+  static_assert(kSWaves * RB * NT * 64 * 16 <= kSWaves * kSlots * RB * 4096, "reduction fits the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * RB * 4096];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
-  const int c0 = blockIdx.x * 8;
-  // 16-row block: rows 0-7 gate channels c0..c0+7, rows 8-15 the same channels' up rows
-  auto row_ptr = [&](int row) {
-    const int ch = min(c0 + (row & 7), I_s - 1);
-    return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
-  };
-  const int nslots = h / KS;
-  const int j_beg = (wave * nslots) / kSWaves, j_end = ((wave + 1) * nslots) / kSWaves;
-  const uint8_t* dsrc[4];
-  stream_sources(dsrc, lane, 0, row_ptr);
+  const int c0 = blockIdx.x * 8 * RB;
+  // row block rb: rows 0-7 gate channels c0+8rb..+7, rows 8-15 the same channels' up rows
+  const uint8_t* dsrc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    stream_sources(dsrc[rb], lane, [&](int row) {
+      const int ch = min(c0 + 8 * rb + (row & 7), I_s - 1);
+      return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
+    });
+  int j_beg, nsl, jstep;
+  wave_slots(h / KS, wave, j_beg, nsl, jstep);
   const uint16_t* xrow[NT];
   bool xok[NT];
 #pragma unroll
@@ -426,17 +501,21 @@ __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
     xok[b] = tok < M;
     xrow[b] = x + (int64_t)min(tok, M - 1) * ldx;
   }
-  f32x4 acc[1][NT];
+  f32x4 acc[RB][NT];
 #pragma unroll
-  for (int b = 0; b < NT; ++b) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_rows<NT, FP8, kSlots>(acc[0], ring_all + wave * kSlots * 4096, dsrc, xrow, xok, j_beg, j_end, lane);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_rows<NT, RB, FP8, kSlots>(acc, ring_all + wave * kSlots * RB * 4096, dsrc, xrow, xok, j_beg, nsl,
+                                   jstep, lane);
 
-  reduce_waves<NT, 1, kSWaves>(acc, wave, lane, [&](int, int b, f32x4 v) {
+  reduce_waves_ring<NT, RB, kSWaves>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
+                                     [&](int rb, int b, f32x4 v) {
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
     if (grp < 2) {
-      const int ch = c0 + 4 * grp;
+      const int ch = c0 + 8 * rb + 4 * grp;
       const int tok = b * 16 + row16;
       if (tok < M && ch < I_s) {
         float a[4];
@@ -456,23 +535,26 @@ __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
   });
 }
 
-template <int NT, bool FP8>
+template <int NT, int RB, bool FP8>
 __global__ __launch_bounds__(kSWaves * 64) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
     float* __restrict__ p, int64_t ldp) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * 4096];
+  static_assert(kSWaves * RB * NT * 64 * 16 <= kSWaves * kSlots * RB * 4096, "reduction fits the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * RB * 4096];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
-  const int n0 = blockIdx.x * 16;
-  auto row_ptr = [&](int row) { return wd + (int64_t)min(n0 + row, h - 1) * ldw * EB; };
-  const int nslots = I_s / KS;
-  const int j_beg = (wave * nslots) / kSWaves, j_end = ((wave + 1) * nslots) / kSWaves;
-  const uint8_t* dsrc[4];
-  stream_sources(dsrc, lane, 0, row_ptr);
+  const int n0 = blockIdx.x * 16 * RB;
+  const uint8_t* dsrc[RB][4];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+    stream_sources(dsrc[rb], lane,
+                   [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
+  int j_beg, nsl, jstep;
+  wave_slots(I_s / KS, wave, j_beg, nsl, jstep);
   const uint16_t* xrow[NT];
   bool xok[NT];
 #pragma unroll
@@ -481,13 +563,17 @@ __global__ __launch_bounds__(kSWaves * 64) void down_stream_kernel(
     xok[b] = tok < M;
     xrow[b] = a_in + (int64_t)min(tok, M - 1) * lda;
   }
-  f32x4 acc[1][NT];
+  f32x4 acc[RB][NT];
 #pragma unroll
-  for (int b = 0; b < NT; ++b) acc[0][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_rows<NT, FP8, kSlots>(acc[0], ring_all + wave * kSlots * 4096, dsrc, xrow, xok, j_beg, j_end, lane);
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_rows<NT, RB, FP8, kSlots>(acc, ring_all + wave * kSlots * RB * 4096, dsrc, xrow, xok, j_beg, nsl,
+                                   jstep, lane);
 
-  reduce_waves<NT, 1, kSWaves>(acc, wave, lane, [&](int, int b, f32x4 v) {
-    const int f = n0 + 4 * grp;
+  reduce_waves_ring<NT, RB, kSWaves>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
+                                     [&](int rb, int b, f32x4 v) {
+    const int f = n0 + 16 * rb + 4 * grp;
     const int tok = b * 16 + row16;
     if (tok < M && f < h) {
       if constexpr (FP8) {
@@ -530,15 +616,23 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
                 a.ldw_down, a.sd, a.p, a.ldp);
 }
 
+#ifndef TPMLP_DECODE_RB_WIDE
+#define TPMLP_DECODE_RB_WIDE 2
+#endif
+
 template <int NT, bool FP8>
 hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
+  // Up to 16 tokens: one 16-row block per wave (most workgroups).  More
+  // tokens: RB row blocks share each activation fragment (see above).
+  constexpr int RB = NT == 1 ? 1 : TPMLP_DECODE_RB_WIDE;
   const dim3 block(kSWaves * 64);
-  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, FP8>, dim3((a.I_s + 7) / 8), block, 0,
-                        stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
+  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
+                        block, 0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
                         (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
   if (e != hipSuccess) return e;
-  return launch(K_DOWN_DECODE, down_stream_kernel<NT, FP8>, dim3((a.h + 15) / 16), block, 0, stream, a.M,
-                a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd, a.p, a.ldp);
+  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB, FP8>, dim3((a.h + 16 * RB - 1) / (16 * RB)), block, 0,
+                stream, a.M, a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd,
+                a.p, a.ldp);
 }
 
 #ifndef TPMLP_DECODE_V2

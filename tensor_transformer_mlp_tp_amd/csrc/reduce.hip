@@ -16,23 +16,53 @@ namespace tpmlp {
 
 namespace {
 
-constexpr int kReduceThreads = 256;
-constexpr int kReduceUnroll = 2;
+// Block shape: 1024 threads for the large (bandwidth-bound) reduces, 256 for
+// small ones (a decode partial of a few hundred KB), where more blocks
+// finish sooner.
+#ifndef TPMLP_REDUCE_THREADS
+#define TPMLP_REDUCE_THREADS 1024
+#endif
+#ifndef TPMLP_REDUCE_UNROLL
+#define TPMLP_REDUCE_UNROLL 1
+#endif
+constexpr int kReduceThreadsSmall = 256;
+constexpr int64_t kReduceSmallN4 = 1 << 20;
+#ifndef TPMLP_REDUCE_NT
+#define TPMLP_REDUCE_NT 1
+#endif
+constexpr int kReduceThreads = TPMLP_REDUCE_THREADS;
+constexpr int kReduceUnroll = TPMLP_REDUCE_UNROLL;
 
-template <int T>
-__global__ __launch_bounds__(kReduceThreads) void partial_reduce_kernel(
+__device__ __forceinline__ f32x4 ld4(const f32x4* p) {
+#if TPMLP_REDUCE_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ void st4(f32x4 v, f32x4* p) {
+#if TPMLP_REDUCE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+template <int T, int THREADS>
+__global__ __launch_bounds__(THREADS) void partial_reduce_kernel(
     PartialPtrs ptrs, int t_rt, float* __restrict__ out, int64_t n) {
   const int t = T > 0 ? T : t_rt;
   const int64_t n4 = n >> 2;
-  const int64_t base = (int64_t)blockIdx.x * (kReduceThreads * kReduceUnroll) + threadIdx.x;
+  const int64_t base = (int64_t)blockIdx.x * (THREADS * kReduceUnroll) + threadIdx.x;
 
   f32x4 acc[kReduceUnroll];
   bool ok[kReduceUnroll];
 #pragma unroll
   for (int u = 0; u < kReduceUnroll; ++u) {
-    const int64_t idx = base + (int64_t)u * kReduceThreads;
+    const int64_t idx = base + (int64_t)u * THREADS;
     ok[u] = idx < n4;
-    acc[u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptrs.p[0]) + idx)
+    acc[u] = ok[u] ? ld4(reinterpret_cast<const f32x4*>(ptrs.p[0]) + idx)
                    : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   if constexpr (T > 0) {
@@ -41,8 +71,8 @@ __global__ __launch_bounds__(kReduceThreads) void partial_reduce_kernel(
     for (int j = 1; j < T; ++j)
 #pragma unroll
       for (int u = 0; u < kReduceUnroll; ++u) {
-        const int64_t idx = base + (int64_t)u * kReduceThreads;
-        v[j - 1][u] = ok[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptrs.p[j]) + idx)
+        const int64_t idx = base + (int64_t)u * THREADS;
+        v[j - 1][u] = ok[u] ? ld4(reinterpret_cast<const f32x4*>(ptrs.p[j]) + idx)
                             : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
@@ -53,15 +83,15 @@ __global__ __launch_bounds__(kReduceThreads) void partial_reduce_kernel(
     for (int j = 1; j < t; ++j) {
 #pragma unroll
       for (int u = 0; u < kReduceUnroll; ++u) {
-        const int64_t idx = base + (int64_t)u * kReduceThreads;
-        if (ok[u]) acc[u] = acc[u] + __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(ptrs.p[j]) + idx);
+        const int64_t idx = base + (int64_t)u * THREADS;
+        if (ok[u]) acc[u] = acc[u] + ld4(reinterpret_cast<const f32x4*>(ptrs.p[j]) + idx);
       }
     }
   }
 #pragma unroll
   for (int u = 0; u < kReduceUnroll; ++u) {
-    const int64_t idx = base + (int64_t)u * kReduceThreads;
-    if (ok[u]) __builtin_nontemporal_store(acc[u], reinterpret_cast<f32x4*>(out) + idx);
+    const int64_t idx = base + (int64_t)u * THREADS;
+    if (ok[u]) st4(acc[u], reinterpret_cast<f32x4*>(out) + idx);
   }
 
   // n % 4 trailing elements: the first block's first threads, scalar.
@@ -76,22 +106,28 @@ __global__ __launch_bounds__(kReduceThreads) void partial_reduce_kernel(
   }
 }
 
+template <int THREADS>
+hipError_t launch_reduce_shape(const PartialPtrs& ptrs, int t, float* out, int64_t n, hipStream_t stream) {
+  const int64_t n4 = n >> 2;
+  const int64_t per_block = (int64_t)THREADS * kReduceUnroll;
+  int64_t blocks = (n4 + per_block - 1) / per_block;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(THREADS);
+  switch (t) {
+    case 1: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<1, THREADS>, grid, block, 0, stream, ptrs, t, out, n);
+    case 2: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<2, THREADS>, grid, block, 0, stream, ptrs, t, out, n);
+    case 4: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<4, THREADS>, grid, block, 0, stream, ptrs, t, out, n);
+    case 8: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<8, THREADS>, grid, block, 0, stream, ptrs, t, out, n);
+    default: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<0, THREADS>, grid, block, 0, stream, ptrs, t, out, n);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_partial_reduce(const PartialPtrs& ptrs, int t, float* out, int64_t n,
                                  hipStream_t stream) {
-  const int64_t n4 = n >> 2;
-  const int64_t per_block = (int64_t)kReduceThreads * kReduceUnroll;
-  int64_t blocks = (n4 + per_block - 1) / per_block;
-  if (blocks < 1) blocks = 1;
-  const dim3 grid((unsigned)blocks), block(kReduceThreads);
-  switch (t) {
-    case 1: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<1>, grid, block, 0, stream, ptrs, t, out, n);
-    case 2: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<2>, grid, block, 0, stream, ptrs, t, out, n);
-    case 4: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<4>, grid, block, 0, stream, ptrs, t, out, n);
-    case 8: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<8>, grid, block, 0, stream, ptrs, t, out, n);
-    default: return launch(K_PARTIAL_REDUCE, partial_reduce_kernel<0>, grid, block, 0, stream, ptrs, t, out, n);
-  }
+  if ((n >> 2) < kReduceSmallN4) return launch_reduce_shape<kReduceThreadsSmall>(ptrs, t, out, n, stream);
+  return launch_reduce_shape<kReduceThreads>(ptrs, t, out, n, stream);
 }
 
 }  // namespace tpmlp
