@@ -428,6 +428,97 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
   __builtin_amdgcn_s_waitcnt(0);  // the ring's last (duplicate) loads are done before LDS is reused
 }
 
+// Same stream with the activations staged through the ring too: each slot
+// also holds the NT token blocks' activation rows for its k range (16 rows x
+// 2*KS bytes per block, direct-loaded whole 128-byte lines, 16-byte chunks
+// XOR-swizzled by row), and the MFMA fragments are read from LDS.  Register
+// fragment loads touch 16 rows x 64 bytes per instruction, half of each line;
+// with more than 16 tokens that doubled line traffic, not the weight stream,
+// is what bounds the kernel.  xsrc[b][i]: this lane's source for activation
+// load i of token block b in slot 0; slot j adds j * 2*KS bytes.
+template <int NT, int RB, bool FP8, int S>
+__device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ring,
+                                               const uint8_t* const (&dsrc)[RB][4],
+                                               const uint8_t* const (&xsrc)[NT][FP8 ? 8 : 4],
+                                               const bool (&xok)[NT], int j_beg, int nsl, int jstep,
+                                               int lane) {
+  constexpr int STEPS = FP8 ? 8 : 4;          // MFMA k-steps (32 k) per slot
+  constexpr int KS = FP8 ? 256 : 128;         // k per slot
+  constexpr int XROWB = 2 * KS;               // activation bytes per row per slot
+  constexpr int XI = FP8 ? 8 : 4;             // activation loads per token block
+  constexpr int XBLK = 16 * XROWB;
+  constexpr int D = 4 * RB + NT * XI;         // direct loads per slot
+  constexpr int SLOT = RB * 4096 + NT * XBLK; // bytes per slot
+  const int r = lane & 15, g = lane >> 4;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if (nsl <= 0) return;
+  auto issue = [&](int j, int pos) {
+    uint8_t* dst = ring + pos * SLOT;
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * 256, dst + rb * 4096 + i * 1024);
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int i = 0; i < XI; ++i)
+        dma16(xsrc[b][i] + (int64_t)j * XROWB, dst + RB * 4096 + b * XBLK + i * 1024);
+  };
+  auto compute = [&](int pos) {
+    const uint8_t* sl = ring + pos * SLOT + r * 256;
+    const uint8_t* xl = ring + pos * SLOT + RB * 4096 + r * XROWB;
+#pragma unroll
+    for (int st = 0; st < STEPS; ++st) {
+      u32x4 xf[NT];
+      const int xc = FP8 ? (8 * (st >> 1) + 2 * g + (st & 1)) : (4 * st + g);
+#pragma unroll
+      for (int b = 0; b < NT; ++b) xf[b] = *reinterpret_cast<const u32x4*>(xl + b * XBLK + ((xc ^ r) * 16));
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        bf16x8 w;
+        if constexpr (FP8) {
+          const int q = 4 * (st >> 1) + g;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
+          w = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+        } else {
+          const int q = 4 * st + g;
+          w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16)));
+        }
+#pragma unroll
+        for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w, as_bf16x8(xok[b] ? xf[b] : zero), acc[rb][b]);
+      }
+    }
+  };
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p) issue(j_beg + min(p, nsl - 1) * jstep, p);
+  int pos = 0;
+  for (int jj = 0; jj < nsl; ++jj) {
+    wait_slot_peeled<S, 0, D, 0>(jj);
+    const int npos = pos == 0 ? S - 1 : pos - 1;   // ring slot of j+S-1 (held j-1)
+    issue(j_beg + min(jj + S - 1, nsl - 1) * jstep, npos);
+    compute(pos);
+    pos = pos == S - 1 ? 0 : pos + 1;
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the ring's last (duplicate) loads are done before LDS is reused
+}
+
+// Activation direct-load sources of this lane: token block b, load i covers
+// rows i*RPI + lane/LPR of the block (LPR lanes per row), logical chunk
+// (lane % LPR) ^ row.
+template <bool FP8, int NT, typename XPtr>
+__device__ __forceinline__ void stream_x_sources(const uint8_t* (&xsrc)[NT][FP8 ? 8 : 4], int lane, XPtr xptr) {
+  constexpr int LPR = FP8 ? 32 : 16;
+  constexpr int RPI = 64 / LPR;
+#pragma unroll
+  for (int b = 0; b < NT; ++b)
+#pragma unroll
+    for (int i = 0; i < (FP8 ? 8 : 4); ++i) {
+      const int row = i * RPI + lane / LPR;
+      const int c = (lane % LPR) ^ row;
+      xsrc[b][i] = reinterpret_cast<const uint8_t*>(xptr(b * 16 + row)) + c * 16;
+    }
+}
+
 // Direct-load sources of this lane for the 4 instructions of a block in slot
 // 0: rows 4i + lane/16 of the block, logical chunk (lane%16) ^ row.
 template <typename RowPtr>
@@ -462,23 +553,37 @@ __device__ __forceinline__ void reduce_waves_ring(f32x4 (&acc)[RB][NT], f32x4* b
 constexpr int kSlots = TPMLP_DECODE_SLOTS;
 constexpr int kSWaves = 4;
 
-// Slots of this wave: interleaved over the workgroup's waves.
+// Slots of this wave: interleaved over the workgroup's WV waves.
+template <int WV>
 __device__ __forceinline__ void wave_slots(int nslots, int wave, int& j_beg, int& nsl, int& jstep) {
   j_beg = wave;
-  jstep = kSWaves;
-  nsl = (nslots - wave + kSWaves - 1) / kSWaves;
+  jstep = WV;
+  nsl = (nslots - wave + WV - 1) / WV;
 }
 
-template <int NT, int RB, bool FP8>
-__global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
+// Ring geometry of a streaming kernel: slot bytes and ring depth.  With the
+// activations in the ring (XD) the slots are larger, so those kernels run two
+// waves per workgroup with three slots each.
+template <int NT, int RB, bool FP8, bool XD>
+struct StreamShape {
+  static constexpr int WV = XD ? 2 : kSWaves;
+  static constexpr int S = XD ? 3 : kSlots;
+  static constexpr int SLOT = RB * 4096 + (XD ? NT * 16 * 2 * (FP8 ? 256 : 128) : 0);
+  static constexpr int RING = WV * S * SLOT;
+  static_assert(WV * RB * NT * 1024 <= RING, "the cross-wave sums fit the ring");
+  static_assert(RING <= 160 * 1024, "LDS");
+};
+
+template <int NT, int RB, bool FP8, bool XD>
+__global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateup_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ x, int64_t ldx,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
     const float* __restrict__ sg, const float* __restrict__ su,
     uint16_t* __restrict__ a_out, int64_t lda) {
+  using SS = StreamShape<NT, RB, FP8, XD>;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
-  static_assert(kSWaves * RB * NT * 64 * 16 <= kSWaves * kSlots * RB * 4096, "reduction fits the rings");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * RB * 4096];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[SS::RING];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
@@ -492,25 +597,29 @@ __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
       return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
     });
   int j_beg, nsl, jstep;
-  wave_slots(h / KS, wave, j_beg, nsl, jstep);
-  const uint16_t* xrow[NT];
+  wave_slots<SS::WV>(h / KS, wave, j_beg, nsl, jstep);
   bool xok[NT];
 #pragma unroll
-  for (int b = 0; b < NT; ++b) {
-    const int tok = b * 16 + row16;
-    xok[b] = tok < M;
-    xrow[b] = x + (int64_t)min(tok, M - 1) * ldx;
-  }
+  for (int b = 0; b < NT; ++b) xok[b] = b * 16 + row16 < M;
   f32x4 acc[RB][NT];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_rows<NT, RB, FP8, kSlots>(acc, ring_all + wave * kSlots * RB * 4096, dsrc, xrow, xok, j_beg, nsl,
-                                   jstep, lane);
+  uint8_t* ring = ring_all + wave * SS::S * SS::SLOT;
+  if constexpr (XD) {
+    const uint8_t* xsrc[NT][FP8 ? 8 : 4];
+    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return x + (int64_t)min(tok, M - 1) * ldx; });
+    stream_rows_xd<NT, RB, FP8, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+  } else {
+    const uint16_t* xrow[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) xrow[b] = x + (int64_t)min(b * 16 + row16, M - 1) * ldx;
+    stream_rows<NT, RB, FP8, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+  }
 
-  reduce_waves_ring<NT, RB, kSWaves>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
-                                     [&](int rb, int b, f32x4 v) {
+  reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
+                                    [&](int rb, int b, f32x4 v) {
     f32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
@@ -535,15 +644,15 @@ __global__ __launch_bounds__(kSWaves * 64) void gateup_stream_kernel(
   });
 }
 
-template <int NT, int RB, bool FP8>
-__global__ __launch_bounds__(kSWaves * 64) void down_stream_kernel(
+template <int NT, int RB, bool FP8, bool XD>
+__global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
     float* __restrict__ p, int64_t ldp) {
+  using SS = StreamShape<NT, RB, FP8, XD>;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
-  static_assert(kSWaves * RB * NT * 64 * 16 <= kSWaves * kSlots * RB * 4096, "reduction fits the rings");
-  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[kSWaves * kSlots * RB * 4096];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_all[SS::RING];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
@@ -554,25 +663,29 @@ __global__ __launch_bounds__(kSWaves * 64) void down_stream_kernel(
     stream_sources(dsrc[rb], lane,
                    [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
   int j_beg, nsl, jstep;
-  wave_slots(I_s / KS, wave, j_beg, nsl, jstep);
-  const uint16_t* xrow[NT];
+  wave_slots<SS::WV>(I_s / KS, wave, j_beg, nsl, jstep);
   bool xok[NT];
 #pragma unroll
-  for (int b = 0; b < NT; ++b) {
-    const int tok = b * 16 + row16;
-    xok[b] = tok < M;
-    xrow[b] = a_in + (int64_t)min(tok, M - 1) * lda;
-  }
+  for (int b = 0; b < NT; ++b) xok[b] = b * 16 + row16 < M;
   f32x4 acc[RB][NT];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_rows<NT, RB, FP8, kSlots>(acc, ring_all + wave * kSlots * RB * 4096, dsrc, xrow, xok, j_beg, nsl,
-                                   jstep, lane);
+  uint8_t* ring = ring_all + wave * SS::S * SS::SLOT;
+  if constexpr (XD) {
+    const uint8_t* xsrc[NT][FP8 ? 8 : 4];
+    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return a_in + (int64_t)min(tok, M - 1) * lda; });
+    stream_rows_xd<NT, RB, FP8, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+  } else {
+    const uint16_t* xrow[NT];
+#pragma unroll
+    for (int b = 0; b < NT; ++b) xrow[b] = a_in + (int64_t)min(b * 16 + row16, M - 1) * lda;
+    stream_rows<NT, RB, FP8, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+  }
 
-  reduce_waves_ring<NT, RB, kSWaves>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
-                                     [&](int rb, int b, f32x4 v) {
+  reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
+                                    [&](int rb, int b, f32x4 v) {
     const int f = n0 + 16 * rb + 4 * grp;
     const int tok = b * 16 + row16;
     if (tok < M && f < h) {
@@ -620,17 +733,25 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
 #define TPMLP_DECODE_RB_WIDE 2
 #endif
 
+#ifndef TPMLP_DECODE_XD
+#define TPMLP_DECODE_XD 1
+#endif
+
 template <int NT, bool FP8>
 hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
-  // Up to 16 tokens: one 16-row block per wave (most workgroups).  More
-  // tokens: RB row blocks share each activation fragment (see above).
+  // Up to 16 tokens: one 16-row block per wave, activations from registers
+  // (most workgroups).  More tokens: RB row blocks per wave share each
+  // activation fragment, and the activations come through the ring (where
+  // its slots fit the LDS: fp8 weights have twice the k per slot).
   constexpr int RB = NT == 1 ? 1 : TPMLP_DECODE_RB_WIDE;
-  const dim3 block(kSWaves * 64);
-  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
-                        block, 0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
-                        (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+  constexpr bool XD = TPMLP_DECODE_XD && NT >= 2 && (!FP8 || NT == 2);
+  const dim3 block(StreamShape<NT, RB, FP8, XD>::WV * 64);
+  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8, XD>,
+                        dim3((a.I_s + 8 * RB - 1) / (8 * RB)), block, 0, stream, a.M, a.h, a.I_s,
+                        (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg,
+                        a.su, (uint16_t*)a.a, a.lda);
   if (e != hipSuccess) return e;
-  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB, FP8>, dim3((a.h + 16 * RB - 1) / (16 * RB)), block, 0,
+  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB, FP8, XD>, dim3((a.h + 16 * RB - 1) / (16 * RB)), block, 0,
                 stream, a.M, a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd,
                 a.p, a.ldp);
 }
