@@ -56,21 +56,6 @@ namespace tpmlp {
 
 namespace {
 
-#ifndef TPMLP_PREFILL_SCHED
-#define TPMLP_PREFILL_SCHED 0
-#endif
-#ifndef TPMLP_PREFILL_SPREAD
-#define TPMLP_PREFILL_SPREAD 0
-#endif
-#ifndef TPMLP_PREFILL_TOUCH_AHEAD
-#define TPMLP_PREFILL_TOUCH_AHEAD 1
-#endif
-constexpr int TOUCH_AHEAD = TPMLP_PREFILL_TOUCH_AHEAD;  // k-tiles between a stage's L2 touch and its loads
-#ifndef TPMLP_PREFILL_MIDBAR
-#define TPMLP_PREFILL_MIDBAR 0
-#endif
-constexpr bool MIDBAR = TPMLP_PREFILL_MIDBAR != 0;
-
 constexpr int BM = 256;      // tokens per tile
 constexpr int BN = 256;      // weight rows per tile
 constexpr int THREADS = 256; // 4 waves
@@ -132,31 +117,6 @@ __device__ __forceinline__ void sched_substep() {
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
   __builtin_amdgcn_sched_group_barrier(0x008, 16 - NDS, 0);
-}
-
-// One sub-step's 16 MFMAs with its NDS fragment reads spread evenly among
-// them (one after every 16/NDS MFMAs), so the workgroup's LDS read demand is
-// not bunched into half of the sub-step.
-template <int NDS>
-__device__ __forceinline__ void sched_substep_spread() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i % (16 / NDS) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-  }
-}
-
-// Like sched_substep, with NVM of the stage's direct loads threaded in as
-// well (one after each of the first NVM MFMAs), so the matrix unit is not left
-// idle while the next stage's loads are issued.
-template <int NDS, int NVM>
-__device__ __forceinline__ void sched_substep_vm() {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    if (i < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if (i < NVM) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-  }
 }
 
 struct TileCoord {
@@ -377,57 +337,12 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       __builtin_amdgcn_sched_group_barrier(0x200, LPS, 0);
       buf ^= 1;
     }
-  } else if constexpr (MIDBAR && NS == 2 && KSUB == 4) {
-    // Fragments read two sub-steps ahead (slot = sub-step), and the barrier
-    // in the middle of the k-tile: after sub-step 1's MFMAs every fragment of
-    // stage kt has been read, so each wave waits for its loads of stage
-    // kt+1, meets the others, refills stage kt's buffer with stage kt+2 and
-    // reads sub-steps 0 and 1 of stage kt+1 under sub-steps 2 and 3's MFMAs.
-    // Up to 16 fragment reads are in flight per wave, which the LDS needs to
-    // stream at the rate the matrix unit consumes them.
-    issue_stage(0, 0);
-    touch_stage(min(1, KT - 1));
-    wait_vmcnt<2>();
-    lds_barrier();
-    issue_stage(min(1, KT - 1), 1);
-    touch_stage(min(2, KT - 1));
-    bf16x8 wf[4][4], xf[4][4];
-    read_frags(lds, lds + XBYTES, 0, wf[0], xf[0]);
-    read_frags(lds, lds + XBYTES, 1, wf[1], xf[1]);
-    int buf = 0;
-    auto mma = [&](int slot) {
-  #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-  #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[slot][cb], xf[slot][tb], acc[cb][tb]);
-    };
-    for (int kt = 0; kt < KT; ++kt) {
-      const uint8_t* sx = lds + buf * SBYTES;
-      read_frags(sx, sx + XBYTES, 2, wf[2], xf[2]);
-      mma(0);
-      read_frags(sx, sx + XBYTES, 3, wf[3], xf[3]);
-      mma(1);
-      sched_substep_spread<FP8 ? 4 : 8>();
-      sched_substep_spread<8>();
-      wait_vmcnt<2>();
-      lds_barrier();
-      issue_stage(min(kt + 2, KT - 1), buf);
-      touch_stage(min(kt + 3, KT - 1));
-      const uint8_t* nx = lds + (buf ^ 1) * SBYTES;
-      read_frags(nx, nx + XBYTES, 0, wf[0], xf[0]);
-      mma(2);
-      read_frags(nx, nx + XBYTES, 1, wf[1], xf[1]);
-      mma(3);
-      __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
-      sched_substep_spread<FP8 ? 4 : 8>();
-      sched_substep_spread<8>();
-      buf ^= 1;
-    }
   } else {
   #pragma unroll
-    for (int s = 0; s < NS - 1; ++s) issue_stage(min(s, KT - 1), s);
-  #pragma unroll
-    for (int s = 0; s < TOUCH_AHEAD; ++s) touch_stage(min(NS - 1 + s, KT - 1));
+    for (int s = 0; s < NS - 1; ++s) {
+      issue_stage(min(s, KT - 1), s);
+      touch_stage(min(s + 1, KT - 1));
+    }
     int buf = 0;
     for (int kt = 0; kt < KT; ++kt) {
       // this wave's loads of stage kt have landed (younger: the touch issued
@@ -436,7 +351,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       lds_barrier();                  // ... and every wave's; stage kt-1 is no longer read
       const int nbuf = buf == 0 ? NS - 1 : buf - 1;   // (kt + NS - 1) % NS
       issue_stage(min(kt + NS - 1, KT - 1), nbuf);
-      touch_stage(min(kt + NS - 1 + TOUCH_AHEAD, KT - 1));
+      touch_stage(min(kt + NS, KT - 1));
       const uint8_t* sx = lds + buf * SBYTES;
       const uint8_t* sw = sx + XBYTES;
       bf16x8 wf[2][4], xf[2][4];
@@ -452,27 +367,6 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       // scheduling: direct loads of stage kt+NS-1, fragments of sub-step 0,
       // then each sub-step's MFMAs with the next sub-step's reads threaded in
       // (fp8 odd sub-steps read activations only)
-#if TPMLP_PREFILL_SCHED
-      // fragments of sub-step 0 first; the stage's direct loads ride along
-      // with the first MFMAs of sub-steps 0 and 1
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      constexpr int VM0 = LPS + 2 < 16 ? LPS + 2 : 16;
-      sched_substep_vm<FP8 ? 4 : 8, VM0>();
-      if constexpr (KSUB == 4) {
-        sched_substep_vm<8, LPS + 2 - VM0>();
-        sched_substep<FP8 ? 4 : 8>();
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-#elif TPMLP_PREFILL_SPREAD
-      __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      sched_substep_spread<FP8 ? 4 : 8>();
-      if constexpr (KSUB == 4) {
-        sched_substep_spread<8>();
-        sched_substep_spread<FP8 ? 4 : 8>();
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-#else
       __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       sched_substep<FP8 ? 4 : 8>();
@@ -481,7 +375,6 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
         sched_substep<FP8 ? 4 : 8>();
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-#endif
       buf = buf == NS - 1 ? 0 : buf + 1;
     }
 }
@@ -565,7 +458,6 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
 #ifndef TPMLP_PREFILL_REG
 #define TPMLP_PREFILL_REG 0
 #endif
-
 
 template <bool FP8>
 hipError_t run_prefill(const ShardArgs& a, hipStream_t stream) {
