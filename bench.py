@@ -19,8 +19,11 @@ HBM byte counters).
 
 The ``roofline`` object is for the step's dominant kernel: algorithmic bytes
 (or FLOP) of its launches divided by their summed durations, taken from HIP
-events that the library attaches to each of its own kernel dispatches during
-the timed steps.  Its ``traffic`` is the HBM bytes per launch that
+events that the library attaches to each of that kernel's dispatches during
+the timed steps (only that kernel's: an event-timed launch costs the host
+about 20 us against 3 us for a plain one, and timing every launch would make
+the decode loop host-bound).  The other kernels' durations come from a
+further pass with every launch timed.  Its ``traffic`` is the HBM bytes per launch that
 rocprofv3's FETCH_SIZE and WRITE_SIZE counters recorded for that kernel
 (scaled by what they read for the copy), kept as text under profiles/ with
 the hash of the kernel's sources at the time; it is null when no record
@@ -173,13 +176,23 @@ class Phase:
 
 # ----------------------------------------------------------------------------- timing
 
-def timed(tp, step_fn, steps, warmup):
+def timed(tp, step_fn, steps, warmup, kinds):
+    """Wall time of `steps` steps after `warmup`, with HIP-event timing of the
+    library's launches of the kernel kinds `kinds` only (an event-timed launch
+    costs the host several times a plain one, which would otherwise make the
+    loop host-bound)."""
     import torch
+    # warm-up with the same timing on: counts the timed launches of a step, so
+    # that every event the timed steps use exists before the clock starts
+    tp.profile_collect()
+    tp.profile_enable(True, kinds)
     for i in range(warmup):
         step_fn(i)
     torch.cuda.synchronize()
-    tp.profile_collect()          # drop anything recorded before the timed region
-    tp.profile_enable(True)
+    tp.profile_enable(False)
+    launches = sum(c for _, c in tp.profile_collect().values())
+    tp.profile_reserve(launches * steps // max(warmup, 1) + 64)
+    tp.profile_enable(True, kinds)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
@@ -189,6 +202,20 @@ def timed(tp, step_fn, steps, warmup):
     tp.profile_enable(False)
     prof = tp.profile_collect()
     return elapsed, prof
+
+
+def breakdown(tp, step_fn, steps, first):
+    """Per-kind kernel durations from a further `steps` steps with every
+    launch event-timed (a pass of its own: not used for throughput)."""
+    import torch
+    torch.cuda.synchronize()
+    tp.profile_collect()
+    tp.profile_enable(True)
+    for i in range(steps):
+        step_fn(first + i)
+    torch.cuda.synchronize()
+    tp.profile_enable(False)
+    return tp.profile_collect()
 
 
 def cpu_info():
@@ -245,7 +272,8 @@ def bench_decode70b(tp, args):
             ph.run(wset)
 
     steps, warmup = args.steps or 400, args.warmup if args.warmup is not None else 40
-    elapsed, prof = timed(tp, step, steps, warmup)
+    elapsed, prof = timed(tp, step, steps, warmup, ["gateup_decode"])
+    prof_all = breakdown(tp, step, steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
     value = step_bytes * steps / elapsed / 1e9
     gu_bytes = steps * sum(workloads.gateup_bytes(ph.M, h, I_s) for ph in phases)
@@ -253,7 +281,7 @@ def bench_decode70b(tp, args):
     red_bytes = steps * sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)
     kern = {}
     for name, b in (("gateup_decode", gu_bytes), ("down_decode", dn_bytes), ("partial_reduce", red_bytes)):
-        ms, cnt = prof.get(name, (0.0, 0))
+        ms, cnt = prof_all.get(name, (0.0, 0))
         kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
                       "GBps": b / (ms * 1e-3) / 1e9 if ms > 0 else None}
     ms, cnt = prof["gateup_decode"]
@@ -262,7 +290,7 @@ def bench_decode70b(tp, args):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
             "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases}}
-    fwd_time_ms = sum(prof[k][0] for k in ("gateup_decode", "down_decode")) / steps
+    fwd_time_ms = sum(prof_all[k][0] for k in ("gateup_decode", "down_decode")) / steps
     fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
     # parity sample at full size, outside the timed region: the last step used set (warmup+steps-1)
     parity = None
@@ -286,7 +314,9 @@ def bench_decode70b(tp, args):
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
                forward_only={"GBps": round(fwd_bytes / (fwd_time_ms * 1e-3) / 1e9, 1),
                              "us_per_step": round(fwd_time_ms * 1e3, 2)},
-               kernels=kern, parity_err_M1=parity)
+               kernels=kern, kernels_note="kernels and forward_only: a further pass of the same "
+                                          "number of steps with every launch event-timed",
+               parity_err_M1=parity)
     if not args.no_cpu_baseline:
         host_parts = [np.zeros(ph.M * h, np.float32) for ph in phases]
 
@@ -315,7 +345,9 @@ def bench_prefill(tp, args, cfg_id, M, label):
         ph.run(sets[0])
 
     steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
-    elapsed, prof = timed(tp, step, steps, warmup)
+    elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"])
+    prof = breakdown(tp, step, steps, warmup + steps)
+    prof["gateup_prefill"] = prof_gu["gateup_prefill"]   # the timed region's own record
     flops = ph.flops()
     value = flops * steps / elapsed / 1e12
     gu_ms, gu_n = prof["gateup_prefill"]
@@ -361,8 +393,10 @@ def bench_fp8(tp, args):
     dec = Phase(tp, 4, 32, h, I_s, t, "bf16", "e4m3fn", False)
     pre = Phase(tp, 4, 2048, h, I_s, t, "bf16", "e4m3fn", False)
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
-    el_d, prof_d = timed(tp, lambda i: dec.run(sets[i % len(sets)]), steps, warmup)
-    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), max(10, steps // 10), 3)
+    el_d, prof_d = timed(tp, lambda i: dec.run(sets[i % len(sets)]), steps, warmup, ["gateup_decode"])
+    prof_d.update({k: v for k, v in breakdown(tp, lambda i: dec.run(sets[i % len(sets)]), steps,
+                                              warmup + steps).items() if k != "gateup_decode"})
+    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), max(10, steps // 10), 3, ["gateup_prefill", "down_prefill"])
     dec_bytes = dec.bytes()
     dec_gbs = dec_bytes * steps / el_d / 1e9
     pre_tf = pre.flops() * max(10, steps // 10) / el_p / 1e12
@@ -393,7 +427,7 @@ def bench_reduce(tp, args, cfg_id):
     parts = [torch.from_numpy(p).cuda() for p in parts_host]
     out = torch.empty_like(parts[0])
     steps, warmup = args.steps or 50, args.warmup if args.warmup is not None else 5
-    elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup)
+    elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup, ["partial_reduce"])
     b = workloads.reduce_bytes(n, t)
     ms, cnt = prof["partial_reduce"]
     achieved = b * cnt / (ms * 1e-3) / 1e9
@@ -420,7 +454,7 @@ def bench_copy(tp, args):
     src = torch.ones(n, dtype=torch.float32, device="cuda")
     out = torch.empty_like(src)
     steps, warmup = args.steps or 20, args.warmup if args.warmup is not None else 3
-    elapsed, prof = timed(tp, lambda i: tp.partial_reduce([src], out=out), steps, warmup)
+    elapsed, prof = timed(tp, lambda i: tp.partial_reduce([src], out=out), steps, warmup, ["partial_reduce"])
     b = workloads.reduce_bytes(n, 1)
     ms, cnt = prof["partial_reduce"]
     achieved = b * cnt / (ms * 1e-3) / 1e9

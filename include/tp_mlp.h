@@ -171,8 +171,20 @@ int32_t tp_kernel_kind_count(void);
 /* Static name of a kernel kind (NULL if out of range). */
 const char* tp_kernel_kind_name(int32_t kind);
 
-/* Turn per-kernel timing on (1) or off (0). */
-tp_status tp_profile_enable(int32_t on);
+/*
+ * Select the kernel kinds to time: bit i of `kinds` times the kernels of
+ * kind i, 0 turns timing off, -1 times every kind.  A timed launch costs the
+ * host noticeably more than a plain one (on the order of 20 us against 3 us
+ * here), so a throughput loop should time only the kinds it reports.
+ */
+tp_status tp_profile_enable(int32_t kinds);
+
+/*
+ * Create event pairs up front for at least `records` timed launches, so
+ * that timing does not create events (a slow host call) inside a measured
+ * loop; without it the record grows on demand.  Synchronous.
+ */
+tp_status tp_profile_reserve(int64_t records);
 
 /*
  * Synchronise the recorded events and add, for each kind i < n_kinds,

@@ -192,8 +192,24 @@ def kernel_kinds():
     return [lib.tp_kernel_kind_name(i).decode() for i in range(lib.tp_kernel_kind_count())]
 
 
-def profile_enable(on=True):
-    _lib.check(_lib.load().tp_profile_enable(1 if on else 0))
+def profile_enable(on=True, kinds=None):
+    """Time the library's launches of the given kernel kinds (names from
+    kernel_kinds(); None = all) while on; off with on=False."""
+    if not on:
+        mask = 0
+    elif kinds is None:
+        mask = -1
+    else:
+        names = kernel_kinds()
+        mask = 0
+        for k in kinds:
+            mask |= 1 << names.index(k)
+    _lib.check(_lib.load().tp_profile_enable(mask))
+
+
+def profile_reserve(records):
+    """Create timing events for `records` launches ahead of a measured loop."""
+    _lib.check(_lib.load().tp_profile_reserve(int(records)))
 
 
 def profile_collect():

@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "tp_kernel_kind_name",
     "tp_profile_enable",
     "tp_profile_collect",
+    "tp_profile_reserve",
 )
 
 
@@ -73,6 +74,8 @@ def load():
     lib.tp_profile_enable.restype = c_i32
     lib.tp_profile_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64), c_i32]
     lib.tp_profile_collect.restype = c_i32
+    lib.tp_profile_reserve.argtypes = [c_i64]
+    lib.tp_profile_reserve.restype = c_i32
     _lib = lib
     return lib
 

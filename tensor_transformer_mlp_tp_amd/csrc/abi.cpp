@@ -103,13 +103,25 @@ struct ProfRec {
   int kind;
 };
 
-bool g_prof_on = false;
+uint32_t g_prof_mask = 0;   // bit i: time kernels of kind i
 std::vector<ProfRec> g_prof_pool;
 size_t g_prof_used = 0;
 
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
     "partial_reduce", "gateup_f32", "down_f32"};
+
+// Appends one start/stop event pair to the timing pool.
+bool prof_grow() {
+  ProfRec r{};
+  if (hipEventCreate(&r.start) != hipSuccess) return false;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return false;
+  }
+  g_prof_pool.push_back(r);
+  return true;
+}
 
 }  // namespace
 
@@ -118,16 +130,8 @@ namespace tpmlp {
 void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop) {
   *start = nullptr;
   *stop = nullptr;
-  if (!g_prof_on) return;
-  if (g_prof_used == g_prof_pool.size()) {
-    ProfRec r{};
-    if (hipEventCreate(&r.start) != hipSuccess) return;
-    if (hipEventCreate(&r.stop) != hipSuccess) {
-      (void)hipEventDestroy(r.start);
-      return;
-    }
-    g_prof_pool.push_back(r);
-  }
+  if (kind < 0 || kind >= 32 || !((g_prof_mask >> kind) & 1u)) return;
+  if (g_prof_used == g_prof_pool.size() && !prof_grow()) return;
   ProfRec& r = g_prof_pool[g_prof_used++];
   r.kind = kind;
   *start = r.start;
@@ -268,8 +272,15 @@ TP_API const char* tp_kernel_kind_name(int32_t kind) {
   return kKindNames[kind];
 }
 
-TP_API tp_status tp_profile_enable(int32_t on) {
-  g_prof_on = on != 0;
+TP_API tp_status tp_profile_enable(int32_t kinds) {
+  g_prof_mask = (uint32_t)kinds;
+  return TP_OK;
+}
+
+TP_API tp_status tp_profile_reserve(int64_t records) {
+  if (records < 0) return fail(TP_ERR_INVALID_ARG, "negative record count");
+  while ((int64_t)g_prof_pool.size() < records)
+    if (!prof_grow()) return fail(TP_ERR_HIP, "hipEventCreate failed while reserving timing records");
   return TP_OK;
 }
 
