@@ -58,7 +58,6 @@ namespace {
 
 constexpr int BM = 256;      // tokens per tile
 constexpr int BN = 256;      // weight rows per tile
-constexpr int THREADS = 256; // 4 waves
 constexpr int GROUP_M = 4;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -107,16 +106,16 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Scheduling groups for one sub-step: its 16 MFMAs with NDS fragment reads
+// Scheduling groups for one sub-step: its NMF MFMAs with NDS fragment reads
 // of the next sub-step threaded one after each of the first NDS MFMAs.
-template <int NDS>
+template <int NDS, int NMF>
 __device__ __forceinline__ void sched_substep() {
 #pragma unroll
   for (int i = 0; i < NDS; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, 16 - NDS, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, NMF - NDS, 0);
 }
 
 struct TileCoord {
@@ -136,13 +135,17 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   return TileCoord{first_m + i % gsize, i / gsize};
 }
 
-template <bool SWIGLU, bool FP8, int BK, int NS, bool REG>
-__global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
+template <bool SWIGLU, bool FP8, int BK, int NS, int WV>
+__global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const uint16_t* __restrict__ act, int64_t ld_act,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
     const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
     int64_t ld_out, int tiles_m, int tiles_n) {
   static_assert(BK == 32 || BK == 64, "stage depth");
+  static_assert(WV == 4 || WV == 8, "waves per workgroup");
+  constexpr int WN = WV / 2;                   // waves across the weight rows (2 across tokens)
+  constexpr int CB = BN / WN / 32;             // 32-row weight blocks per wave
+  constexpr int TB = BM / 2 / 32;              // 32-token blocks per wave
   constexpr int EB = FP8 ? 1 : 2;              // weight bytes per element
   constexpr int KSUB = BK / 16;                // MFMA sub-steps per stage
   constexpr int XROWB = BK * 2;                // bytes per LDS activation row
@@ -150,8 +153,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   constexpr int XBYTES = BM * XROWB;
   constexpr int WBYTES = BN * WROWB;
   constexpr int SBYTES = XBYTES + WBYTES;
-  constexpr int XINST = XBYTES / 1024 / 4;     // 1 KB direct loads per wave per stage
-  constexpr int WINST = WBYTES / 1024 / 4;
+  constexpr int XINST = XBYTES / 1024 / WV;    // 1 KB direct loads per wave per stage
+  constexpr int WINST = WBYTES / 1024 / WV;
   constexpr int LPS = XINST + WINST;           // loads per wave per stage
   constexpr int TILE_N = SWIGLU ? BN / 2 : BN; // output columns per tile
   constexpr int XRPI = 1024 / XROWB;           // rows per 1 KB load
@@ -159,13 +162,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   constexpr int XCH = XROWB / 16;              // 16-byte chunks per row
   constexpr int WCH = WROWB / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + 4 * 512];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + WV * 512];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int r32 = lane & 31, g = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
 
   const TileCoord tc = tile_of_block(blockIdx.x, tiles_m, tiles_n);
   const int m0 = tc.tm * BM;
@@ -202,12 +205,14 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   // 4-byte direct-to-LDS load into a scratch area nobody reads (no VGPR is
   // written, so nothing waits on it).  The misses of a k-tile are then in
   // flight one k-tile before its own loads, which find the lines in L2.
-  const uint8_t* tx = reinterpret_cast<const uint8_t*>(act + (int64_t)min(m0 + tid, M - 1) * ld_act);
+  // (with 8 waves the upper 256 threads touch the same lines again)
+  const int trow = tid & 255;
+  const uint8_t* tx = reinterpret_cast<const uint8_t*>(act + (int64_t)min(m0 + trow, M - 1) * ld_act);
   const uint8_t* tw;
   if constexpr (SWIGLU)
-    tw = (tid < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (tid & (BN / 2 - 1)), N - 1) * ldw * EB;
+    tw = (trow < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (trow & (BN / 2 - 1)), N - 1) * ldw * EB;
   else
-    tw = w0 + (int64_t)min(n0 + tid, N - 1) * ldw * EB;
+    tw = w0 + (int64_t)min(n0 + trow, N - 1) * ldw * EB;
   uint8_t* tdst = lds + NS * SBYTES + wave * 512;
   auto touch_stage = [&](int kt) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tx + (int64_t)kt * BK * 2),
@@ -223,41 +228,25 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
 #pragma unroll
     for (int i = 0; i < WINST; ++i) load_lds16(wsrc[i] + (int64_t)kt * BK * EB, wdst + i * 1024);
   };
-  // Register-staged alternative: the same 16-byte pieces go global -> VGPR
-  // -> LDS (same LDS slots as the direct loads would fill).
-  u32x4 rx[REG ? XINST : 1], rw[REG ? WINST : 1];
-  auto load_regs = [&](int kt) {
+  // ---- fragment rows of this lane inside a stage.  Gate/up: the wave's
+  // first CB/2 weight blocks are gate rows of its channels, the last CB/2 the
+  // same channels' up rows.
+  int wrow[CB], xrow[TB];
 #pragma unroll
-    for (int i = 0; i < XINST; ++i) rx[i] = *reinterpret_cast<const u32x4*>(xsrc[i] + (int64_t)kt * BK * 2);
-#pragma unroll
-    for (int i = 0; i < WINST; ++i) rw[i] = *reinterpret_cast<const u32x4*>(wsrc[i] + (int64_t)kt * BK * EB);
-  };
-  auto store_regs = [&](int buf) {
-    uint8_t* xdst = lds + buf * SBYTES + wave * XINST * 1024 + lane * 16;
-    uint8_t* wdst = lds + buf * SBYTES + XBYTES + wave * WINST * 1024 + lane * 16;
-#pragma unroll
-    for (int i = 0; i < XINST; ++i) *reinterpret_cast<u32x4*>(xdst + i * 1024) = rx[i];
-#pragma unroll
-    for (int i = 0; i < WINST; ++i) *reinterpret_cast<u32x4*>(wdst + i * 1024) = rw[i];
-  };
-
-  // ---- fragment rows of this lane inside a stage
-  int wrow[4], xrow[4];
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
+  for (int cb = 0; cb < CB; ++cb) {
     if constexpr (SWIGLU)
-      wrow[cb] = (cb < 2 ? 0 : BN / 2) + wn * 64 + (cb & 1) * 32 + r32;
+      wrow[cb] = (cb < CB / 2 ? 0 : BN / 2) + wn * (BN / 2 / WN) + (cb % (CB / 2)) * 32 + r32;
     else
-      wrow[cb] = wn * 128 + cb * 32 + r32;
+      wrow[cb] = wn * (BN / WN) + cb * 32 + r32;
   }
 #pragma unroll
-  for (int tb = 0; tb < 4; ++tb) xrow[tb] = wm * 128 + tb * 32 + r32;
+  for (int tb = 0; tb < TB; ++tb) xrow[tb] = wm * (BM / 2) + tb * 32 + r32;
 
-  f32x16 acc[4][4];
+  f32x16 acc[CB][TB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb)
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
 
@@ -266,8 +255,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   // 16-byte chunk kk+g (16 codes) once; its low 8 codes serve sub-step kk and
   // its high 8 codes sub-step kk+1, so the activation chunk of 8 elements is
   // 4*(kk/2) + 2g + kk%2.
-  u32x4 wq[4];
-  auto read_w = [&](const uint8_t* sw, int kk, int cb, bf16x8 (&wf)[4]) {
+  u32x4 wq[CB];
+  auto read_w = [&](const uint8_t* sw, int kk, int cb, bf16x8 (&wf)[CB]) {
     const int r = wrow[cb];
     if constexpr (FP8) {
       if ((kk & 1) == 0) {
@@ -281,19 +270,19 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       wf[cb] = as_bf16x8(lds_read16(sw + r * WROWB + ((ch ^ swz<WROWB>(r)) * 16)));
     }
   };
-  auto read_x = [&](const uint8_t* sx, int kk, int tb, bf16x8 (&xf)[4]) {
+  auto read_x = [&](const uint8_t* sx, int kk, int tb, bf16x8 (&xf)[TB]) {
     const int r = xrow[tb];
     const int ch = FP8 ? (4 * (kk >> 1) + 2 * g + (kk & 1)) : (2 * kk + g);
     xf[tb] = as_bf16x8(lds_read16(sx + r * XROWB + ((ch ^ swz<XROWB>(r)) * 16)));
   };
   // Read order = order of first use by the sub-step's MFMAs (cb-major):
-  // w0, x0..x3, then w1..w3.
-  auto read_frags = [&](const uint8_t* sx, const uint8_t* sw, int kk, bf16x8 (&wf)[4], bf16x8 (&xf)[4]) {
+  // w0, all x, then the other w.
+  auto read_frags = [&](const uint8_t* sx, const uint8_t* sw, int kk, bf16x8 (&wf)[CB], bf16x8 (&xf)[TB]) {
     read_w(sw, kk, 0, wf);
 #pragma unroll
-    for (int tb = 0; tb < 4; ++tb) read_x(sx, kk, tb, xf);
+    for (int tb = 0; tb < TB; ++tb) read_x(sx, kk, tb, xf);
 #pragma unroll
-    for (int cb = 1; cb < 4; ++cb) read_w(sw, kk, cb, wf);
+    for (int cb = 1; cb < CB; ++cb) read_w(sw, kk, cb, wf);
   };
 
   // Main loop, one barrier per k-tile.  Stages 0 .. NS-2 are issued up front;
@@ -305,39 +294,7 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   // scheduling groups thread the fragment reads of sub-step 1 between the
   // MFMAs of sub-step 0.
   const int KT = K / BK;
-  if constexpr (REG) {
-    static_assert(NS == 2, "register staging uses two LDS stages");
-    load_regs(0);
-    store_regs(0);
-    int buf = 0;
-    for (int kt = 0; kt < KT; ++kt) {
-      lds_barrier();  // every wave's writes of stage kt are done; stage kt-1 is no longer read
-      load_regs(min(kt + 1, KT - 1));
-      const uint8_t* sx = lds + buf * SBYTES;
-      const uint8_t* sw = sx + XBYTES;
-      bf16x8 wf[2][4], xf[2][4];
-      read_frags(sx, sw, 0, wf[0], xf[0]);
-#pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk) {
-        if (kk + 1 < KSUB) read_frags(sx, sw, kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-          for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
-      }
-      store_regs(buf ^ 1);
-      __builtin_amdgcn_sched_group_barrier(0x020, LPS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      sched_substep<FP8 ? 4 : 8>();
-      if constexpr (KSUB == 4) {
-        sched_substep<8>();
-        sched_substep<FP8 ? 4 : 8>();
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, LPS, 0);
-      buf ^= 1;
-    }
-  } else {
+  {
   #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
       issue_stage(min(s, KT - 1), s);
@@ -354,27 +311,28 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
       touch_stage(min(kt + NS, KT - 1));
       const uint8_t* sx = lds + buf * SBYTES;
       const uint8_t* sw = sx + XBYTES;
-      bf16x8 wf[2][4], xf[2][4];
+      bf16x8 wf[2][CB], xf[2][TB];
       read_frags(sx, sw, 0, wf[0], xf[0]);
   #pragma unroll
       for (int kk = 0; kk < KSUB; ++kk) {
         if (kk + 1 < KSUB) read_frags(sx, sw, kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
   #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < CB; ++cb)
   #pragma unroll
-          for (int tb = 0; tb < 4; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+          for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
       }
       // scheduling: direct loads of stage kt+NS-1, fragments of sub-step 0,
       // then each sub-step's MFMAs with the next sub-step's reads threaded in
       // (fp8 odd sub-steps read activations only)
+      constexpr int NMF = CB * TB, NRD = CB + TB, NRX = FP8 ? TB : CB + TB;
       __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      sched_substep<FP8 ? 4 : 8>();
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      sched_substep<NRX, NMF>();
       if constexpr (KSUB == 4) {
-        sched_substep<8>();
-        sched_substep<FP8 ? 4 : 8>();
+        sched_substep<NRD, NMF>();
+        sched_substep<NRX, NMF>();
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
       buf = buf == NS - 1 ? 0 : buf + 1;
     }
 }
@@ -385,10 +343,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   if constexpr (SWIGLU) {
     uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
+    for (int cb = 0; cb < CB / 2; ++cb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int ch = n0 + wn * 64 + cb * 32 + 8 * j + 4 * g;  // channels ch .. ch+3
+        const int ch = n0 + wn * (BN / 2 / WN) + cb * 32 + 8 * j + 4 * g;  // channels ch .. ch+3
         if (ch >= N) continue;
         float sgv[4] = {1.f, 1.f, 1.f, 1.f}, suv[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (FP8) {
@@ -399,13 +357,13 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
           }
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int tok = m0 + wm * 128 + tb * 32 + r32;
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
           if (tok >= M) continue;
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float gv = acc[cb][tb][4 * j + i], uv = acc[cb + 2][tb][4 * j + i];
+            float gv = acc[cb][tb][4 * j + i], uv = acc[cb + CB / 2][tb][4 * j + i];
             if constexpr (FP8) {
               gv *= sgv[i];
               uv *= suv[i];
@@ -420,10 +378,10 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
   } else {
     float* p = reinterpret_cast<float*>(out);
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int f = n0 + wn * 128 + cb * 32 + 8 * j + 4 * g;  // features f .. f+3
+        const int f = n0 + wn * (BN / WN) + cb * 32 + 8 * j + 4 * g;  // features f .. f+3
         if (f >= N) continue;
         float sv[4] = {1.f, 1.f, 1.f, 1.f};
         if constexpr (FP8) {
@@ -431,8 +389,8 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
           for (int i = 0; i < 4; ++i) sv[i] = s0[f + i];
         }
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const int tok = m0 + wm * 128 + tb * 32 + r32;
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
           if (tok >= M) continue;
           f32x4 v;
 #pragma unroll
@@ -455,28 +413,28 @@ __global__ __launch_bounds__(THREADS, 1) void gemm_kernel(
 #ifndef TPMLP_PREFILL_NS_FP8
 #define TPMLP_PREFILL_NS_FP8 3
 #endif
-#ifndef TPMLP_PREFILL_REG
-#define TPMLP_PREFILL_REG 0
+#ifndef TPMLP_PREFILL_WAVES
+#define TPMLP_PREFILL_WAVES 4
 #endif
 
 template <bool FP8>
 hipError_t run_prefill(const ShardArgs& a, hipStream_t stream) {
   constexpr int BK = TPMLP_PREFILL_BK;
   constexpr int NS = FP8 ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
-  constexpr bool REG = TPMLP_PREFILL_REG != 0;
+  constexpr int WV = TPMLP_PREFILL_WAVES;
   const int tiles_m = (a.M + BM - 1) / BM;
-  const dim3 block(THREADS);
+  const dim3 block(WV * 64);
   {
     const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
-    hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, BK, NS, REG>, grid, block, 0, stream, a.M, a.I_s,
+    hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.I_s,
                           a.h, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
                           (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m, tiles_n);
     if (e != hipSuccess) return e;
   }
   const int tiles_n = (a.h + BN - 1) / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
-  return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8, BK, NS, REG>, grid, block, 0, stream, a.M, a.h, a.I_s,
+  return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.h, a.I_s,
                 (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
                 a.ldw_down, a.sd, (const float*)nullptr, (void*)a.p, a.ldp, tiles_m, tiles_n);
 }
