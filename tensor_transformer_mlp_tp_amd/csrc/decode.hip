@@ -567,8 +567,8 @@ __device__ __forceinline__ void wave_slots(int nslots, int wave, int& j_beg, int
 template <int NT, int RB, bool FP8, bool XD>
 struct StreamShape {
   static constexpr int WV = XD ? 2 : kSWaves;
-  static constexpr int S = XD ? 3 : kSlots;
   static constexpr int SLOT = RB * 4096 + (XD ? NT * 16 * 2 * (FP8 ? 256 : 128) : 0);
+  static constexpr int S = XD ? (WV * 3 * SLOT <= 160 * 1024 ? 3 : 2) : kSlots;
   static constexpr int RING = WV * S * SLOT;
   static_assert(WV * RB * NT * 1024 <= RING, "the cross-wave sums fit the ring");
   static_assert(RING <= 160 * 1024, "LDS");
@@ -732,6 +732,12 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
 #ifndef TPMLP_DECODE_RB_WIDE
 #define TPMLP_DECODE_RB_WIDE 2
 #endif
+#ifndef TPMLP_DECODE_RB_XD_FP8_GU
+#define TPMLP_DECODE_RB_XD_FP8_GU 4
+#endif
+#ifndef TPMLP_DECODE_RB_XD_FP8_DN
+#define TPMLP_DECODE_RB_XD_FP8_DN 2
+#endif
 
 #ifndef TPMLP_DECODE_XD
 #define TPMLP_DECODE_XD 1
@@ -743,17 +749,17 @@ hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
   // (most workgroups).  More tokens: RB row blocks per wave share each
   // activation fragment, and the activations come through the ring (where
   // its slots fit the LDS: fp8 weights have twice the k per slot).
-  constexpr int RB = NT == 1 ? 1 : TPMLP_DECODE_RB_WIDE;
   constexpr bool XD = TPMLP_DECODE_XD && NT >= 2 && (!FP8 || NT == 2);
-  const dim3 block(StreamShape<NT, RB, FP8, XD>::WV * 64);
-  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8, XD>,
-                        dim3((a.I_s + 8 * RB - 1) / (8 * RB)), block, 0, stream, a.M, a.h, a.I_s,
-                        (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg,
-                        a.su, (uint16_t*)a.a, a.lda);
+  constexpr int RB_GU = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
+  constexpr int RB_DN = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
+  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB_GU, FP8, XD>,
+                        dim3((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU)), dim3(StreamShape<NT, RB_GU, FP8, XD>::WV * 64),
+                        0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
+                        (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
   if (e != hipSuccess) return e;
-  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB, FP8, XD>, dim3((a.h + 16 * RB - 1) / (16 * RB)), block, 0,
-                stream, a.M, a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd,
-                a.p, a.ldp);
+  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB_DN, FP8, XD>, dim3((a.h + 16 * RB_DN - 1) / (16 * RB_DN)),
+                dim3(StreamShape<NT, RB_DN, FP8, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.a,
+                a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd, a.p, a.ldp);
 }
 
 #ifndef TPMLP_DECODE_V2
