@@ -404,18 +404,30 @@ def bench_fp8(tp, args):
     gu_gbs = workloads.gateup_bytes(32, h, I_s, "bf16", "e4m3fn") * gu_n / (gu_ms * 1e-3) / 1e9
     pgu_ms, pgu_n = prof_p["gateup_prefill"]
     pgu_tf = 4 * 2048 * h * I_s * pgu_n / (pgu_ms * 1e-3) / 1e12
-    return dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
+    out = dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
                 ms_per_step=round(1e3 * el_d / steps, 5), higher_is_better=True, scaling="weak",
                 vs_baseline=None, dtype="bf16 (fp8 e4m3fn weights)", data="synthetic",
                 config={"workload": "70B-shaped TP=4 rank, fp8 e4m3fn weights + fp32 row scales: decode M=32 "
                                     "(value) and prefill M=2048", "h": h, "I_s": I_s, "t": t,
                         "weight_sets": len(sets)},
                 roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "gateup_decode"},
+                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                          "traffic": recorded_traffic("gateup_decode", "fp8_70b"), "kernel": "gateup_decode"},
                 prefill={"M": 2048, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
                          "gateup_TFLOPs": round(pgu_tf, 1), "kernels": {k: {"avg_us": 1e3 * v[0] / v[1]}
                                                                        for k, v in prof_p.items()}},
                 kernels={k: {"avg_us": 1e3 * v[0] / v[1]} for k, v in prof_d.items()})
+    if not args.no_cpu_baseline:
+        import oracle
+
+        def once():
+            oracle.rank_partial_from_storage(dec.x_host, "bf16", host0["w_gate"], host0["w_up"], host0["w_down"],
+                                             "e4m3fn", host0["s_gate"], host0["s_up"], host0["s_down"])
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(once, dec_bytes / 1e9, "GB/s",
+                                           "one M=32 rank partial from the fp8 weight bytes and scales "
+                                           "(the decode value's unit of work), repeated >= 10 s")
+    return out
 
 
 def bench_reduce(tp, args, cfg_id):
