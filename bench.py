@@ -145,7 +145,6 @@ class Phase:
         if with_reduce:
             others = workloads.make_partials(cfg_id, t - 1, M * h, weight_set=M)
             self.others = [torch.from_numpy(o).cuda() for o in others]
-            self.reduced = torch.empty(M * h, dtype=torch.float32, device="cuda")
 
         self.calls = {}
 
@@ -156,8 +155,9 @@ class Phase:
             fwd = self.tp.prepare_shard_forward(self.x, wset["w_gate"], wset["w_up"], wset["w_down"], t=self.t,
                                                 k=0, s_gate=wset["s_gate"], s_up=wset["s_up"],
                                                 s_down=wset["s_down"], partial=self.partial, workspace=self.ws)
-            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others, out=self.reduced) \
-                if self.with_reduce else None
+            # in place into the rank's own partial, as the all-reduce does
+            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others,
+                                                 out=self.partial.view(-1)) if self.with_reduce else None
             self.calls[key] = (fwd, red)
         fwd, red = self.calls[key]
         fwd()
@@ -292,11 +292,13 @@ def bench_decode70b(tp, args):
             "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases}}
     fwd_time_ms = sum(prof_all[k][0] for k in ("gateup_decode", "down_decode")) / steps
     fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
-    # parity sample at full size, outside the timed region: the last step used set (warmup+steps-1)
+    # parity sample at full size, outside the timed region: the M=1 forward alone on weight set 0
+    # (the step's reduce overwrites the partial in place)
     parity = None
     if not args.no_cpu_baseline:
         ph = phases[0]
-        step(0)  # set 0
+        ph.run(sets[0])
+        ph.calls[id(sets[0])][0]()
         import torch
         torch.cuda.synchronize()
         ref = oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
@@ -437,7 +439,9 @@ def bench_reduce(tp, args, cfg_id):
     n, t = c["reduce_n"], c["t"]
     parts_host = workloads.make_partials(cfg_id, t, n)
     parts = [torch.from_numpy(p).cuda() for p in parts_host]
-    out = torch.empty_like(parts[0])
+    # in place into partial 0, as the all-reduce leaves the sum in each rank's own buffer
+    # (the values grow step by step; the work and the bytes do not change)
+    out = parts[0]
     steps, warmup = args.steps or 50, args.warmup if args.warmup is not None else 5
     elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup, ["partial_reduce"])
     b = workloads.reduce_bytes(n, t)
@@ -447,7 +451,8 @@ def bench_reduce(tp, args, cfg_id):
     res = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="f32", data="synthetic",
-               config={"workload": "%d-way fp32 partial reduce of %d elements" % (t, n), "t": t, "n": n},
+               config={"workload": "%d-way fp32 partial reduce of %d elements, in place into partial 0"
+                                   % (t, n), "t": t, "n": n, "in_place": True},
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("partial_reduce", args.workload), "kernel": "partial_reduce"})
