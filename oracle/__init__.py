@@ -29,6 +29,10 @@ Sources (the web pages this build follows):
   "What must remain true about the layout" and "What must stay true after
   deployment": the split must compute the same function as the unsplit
   model, checked split-against-unsplit on a small configuration.
+* The same chapter, section 12.3.1 "Sequence Parallelism for LayerNorm and
+  Dropout": under sequence parallelism the all-reduce becomes a
+  reduce-scatter (rank k keeps the reduced rows of its sequence slice) and
+  the next column-parallel projection reads the all-gathered sequence.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, a library special case, the Megatron invariant,
@@ -43,6 +47,8 @@ from .mlp import (
     shard_slice,
     shard_of_full,
     fold_fp32,
+    gather_rows,
+    reduce_scatter_fp32,
     rank_partial_from_storage,
     rms_normalised_max_error,
 )
@@ -57,6 +63,8 @@ __all__ = [
     "shard_slice",
     "shard_of_full",
     "fold_fp32",
+    "gather_rows",
+    "reduce_scatter_fp32",
     "rank_partial_from_storage",
     "rms_normalised_max_error",
 ]

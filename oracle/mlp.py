@@ -97,6 +97,26 @@ def fold_fp32(partials):
     return y
 
 
+def gather_rows(blocks):
+    """All-gather of the t ranks' sequence slices: X is their row
+    concatenation, block j holding rows [j*s/t, (j+1)*s/t) (sequence
+    parallelism, section 12.3.1 of the arunshar.com chapter, step 3)."""
+    return np.concatenate([np.asarray(b) for b in blocks], axis=0)
+
+
+def reduce_scatter_fp32(partials, k):
+    """Rank k's part of the reduce-scatter that replaces the all-reduce under
+    sequence parallelism (section 12.3.1 of the arunshar.com chapter, step 1):
+    the fully reduced rows [k*rows/t, (k+1)*rows/t), t = len(partials), of the
+    same fixed-order float32 sum as fold_fp32."""
+    t = len(partials)
+    rows = np.asarray(partials[0]).shape[0]
+    if rows % t:
+        raise ValueError("rows must be a multiple of t")
+    r = rows // t
+    return fold_fp32([np.asarray(p)[k * r:(k + 1) * r] for p in partials])
+
+
 def _decode(arr, dtype):
     if dtype == "bf16":
         return bf16_bits_to_f64(arr)

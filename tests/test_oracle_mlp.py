@@ -234,3 +234,46 @@ def test_error_metric():
     out = np.array([3.5, -4.0])
     assert oracle.rms_normalised_max_error(out, ref) == pytest.approx(0.5 / math.sqrt(12.5))
     assert oracle.rms_normalised_max_error(ref, ref) == 0.0
+
+
+# ------------------------------------------------------------ sequence-parallel forms (12.3.1)
+
+def test_reduce_scatter_rows_closed_form():
+    # partial j, row i holds i * 1000 + j (exact in float32): rank k's rows of the
+    # sum are sum_j (i * 1000 + j) = t * i * 1000 + t (t - 1) / 2 for its rows i only
+    t, rows, cols = 4, 12, 5
+    parts = [np.repeat((np.arange(rows) * 1000.0 + j)[:, None], cols, axis=1).astype(np.float32)
+             for j in range(t)]
+    for k in range(t):
+        got = oracle.reduce_scatter_fp32(parts, k)
+        i = np.arange(k * rows // t, (k + 1) * rows // t)
+        want = (t * i * 1000.0 + t * (t - 1) / 2)[:, None] * np.ones(cols)
+        assert got.shape == (rows // t, cols)
+        assert np.array_equal(got, want.astype(np.float32))
+
+
+def test_reduce_scatter_tiles_the_full_fold():
+    # the t ranks' reduce-scatter outputs, stacked in rank order, are the full fold, bit for bit
+    rng = np.random.Generator(np.random.PCG64(17))
+    t = 8
+    parts = [(rng.standard_normal((16, 24)) * 10.0 ** rng.integers(-3, 4)).astype(np.float32) for _ in range(t)]
+    full = oracle.fold_fp32(parts)
+    stacked = np.concatenate([oracle.reduce_scatter_fp32(parts, k) for k in range(t)], axis=0)
+    assert np.array_equal(stacked.view(np.uint32), full.view(np.uint32))
+    with pytest.raises(ValueError):
+        oracle.reduce_scatter_fp32([p[:15] for p in parts], 0)
+
+
+def test_gather_rows_then_shard_is_the_unsplit_input():
+    # row blocks of a sequence, gathered, give back the sequence; the MLP of the
+    # gathered rows equals, row block by row block, the MLP of each block
+    rng = np.random.Generator(np.random.PCG64(18))
+    t, s, h, I = 4, 8, 6, 10
+    x = rng.standard_normal((s, h))
+    blocks = [x[j * s // t:(j + 1) * s // t] for j in range(t)]
+    assert np.array_equal(oracle.gather_rows(blocks), x)
+    wg, wu, wd = rng.standard_normal((I, h)), rng.standard_normal((I, h)), rng.standard_normal((h, I))
+    y = oracle.mlp_full(oracle.gather_rows(blocks), wg, wu, wd)
+    for j in range(t):
+        np.testing.assert_allclose(y[j * s // t:(j + 1) * s // t], oracle.mlp_full(blocks[j], wg, wu, wd),
+                                   rtol=1e-13, atol=1e-13)
