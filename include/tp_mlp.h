@@ -151,6 +151,55 @@ tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full,
 tp_status tp_partial_reduce(int64_t n, int32_t t, const float* const* partials,
                             float* out, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Sequence-parallel forms ("Chapter 12 Parallelism Strategies",
+ * arunshar.com, section 12.3.1: with sequence parallelism the all-reduce
+ * after the row-parallel projection becomes a reduce-scatter, rank k keeping
+ * the fully reduced rows of sequence positions [k*s/t, (k+1)*s/t), and the
+ * column-parallel projection that follows runs on the all-gathered
+ * sequence).  The tokens M play the role of the sequence positions.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * tp_mlp_shard_forward with the activation given as the t ranks' row blocks
+ * instead of one gathered matrix: x_blocks is a HOST array of t device
+ * pointers, block j holding rows [j*M/t, (j+1)*M/t) of X (M/t x h, leading
+ * dimension ldx).  The kernels read the rows from the blocks in place, so
+ * the gathered X is never formed.  Requires M % t == 0; every other argument,
+ * requirement and the result (bit for bit) are those of tp_mlp_shard_forward
+ * on the row-concatenated X.
+ */
+tp_status tp_mlp_shard_forward_sp(int64_t M, int64_t h, int64_t I_full,
+                                  int32_t t, int32_t k,
+                                  int32_t act_dtype, int32_t w_dtype,
+                                  const void* const* x_blocks, int64_t ldx,
+                                  const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                  const void* w_down, int64_t ldw_down,
+                                  const float* s_gate, const float* s_up,
+                                  const float* s_down,
+                                  float* partial, int64_t ldp,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* stream);
+
+/*
+ * Rank k's share of the reduce-scatter: for the t partials, each `rows` x
+ * row_len contiguous fp32 (row-major, no padding), out receives rows
+ * [k*rows/t, (k+1)*rows/t) of their left-fold sum, i.e. tp_partial_reduce
+ * over the n = rows/t * row_len elements starting at element k*n of every
+ * partial (same order, same bits).
+ *
+ *   rows, row_len   rows % t == 0; rows/t * row_len a multiple of 4 (else
+ *              TP_ERR_UNSUPPORTED); a zero count is a no-op.
+ *   t, k       1 <= t <= 64, 0 <= k < t.
+ *   partials   HOST array of t device pointers (16-byte aligned).
+ *   out        rows/t x row_len fp32, 16-byte aligned.  May be rank k's
+ *              slice of partials[0] (partials[0] + k*n, in place); must not
+ *              otherwise overlap the slices read.
+ */
+tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_t t, int32_t k,
+                                    const float* const* partials, float* out,
+                                    void* stream);
+
 /* Static text for a status code. */
 const char* tp_status_string(int32_t status);
 

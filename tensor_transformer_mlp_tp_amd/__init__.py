@@ -112,13 +112,44 @@ def prepare_shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=No
                           partial=None, workspace=None, stream=None):
     """Validate and marshal a shard_forward once; returns a PreparedCall
     (attribute ``partial`` is the output tensor)."""
-    device = x.device
-    for name, m in (("x", x), ("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+    return _prepare_forward([x], False, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, partial, workspace,
+                            stream)
+
+
+def shard_forward_sp(x_blocks, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,
+                     partial=None, workspace=None, stream=None):
+    """shard_forward with X given as the t ranks' row blocks (sequence-parallel
+    input, ``include/tp_mlp.h``: tp_mlp_shard_forward_sp): ``x_blocks`` is a
+    sequence of t (M/t, h) tensors with one leading dimension; the result
+    equals shard_forward on their row concatenation, bit for bit."""
+    call = prepare_shard_forward_sp(x_blocks, w_gate, w_up, w_down, t=t, k=k, s_gate=s_gate, s_up=s_up,
+                                    s_down=s_down, partial=partial, workspace=workspace, stream=stream)
+    call()
+    return call.partial
+
+
+def prepare_shard_forward_sp(x_blocks, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,
+                             partial=None, workspace=None, stream=None):
+    """Marshal a shard_forward_sp once; returns a PreparedCall."""
+    if len(x_blocks) != int(t):
+        raise ValueError("need t = %d row blocks, got %d" % (int(t), len(x_blocks)))
+    return _prepare_forward(list(x_blocks), True, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, partial,
+                            workspace, stream)
+
+
+def _prepare_forward(xs, sp, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, partial, workspace, stream):
+    x0 = xs[0]
+    device = x0.device
+    for j, xb in enumerate(xs):
+        _check_matrix("x" if not sp else "x_blocks[%d]" % j, xb, device)
+        if xb.shape != x0.shape or xb.dtype != x0.dtype or xb.stride(0) != x0.stride(0):
+            raise ValueError("row blocks must share shape, dtype and leading dimension")
+    for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
         _check_matrix(name, m, device)
-    M, h = x.shape
+    M, h = x0.shape[0] * len(xs), x0.shape[1]
     I_s = w_gate.shape[0]
     I_full = I_s * int(t)
-    act, wc = _act_code(x.dtype), _w_code(w_gate.dtype)
+    act, wc = _act_code(x0.dtype), _w_code(w_gate.dtype)
     if _w_code(w_up.dtype) != wc or _w_code(w_down.dtype) != wc:
         raise TypeError("w_gate, w_up and w_down must share a dtype")
     if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
@@ -143,12 +174,16 @@ def prepare_shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=No
     elif workspace.device != device:
         raise ValueError("workspace must be on %s" % device)
     ws_bytes = workspace.numel() * workspace.element_size()
+    if sp:
+        xarg = (ctypes.c_void_p * len(xs))(*[xb.data_ptr() for xb in xs])
+        fn = lib.tp_mlp_shard_forward_sp
+    else:
+        xarg, fn = _ptr(x0), lib.tp_mlp_shard_forward
     args = (M, h, I_full, int(t), int(k), act, wc,
-            _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+            xarg, x0.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
             _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down),
             _ptr(partial), partial.stride(0), _ptr(workspace), ws_bytes, _stream_of(device, stream))
-    call = PreparedCall(lib.tp_mlp_shard_forward, args,
-                        (x, w_gate, w_up, w_down, s_gate, s_up, s_down, partial, workspace))
+    call = PreparedCall(fn, args, (list(xs), w_gate, w_up, w_down, s_gate, s_up, s_down, partial, workspace))
     call.partial = partial
     return call
 
@@ -182,6 +217,44 @@ def prepare_partial_reduce(partials, out=None, stream=None):
     lib = _lib.load()
     call = PreparedCall(lib.tp_partial_reduce,
                         (p0.numel(), len(partials), arr, _ptr(out), _stream_of(device, stream)),
+                        (list(partials), out))
+    call.out = out
+    return call
+
+
+def partial_reduce_scatter(partials, k, out=None, stream=None):
+    """Rank k's rows of the fixed-order sum (reduce-scatter form,
+    ``include/tp_mlp.h``: tp_partial_reduce_scatter): ``partials`` are t
+    contiguous float32 (rows, ...) tensors, rows % t == 0; returns rows
+    [k*rows/t, (k+1)*rows/t) of their left-fold sum."""
+    call = prepare_partial_reduce_scatter(partials, k, out=out, stream=stream)
+    call()
+    return call.out
+
+
+def prepare_partial_reduce_scatter(partials, k, out=None, stream=None):
+    """Marshal a partial_reduce_scatter once; returns a PreparedCall."""
+    t = len(partials)
+    if t < 1:
+        raise ValueError("need at least one partial")
+    p0 = partials[0]
+    device = p0.device
+    for i, p in enumerate(partials):
+        if p.dtype != torch.float32 or p.device != device or not p.is_contiguous() or p.shape != p0.shape:
+            raise ValueError("partials[%d] must be a contiguous float32 tensor shaped like partials[0]" % i)
+    rows = p0.shape[0] if p0.dim() > 0 else 1
+    row_len = p0.numel() // max(rows, 1)
+    if rows % t:
+        raise ValueError("rows (%d) must be a multiple of t (%d)" % (rows, t))
+    shape = (rows // t,) + tuple(p0.shape[1:])
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=device)
+    elif out.dtype != torch.float32 or out.device != device or not out.is_contiguous() or tuple(out.shape) != shape:
+        raise ValueError("out must be a contiguous float32 tensor of shape %s" % (shape,))
+    arr = (ctypes.c_void_p * t)(*[p.data_ptr() for p in partials])
+    lib = _lib.load()
+    call = PreparedCall(lib.tp_partial_reduce_scatter,
+                        (rows, row_len, t, int(k), arr, _ptr(out), _stream_of(device, stream)),
                         (list(partials), out))
     call.out = out
     return call

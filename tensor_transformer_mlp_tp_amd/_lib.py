@@ -22,6 +22,8 @@ EXPORTED_SYMBOLS = (
     "tp_mlp_workspace_bytes",
     "tp_mlp_shard_forward",
     "tp_partial_reduce",
+    "tp_mlp_shard_forward_sp",
+    "tp_partial_reduce_scatter",
     "tp_status_string",
     "tp_last_error",
     "tp_kernel_kind_count",
@@ -62,6 +64,12 @@ def load():
     lib.tp_mlp_shard_forward.restype = c_i32
     lib.tp_partial_reduce.argtypes = [c_i64, c_i32, ctypes.POINTER(vp), vp, vp]
     lib.tp_partial_reduce.restype = c_i32
+    lib.tp_mlp_shard_forward_sp.argtypes = [
+        c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
+        ctypes.POINTER(vp), c_i64, vp, vp, c_i64, vp, c_i64, vp, vp, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
+    lib.tp_mlp_shard_forward_sp.restype = c_i32
+    lib.tp_partial_reduce_scatter.argtypes = [c_i64, c_i64, c_i32, c_i32, ctypes.POINTER(vp), vp, vp]
+    lib.tp_partial_reduce_scatter.restype = c_i32
     lib.tp_status_string.argtypes = [c_i32]
     lib.tp_status_string.restype = ctypes.c_char_p
     lib.tp_last_error.argtypes = []

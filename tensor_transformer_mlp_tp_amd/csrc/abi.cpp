@@ -146,18 +146,23 @@ TP_API size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32
   return (size_t)workspace_need(M, I_full / t, act_dtype);
 }
 
-TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
-                                      int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
-                                      const void* w_gate, const void* w_up, int64_t ldw_gu,
-                                      const void* w_down, int64_t ldw_down, const float* s_gate,
-                                      const float* s_up, const float* s_down, float* partial,
-                                      int64_t ldp, void* workspace, size_t workspace_bytes,
-                                      void* stream) {
+namespace {
+
+// Checks and launch shared by the contiguous and the row-block forms of the
+// forward.  x_blocks[0..nb): the activation row blocks, rows_per_block rows
+// each (nb * rows_per_block == M).
+tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k, int32_t act_dtype,
+                       int32_t w_dtype, const void* const* x_blocks, int nb, int64_t rows_per_block,
+                       int64_t ldx, const void* w_gate, const void* w_up, int64_t ldw_gu, const void* w_down,
+                       int64_t ldw_down, const float* s_gate, const float* s_up, const float* s_down,
+                       float* partial, int64_t ldp, void* workspace, size_t workspace_bytes, void* stream) {
   tp_status st = check_shapes(M, h, I_full, t, k, act_dtype, w_dtype);
   if (st != TP_OK) return st;
   const int64_t I_s = I_full / t;
-  if (!x || !w_gate || !w_up || !w_down || !partial)
+  if (!x_blocks || !w_gate || !w_up || !w_down || !partial)
     return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  for (int b = 0; b < nb; ++b)
+    if (!x_blocks[b]) return fail(TP_ERR_INVALID_ARG, "null activation pointer (block %d)", b);
   const bool fp8 = w_dtype == TP_FP8_E4M3FN;
   if (fp8 && (!s_gate || !s_up || !s_down))
     return fail(TP_ERR_INVALID_ARG, "fp8 weights need s_gate, s_up and s_down");
@@ -172,38 +177,46 @@ TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int3
     return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
                 (unsigned long long)workspace_bytes);
   const int ea = elem_bytes(act_dtype), ew = elem_bytes(w_dtype);
+  const size_t amin = act_dtype == TP_BF16 ? 16 : 4;
+  for (int b = 0; b < nb; ++b)
+    if (!aligned(x_blocks[b], amin))
+      return fail(TP_ERR_UNSUPPORTED, "activation pointers must be %d-byte aligned", (int)amin);
   if (act_dtype == TP_BF16) {
-    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) ||
-        !aligned(partial, 16))
+    if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(partial, 16))
       return fail(TP_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
     if ((ldx * ea) % 16 || (ldw_gu * ew) % 16 || (ldw_down * ew) % 16 || (ldp * 4) % 16)
       return fail(TP_ERR_UNSUPPORTED, "rows must start 16-byte aligned (leading dimensions)");
     if (fp8 && (!aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4)))
       return fail(TP_ERR_UNSUPPORTED, "scale pointers must be 4-byte aligned");
   } else {
-    if (!aligned(x, 4) || !aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) ||
-        !aligned(partial, 4))
+    if (!aligned(w_gate, 4) || !aligned(w_up, 4) || !aligned(w_down, 4) || !aligned(partial, 4))
       return fail(TP_ERR_UNSUPPORTED, "fp32 pointers must be 4-byte aligned");
   }
   if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
 
   const Extent ep = extent(partial, M, h, ldp, 4);
-  const Extent ins[5] = {extent(x, M, h, ldx, ea), extent(w_gate, I_s, h, ldw_gu, ew),
-                         extent(w_up, I_s, h, ldw_gu, ew), extent(w_down, h, I_s, ldw_down, ew),
-                         Extent{reinterpret_cast<uintptr_t>(workspace),
-                                reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need}};
+  const Extent ewk{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need};
+  const Extent ins[4] = {extent(w_gate, I_s, h, ldw_gu, ew), extent(w_up, I_s, h, ldw_gu, ew),
+                         extent(w_down, h, I_s, ldw_down, ew), ewk};
   for (const Extent& e : ins)
     if (overlap(ep, e)) return fail(TP_ERR_INVALID_ARG, "partial overlaps an input or the workspace");
-  const Extent ew_ = ins[4];
-  for (int i = 0; i < 4; ++i)
-    if (overlap(ew_, ins[i])) return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input");
+  for (int i = 0; i < 3; ++i)
+    if (overlap(ewk, ins[i])) return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input");
+  for (int b = 0; b < nb; ++b) {
+    const Extent ex = extent(x_blocks[b], rows_per_block, h, ldx, ea);
+    if (overlap(ep, ex)) return fail(TP_ERR_INVALID_ARG, "partial overlaps the activations");
+    if (overlap(ewk, ex)) return fail(TP_ERR_INVALID_ARG, "workspace overlaps the activations");
+  }
 
   tpmlp::ShardArgs a;
   a.M = (int)M;
   a.h = (int)h;
   a.I_s = (int)I_s;
-  a.x = x;
-  a.ldx = ldx;
+  a.x = tpmlp::XRows{};
+  for (int b = 0; b < nb; ++b) a.x.p[b] = x_blocks[b];
+  a.x.nb = nb;
+  a.x.rows = (int)rows_per_block;
+  a.x.ld = ldx;
   a.wg = w_gate;
   a.wu = w_up;
   a.ldw_gu = ldw_gu;
@@ -228,6 +241,35 @@ TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int3
   return from_hip(e, "kernel launch");
 }
 
+}  // namespace
+
+TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                      int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
+                                      const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                      const void* w_down, int64_t ldw_down, const float* s_gate,
+                                      const float* s_up, const float* s_down, float* partial,
+                                      int64_t ldp, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  const void* blocks[1] = {x};
+  return forward_impl(M, h, I_full, t, k, act_dtype, w_dtype, blocks, 1, M, ldx, w_gate, w_up, ldw_gu, w_down,
+                      ldw_down, s_gate, s_up, s_down, partial, ldp, workspace, workspace_bytes, stream);
+}
+
+TP_API tp_status tp_mlp_shard_forward_sp(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                         int32_t act_dtype, int32_t w_dtype, const void* const* x_blocks,
+                                         int64_t ldx, const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                         const void* w_down, int64_t ldw_down, const float* s_gate,
+                                         const float* s_up, const float* s_down, float* partial, int64_t ldp,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (t < 1 || t > tpmlp::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "t must be in [1, %d] (got %d)", tpmlp::kMaxPartials, t);
+  if (M < 1 || M % t != 0)
+    return fail(TP_ERR_INVALID_ARG, "M (%lld) must be a positive multiple of t (%d)", (long long)M, t);
+  if (!x_blocks) return fail(TP_ERR_INVALID_ARG, "null x_blocks array");
+  return forward_impl(M, h, I_full, t, k, act_dtype, w_dtype, x_blocks, t, M / t, ldx, w_gate, w_up, ldw_gu,
+                      w_down, ldw_down, s_gate, s_up, s_down, partial, ldp, workspace, workspace_bytes, stream);
+}
+
 TP_API tp_status tp_partial_reduce(int64_t n, int32_t t, const float* const* partials, float* out,
                                    void* stream) {
   if (n < 0) return fail(TP_ERR_INVALID_ARG, "n must be >= 0");
@@ -250,6 +292,25 @@ TP_API tp_status tp_partial_reduce(int64_t n, int32_t t, const float* const* par
   if (!aligned(out, 16)) return fail(TP_ERR_UNSUPPORTED, "out not 16-byte aligned");
   return from_hip(tpmlp::launch_partial_reduce(ptrs, t, out, n, reinterpret_cast<hipStream_t>(stream)),
                   "kernel launch");
+}
+
+TP_API tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_t t, int32_t k,
+                                           const float* const* partials, float* out, void* stream) {
+  if (t < 1 || t > tpmlp::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "t must be in [1, %d] (got %d)", tpmlp::kMaxPartials, t);
+  if (k < 0 || k >= t) return fail(TP_ERR_INVALID_ARG, "k must be in [0, t) (got k=%d, t=%d)", k, t);
+  if (rows < 0 || row_len < 0 || rows % t != 0)
+    return fail(TP_ERR_INVALID_ARG, "rows (%lld) must be a non-negative multiple of t (%d)", (long long)rows, t);
+  if (!partials) return fail(TP_ERR_INVALID_ARG, "null partials array");
+  const int64_t n = rows / t * row_len;
+  if (n == 0) return TP_OK;
+  if ((n * 4) % 16) return fail(TP_ERR_UNSUPPORTED, "rows/t * row_len must be a multiple of 4");
+  const float* shifted[tpmlp::kMaxPartials];
+  for (int j = 0; j < t; ++j) {
+    if (!partials[j]) return fail(TP_ERR_INVALID_ARG, "partials[%d] is null", j);
+    shifted[j] = partials[j] + (int64_t)k * n;
+  }
+  return tp_partial_reduce(n, t, shifted, out, stream);
 }
 
 TP_API const char* tp_status_string(int32_t status) {

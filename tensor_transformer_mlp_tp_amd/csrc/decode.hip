@@ -162,7 +162,7 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[RB][NT], int wave, int
 
 template <int NT, int RB, int WAVES, int UNROLL, bool FP8>
 __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
-    int M, int h, int I_s, const uint16_t* __restrict__ x, int64_t ldx,
+    int M, int h, int I_s, const XRows xr,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
     const float* __restrict__ sg, const float* __restrict__ su,
     uint16_t* __restrict__ a_out, int64_t lda) {
@@ -186,7 +186,7 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   for (int b = 0; b < NT; ++b) {
     const int tok = b * 16 + row16;
     xok[b] = tok < M;
-    xrow[b] = x + (int64_t)min(tok, M - 1) * ldx;
+    xrow[b] = x_row<uint16_t>(xr, min(tok, M - 1));
   }
 
   const int nsteps = h / KSTEP;
@@ -576,7 +576,7 @@ struct StreamShape {
 
 template <int NT, int RB, bool FP8, bool XD>
 __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateup_stream_kernel(
-    int M, int h, int I_s, const uint16_t* __restrict__ x, int64_t ldx,
+    int M, int h, int I_s, const XRows xr,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
     const float* __restrict__ sg, const float* __restrict__ su,
     uint16_t* __restrict__ a_out, int64_t lda) {
@@ -609,12 +609,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
   uint8_t* ring = ring_all + wave * SS::S * SS::SLOT;
   if constexpr (XD) {
     const uint8_t* xsrc[NT][FP8 ? 8 : 4];
-    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return x + (int64_t)min(tok, M - 1) * ldx; });
+    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return x_row<uint16_t>(xr, min(tok, M - 1)); });
     stream_rows_xd<NT, RB, FP8, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
-    for (int b = 0; b < NT; ++b) xrow[b] = x + (int64_t)min(b * 16 + row16, M - 1) * ldx;
+    for (int b = 0; b < NT; ++b) xrow[b] = x_row<uint16_t>(xr, min(b * 16 + row16, M - 1));
     stream_rows<NT, RB, FP8, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
@@ -719,7 +719,7 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
   const dim3 block(kWaves * 64);
   const dim3 grid_gu((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU));
   hipError_t e = launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB_GU, kWaves, UN_GU, FP8>, grid_gu,
-                        block, 0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx,
+                        block, 0, stream, a.M, a.h, a.I_s, a.x,
                         (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su,
                         (uint16_t*)a.a, a.lda);
   if (e != hipSuccess) return e;
@@ -754,7 +754,7 @@ hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
   constexpr int RB_DN = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
   hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB_GU, FP8, XD>,
                         dim3((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU)), dim3(StreamShape<NT, RB_GU, FP8, XD>::WV * 64),
-                        0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
+                        0, stream, a.M, a.h, a.I_s, a.x, (const uint8_t*)a.wg,
                         (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
   if (e != hipSuccess) return e;
   return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB_DN, FP8, XD>, dim3((a.h + 16 * RB_DN - 1) / (16 * RB_DN)),

@@ -23,14 +23,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __global__ __launch_bounds__(kF32Waves * 64) void gateup_f32_kernel(
-    int M, int h, int I_s, const float* __restrict__ x, int64_t ldx,
+    int M, int h, int I_s, const XRows xrows,
     const float* __restrict__ wg, const float* __restrict__ wu, int64_t ldw,
     float* __restrict__ a_out, int64_t lda) {
   const int lane = threadIdx.x & 63;
   const int64_t id = (int64_t)blockIdx.x * kF32Waves + (threadIdx.x >> 6);
   if (id >= (int64_t)M * I_s) return;  // whole wave leaves together
   const int m = (int)(id / I_s), j = (int)(id % I_s);
-  const float* xr = x + (int64_t)m * ldx;
+  const float* xr = x_row<float>(xrows, m);
   const float* gr = wg + (int64_t)j * ldw;
   const float* ur = wu + (int64_t)j * ldw;
   float g = 0.f, u = 0.f;
@@ -65,7 +65,7 @@ hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream) {
   const dim3 block(kF32Waves * 64);
   const int64_t g1 = ((int64_t)a.M * a.I_s + kF32Waves - 1) / kF32Waves;
   hipError_t e = launch(K_GATEUP_F32, gateup_f32_kernel, dim3((unsigned)g1), block, 0, stream, a.M,
-                        a.h, a.I_s, (const float*)a.x, a.ldx, (const float*)a.wg,
+                        a.h, a.I_s, a.x, (const float*)a.wg,
                         (const float*)a.wu, a.ldw_gu, (float*)a.a, a.lda);
   if (e != hipSuccess) return e;
   const int64_t g2 = ((int64_t)a.M * a.h + kF32Waves - 1) / kF32Waves;

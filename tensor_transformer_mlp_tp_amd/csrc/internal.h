@@ -12,11 +12,32 @@ struct PartialPtrs {
   const float* p[kMaxPartials];
 };
 
+// The activation rows X (M x h): nb row blocks of `rows` rows each, block b
+// holding rows b*rows .. b*rows+rows-1 with leading dimension ld (elements).
+// A contiguous X is one block of M rows; the sequence-parallel form passes
+// the t ranks' row blocks as they are (the gathered X is never built).
+struct XRows {
+  const void* p[kMaxPartials];
+  int nb;
+  int rows;
+  int64_t ld;
+};
+
+// Row `row` of X.  The block is chosen with wave-uniform indices only, so
+// the pointer table stays in the kernel-argument segment.
+template <typename T>
+__device__ __forceinline__ const T* x_row(const XRows& xr, int row) {
+  const int b = row / xr.rows;
+  const void* base = xr.p[0];
+  for (int i = 1; i < xr.nb; ++i)
+    if (i == b) base = xr.p[i];
+  return reinterpret_cast<const T*>(base) + (int64_t)(row - b * xr.rows) * xr.ld;
+}
+
 // One rank's forward, already validated.  Pointers are device addresses.
 struct ShardArgs {
   int M, h, I_s;
-  const void* x;            // M x h, bf16 or fp32
-  int64_t ldx;
+  XRows x;                  // M x h, bf16 or fp32
   const void* wg;           // I_s x h
   const void* wu;           // I_s x h
   int64_t ldw_gu;

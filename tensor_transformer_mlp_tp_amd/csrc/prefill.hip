@@ -137,7 +137,7 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
 
 template <bool SWIGLU, bool FP8, int BK, int NS, int WV>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
-    int M, int N, int K, const uint16_t* __restrict__ act, int64_t ld_act,
+    int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
     const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
     int64_t ld_out, int tiles_m, int tiles_n) {
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     const int row = (wave * XINST + i) * XRPI + lane / XCH;
     const int c = (lane % XCH) ^ swz<XROWB>(row);
     const int tok = min(m0 + row, M - 1);
-    xsrc[i] = reinterpret_cast<const uint8_t*>(act + (int64_t)tok * ld_act) + c * 16;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, tok)) + c * 16;
   }
   const uint8_t* wsrc[WINST];
 #pragma unroll
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // flight one k-tile before its own loads, which find the lines in L2.
   // (with 8 waves the upper 256 threads touch the same lines again)
   const int trow = tid & 255;
-  const uint8_t* tx = reinterpret_cast<const uint8_t*>(act + (int64_t)min(m0 + trow, M - 1) * ld_act);
+  const uint8_t* tx = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, min(m0 + trow, M - 1)));
   const uint8_t* tw;
   if constexpr (SWIGLU)
     tw = (trow < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (trow & (BN / 2 - 1)), N - 1) * ldw * EB;
@@ -428,14 +428,19 @@ hipError_t run_prefill(const ShardArgs& a, hipStream_t stream) {
     const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
     const dim3 grid((unsigned)(tiles_m * tiles_n));
     hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.I_s,
-                          a.h, (const uint16_t*)a.x, a.ldx, (const uint8_t*)a.wg,
+                          a.h, a.x, (const uint8_t*)a.wg,
                           (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m, tiles_n);
     if (e != hipSuccess) return e;
   }
   const int tiles_n = (a.h + BN - 1) / BN;
   const dim3 grid((unsigned)(tiles_m * tiles_n));
+  XRows ar{};
+  ar.p[0] = a.a;
+  ar.nb = 1;
+  ar.rows = a.M;
+  ar.ld = a.lda;
   return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.h, a.I_s,
-                (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
+                ar, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
                 a.ldw_down, a.sd, (const float*)nullptr, (void*)a.p, a.ldp, tiles_m, tiles_n);
 }
 

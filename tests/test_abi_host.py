@@ -146,3 +146,51 @@ def test_reduce_empty_is_noop():
     assert reduce_call(0, 3, None, None) == _lib.TP_OK
     # t is still validated
     assert reduce_call(0, 0, None, None) == _lib.TP_ERR_INVALID_ARG
+
+
+def fwd_sp(blocks, M=4, h=128, I=256, t=2, k=0, ldx=None, **kw):
+    lib = _lib.load()
+    I_s = I // t if t else 1
+    arr = None if blocks is None else (ctypes.c_void_p * len(blocks))(*blocks)
+    return lib.tp_mlp_shard_forward_sp(M, h, I, t, k, BF16, BF16, arr, ldx if ldx is not None else h,
+                                       P * 2, P * 3, h, P * 4, I_s, None, None, None, kw.get("p", P * 8), h,
+                                       kw.get("ws", P * 16), 1 << 20, None)
+
+
+@pytest.mark.parametrize("blocks,kw,status", [
+    (None, {}, _lib.TP_ERR_INVALID_ARG),                           # no block array
+    ([P, None], {}, _lib.TP_ERR_INVALID_ARG),                      # a null block
+    ([P, P * 32], dict(M=5), _lib.TP_ERR_INVALID_ARG),             # M % t
+    ([P, P * 32], dict(t=0), _lib.TP_ERR_INVALID_ARG),
+    ([P, P * 32], dict(k=2), _lib.TP_ERR_INVALID_ARG),
+    ([P, P * 32 + 4], {}, _lib.TP_ERR_UNSUPPORTED),                # misaligned block
+    ([P, P * 8], {}, _lib.TP_ERR_INVALID_ARG),                     # block overlaps the partial
+    ([P, P * 16], {}, _lib.TP_ERR_INVALID_ARG),                    # block overlaps the workspace
+])
+def test_forward_sp_rejects(blocks, kw, status):
+    assert fwd_sp(blocks, **kw) == status
+
+
+def rs_call(rows, row_len, t, k, ptrs, out):
+    lib = _lib.load()
+    arr = None if ptrs is None else (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return lib.tp_partial_reduce_scatter(rows, row_len, t, k, arr, out, None)
+
+
+@pytest.mark.parametrize("rows,row_len,t,k,ptrs,out,status", [
+    (8, 16, 0, 0, [P], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (8, 16, 2, 2, [P, P * 2], P * 4, _lib.TP_ERR_INVALID_ARG),         # k >= t
+    (8, 16, 2, -1, [P, P * 2], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (9, 16, 2, 0, [P, P * 2], P * 4, _lib.TP_ERR_INVALID_ARG),         # rows % t
+    (8, 16, 2, 0, None, P * 4, _lib.TP_ERR_INVALID_ARG),
+    (8, 16, 2, 0, [P, None], P * 4, _lib.TP_ERR_INVALID_ARG),
+    (4, 3, 2, 0, [P, P * 2], P * 4, _lib.TP_ERR_UNSUPPORTED),          # rows/t * row_len % 4
+    (8, 16, 2, 1, [P, P * 2], P * 2 + 64 * 4, _lib.TP_ERR_INVALID_ARG),  # out = rank 1's slice of partials[1]
+])
+def test_reduce_scatter_rejects(rows, row_len, t, k, ptrs, out, status):
+    assert rs_call(rows, row_len, t, k, ptrs, out) == status
+
+
+def test_reduce_scatter_empty_is_noop():
+    assert rs_call(0, 16, 2, 1, [P, P * 2], P * 4) == _lib.TP_OK
+    assert rs_call(8, 0, 2, 1, None, None) == _lib.TP_ERR_INVALID_ARG   # the array is checked first
