@@ -13,7 +13,9 @@ cache.  ``value`` is algorithmic bytes per second over the timed steps.
 
 Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
 (TP=4 fp8 weights: decode M=32 and prefill M=2048), prefill405b (8192 tokens),
-reduce70b / reduce405b (the 8-way reduces alone), copy (the reduce with one
+reduce70b / reduce405b (the 8-way reduces alone), sp_prefill70b (the
+sequence-parallel form: forward over eight row blocks of X, reduce-scatter),
+copy (the reduce with one
 buffer over 1 GiB: a plain copy of known size, the calibration run for the
 HBM byte counters).
 
@@ -59,7 +61,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode70b",
                     choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
-                             "copy"])
+                             "sp_prefill70b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     return ap.parse_args()
@@ -464,6 +466,67 @@ def bench_reduce(tp, args, cfg_id):
     return res
 
 
+def bench_sp_prefill(tp, args):
+    """Sequence-parallel form of the 70B TP=8 prefill step: the forward reads X
+    from the eight ranks' 512-token row blocks, and the 8-way sum is the
+    reduce-scatter that leaves rank 0 its 512 rows."""
+    import torch
+    import oracle
+    cfg_id, M = 3, 4096
+    c = workloads.CONFIGS[cfg_id]
+    h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
+    sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], 1)
+    x_host = workloads.make_x(cfg_id, M, h, "bf16")
+    r = M // t
+    blocks = [to_dev(np.ascontiguousarray(x_host[j * r:(j + 1) * r]), "bf16") for j in range(t)]
+    partial = torch.empty((M, h), dtype=torch.float32, device="cuda")
+    nbytes = tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16, torch.bfloat16)
+    ws = tp.alloc_workspace(nbytes, "cuda")
+    others = [torch.from_numpy(o).cuda().view(M, h) for o in workloads.make_partials(cfg_id, t - 1, M * h)]
+    out = torch.empty((r, h), dtype=torch.float32, device="cuda")
+    fwd = tp.prepare_shard_forward_sp(blocks, sets[0]["w_gate"], sets[0]["w_up"], sets[0]["w_down"], t=t, k=0,
+                                      partial=partial, workspace=ws)
+    rs = tp.prepare_partial_reduce_scatter([partial] + others, 0, out=out)
+
+    def step(i):
+        fwd()
+        rs()
+
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"])
+    prof = breakdown(tp, step, steps, warmup + steps)
+    flops = workloads.forward_flops(M, h, I_s)
+    value = flops * steps / elapsed / 1e12
+    gu_ms, gu_n = prof_gu["gateup_prefill"]
+    gu_tf = 4 * M * h * I_s * gu_n / (gu_ms * 1e-3) / 1e12
+    rs_ms, rs_n = prof["partial_reduce"]
+    rs_bytes = workloads.reduce_bytes(r * h, t)
+    out_d = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
+                 ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
+                 vs_baseline=None, dtype="bf16", data="synthetic",
+                 config={"workload": "sequence-parallel 70B-shaped TP=8 rank prefill: forward over 8 row blocks "
+                                     "of 512 tokens (h=8192, I_s=3584, bf16) + reduce-scatter of rank 0's 512 "
+                                     "rows of the 8-way fp32 sum", "M": M, "h": h, "I_s": I_s, "t": t},
+                 roofline={"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
+                           "traffic": recorded_traffic("gateup_prefill", "prefill70b"), "kernel": "gateup_prefill"},
+                 kernels={k: {"launches": v[1], "avg_us": 1e3 * v[0] / v[1]} for k, v in prof.items()},
+                 reduce_scatter={"GBps": round(rs_bytes * rs_n / (rs_ms * 1e-3) / 1e9, 1),
+                                 "frac_hbm": round(rs_bytes * rs_n / (rs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    if not args.no_cpu_baseline:
+        rows = np.arange(0, M, r)[:8]
+
+        def once():
+            xg = oracle.gather_rows([x_host[j * r:(j + 1) * r] for j in range(t)])
+            oracle.rank_partial_from_storage(xg[rows], "bf16", host0["w_gate"], host0["w_up"], host0["w_down"],
+                                             "bf16")
+        log("timing the CPU oracle")
+        out_d["cpu_baseline"] = cpu_baseline(once, workloads.forward_flops(len(rows), h, I_s) / 1e12, "TFLOP/s",
+                                             "gather of the row blocks + rank partial for %d token rows, "
+                                             "repeated >= 10 s" % len(rows))
+    return out_d
+
+
 def bench_copy(tp, args):
     """One-buffer reduce over 1 GiB: reads n*4 bytes and writes n*4 bytes, nothing else."""
     import torch
@@ -511,6 +574,8 @@ def main():
         out = bench_reduce(tp, args, 3)
     elif args.workload == "copy":
         out = bench_copy(tp, args)
+    elif args.workload == "sp_prefill70b":
+        out = bench_sp_prefill(tp, args)
     else:
         out = bench_reduce(tp, args, 5)
     print(json.dumps(out), flush=True)
