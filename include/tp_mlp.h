@@ -200,6 +200,101 @@ tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_t t, in
                                     const float* const* partials, float* out,
                                     void* stream);
 
+/* ------------------------------------------------------------------------
+ * Attention-block projections of one rank.  "Build a model sharding system
+ * for serving 70B+ parameter models" (scalablesystem.dev), section "The
+ * Tensor-Parallel Shard Group", class TPAttentionBlock: the QKV projection is
+ * column-parallel (each rank computes the projections of its own attention
+ * heads, no communication), attention runs locally over those heads, and the
+ * output projection is row-parallel, its partials summed by an all-reduce.
+ * "Chapter 12 Parallelism Strategies" (arunshar.com), section 12.2.1: rank k
+ * handles n_heads/t heads.  Grouped-query attention: the KV-head count must
+ * divide by the TP degree (scalablesystem.dev, the interview question on
+ * uneven division); when the degree is a multiple of the KV-head count, each
+ * rank keeps one KV head and the heads are replicated ("Tensor, Pipeline and
+ * Expert Parallelism: One Model, Many GPUs", vidyal.ai, section "The KV
+ * cache splits too, until it doesn't").
+ *
+ * With q_loc = n_heads/t and kv_loc = n_kv_heads/t (or 1 when t is a multiple
+ * of n_kv_heads), rank k's QKV width is n_loc = (q_loc + 2*kv_loc)*head_dim and
+ *
+ *     QKV_k = X * W_qkv_k^T      (M x n_loc, fp32 accumulate, stored in the
+ *                                 activation dtype: bf16 RNE, or fp32)
+ *     P_k   = O_k * W_o_k^T      (M x h, fp32), O_k = the rank's attention
+ *                                 output, M x q_loc*head_dim
+ *
+ * and the t partials P_k sum (tp_partial_reduce) to O * W_o^T.  The attention
+ * core between the two is not part of this library.
+ * ---------------------------------------------------------------------- */
+
+/*
+ * n_loc, the width of one rank's QKV output (and the row count of its
+ * W_qkv_k), or -1 if the heads do not split over t (see tp_attn_qkv_forward).
+ */
+int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int32_t t);
+
+/*
+ * Rank k's column-parallel QKV projection.
+ *
+ *   M          tokens, M >= 1.
+ *   h          hidden size (the projection's input features).
+ *   n_heads, n_kv_heads, head_dim   query heads, key/value heads (grouped
+ *              query attention: n_heads % n_kv_heads == 0) and head size.
+ *              n_heads % t == 0, and n_kv_heads % t == 0 or t % n_kv_heads
+ *              == 0; else TP_ERR_INVALID_ARG.
+ *   t, k       TP degree (1..64), rank index (validated; selects no data).
+ *   act_dtype, w_dtype   as tp_mlp_shard_forward: (bf16, bf16),
+ *              (bf16, fp8 e4m3fn), (fp32, fp32).
+ *   x          M x h, leading dimension ldx >= h.
+ *   w_qkv      n_loc x h ((out, in) layout), leading dimension ldw >= h: the
+ *              rank's rows in the order [its q_loc query heads | its kv_loc
+ *              key heads | its kv_loc value heads], head_dim rows per head,
+ *              heads in their global order.  Rank k holds query heads
+ *              [k*q_loc, (k+1)*q_loc) and key/value heads [k*kv_loc,
+ *              (k+1)*kv_loc), or, replicated, head k / (t / n_kv_heads).
+ *   s_qkv      fp8 only: n_loc fp32 per-row scales (weight = code * scale of
+ *              its row); NULL otherwise.
+ *   qkv        M x n_loc output in the activation dtype, leading dimension
+ *              ldq >= n_loc, same column order as w_qkv's rows; overwritten;
+ *              must not overlap an input.
+ *
+ * Requirements (else TP_ERR_UNSUPPORTED): with bf16 activations h % 64 == 0
+ * and n_loc % 16 == 0, pointers and rows 16-byte aligned, scales 4-byte
+ * aligned; with fp32, 4-byte alignment.  No workspace.  Deterministic.
+ */
+tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
+                              int64_t head_dim, int32_t t, int32_t k,
+                              int32_t act_dtype, int32_t w_dtype,
+                              const void* x, int64_t ldx,
+                              const void* w_qkv, int64_t ldw, const float* s_qkv,
+                              void* qkv, int64_t ldq, void* stream);
+
+/*
+ * Rank k's row-parallel output projection: partial P_k (M x h fp32).
+ *
+ *   n_heads, head_dim   q_loc = n_heads / t query heads per rank
+ *              (n_heads % t == 0, else TP_ERR_INVALID_ARG); the input width
+ *              is K = q_loc * head_dim.
+ *   attn       M x K, the rank's attention output (its heads in global
+ *              order), activation dtype, leading dimension lda >= K.
+ *   w_o        h x K ((out, in) layout: the rank's column block of the full
+ *              h x n_heads*head_dim matrix), leading dimension ldw >= K.  A
+ *              caller holding the full matrix passes the pointer to column
+ *              k*K and ldw = n_heads*head_dim.
+ *   s_o        fp8 only: h fp32 per-row scales; NULL otherwise.
+ *   partial    M x h fp32, leading dimension ldp >= h; overwritten; must not
+ *              overlap an input.
+ *
+ * Other arguments and requirements as tp_attn_qkv_forward, with K in place
+ * of h (K % 64 == 0) and h in place of n_loc (h % 16 == 0).
+ */
+tp_status tp_attn_out_forward(int64_t M, int64_t h, int64_t n_heads, int64_t head_dim,
+                              int32_t t, int32_t k,
+                              int32_t act_dtype, int32_t w_dtype,
+                              const void* attn, int64_t lda,
+                              const void* w_o, int64_t ldw, const float* s_o,
+                              float* partial, int64_t ldp, void* stream);
+
 /* Static text for a status code. */
 const char* tp_status_string(int32_t status);
 

@@ -33,6 +33,11 @@ Sources (the web pages this build follows):
   Dropout": under sequence parallelism the all-reduce becomes a
   reduce-scatter (rank k keeps the reduced rows of its sequence slice) and
   the next column-parallel projection reads the all-gathered sequence.
+* ``oracle/attn.py``: the attention block's projections under the same split
+  (TPAttentionBlock of the scalablesystem.dev section above; heads per rank
+  in section 12.2.1 of the arunshar.com chapter; grouped-query KV heads split
+  or replicated per "The KV cache splits too, until it doesn't" on the
+  vidyal.ai page).
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 (brute force, closed forms, a library special case, the Megatron invariant,
@@ -40,6 +45,14 @@ format tables).  No function is "parity unpinned".
 """
 
 from .formats import bf16_bits_to_f64, e4m3fn_to_f64, E4M3FN_MAX
+from .attn import (
+    local_heads,
+    head_rows,
+    qkv_rank_weight,
+    o_proj_rank_weight,
+    linear,
+    linear_from_storage,
+)
 from .mlp import (
     silu,
     mlp_full,
@@ -54,6 +67,12 @@ from .mlp import (
 )
 
 __all__ = [
+    "local_heads",
+    "head_rows",
+    "qkv_rank_weight",
+    "o_proj_rank_weight",
+    "linear",
+    "linear_from_storage",
     "bf16_bits_to_f64",
     "e4m3fn_to_f64",
     "E4M3FN_MAX",

@@ -8,6 +8,11 @@ library's HIP kernels.
 
     P_k = (SiLU(X W_gate_k^T) * (X W_up_k^T)) W_down_k^T      (shard_forward)
     Y   = (((P_0 + P_1) + P_2) + ...) + P_{t-1}              (partial_reduce)
+
+and the attention block's two projections of the same rank:
+
+    QKV_k = X W_qkv_k^T                                        (attn_qkv_forward)
+    P_k   = O_k W_o_k^T                                        (attn_out_forward)
 """
 
 import ctypes
@@ -19,6 +24,9 @@ from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, EXPORTED_SYMBOLS,  #
                    LIB_PATH, load)
 
 __all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
+           "shard_forward_sp", "prepare_shard_forward_sp", "partial_reduce_scatter",
+           "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_forward", "prepare_attn_qkv_forward",
+           "attn_out_forward", "prepare_attn_out_forward", "profile_reserve",
            "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "kernel_kinds",
            "TPError", "load"]
 
@@ -257,6 +265,92 @@ def prepare_partial_reduce_scatter(partials, k, out=None, stream=None):
                         (rows, row_len, t, int(k), arr, _ptr(out), _stream_of(device, stream)),
                         (list(partials), out))
     call.out = out
+    return call
+
+
+def attn_qkv_width(n_heads, n_kv_heads, head_dim, t):
+    """Width n_loc of one rank's QKV output, or -1 if the heads do not split
+    over t (``include/tp_mlp.h``: tp_attn_qkv_width)."""
+    return int(_lib.load().tp_attn_qkv_width(int(n_heads), int(n_kv_heads), int(head_dim), int(t)))
+
+
+def _check_scales(s, device):
+    if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
+        raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+
+
+def attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s_qkv=None, out=None, stream=None):
+    """Rank k's column-parallel QKV projection X W_qkv_k^T (M x n_loc, in x's
+    dtype); ``w_qkv`` is the rank's (n_loc, h) rows [q heads | k heads | v
+    heads] (``include/tp_mlp.h``: tp_attn_qkv_forward)."""
+    call = prepare_attn_qkv_forward(x, w_qkv, n_heads=n_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, t=t,
+                                    k=k, s_qkv=s_qkv, out=out, stream=stream)
+    call()
+    return call.out
+
+
+def prepare_attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s_qkv=None, out=None,
+                             stream=None):
+    """Marshal an attn_qkv_forward once; returns a PreparedCall (``out``)."""
+    device = x.device
+    _check_matrix("x", x, device)
+    _check_matrix("w_qkv", w_qkv, device)
+    _check_scales(s_qkv, device)
+    M, h = x.shape
+    n_loc = attn_qkv_width(n_heads, n_kv_heads, head_dim, t)
+    if n_loc < 0:
+        raise ValueError("heads (%d query, %d kv) do not split over t = %d" % (n_heads, n_kv_heads, t))
+    if tuple(w_qkv.shape) != (n_loc, h):
+        raise ValueError("w_qkv must be (%d, %d), got %s" % (n_loc, h, tuple(w_qkv.shape)))
+    if out is None:
+        out = torch.empty((M, n_loc), dtype=x.dtype, device=device)
+    else:
+        _check_matrix("out", out, device)
+        if out.dtype != x.dtype or tuple(out.shape) != (M, n_loc):
+            raise ValueError("out must be %s of shape (%d, %d)" % (x.dtype, M, n_loc))
+    lib = _lib.load()
+    args = (M, h, int(n_heads), int(n_kv_heads), int(head_dim), int(t), int(k), _act_code(x.dtype),
+            _w_code(w_qkv.dtype), _ptr(x), x.stride(0), _ptr(w_qkv), w_qkv.stride(0), _ptr(s_qkv), _ptr(out),
+            out.stride(0), _stream_of(device, stream))
+    call = PreparedCall(lib.tp_attn_qkv_forward, args, (x, w_qkv, s_qkv, out))
+    call.out = out
+    return call
+
+
+def attn_out_forward(attn, w_o, *, n_heads, head_dim, t, k, s_o=None, partial=None, stream=None):
+    """Rank k's row-parallel output projection: fp32 partial O_k W_o_k^T
+    (M x h); ``attn`` is (M, n_heads/t*head_dim), ``w_o`` the rank's (h,
+    n_heads/t*head_dim) column block (``include/tp_mlp.h``:
+    tp_attn_out_forward)."""
+    call = prepare_attn_out_forward(attn, w_o, n_heads=n_heads, head_dim=head_dim, t=t, k=k, s_o=s_o,
+                                    partial=partial, stream=stream)
+    call()
+    return call.partial
+
+
+def prepare_attn_out_forward(attn, w_o, *, n_heads, head_dim, t, k, s_o=None, partial=None, stream=None):
+    """Marshal an attn_out_forward once; returns a PreparedCall (``partial``)."""
+    device = attn.device
+    _check_matrix("attn", attn, device)
+    _check_matrix("w_o", w_o, device)
+    _check_scales(s_o, device)
+    M, K = attn.shape
+    h = w_o.shape[0]
+    if int(n_heads) % int(t) or K != int(n_heads) // int(t) * int(head_dim) or w_o.shape[1] != K:
+        raise ValueError("attn (%d, %d) and w_o %s do not match n_heads/t * head_dim = %s"
+                         % (M, K, tuple(w_o.shape), int(n_heads) / int(t) * int(head_dim)))
+    if partial is None:
+        partial = torch.empty((M, h), dtype=torch.float32, device=device)
+    else:
+        _check_matrix("partial", partial, device)
+        if partial.dtype != torch.float32 or tuple(partial.shape) != (M, h):
+            raise ValueError("partial must be float32 of shape (%d, %d)" % (M, h))
+    lib = _lib.load()
+    args = (M, h, int(n_heads), int(head_dim), int(t), int(k), _act_code(attn.dtype), _w_code(w_o.dtype),
+            _ptr(attn), attn.stride(0), _ptr(w_o), w_o.stride(0), _ptr(s_o), _ptr(partial), partial.stride(0),
+            _stream_of(device, stream))
+    call = PreparedCall(lib.tp_attn_out_forward, args, (attn, w_o, s_o, partial))
+    call.partial = partial
     return call
 
 

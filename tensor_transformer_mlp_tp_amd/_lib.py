@@ -24,6 +24,9 @@ EXPORTED_SYMBOLS = (
     "tp_partial_reduce",
     "tp_mlp_shard_forward_sp",
     "tp_partial_reduce_scatter",
+    "tp_attn_qkv_width",
+    "tp_attn_qkv_forward",
+    "tp_attn_out_forward",
     "tp_status_string",
     "tp_last_error",
     "tp_kernel_kind_count",
@@ -70,6 +73,16 @@ def load():
     lib.tp_mlp_shard_forward_sp.restype = c_i32
     lib.tp_partial_reduce_scatter.argtypes = [c_i64, c_i64, c_i32, c_i32, ctypes.POINTER(vp), vp, vp]
     lib.tp_partial_reduce_scatter.restype = c_i32
+    lib.tp_attn_qkv_width.argtypes = [c_i64, c_i64, c_i64, c_i32]
+    lib.tp_attn_qkv_width.restype = c_i64
+    lib.tp_attn_qkv_forward.argtypes = [
+        c_i64, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
+        vp, c_i64, vp, c_i64, vp, vp, c_i64, vp]
+    lib.tp_attn_qkv_forward.restype = c_i32
+    lib.tp_attn_out_forward.argtypes = [
+        c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
+        vp, c_i64, vp, c_i64, vp, vp, c_i64, vp]
+    lib.tp_attn_out_forward.restype = c_i32
     lib.tp_status_string.argtypes = [c_i32]
     lib.tp_status_string.restype = ctypes.c_char_p
     lib.tp_last_error.argtypes = []

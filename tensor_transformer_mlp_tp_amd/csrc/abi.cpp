@@ -109,7 +109,8 @@ size_t g_prof_used = 0;
 
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
-    "partial_reduce", "gateup_f32", "down_f32"};
+    "partial_reduce", "gateup_f32", "down_f32", "qkv_decode", "qkv_prefill",
+    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32"};
 
 // Appends one start/stop event pair to the timing pool.
 bool prof_grow() {
@@ -311,6 +312,144 @@ TP_API tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_
     shifted[j] = partials[j] + (int64_t)k * n;
   }
   return tp_partial_reduce(n, t, shifted, out, stream);
+}
+
+// ------------------------------------------------------------ attention
+
+namespace {
+
+// Local heads of one rank: query heads split evenly; KV heads split evenly,
+// or, when the group is a multiple of the KV-head count, one KV head per rank
+// (replicated over t / n_kv_heads ranks).  Returns false if neither holds.
+bool attn_local_heads(int64_t n_heads, int64_t n_kv_heads, int32_t t, int64_t* q_loc, int64_t* kv_loc) {
+  if (t < 1 || n_heads < 1 || n_kv_heads < 1 || n_heads % t != 0) return false;
+  if (n_heads % n_kv_heads != 0) return false;  // grouped-query: whole groups
+  if (n_kv_heads % t == 0)
+    *kv_loc = n_kv_heads / t;
+  else if (t % n_kv_heads == 0)
+    *kv_loc = 1;
+  else
+    return false;
+  *q_loc = n_heads / t;
+  return true;
+}
+
+// Checks and launch shared by the attention projections:
+// out (M x N) = a (M x K) * w^T, w N x K, out in the activation dtype
+// (out_f32 forces fp32).
+tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype, const void* a,
+                      int64_t lda, const void* w, int64_t ldw, const float* s, void* out, int64_t ldo,
+                      bool out_f32, int kind_decode, int kind_prefill, int kind_f32, void* stream) {
+  if (elem_bytes(act_dtype) == 0 || elem_bytes(w_dtype) == 0)
+    return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act_dtype, w_dtype);
+  if (act_dtype == TP_FP8_E4M3FN) return fail(TP_ERR_UNSUPPORTED, "fp8 activations are not supported");
+  const bool ok_pair = (act_dtype == TP_BF16 && (w_dtype == TP_BF16 || w_dtype == TP_FP8_E4M3FN)) ||
+                       (act_dtype == TP_F32 && w_dtype == TP_F32);
+  if (!ok_pair) return fail(TP_ERR_UNSUPPORTED, "unsupported dtype pair (act=%d, w=%d)", act_dtype, w_dtype);
+  if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
+  if (act_dtype == TP_BF16 && (K % 64 != 0 || N % 16 != 0))
+    return fail(TP_ERR_UNSUPPORTED, "bf16/fp8 paths need K %% 64 == 0 and N %% 16 == 0 (K=%lld, N=%lld)",
+                (long long)K, (long long)N);
+  if (!a || !w || !out) return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  const bool fp8 = w_dtype == TP_FP8_E4M3FN;
+  if (fp8 && !s) return fail(TP_ERR_INVALID_ARG, "fp8 weights need their scales");
+  if (!fp8 && s) return fail(TP_ERR_INVALID_ARG, "scales are only accepted with fp8 weights");
+  if (lda < K || ldw < K || ldo < N)
+    return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length (lda=%lld ldw=%lld ldo=%lld)",
+                (long long)lda, (long long)ldw, (long long)ldo);
+  const int ea = elem_bytes(act_dtype), ew = elem_bytes(w_dtype);
+  const int eo = out_f32 ? 4 : ea;
+  if (act_dtype == TP_BF16) {
+    if (!aligned(a, 16) || !aligned(w, 16) || !aligned(out, 16))
+      return fail(TP_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+    if ((lda * ea) % 16 || (ldw * ew) % 16 || (ldo * eo) % 16)
+      return fail(TP_ERR_UNSUPPORTED, "rows must start 16-byte aligned (leading dimensions)");
+    if (fp8 && !aligned(s, 4)) return fail(TP_ERR_UNSUPPORTED, "scale pointer must be 4-byte aligned");
+  } else if (!aligned(a, 4) || !aligned(w, 4) || !aligned(out, 4)) {
+    return fail(TP_ERR_UNSUPPORTED, "fp32 pointers must be 4-byte aligned");
+  }
+  const Extent e_out = extent(out, M, N, ldo, eo);
+  if (overlap(e_out, extent(a, M, K, lda, ea)) || overlap(e_out, extent(w, N, K, ldw, ew)) ||
+      (s && overlap(e_out, extent(s, 1, N, N, 4))))
+    return fail(TP_ERR_INVALID_ARG, "output overlaps an input");
+
+  tpmlp::RowGemm g;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.a = a;
+  g.lda = lda;
+  g.w = w;
+  g.ldw = ldw;
+  g.s = s;
+  g.out = out;
+  g.ldo = ldo;
+  g.out_bf16 = act_dtype == TP_BF16 && !out_f32;
+  g.fp8 = fp8;
+  g.kind_decode = kind_decode;
+  g.kind_prefill = kind_prefill;
+  g.kind_f32 = kind_f32;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (act_dtype == TP_F32)
+    e = tpmlp::launch_rowgemm_f32(g, st);
+  else if (M <= tpmlp::kDecodeMaxM)
+    e = tpmlp::launch_rowgemm_decode(g, st);
+  else
+    e = tpmlp::launch_rowgemm_prefill(g, st);
+  return from_hip(e, "kernel launch");
+}
+
+tp_status check_attn(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int32_t t,
+                     int32_t k, int64_t* q_loc, int64_t* kv_loc) {
+  if (M < 1 || h < 1 || head_dim < 1)
+    return fail(TP_ERR_INVALID_ARG, "M, h and head_dim must be >= 1 (got %lld, %lld, %lld)", (long long)M,
+                (long long)h, (long long)head_dim);
+  if (t < 1 || t > tpmlp::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "t must be in [1, %d] (got %d)", tpmlp::kMaxPartials, t);
+  if (k < 0 || k >= t) return fail(TP_ERR_INVALID_ARG, "k must be in [0, t) (got k=%d, t=%d)", k, t);
+  if (!attn_local_heads(n_heads, n_kv_heads, t, q_loc, kv_loc))
+    return fail(TP_ERR_INVALID_ARG,
+                "heads do not split over t=%d (n_heads=%lld must divide by t and by n_kv_heads=%lld; "
+                "n_kv_heads must divide by t or t by n_kv_heads)",
+                t, (long long)n_heads, (long long)n_kv_heads);
+  if (n_heads * head_dim > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
+  return TP_OK;
+}
+
+}  // namespace
+
+TP_API int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim, int32_t t) {
+  int64_t q_loc = 0, kv_loc = 0;
+  if (head_dim < 1 || head_dim > kMaxDim || t > tpmlp::kMaxPartials ||
+      !attn_local_heads(n_heads, n_kv_heads, t, &q_loc, &kv_loc))
+    return -1;
+  return (q_loc + 2 * kv_loc) * head_dim;
+}
+
+TP_API tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
+                                     int64_t head_dim, int32_t t, int32_t k, int32_t act_dtype,
+                                     int32_t w_dtype, const void* x, int64_t ldx, const void* w_qkv,
+                                     int64_t ldw, const float* s_qkv, void* qkv, int64_t ldq, void* stream) {
+  int64_t q_loc = 0, kv_loc = 0;
+  tp_status st = check_attn(M, h, n_heads, n_kv_heads, head_dim, t, k, &q_loc, &kv_loc);
+  if (st != TP_OK) return st;
+  const int64_t n_loc = (q_loc + 2 * kv_loc) * head_dim;
+  return linear_impl(M, n_loc, h, act_dtype, w_dtype, x, ldx, w_qkv, ldw, s_qkv, qkv, ldq, false,
+                     tpmlp::K_QKV_DECODE, tpmlp::K_QKV_PREFILL, tpmlp::K_QKV_F32, stream);
+}
+
+TP_API tp_status tp_attn_out_forward(int64_t M, int64_t h, int64_t n_heads, int64_t head_dim, int32_t t,
+                                     int32_t k, int32_t act_dtype, int32_t w_dtype, const void* attn,
+                                     int64_t lda, const void* w_o, int64_t ldw, const float* s_o,
+                                     float* partial, int64_t ldp, void* stream) {
+  int64_t q_loc = 0, kv_loc = 0;
+  // the output projection sees only the query heads; any KV count that
+  // splits them is accepted (n_kv_heads = n_heads)
+  tp_status st = check_attn(M, h, n_heads, n_heads, head_dim, t, k, &q_loc, &kv_loc);
+  if (st != TP_OK) return st;
+  return linear_impl(M, h, q_loc * head_dim, act_dtype, w_dtype, attn, lda, w_o, ldw, s_o, partial, ldp, true,
+                     tpmlp::K_OPROJ_DECODE, tpmlp::K_OPROJ_PREFILL, tpmlp::K_OPROJ_F32, stream);
 }
 
 TP_API const char* tp_status_string(int32_t status) {

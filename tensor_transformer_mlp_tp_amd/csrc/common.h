@@ -5,6 +5,8 @@
 #include <hip/hip_ext.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace tpmlp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -13,17 +15,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-// Kernel kinds for the timing record (kept in sync with kKindNames in abi.cpp).
-enum KernelKind : int {
-  K_GATEUP_DECODE = 0,
-  K_DOWN_DECODE = 1,
-  K_GATEUP_PREFILL = 2,
-  K_DOWN_PREFILL = 3,
-  K_PARTIAL_REDUCE = 4,
-  K_GATEUP_F32 = 5,
-  K_DOWN_F32 = 6,
-  K_NUM_KINDS = 7
-};
 
 // Implemented in abi.cpp: returns the start/stop events to attach to the next
 // launch of `kind` when timing is on, or null events.
@@ -73,6 +64,18 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Four consecutive outputs at element index idx of `out`: fp32, or bf16
+// rounded to nearest even (OBF).
+template <bool OBF>
+__device__ __forceinline__ void store_out4(void* out, int64_t idx, f32x4 v) {
+  if constexpr (OBF) {
+    const u32x2 pk = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + idx) = pk;
+  } else {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + idx) = v;
+  }
+}
 
 // 16x16x32 bf16 MFMA: D(16x16) += A(16x32) * B(32x16).  Lane l supplies row
 // (l % 16) of A and column (l % 16) of B, each with the eight k values of

@@ -224,11 +224,12 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   });
 }
 
-template <int NT, int RB, int WAVES, int UNROLL, bool FP8>
+// out (M x N) = a_in (M x K) * wd^T, wd N x K; fp32 or bf16 (OBF) output.
+template <int NT, int RB, int WAVES, int UNROLL, bool FP8, bool OBF>
 __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
-    float* __restrict__ p, int64_t ldp) {
+    void* __restrict__ p, int64_t ldp) {
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KSTEP = FP8 ? 64 : 32;
   const int lane = threadIdx.x & 63;
@@ -270,7 +271,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
       }
-      *reinterpret_cast<f32x4*>(p + (int64_t)tok * ldp + f) = v;
+      store_out4<OBF>(p, (int64_t)tok * ldp + f, v);
     }
   });
 }
@@ -644,11 +645,11 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
   });
 }
 
-template <int NT, int RB, bool FP8, bool XD>
+template <int NT, int RB, bool FP8, bool XD, bool OBF>
 __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
-    float* __restrict__ p, int64_t ldp) {
+    void* __restrict__ p, int64_t ldp) {
   using SS = StreamShape<NT, RB, FP8, XD>;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
@@ -693,7 +694,7 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
       }
-      *reinterpret_cast<f32x4*>(p + (int64_t)tok * ldp + f) = v;
+      store_out4<OBF>(p, (int64_t)tok * ldp + f, v);
     }
   });
 }
@@ -709,24 +710,22 @@ constexpr int kWaves = TPMLP_DECODE_WAVES;
 constexpr int kUnroll = TPMLP_DECODE_UNROLL;
 
 template <int NT, bool FP8>
-hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
+hipError_t gateup_v1(const ShardArgs& a, hipStream_t stream) {
   // Row blocks per workgroup: with more token blocks, two weight blocks share
   // each activation fragment load.  Batches shrink as fragments per step grow.
-  constexpr int RB_GU = NT >= 3 ? 2 : 1;
-  constexpr int UN_GU = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
-  constexpr int RB_DN = 1;
-  constexpr int UN_DN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
-  const dim3 block(kWaves * 64);
-  const dim3 grid_gu((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU));
-  hipError_t e = launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB_GU, kWaves, UN_GU, FP8>, grid_gu,
-                        block, 0, stream, a.M, a.h, a.I_s, a.x,
-                        (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su,
-                        (uint16_t*)a.a, a.lda);
-  if (e != hipSuccess) return e;
-  const dim3 grid_dn((a.h + 16 * RB_DN - 1) / (16 * RB_DN));
-  return launch(K_DOWN_DECODE, down_decode_kernel<NT, RB_DN, kWaves, UN_DN, FP8>, grid_dn, block, 0,
-                stream, a.M, a.h, a.I_s, (const uint16_t*)a.a, a.lda, (const uint8_t*)a.wd,
-                a.ldw_down, a.sd, a.p, a.ldp);
+  constexpr int RB = NT >= 3 ? 2 : 1;
+  constexpr int UN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
+  return launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB, kWaves, UN, FP8>,
+                dim3((a.I_s + 8 * RB - 1) / (8 * RB)), dim3(kWaves * 64), 0, stream, a.M, a.h, a.I_s, a.x,
+                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+}
+
+template <int NT, bool FP8, bool OBF>
+hipError_t rowgemm_v1(const RowGemm& g, hipStream_t stream) {
+  constexpr int UN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
+  return launch(g.kind_decode, down_decode_kernel<NT, 1, kWaves, UN, FP8, OBF>, dim3((g.N + 15) / 16),
+                dim3(kWaves * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a, g.lda,
+                (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo);
 }
 
 #ifndef TPMLP_DECODE_RB_WIDE
@@ -743,56 +742,78 @@ hipError_t run_decode(const ShardArgs& a, hipStream_t stream) {
 #define TPMLP_DECODE_XD 1
 #endif
 
+// Up to 16 tokens: one 16-row block per wave, activations from registers
+// (most workgroups).  More tokens: RB row blocks per wave share each
+// activation fragment, and the activations come through the ring (where its
+// slots fit the LDS: fp8 weights have twice the k per slot).
 template <int NT, bool FP8>
-hipError_t run_stream(const ShardArgs& a, hipStream_t stream) {
-  // Up to 16 tokens: one 16-row block per wave, activations from registers
-  // (most workgroups).  More tokens: RB row blocks per wave share each
-  // activation fragment, and the activations come through the ring (where
-  // its slots fit the LDS: fp8 weights have twice the k per slot).
-  constexpr bool XD = TPMLP_DECODE_XD && NT >= 2 && (!FP8 || NT == 2);
-  constexpr int RB_GU = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
-  constexpr int RB_DN = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
-  hipError_t e = launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB_GU, FP8, XD>,
-                        dim3((a.I_s + 8 * RB_GU - 1) / (8 * RB_GU)), dim3(StreamShape<NT, RB_GU, FP8, XD>::WV * 64),
-                        0, stream, a.M, a.h, a.I_s, a.x, (const uint8_t*)a.wg,
-                        (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
-  if (e != hipSuccess) return e;
-  return launch(K_DOWN_DECODE, down_stream_kernel<NT, RB_DN, FP8, XD>, dim3((a.h + 16 * RB_DN - 1) / (16 * RB_DN)),
-                dim3(StreamShape<NT, RB_DN, FP8, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, (const uint16_t*)a.a,
-                a.lda, (const uint8_t*)a.wd, a.ldw_down, a.sd, a.p, a.ldp);
+constexpr bool kStreamXD = TPMLP_DECODE_XD && NT >= 2 && (!FP8 || NT == 2);
+
+template <int NT, bool FP8>
+hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
+  constexpr bool XD = kStreamXD<NT, FP8>;
+  constexpr int RB = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
+  return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8, XD>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
+                dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, a.x,
+                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+}
+
+template <int NT, bool FP8, bool OBF>
+hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
+  constexpr bool XD = kStreamXD<NT, FP8>;
+  constexpr int RB = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
+  return launch(g.kind_decode, down_stream_kernel<NT, RB, FP8, XD, OBF>, dim3((g.N + 16 * RB - 1) / (16 * RB)),
+                dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a,
+                g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo);
 }
 
 #ifndef TPMLP_DECODE_V2
 #define TPMLP_DECODE_V2 1
 #endif
+
+// The streaming kernels move whole 16-row x 256-byte slots along K: they need
+// K to be a multiple of 128 (bf16) / 256 (fp8) k-values; other shapes use the
+// register-batch kernels, which step 32 / 64 k-values at a time.
 template <bool FP8>
-hipError_t run_decode_nt(const ShardArgs& a, hipStream_t stream) {
-  // The streaming kernels move whole 16-row x 256-byte slots: they need h and
-  // I_s to be multiples of 128 (bf16) / 256 (fp8) k-values; other shapes use
-  // the register-batch kernels, which step 32 / 64 k-values at a time.
-  constexpr int KS = FP8 ? 256 : 128;
-  if (TPMLP_DECODE_V2 && a.h % KS == 0 && a.I_s % KS == 0) {
-    switch ((a.M + 15) / 16) {
-      case 1: return run_stream<1, FP8>(a, stream);
-      case 2: return run_stream<2, FP8>(a, stream);
-      case 3: return run_stream<3, FP8>(a, stream);
-      case 4: return run_stream<4, FP8>(a, stream);
-      default: return hipErrorInvalidValue;
-    }
-  }
+constexpr bool streams(int K) {
+  return TPMLP_DECODE_V2 && K % (FP8 ? 256 : 128) == 0;
+}
+
+template <bool FP8>
+hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
+  const bool st = streams<FP8>(a.h);
   switch ((a.M + 15) / 16) {
-    case 1: return run_decode<1, FP8>(a, stream);
-    case 2: return run_decode<2, FP8>(a, stream);
-    case 3: return run_decode<3, FP8>(a, stream);
-    case 4: return run_decode<4, FP8>(a, stream);
+    case 1: return st ? gateup_stream<1, FP8>(a, stream) : gateup_v1<1, FP8>(a, stream);
+    case 2: return st ? gateup_stream<2, FP8>(a, stream) : gateup_v1<2, FP8>(a, stream);
+    case 3: return st ? gateup_stream<3, FP8>(a, stream) : gateup_v1<3, FP8>(a, stream);
+    case 4: return st ? gateup_stream<4, FP8>(a, stream) : gateup_v1<4, FP8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool FP8, bool OBF>
+hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
+  const bool st = streams<FP8>(g.K);
+  switch ((g.M + 15) / 16) {
+    case 1: return st ? rowgemm_stream<1, FP8, OBF>(g, stream) : rowgemm_v1<1, FP8, OBF>(g, stream);
+    case 2: return st ? rowgemm_stream<2, FP8, OBF>(g, stream) : rowgemm_v1<2, FP8, OBF>(g, stream);
+    case 3: return st ? rowgemm_stream<3, FP8, OBF>(g, stream) : rowgemm_v1<3, FP8, OBF>(g, stream);
+    case 4: return st ? rowgemm_stream<4, FP8, OBF>(g, stream) : rowgemm_v1<4, FP8, OBF>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
+hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
+  if (g.fp8) return g.out_bf16 ? run_rowgemm<true, true>(g, stream) : run_rowgemm<true, false>(g, stream);
+  return g.out_bf16 ? run_rowgemm<false, true>(g, stream) : run_rowgemm<false, false>(g, stream);
+}
+
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream) {
-  return a.fp8 ? run_decode_nt<true>(a, stream) : run_decode_nt<false>(a, stream);
+  hipError_t e = a.fp8 ? run_gateup<true>(a, stream) : run_gateup<false>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_rowgemm_decode(down_of(a), stream);
 }
 
 }  // namespace tpmlp

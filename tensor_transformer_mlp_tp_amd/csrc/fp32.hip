@@ -3,6 +3,8 @@
 // then the row-parallel down projection to an fp32 partial; "The
 // Tensor-Parallel Shard Group", scalablesystem.dev).
 //
+// The same row kernel serves the attention block's projections in fp32.
+//
 // This is the precision path for small problems and checks, not a
 // throughput path: one wave per output element, lanes split the dot product
 // and a butterfly of cross-lane adds finishes it (every lane ends with the
@@ -61,6 +63,12 @@ __global__ __launch_bounds__(kF32Waves * 64) void down_f32_kernel(
 
 }  // namespace
 
+hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream) {
+  const int64_t blocks = ((int64_t)g.M * g.N + kF32Waves - 1) / kF32Waves;
+  return launch(g.kind_f32, down_f32_kernel, dim3((unsigned)blocks), dim3(kF32Waves * 64), 0, stream, g.M,
+                g.N, g.K, (const float*)g.a, g.lda, (const float*)g.w, g.ldw, (float*)g.out, g.ldo);
+}
+
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream) {
   const dim3 block(kF32Waves * 64);
   const int64_t g1 = ((int64_t)a.M * a.I_s + kF32Waves - 1) / kF32Waves;
@@ -68,9 +76,7 @@ hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream) {
                         a.h, a.I_s, a.x, (const float*)a.wg,
                         (const float*)a.wu, a.ldw_gu, (float*)a.a, a.lda);
   if (e != hipSuccess) return e;
-  const int64_t g2 = ((int64_t)a.M * a.h + kF32Waves - 1) / kF32Waves;
-  return launch(K_DOWN_F32, down_f32_kernel, dim3((unsigned)g2), block, 0, stream, a.M, a.h, a.I_s,
-                (const float*)a.a, a.lda, (const float*)a.wd, a.ldw_down, a.p, a.ldp);
+  return launch_rowgemm_f32(down_of(a), stream);
 }
 
 }  // namespace tpmlp

@@ -6,6 +6,24 @@
 
 namespace tpmlp {
 
+// Kernel kinds for the timing record (kept in sync with kKindNames in abi.cpp).
+enum KernelKind : int {
+  K_GATEUP_DECODE = 0,
+  K_DOWN_DECODE = 1,
+  K_GATEUP_PREFILL = 2,
+  K_DOWN_PREFILL = 3,
+  K_PARTIAL_REDUCE = 4,
+  K_GATEUP_F32 = 5,
+  K_DOWN_F32 = 6,
+  K_QKV_DECODE = 7,
+  K_QKV_PREFILL = 8,
+  K_OPROJ_DECODE = 9,
+  K_OPROJ_PREFILL = 10,
+  K_QKV_F32 = 11,
+  K_OPROJ_F32 = 12,
+  K_NUM_KINDS = 13
+};
+
 constexpr int kMaxPartials = 64;
 
 struct PartialPtrs {
@@ -53,13 +71,45 @@ struct ShardArgs {
   bool fp8;                 // weights are e4m3fn codes
 };
 
+// out (M x N) = A (M x K) * W^T with W (N x K, (out, in) layout), fp32
+// accumulation, fp8 W scaled per output row, out fp32 or bf16: the down
+// projection of the MLP and the attention block's projections.
+struct RowGemm {
+  int M, N, K;
+  const void* a;            // M x K, bf16 (fp32 on the fp32 path)
+  int64_t lda;
+  const void* w;            // N x K, bf16 / fp8 codes / fp32
+  int64_t ldw;
+  const float* s;           // fp8 only: N per-row scales
+  void* out;                // M x N
+  int64_t ldo;
+  bool out_bf16;            // else fp32
+  bool fp8;
+  int kind_decode, kind_prefill, kind_f32;  // timing kinds of the three paths
+};
+
 // Largest M served by the weight-streaming (decode) kernels.
 constexpr int kDecodeMaxM = 64;
 
 hipError_t launch_partial_reduce(const PartialPtrs& ptrs, int t, float* out, int64_t n,
                                  hipStream_t stream);
+// The MLP's down projection of a shard: partial (M x h fp32) = a (M x I_s) * wd^T.
+inline RowGemm down_of(const ShardArgs& s) {
+  RowGemm g;
+  g.M = s.M; g.N = s.h; g.K = s.I_s;
+  g.a = s.a; g.lda = s.lda;
+  g.w = s.wd; g.ldw = s.ldw_down; g.s = s.sd;
+  g.out = s.p; g.ldo = s.ldp;
+  g.out_bf16 = false; g.fp8 = s.fp8;
+  g.kind_decode = K_DOWN_DECODE; g.kind_prefill = K_DOWN_PREFILL; g.kind_f32 = K_DOWN_F32;
+  return g;
+}
+
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
+hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
+hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
+hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
 
 }  // namespace tpmlp

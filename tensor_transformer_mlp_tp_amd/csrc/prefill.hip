@@ -135,7 +135,7 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   return TileCoord{first_m + i % gsize, i / gsize};
 }
 
-template <bool SWIGLU, bool FP8, int BK, int NS, int WV>
+template <bool SWIGLU, bool FP8, int BK, int NS, int WV, bool OBF>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
@@ -376,7 +376,6 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
       }
     }
   } else {
-    float* p = reinterpret_cast<float*>(out);
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -395,7 +394,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
           f32x4 v;
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
-          *reinterpret_cast<f32x4*>(p + (int64_t)tok * ld_out + f) = v;
+          store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
         }
       }
     }
@@ -417,37 +416,47 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 #define TPMLP_PREFILL_WAVES 4
 #endif
 
+constexpr int kBK = TPMLP_PREFILL_BK;
+constexpr int kWV = TPMLP_PREFILL_WAVES;
 template <bool FP8>
-hipError_t run_prefill(const ShardArgs& a, hipStream_t stream) {
-  constexpr int BK = TPMLP_PREFILL_BK;
-  constexpr int NS = FP8 ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
-  constexpr int WV = TPMLP_PREFILL_WAVES;
+constexpr int kNS = FP8 ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
+
+template <bool FP8>
+hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.M + BM - 1) / BM;
-  const dim3 block(WV * 64);
-  {
-    const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
-    hipError_t e = launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.I_s,
-                          a.h, a.x, (const uint8_t*)a.wg,
-                          (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m, tiles_n);
-    if (e != hipSuccess) return e;
-  }
-  const int tiles_n = (a.h + BN - 1) / BN;
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
+  return launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, kBK, kNS<FP8>, kWV, false>,
+                dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, a.x,
+                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m,
+                tiles_n);
+}
+
+template <bool FP8, bool OBF>
+hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
+  const int tiles_m = (g.M + BM - 1) / BM;
+  const int tiles_n = (g.N + BN - 1) / BN;
   XRows ar{};
-  ar.p[0] = a.a;
+  ar.p[0] = g.a;
   ar.nb = 1;
-  ar.rows = a.M;
-  ar.ld = a.lda;
-  return launch(K_DOWN_PREFILL, gemm_kernel<false, FP8, BK, NS, WV>, grid, block, 0, stream, a.M, a.h, a.I_s,
-                ar, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
-                a.ldw_down, a.sd, (const float*)nullptr, (void*)a.p, a.ldp, tiles_m, tiles_n);
+  ar.rows = g.M;
+  ar.ld = g.lda;
+  return launch(g.kind_prefill, gemm_kernel<false, FP8, kBK, kNS<FP8>, kWV, OBF>,
+                dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
+                (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr, g.out, g.ldo,
+                tiles_m, tiles_n);
 }
 
 }  // namespace
 
+hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
+  if (g.fp8) return g.out_bf16 ? run_rowgemm<true, true>(g, stream) : run_rowgemm<true, false>(g, stream);
+  return g.out_bf16 ? run_rowgemm<false, true>(g, stream) : run_rowgemm<false, false>(g, stream);
+}
+
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
-  return a.fp8 ? run_prefill<true>(a, stream) : run_prefill<false>(a, stream);
+  hipError_t e = a.fp8 ? run_gateup<true>(a, stream) : run_gateup<false>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_rowgemm_prefill(down_of(a), stream);
 }
 
 }  // namespace tpmlp

@@ -194,3 +194,80 @@ def test_reduce_scatter_rejects(rows, row_len, t, k, ptrs, out, status):
 def test_reduce_scatter_empty_is_noop():
     assert rs_call(0, 16, 2, 1, [P, P * 2], P * 4) == _lib.TP_OK
     assert rs_call(8, 0, 2, 1, None, None) == _lib.TP_ERR_INVALID_ARG   # the array is checked first
+
+
+# ------------------------------------------------------------- attention
+
+def test_attn_qkv_width():
+    lib = _lib.load()
+    assert lib.tp_attn_qkv_width(64, 8, 128, 8) == (8 + 2) * 128       # 70B at TP = 8
+    assert lib.tp_attn_qkv_width(64, 8, 128, 16) == (4 + 2) * 128      # KV heads replicated
+    assert lib.tp_attn_qkv_width(64, 8, 128, 1) == (64 + 16) * 128
+    assert lib.tp_attn_qkv_width(64, 8, 128, 3) == -1                  # 64 % 3
+    assert lib.tp_attn_qkv_width(64, 8, 128, 128) == -1                # t above 64 / above the heads
+    assert lib.tp_attn_qkv_width(48, 6, 128, 4) == -1                  # 6 KV heads, t = 4: neither divides
+    assert lib.tp_attn_qkv_width(64, 6, 128, 2) == -1                  # 64 % 6: groups not whole
+    assert lib.tp_attn_qkv_width(64, 8, 0, 8) == -1
+
+
+def qkv_call(M=1, h=128, nh=8, nkv=2, d=32, t=2, k=0, act=BF16, w=BF16, x=P, ldx=None, wq=P * 2, ldw=None,
+             s=None, out=P * 8, ldq=None):
+    lib = _lib.load()
+    n_loc = lib.tp_attn_qkv_width(nh, nkv, d, t) if t > 0 else 16
+    n_loc = max(int(n_loc), 16)
+    return lib.tp_attn_qkv_forward(M, h, nh, nkv, d, t, k, act, w, x, ldx if ldx is not None else h, wq,
+                                   ldw if ldw is not None else h, s, out, ldq if ldq is not None else n_loc, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nh=6, nkv=4), _lib.TP_ERR_INVALID_ARG),   # 6 % 4: KV groups not whole
+    (dict(nh=9, nkv=3, t=2), _lib.TP_ERR_INVALID_ARG),  # 9 % 2
+    (dict(nkv=3, nh=9, t=6), _lib.TP_ERR_INVALID_ARG),
+    (dict(t=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(k=2), _lib.TP_ERR_INVALID_ARG),
+    (dict(M=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(d=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(x=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(out=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(w=FP8), _lib.TP_ERR_INVALID_ARG),         # fp8 without scales
+    (dict(s=P * 4), _lib.TP_ERR_INVALID_ARG),       # scales with bf16 weights
+    (dict(act=F32, w=BF16), _lib.TP_ERR_UNSUPPORTED),
+    (dict(h=96), _lib.TP_ERR_UNSUPPORTED),          # h % 64
+    (dict(d=36), _lib.TP_ERR_UNSUPPORTED),          # n_loc = 216, not a multiple of 16
+    (dict(ldx=64), _lib.TP_ERR_INVALID_ARG),
+    (dict(ldq=100), _lib.TP_ERR_INVALID_ARG),
+    (dict(x=P + 2), _lib.TP_ERR_UNSUPPORTED),
+    (dict(ldw=132), _lib.TP_ERR_UNSUPPORTED),
+    (dict(out=P * 2 + 64), _lib.TP_ERR_INVALID_ARG),   # output overlaps the weight
+    (dict(out=P), _lib.TP_ERR_INVALID_ARG),            # output overlaps x
+])
+def test_attn_qkv_rejects(kw, status):
+    lib = _lib.load()
+    assert qkv_call(**kw) == status
+    assert lib.tp_last_error() not in (b"", None)
+
+
+def oproj_call(M=1, h=128, nh=8, d=32, t=2, k=0, act=BF16, w=BF16, a=P, lda=None, wo=P * 2, ldw=None,
+               s=None, p=P * 8, ldp=None):
+    lib = _lib.load()
+    K = nh // t * d if t > 0 and nh % t == 0 else 64
+    return lib.tp_attn_out_forward(M, h, nh, d, t, k, act, w, a, lda if lda is not None else K, wo,
+                                   ldw if ldw is not None else K, s, p, ldp if ldp is not None else h, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(nh=6, t=4), _lib.TP_ERR_INVALID_ARG),     # 6 % 4
+    (dict(t=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(k=-1), _lib.TP_ERR_INVALID_ARG),
+    (dict(h=0), _lib.TP_ERR_INVALID_ARG),
+    (dict(a=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(w=FP8), _lib.TP_ERR_INVALID_ARG),
+    (dict(d=24), _lib.TP_ERR_UNSUPPORTED),          # K = 96, not a multiple of 64
+    (dict(h=120), _lib.TP_ERR_UNSUPPORTED),         # h % 16
+    (dict(lda=64 + 32, d=48), _lib.TP_ERR_INVALID_ARG),  # lda < K = 192
+    (dict(ldp=64), _lib.TP_ERR_INVALID_ARG),
+    (dict(p=P * 8 + 4), _lib.TP_ERR_UNSUPPORTED),
+    (dict(p=P), _lib.TP_ERR_INVALID_ARG),           # partial overlaps the input
+])
+def test_attn_out_rejects(kw, status):
+    assert oproj_call(**kw) == status

@@ -18,7 +18,9 @@ Recipe (one rule for every tensor):
 
 Seeds: ``seed = 1000 * config_id + tensor_id + 1_000_000 * weight_set`` with
 tensor ids X = 1, W_gate = 2 + 10 k, W_up = 3 + 10 k, W_down = 4 + 10 k for
-shard k, and partial buffer j = 100 + j.  ``weight_set`` 0 is the set the
+shard k, and partial buffer j = 100 + j; for the attention projections
+W_qkv = 5 + 10 k, W_o = 6 + 10 k, the output projection's input O = 7, and
+the full W_q, W_k, W_v, W_o of the split-against-unsplit case 200 .. 203.  ``weight_set`` 0 is the set the
 parity tests use; the benchmark rotates through further sets so that weight
 reads come from HBM rather than from the 256 MB last-level cache.
 
@@ -58,6 +60,34 @@ CONFIGS = {
 
 TENSOR_X = 1
 TENSOR_PARTIAL_BASE = 100
+
+# Attention-block projections of one rank (Llama 3.1 70B: 64 query heads,
+# 8 KV heads of size 128; "Constraints" section of the scalablesystem.dev page
+# and "The KV cache splits too, until it doesn't" on the vidyal.ai page).
+# O stands for the attention output of the rank's heads (the input of the
+# output projection), drawn like X.
+ATTN_CONFIGS = {
+    6: dict(name="llama70b_tp8_attn", desc="70B-shaped TP=8 rank, attention projections",
+            M=(1, 8, 64, 4096), h=8192, n_heads=64, n_kv_heads=8, head_dim=128, t=8,
+            act="bf16", w="bf16", std_x=1.0, std_w=0.02),
+    7: dict(name="llama70b_tp4_attn_fp8", desc="70B-shaped TP=4 rank, attention projections, fp8 weights",
+            M=(32, 2048), h=8192, n_heads=64, n_kv_heads=8, head_dim=128, t=4,
+            act="bf16", w="e4m3fn", std_x=1.0, std_w=0.02),
+    8: dict(name="tiny_attn_t4", desc="tiny attention projections, t=4 (KV heads replicated)",
+            M=(16,), h=256, n_heads=8, n_kv_heads=2, head_dim=32, t=4,
+            act="f32", w="f32", std_x=1.0, std_w=1.0 / 16.0),
+}
+
+TENSOR_O = 7
+TENSOR_WQ_FULL, TENSOR_WK_FULL, TENSOR_WV_FULL, TENSOR_WO_FULL = 200, 201, 202, 203
+
+
+def tensor_id_qkv(k):
+    return 5 + 10 * k
+
+
+def tensor_id_o(k):
+    return 6 + 10 * k
 
 
 def tensor_id_gate(k):
@@ -210,6 +240,38 @@ def make_partials(config_id, t, n, weight_set=0):
                      list(range(t)))
 
 
+def attn_widths(n_heads, n_kv_heads, head_dim, t):
+    """(n_loc, K_o): a rank's QKV output width and output-projection input
+    width.  KV heads split over t, or one per rank when t is a multiple of
+    their count."""
+    q_loc = n_heads // t
+    kv_loc = n_kv_heads // t if n_kv_heads % t == 0 else 1
+    return (q_loc + 2 * kv_loc) * head_dim, q_loc * head_dim
+
+
+def make_attn_weights(config_id, h, n_loc, k_o, k, dtype, std, weight_set=0):
+    """Rank k's projection weights drawn directly: W_qkv_k (n_loc x h) and
+    W_o_k (h x k_o), storage arrays plus (e4m3fn) per-row scales."""
+    jobs = [(tensor_id_qkv(k), (n_loc, h)), (tensor_id_o(k), (h, k_o))]
+    q, o = _parallel(lambda j: to_storage(draw_f32(seed_of(config_id, j[0], weight_set), j[1], std), dtype), jobs)
+    return dict(w_qkv=q["data"], s_qkv=q["scale"], w_o=o["data"], s_o=o["scale"])
+
+
+def make_attn_out_input(config_id, M, k_o, dtype, std=1.0, weight_set=0):
+    """The output projection's input O_k (M x k_o) in storage form."""
+    return to_storage(draw_f32(seed_of(config_id, TENSOR_O, weight_set), (M, k_o), std), dtype)["data"]
+
+
+def make_attn_full_weights(config_id, h, n_heads, n_kv_heads, head_dim, dtype, std, weight_set=0):
+    """Full W_q, W_k, W_v (per-head stacked rows, x h) and W_o (h x n_heads*d)
+    for the split-against-unsplit case."""
+    jobs = [(TENSOR_WQ_FULL, (n_heads * head_dim, h)), (TENSOR_WK_FULL, (n_kv_heads * head_dim, h)),
+            (TENSOR_WV_FULL, (n_kv_heads * head_dim, h)), (TENSOR_WO_FULL, (h, n_heads * head_dim))]
+    q, kk, v, o = _parallel(
+        lambda j: to_storage(draw_f32(seed_of(config_id, j[0], weight_set), j[1], std), dtype), jobs)
+    return dict(w_q=q["data"], w_k=kk["data"], w_v=v["data"], w_o=o["data"])
+
+
 # ---------------------------------------------------------------------------
 # accounting (algorithmic bytes and FLOPs; no arithmetic of the method)
 # ---------------------------------------------------------------------------
@@ -253,3 +315,16 @@ def down_bytes(M, h, I_s, act="bf16", w="bf16"):
 def reduce_bytes(n, t):
     """t fp32 reads plus one fp32 write per element."""
     return int((t + 1) * 4 * n)
+
+
+def linear_flops(M, N, K):
+    return 2 * int(M) * int(N) * int(K)
+
+
+def linear_bytes(M, N, K, act="bf16", w="bf16", out="bf16"):
+    """Algorithmic bytes of one projection: weight, input and output once
+    (+ per-row scales for e4m3fn)."""
+    b = N * K * BYTES[w] + M * K * BYTES[act] + M * N * BYTES[out]
+    if w == "e4m3fn":
+        b += N * 4
+    return int(b)
