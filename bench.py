@@ -15,6 +15,9 @@ Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
 (TP=4 fp8 weights: decode M=32 and prefill M=2048), prefill405b (8192 tokens),
 reduce70b / reduce405b (the 8-way reduces alone), sp_prefill70b (the
 sequence-parallel form: forward over eight row blocks of X, reduce-scatter),
+attn70b / attn_prefill70b (the same rank's attention-block projections: QKV,
+output projection to an fp32 partial, 8-way reduce; decode M=1, 8, 64 and
+prefill M=4096),
 copy (the reduce with one
 buffer over 1 GiB: a plain copy of known size, the calibration run for the
 HBM byte counters).
@@ -61,16 +64,18 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode70b",
                     choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
-                             "sp_prefill70b", "copy"])
+                             "sp_prefill70b", "attn70b", "attn_prefill70b", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     return ap.parse_args()
 
 
 KERNEL_SOURCES = {
-    "gateup_decode": ("decode.hip", "common.h"),
-    "gateup_prefill": ("prefill.hip", "common.h"),
-    "partial_reduce": ("reduce.hip", "common.h"),
+    "gateup_decode": ("decode.hip", "common.h", "internal.h"),
+    "gateup_prefill": ("prefill.hip", "common.h", "internal.h"),
+    "partial_reduce": ("reduce.hip", "common.h", "internal.h"),
+    "qkv_decode": ("decode.hip", "common.h", "internal.h"),
+    "qkv_prefill": ("prefill.hip", "common.h", "internal.h"),
 }
 
 
@@ -527,6 +532,222 @@ def bench_sp_prefill(tp, args):
     return out_d
 
 
+class AttnPhase:
+    """The attention block's two projections of a rank at M tokens (+ the
+    8-way reduce of the output projection's partial), buffers preallocated."""
+
+    def __init__(self, tp, cfg_id, M, c, with_reduce):
+        import torch
+        self.tp, self.M, self.c = tp, M, c
+        self.h, self.t = c["h"], c["t"]
+        self.n_loc, self.k_o = workloads.attn_widths(c["n_heads"], c["n_kv_heads"], c["head_dim"], c["t"])
+        self.x_host = workloads.make_x(cfg_id, M, self.h, "bf16")
+        self.o_host = workloads.make_attn_out_input(cfg_id, M, self.k_o, "bf16")
+        self.x, self.o = to_dev(self.x_host, "bf16"), to_dev(self.o_host, "bf16")
+        self.qkv = torch.empty((M, self.n_loc), dtype=torch.bfloat16, device="cuda")
+        self.partial = torch.empty((M, self.h), dtype=torch.float32, device="cuda")
+        self.with_reduce = with_reduce
+        if with_reduce:
+            self.others = [torch.from_numpy(o).cuda()
+                           for o in workloads.make_partials(cfg_id, self.t - 1, M * self.h, weight_set=M)]
+        self.calls = {}
+
+    def run(self, wset, time_qkv=None):
+        """time_qkv: (library, kind mask) to event-time this call's QKV launch only."""
+        key = id(wset)
+        if key not in self.calls:
+            c = self.c
+            q = self.tp.prepare_attn_qkv_forward(self.x, wset["w_qkv"], n_heads=c["n_heads"],
+                                                 n_kv_heads=c["n_kv_heads"], head_dim=c["head_dim"], t=self.t,
+                                                 k=0, s_qkv=wset["s_qkv"], out=self.qkv)
+            o = self.tp.prepare_attn_out_forward(self.o, wset["w_o"], n_heads=c["n_heads"], head_dim=c["head_dim"],
+                                                 t=self.t, k=0, s_o=wset["s_o"], partial=self.partial)
+            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others,
+                                                 out=self.partial.view(-1)) if self.with_reduce else None
+            self.calls[key] = (q, o, red)
+        q, o, red = self.calls[key]
+        if time_qkv is not None:
+            time_qkv[0].tp_profile_enable(time_qkv[1])
+            q()
+            time_qkv[0].tp_profile_enable(0)
+        else:
+            q()
+        o()
+        if red is not None:
+            red()
+
+    def qkv_bytes(self, w="bf16"):
+        return workloads.linear_bytes(self.M, self.n_loc, self.h, "bf16", w, "bf16")
+
+    def oproj_bytes(self, w="bf16"):
+        return workloads.linear_bytes(self.M, self.h, self.k_o, "bf16", w, "f32")
+
+    def bytes(self, w="bf16"):
+        b = self.qkv_bytes(w) + self.oproj_bytes(w)
+        if self.with_reduce:
+            b += workloads.reduce_bytes(self.M * self.h, self.t)
+        return b
+
+    def flops(self):
+        return workloads.linear_flops(self.M, self.n_loc, self.h) + workloads.linear_flops(self.M, self.h, self.k_o)
+
+
+def attn_weight_sets(cfg_id, c, n_sets):
+    import torch
+    n_loc, k_o = workloads.attn_widths(c["n_heads"], c["n_kv_heads"], c["head_dim"], c["t"])
+    sets = []
+    for s in range(n_sets):
+        ws = workloads.make_attn_weights(cfg_id, c["h"], n_loc, k_o, 0, c["w"], c["std_w"], weight_set=s)
+        sets.append(dict(w_qkv=to_dev(ws["w_qkv"], c["w"]), w_o=to_dev(ws["w_o"], c["w"]),
+                         s_qkv=None if ws["s_qkv"] is None else torch.from_numpy(ws["s_qkv"]).cuda(),
+                         s_o=None if ws["s_o"] is None else torch.from_numpy(ws["s_o"]).cuda()))
+        if s == 0:
+            host0 = ws
+    return sets, host0
+
+
+def bench_attn_decode(tp, args):
+    """70B-shaped TP=8 rank, attention projections at decode: for M = 1, 8 and
+    64 tokens, the column-parallel QKV projection (8 query heads + 1 KV head:
+    1280 columns), the row-parallel output projection (1024 -> 8192, fp32
+    partial) and the 8-way reduce of that partial."""
+    import oracle
+    cfg_id = 6
+    c = workloads.ATTN_CONFIGS[cfg_id]
+    h, t = c["h"], c["t"]
+    # 36 MiB of weights per set: enough sets that a step's weights come from HBM
+    n_sets = max(args.weight_sets, 16)
+    log("generating %d weight sets of the 70B TP=8 attention projections" % n_sets)
+    sets, host0 = attn_weight_sets(cfg_id, c, n_sets)
+    phases = [AttnPhase(tp, cfg_id, M, c, True) for M in (1, 8, 64)]
+    # An event-timed launch costs the host ~25 us against ~3 us for a plain
+    # one, and this step's kernels are short: timing all three QKV launches
+    # would make the loop host-bound.  Step i times the QKV launch of phase
+    # i % 3 only, so each M is sampled on a third of the timed steps.
+    lib = tp.load()
+    qmask = 1 << tp.kernel_kinds().index("qkv_decode")
+
+    def step(i):
+        wset = sets[i % len(sets)]
+        for idx, ph in enumerate(phases):
+            ph.run(wset, (lib, qmask) if i % 3 == idx else None)
+
+    def step_plain(i):
+        wset = sets[i % len(sets)]
+        for ph in phases:
+            ph.run(wset)
+
+    steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
+    elapsed, prof = timed(tp, step, steps, warmup, [])
+    prof_all = breakdown(tp, step_plain, steps, warmup + steps)
+    step_bytes = sum(ph.bytes() for ph in phases)
+    value = step_bytes * steps / elapsed / 1e9
+    per = {"qkv_decode": sum(ph.qkv_bytes() for ph in phases), "oproj_decode": sum(ph.oproj_bytes() for ph in phases),
+           "partial_reduce": sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)}
+    kern = {}
+    for name, b in per.items():
+        ms, cnt = prof_all.get(name, (0.0, 0))
+        kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
+                      "GBps": round(b * steps / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+    ms, cnt = prof["qkv_decode"]
+    # the timed launches: phase idx on the steps i with i % 3 == idx
+    timed_bytes = sum(ph.qkv_bytes() * sum(1 for i in range(warmup, warmup + steps) if i % 3 == idx)
+                      for idx, ph in enumerate(phases))
+    assert cnt == steps
+    achieved = timed_bytes / (ms * 1e-3) / 1e9
+    parity = None
+    if not args.no_cpu_baseline:
+        import torch
+        ph = phases[0]
+        ph.run(sets[0])
+        ph.calls[id(sets[0])][1]()   # the output projection alone (the step's reduce ran in place)
+        torch.cuda.synchronize()
+        ref_q = oracle.linear_from_storage(ph.x_host, "bf16", host0["w_qkv"], "bf16")
+        ref_p = oracle.linear_from_storage(ph.o_host, "bf16", host0["w_o"], "bf16")
+        q_bits = ph.qkv.view(torch.int16).cpu().numpy().view(np.uint16)
+        parity = {"qkv": oracle.rms_normalised_max_error(oracle.bf16_bits_to_f64(q_bits), ref_q),
+                  "oproj": oracle.rms_normalised_max_error(ph.partial.cpu().numpy(), ref_p)}
+    out = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 5), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic",
+               config={"workload": "70B-shaped TP=8 rank attention projections at decode (h=8192, 64/8 heads "
+                                   "of 128: QKV 8192->1280 bf16 out, o_proj 1024->8192 fp32 partial, bf16 "
+                                   "weights) at M=1, 8 and 64, each o_proj partial followed by the 8-way "
+                                   "fp32 reduce", "M": [1, 8, 64], "h": h, "t": t, "weight_sets": n_sets},
+               roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("qkv_decode", "attn70b"), "kernel": "qkv_decode",
+                         "per_launch_bytes": {str(ph.M): ph.qkv_bytes() for ph in phases}},
+               frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4), kernels=kern,
+               kernels_note="kernels: a further pass of the same number of steps with every launch event-timed",
+               parity_err_M1=parity)
+    if not args.no_cpu_baseline:
+        hp = [[np.zeros(ph.M * h, np.float32)] * (t - 1) for ph in phases]
+
+        def once():
+            for ph, others in zip(phases, hp):
+                oracle.linear_from_storage(ph.x_host, "bf16", host0["w_qkv"], "bf16")
+                p = oracle.linear_from_storage(ph.o_host, "bf16", host0["w_o"], "bf16")
+                oracle.fold_fp32([p.astype(np.float32).reshape(-1)] + others)
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(once, step_bytes / 1e9, "GB/s",
+                                           "one full step (M=1, 8, 64 QKV and o_proj from the bf16 weight "
+                                           "bytes + 8-way fp32 folds), repeated >= 10 s")
+    return out
+
+
+def bench_attn_prefill(tp, args):
+    """70B-shaped TP=8 rank, attention projections at prefill (M = 4096):
+    QKV, output projection and the 8-way reduce of its partial."""
+    import oracle
+    cfg_id, M = 6, 4096
+    c = workloads.ATTN_CONFIGS[cfg_id]
+    h, t = c["h"], c["t"]
+    sets, host0 = attn_weight_sets(cfg_id, c, 1)
+    ph = AttnPhase(tp, cfg_id, M, c, True)
+
+    def step(i):
+        ph.run(sets[0])
+
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    elapsed, prof_q = timed(tp, step, steps, warmup, ["qkv_prefill"])
+    prof = breakdown(tp, step, steps, warmup + steps)
+    prof["qkv_prefill"] = prof_q["qkv_prefill"]
+    value = ph.flops() * steps / elapsed / 1e12
+    f = {"qkv_prefill": workloads.linear_flops(M, ph.n_loc, h), "oproj_prefill": workloads.linear_flops(M, h, ph.k_o)}
+    kern = {}
+    for name, fl in f.items():
+        ms, n = prof[name]
+        kern[name] = {"launches": n, "avg_us": 1e3 * ms / n, "TFLOPs": round(fl * n / (ms * 1e-3) / 1e12, 1)}
+    ms, n = prof["partial_reduce"]
+    kern["partial_reduce"] = {"launches": n, "avg_us": 1e3 * ms / n,
+                              "GBps": round(workloads.reduce_bytes(M * h, t) * n / (ms * 1e-3) / 1e9, 1)}
+    q_tf = kern["qkv_prefill"]["TFLOPs"]
+    out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16", data="synthetic",
+               config={"workload": "70B-shaped TP=8 rank attention projections at prefill, M=4096 (QKV "
+                                   "8192->1280, o_proj 1024->8192 fp32 partial, bf16) + 8-way fp32 reduce of "
+                                   "4096x8192", "M": M, "h": h, "t": t},
+               roofline={"bound": "mfma", "achieved": q_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(q_tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("qkv_prefill", "attn_prefill70b"), "kernel": "qkv_prefill",
+                         "per_launch_flop": f["qkv_prefill"]},
+               kernels=kern)
+    if not args.no_cpu_baseline:
+        rows = np.arange(0, M, M // 16)
+
+        def once():
+            oracle.linear_from_storage(ph.x_host[rows], "bf16", host0["w_qkv"], "bf16")
+            oracle.linear_from_storage(ph.o_host[rows], "bf16", host0["w_o"], "bf16")
+        log("timing the CPU oracle")
+        fl = workloads.linear_flops(len(rows), ph.n_loc, h) + workloads.linear_flops(len(rows), h, ph.k_o)
+        out["cpu_baseline"] = cpu_baseline(once, fl / 1e12, "TFLOP/s",
+                                           "QKV and o_proj for %d of the %d token rows (decoding the weight "
+                                           "bytes each time), repeated >= 10 s" % (len(rows), M))
+    return out
+
+
 def bench_copy(tp, args):
     """One-buffer reduce over 1 GiB: reads n*4 bytes and writes n*4 bytes, nothing else."""
     import torch
@@ -576,6 +797,10 @@ def main():
         out = bench_copy(tp, args)
     elif args.workload == "sp_prefill70b":
         out = bench_sp_prefill(tp, args)
+    elif args.workload == "attn70b":
+        out = bench_attn_decode(tp, args)
+    elif args.workload == "attn_prefill70b":
+        out = bench_attn_prefill(tp, args)
     else:
         out = bench_reduce(tp, args, 5)
     print(json.dumps(out), flush=True)

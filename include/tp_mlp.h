@@ -257,17 +257,33 @@ int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
  *   qkv        M x n_loc output in the activation dtype, leading dimension
  *              ldq >= n_loc, same column order as w_qkv's rows; overwritten;
  *              must not overlap an input.
+ *   workspace, workspace_bytes   device scratch of at least
+ *              tp_attn_qkv_workspace_bytes(...) bytes, 256-byte aligned, not
+ *              overlapping any argument; may be NULL when that size is 0.
+ *              It holds fp32 sums over ranges of h when the projection is
+ *              split along h across workgroups (a narrow output: few rows of
+ *              W to spread over the chip).  Contents on entry are ignored;
+ *              concurrent calls must not share it.
  *
  * Requirements (else TP_ERR_UNSUPPORTED): with bf16 activations h % 64 == 0
  * and n_loc % 16 == 0, pointers and rows 16-byte aligned, scales 4-byte
- * aligned; with fp32, 4-byte alignment.  No workspace.  Deterministic.
+ * aligned; with fp32, 4-byte alignment.  Deterministic: the split and the
+ * order of the partial sums depend on the shape only.
  */
 tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
                               int64_t head_dim, int32_t t, int32_t k,
                               int32_t act_dtype, int32_t w_dtype,
                               const void* x, int64_t ldx,
                               const void* w_qkv, int64_t ldw, const float* s_qkv,
-                              void* qkv, int64_t ldq, void* stream);
+                              void* qkv, int64_t ldq,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes tp_attn_qkv_forward needs for these arguments (0 if none
+ * is needed or the arguments are invalid).
+ */
+size_t tp_attn_qkv_workspace_bytes(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
+                                   int64_t head_dim, int32_t t, int32_t act_dtype, int32_t w_dtype);
 
 /*
  * Rank k's row-parallel output projection: partial P_k (M x h fp32).
@@ -286,7 +302,7 @@ tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_k
  *              overlap an input.
  *
  * Other arguments and requirements as tp_attn_qkv_forward, with K in place
- * of h (K % 64 == 0) and h in place of n_loc (h % 16 == 0).
+ * of h (K % 64 == 0) and h in place of n_loc (h % 16 == 0).  No workspace.
  */
 tp_status tp_attn_out_forward(int64_t M, int64_t h, int64_t n_heads, int64_t head_dim,
                               int32_t t, int32_t k,

@@ -25,7 +25,7 @@ from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, EXPORTED_SYMBOLS,  #
 
 __all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
            "shard_forward_sp", "prepare_shard_forward_sp", "partial_reduce_scatter",
-           "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_forward", "prepare_attn_qkv_forward",
+           "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_workspace_bytes", "attn_qkv_forward", "prepare_attn_qkv_forward",
            "attn_out_forward", "prepare_attn_out_forward", "profile_reserve",
            "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "kernel_kinds",
            "TPError", "load"]
@@ -279,18 +279,27 @@ def _check_scales(s, device):
         raise ValueError("scales must be contiguous float32 tensors on %s" % device)
 
 
-def attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s_qkv=None, out=None, stream=None):
+def attn_qkv_workspace_bytes(M, h, n_heads, n_kv_heads, head_dim, t, act_dtype=torch.bfloat16,
+                             w_dtype=torch.bfloat16):
+    """Bytes of device workspace ``attn_qkv_forward`` needs (often 0)."""
+    return int(_lib.load().tp_attn_qkv_workspace_bytes(int(M), int(h), int(n_heads), int(n_kv_heads),
+                                                       int(head_dim), int(t), _act_code(act_dtype),
+                                                       _w_code(w_dtype)))
+
+
+def attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s_qkv=None, out=None, workspace=None,
+                     stream=None):
     """Rank k's column-parallel QKV projection X W_qkv_k^T (M x n_loc, in x's
     dtype); ``w_qkv`` is the rank's (n_loc, h) rows [q heads | k heads | v
     heads] (``include/tp_mlp.h``: tp_attn_qkv_forward)."""
     call = prepare_attn_qkv_forward(x, w_qkv, n_heads=n_heads, n_kv_heads=n_kv_heads, head_dim=head_dim, t=t,
-                                    k=k, s_qkv=s_qkv, out=out, stream=stream)
+                                    k=k, s_qkv=s_qkv, out=out, workspace=workspace, stream=stream)
     call()
     return call.out
 
 
 def prepare_attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s_qkv=None, out=None,
-                             stream=None):
+                             workspace=None, stream=None):
     """Marshal an attn_qkv_forward once; returns a PreparedCall (``out``)."""
     device = x.device
     _check_matrix("x", x, device)
@@ -309,10 +318,16 @@ def prepare_attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s
         if out.dtype != x.dtype or tuple(out.shape) != (M, n_loc):
             raise ValueError("out must be %s of shape (%d, %d)" % (x.dtype, M, n_loc))
     lib = _lib.load()
+    need = attn_qkv_workspace_bytes(M, h, n_heads, n_kv_heads, head_dim, t, x.dtype, w_qkv.dtype)
+    if workspace is None and need > 0:
+        workspace = alloc_workspace(need, device)
+    elif workspace is not None and workspace.device != device:
+        raise ValueError("workspace must be on %s" % device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (M, h, int(n_heads), int(n_kv_heads), int(head_dim), int(t), int(k), _act_code(x.dtype),
             _w_code(w_qkv.dtype), _ptr(x), x.stride(0), _ptr(w_qkv), w_qkv.stride(0), _ptr(s_qkv), _ptr(out),
-            out.stride(0), _stream_of(device, stream))
-    call = PreparedCall(lib.tp_attn_qkv_forward, args, (x, w_qkv, s_qkv, out))
+            out.stride(0), _ptr(workspace), ws_bytes, _stream_of(device, stream))
+    call = PreparedCall(lib.tp_attn_qkv_forward, args, (x, w_qkv, s_qkv, out, workspace))
     call.out = out
     return call
 

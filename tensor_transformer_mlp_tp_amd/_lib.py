@@ -26,6 +26,7 @@ EXPORTED_SYMBOLS = (
     "tp_partial_reduce_scatter",
     "tp_attn_qkv_width",
     "tp_attn_qkv_forward",
+    "tp_attn_qkv_workspace_bytes",
     "tp_attn_out_forward",
     "tp_status_string",
     "tp_last_error",
@@ -77,7 +78,9 @@ def load():
     lib.tp_attn_qkv_width.restype = c_i64
     lib.tp_attn_qkv_forward.argtypes = [
         c_i64, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
-        vp, c_i64, vp, c_i64, vp, vp, c_i64, vp]
+        vp, c_i64, vp, c_i64, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
+    lib.tp_attn_qkv_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32]
+    lib.tp_attn_qkv_workspace_bytes.restype = ctypes.c_size_t
     lib.tp_attn_qkv_forward.restype = c_i32
     lib.tp_attn_out_forward.argtypes = [
         c_i64, c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,

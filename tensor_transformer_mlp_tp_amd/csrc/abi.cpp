@@ -110,7 +110,7 @@ size_t g_prof_used = 0;
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
     "partial_reduce", "gateup_f32", "down_f32", "qkv_decode", "qkv_prefill",
-    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32"};
+    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish"};
 
 // Appends one start/stop event pair to the timing pool.
 bool prof_grow() {
@@ -337,9 +337,16 @@ bool attn_local_heads(int64_t n_heads, int64_t n_kv_heads, int32_t t, int64_t* q
 // Checks and launch shared by the attention projections:
 // out (M x N) = a (M x K) * w^T, w N x K, out in the activation dtype
 // (out_f32 forces fp32).
+// Split-K scratch the projection needs (bytes, before rounding).
+int64_t linear_workspace_need(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype) {
+  if (act_dtype != TP_BF16 || M > tpmlp::kDecodeMaxM) return 0;
+  return tpmlp::rowgemm_decode_workspace_bytes((int)M, (int)N, (int)K, w_dtype == TP_FP8_E4M3FN);
+}
+
 tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype, const void* a,
                       int64_t lda, const void* w, int64_t ldw, const float* s, void* out, int64_t ldo,
-                      bool out_f32, int kind_decode, int kind_prefill, int kind_f32, void* stream) {
+                      bool out_f32, void* workspace, size_t workspace_bytes, bool has_workspace,
+                      int kind_decode, int kind_prefill, int kind_f32, void* stream) {
   if (elem_bytes(act_dtype) == 0 || elem_bytes(w_dtype) == 0)
     return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act_dtype, w_dtype);
   if (act_dtype == TP_FP8_E4M3FN) return fail(TP_ERR_UNSUPPORTED, "fp8 activations are not supported");
@@ -372,6 +379,17 @@ tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_
   if (overlap(e_out, extent(a, M, K, lda, ea)) || overlap(e_out, extent(w, N, K, ldw, ew)) ||
       (s && overlap(e_out, extent(s, 1, N, N, 4))))
     return fail(TP_ERR_INVALID_ARG, "output overlaps an input");
+  const int64_t need = has_workspace ? linear_workspace_need(M, N, K, act_dtype, w_dtype) : 0;
+  if (need > 0) {
+    if (!workspace || (int64_t)workspace_bytes < need)
+      return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
+                  (unsigned long long)workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+    const Extent ew_ = {reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need};
+    if (overlap(ew_, e_out) || overlap(ew_, extent(a, M, K, lda, ea)) || overlap(ew_, extent(w, N, K, ldw, ew)) ||
+        (s && overlap(ew_, extent(s, 1, N, N, 4))))
+      return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input or the output");
+  }
 
   tpmlp::RowGemm g;
   g.M = (int)M;
@@ -386,6 +404,7 @@ tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_
   g.ldo = ldo;
   g.out_bf16 = act_dtype == TP_BF16 && !out_f32;
   g.fp8 = fp8;
+  g.ws = need > 0 ? static_cast<float*>(workspace) : nullptr;
   g.kind_decode = kind_decode;
   g.kind_prefill = kind_prefill;
   g.kind_f32 = kind_f32;
@@ -427,16 +446,29 @@ TP_API int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t he
   return (q_loc + 2 * kv_loc) * head_dim;
 }
 
+TP_API size_t tp_attn_qkv_workspace_bytes(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
+                                          int64_t head_dim, int32_t t, int32_t act_dtype, int32_t w_dtype) {
+  int64_t q_loc = 0, kv_loc = 0;
+  if (M < 1 || M > kMaxDim || h < 1 || h > kMaxDim || head_dim < 1 || t < 1 || t > tpmlp::kMaxPartials ||
+      !attn_local_heads(n_heads, n_kv_heads, t, &q_loc, &kv_loc) || n_heads * head_dim > kMaxDim)
+    return 0;
+  if (elem_bytes(act_dtype) == 0 || elem_bytes(w_dtype) == 0) return 0;
+  const int64_t n_loc = (q_loc + 2 * kv_loc) * head_dim;
+  if (act_dtype == TP_BF16 && (h % 64 != 0 || n_loc % 16 != 0)) return 0;
+  return (size_t)round_up(linear_workspace_need(M, n_loc, h, act_dtype, w_dtype), 256);
+}
+
 TP_API tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
                                      int64_t head_dim, int32_t t, int32_t k, int32_t act_dtype,
                                      int32_t w_dtype, const void* x, int64_t ldx, const void* w_qkv,
-                                     int64_t ldw, const float* s_qkv, void* qkv, int64_t ldq, void* stream) {
+                                     int64_t ldw, const float* s_qkv, void* qkv, int64_t ldq,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
   int64_t q_loc = 0, kv_loc = 0;
   tp_status st = check_attn(M, h, n_heads, n_kv_heads, head_dim, t, k, &q_loc, &kv_loc);
   if (st != TP_OK) return st;
   const int64_t n_loc = (q_loc + 2 * kv_loc) * head_dim;
-  return linear_impl(M, n_loc, h, act_dtype, w_dtype, x, ldx, w_qkv, ldw, s_qkv, qkv, ldq, false,
-                     tpmlp::K_QKV_DECODE, tpmlp::K_QKV_PREFILL, tpmlp::K_QKV_F32, stream);
+  return linear_impl(M, n_loc, h, act_dtype, w_dtype, x, ldx, w_qkv, ldw, s_qkv, qkv, ldq, false, workspace,
+                     workspace_bytes, true, tpmlp::K_QKV_DECODE, tpmlp::K_QKV_PREFILL, tpmlp::K_QKV_F32, stream);
 }
 
 TP_API tp_status tp_attn_out_forward(int64_t M, int64_t h, int64_t n_heads, int64_t head_dim, int32_t t,
@@ -449,7 +481,8 @@ TP_API tp_status tp_attn_out_forward(int64_t M, int64_t h, int64_t n_heads, int6
   tp_status st = check_attn(M, h, n_heads, n_heads, head_dim, t, k, &q_loc, &kv_loc);
   if (st != TP_OK) return st;
   return linear_impl(M, h, q_loc * head_dim, act_dtype, w_dtype, attn, lda, w_o, ldw, s_o, partial, ldp, true,
-                     tpmlp::K_OPROJ_DECODE, tpmlp::K_OPROJ_PREFILL, tpmlp::K_OPROJ_F32, stream);
+                     nullptr, 0, false, tpmlp::K_OPROJ_DECODE, tpmlp::K_OPROJ_PREFILL, tpmlp::K_OPROJ_F32,
+                     stream);
 }
 
 TP_API const char* tp_status_string(int32_t status) {

@@ -645,11 +645,16 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
   });
 }
 
+// Split K (gridDim.y = nseg > 1): workgroup (x, y) streams the y-th of nseg
+// contiguous ranges of the K slots and stores its unscaled fp32 sums to
+// seg_out[y] (M x h, dense); splitk_finish_kernel adds the nseg ranges in
+// order.  Skinny outputs (few 16-row blocks, long K) need it to keep enough
+// loads in flight across the chip.
 template <int NT, int RB, bool FP8, bool XD, bool OBF>
 __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
-    void* __restrict__ p, int64_t ldp) {
+    void* __restrict__ p, int64_t ldp, int nseg, float* __restrict__ seg_out) {
   using SS = StreamShape<NT, RB, FP8, XD>;
   constexpr int EB = FP8 ? 1 : 2;
   constexpr int KS = FP8 ? 256 : 128;
@@ -664,7 +669,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
     stream_sources(dsrc[rb], lane,
                    [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
   int j_beg, nsl, jstep;
-  wave_slots<SS::WV>(I_s / KS, wave, j_beg, nsl, jstep);
+  const int nslots = I_s / KS;
+  const int seg = blockIdx.y;
+  const int s0 = (int)((int64_t)seg * nslots / nseg);
+  const int s1 = (int)((int64_t)(seg + 1) * nslots / nseg);
+  wave_slots<SS::WV>(s1 - s0, wave, j_beg, nsl, jstep);
+  j_beg += s0;
   bool xok[NT];
 #pragma unroll
   for (int b = 0; b < NT; ++b) xok[b] = b * 16 + row16 < M;
@@ -690,6 +700,10 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
     const int f = n0 + 16 * rb + 4 * grp;
     const int tok = b * 16 + row16;
     if (tok < M && f < h) {
+      if (nseg > 1) {
+        store_out4<false>(seg_out, ((int64_t)seg * M + tok) * h + f, v);
+        return;
+      }
       if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
@@ -697,6 +711,26 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
       store_out4<OBF>(p, (int64_t)tok * ldp + f, v);
     }
   });
+}
+
+// out = (((seg[0] + seg[1]) + ...) + seg[nseg-1]) (* row scale), four
+// outputs per thread (N % 4 == 0, so a group never crosses a row).
+template <bool FP8, bool OBF>
+__global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int nseg, const float* __restrict__ seg,
+                                                            const float* __restrict__ s, void* __restrict__ out,
+                                                            int64_t ldo) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)M * N;
+  const int64_t e = 4 * g;
+  if (e >= total) return;
+  const int tok = (int)(e / N), f = (int)(e % N);
+  f32x4 v = *reinterpret_cast<const f32x4*>(seg + e);
+  for (int q = 1; q < nseg; ++q) v = v + *reinterpret_cast<const f32x4*>(seg + q * total + e);
+  if constexpr (FP8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] *= s[f + i];
+  }
+  store_out4<OBF>(out, (int64_t)tok * ldo + f, v);
 }
 
 // Launch shape (waves per workgroup splitting K; steps per register batch).
@@ -758,13 +792,44 @@ hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
 }
 
+template <int NT, bool FP8>
+constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, FP8> && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
+
+// K split of a streaming row GEMM.  A narrow output (few 16-row blocks, e.g.
+// a rank's QKV projection: 80 blocks for 1280 rows) keeps too few loads in
+// flight across the chip; its K slots are then split into nseg contiguous
+// ranges over a second grid dimension (two launches: the split sums, then
+// their ordered sum), aiming at about four waves per CU, with each wave
+// keeping at least two slots.  (Sixteen waves per row block instead of a
+// split was measured slower: per-CU streaming rate, not wave count, is the
+// limit.)
+#ifndef TPMLP_SPLIT_TARGET_WAVES
+#define TPMLP_SPLIT_TARGET_WAVES 1024
+#endif
+
+template <int NT, bool FP8>
+int stream_splits(int N, int K) {
+  constexpr int RB = kRowRB<NT, FP8>;
+  constexpr int WV = StreamShape<NT, RB, FP8, kStreamXD<NT, FP8>>::WV;
+  const int blocks = (N + 16 * RB - 1) / (16 * RB);
+  const int want = (TPMLP_SPLIT_TARGET_WAVES + blocks * WV - 1) / (blocks * WV);
+  const int cap = K / (FP8 ? 256 : 128) / (2 * WV);
+  return max(1, min(want, cap));
+}
+
 template <int NT, bool FP8, bool OBF>
 hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, FP8>;
-  constexpr int RB = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
-  return launch(g.kind_decode, down_stream_kernel<NT, RB, FP8, XD, OBF>, dim3((g.N + 16 * RB - 1) / (16 * RB)),
-                dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a,
-                g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo);
+  constexpr int RB = kRowRB<NT, FP8>;
+  const int nseg = g.ws ? stream_splits<NT, FP8>(g.N, g.K) : 1;
+  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg);
+  hipError_t e = launch(g.kind_decode, down_stream_kernel<NT, RB, FP8, XD, OBF>, grid,
+                        dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, g.M, g.N, g.K,
+                        (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
+  if (e != hipSuccess || nseg == 1) return e;
+  const int64_t groups = (int64_t)g.M * g.N / 4;
+  return launch(K_SPLITK_FINISH, splitk_finish_kernel<FP8, OBF>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
+                0, stream, g.M, g.N, nseg, (const float*)g.ws, g.s, g.out, g.ldo);
 }
 
 #ifndef TPMLP_DECODE_V2
@@ -804,6 +869,20 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
 }
 
 }  // namespace
+
+int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, bool fp8) {
+  if (M < 1 || M > kDecodeMaxM) return 0;
+  int nseg = 1;
+  if (fp8 ? streams<true>(K) : streams<false>(K)) {
+    switch ((M + 15) / 16) {
+      case 1: nseg = fp8 ? stream_splits<1, true>(N, K) : stream_splits<1, false>(N, K); break;
+      case 2: nseg = fp8 ? stream_splits<2, true>(N, K) : stream_splits<2, false>(N, K); break;
+      case 3: nseg = fp8 ? stream_splits<3, true>(N, K) : stream_splits<3, false>(N, K); break;
+      default: nseg = fp8 ? stream_splits<4, true>(N, K) : stream_splits<4, false>(N, K); break;
+    }
+  }
+  return nseg > 1 ? (int64_t)nseg * M * N * 4 : 0;
+}
 
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
   if (g.fp8) return g.out_bf16 ? run_rowgemm<true, true>(g, stream) : run_rowgemm<true, false>(g, stream);

@@ -21,7 +21,8 @@ enum KernelKind : int {
   K_OPROJ_PREFILL = 10,
   K_QKV_F32 = 11,
   K_OPROJ_F32 = 12,
-  K_NUM_KINDS = 13
+  K_SPLITK_FINISH = 13,
+  K_NUM_KINDS = 14
 };
 
 constexpr int kMaxPartials = 64;
@@ -85,6 +86,7 @@ struct RowGemm {
   int64_t ldo;
   bool out_bf16;            // else fp32
   bool fp8;
+  float* ws;                // split-K scratch (null: no split), 16-byte aligned
   int kind_decode, kind_prefill, kind_f32;  // timing kinds of the three paths
 };
 
@@ -100,7 +102,7 @@ inline RowGemm down_of(const ShardArgs& s) {
   g.a = s.a; g.lda = s.lda;
   g.w = s.wd; g.ldw = s.ldw_down; g.s = s.sd;
   g.out = s.p; g.ldo = s.ldp;
-  g.out_bf16 = false; g.fp8 = s.fp8;
+  g.out_bf16 = false; g.fp8 = s.fp8; g.ws = nullptr;
   g.kind_decode = K_DOWN_DECODE; g.kind_prefill = K_DOWN_PREFILL; g.kind_f32 = K_DOWN_F32;
   return g;
 }
@@ -109,6 +111,8 @@ hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
+// Split-K scratch bytes launch_rowgemm_decode uses for this shape (0: none).
+int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, bool fp8);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
 hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
 

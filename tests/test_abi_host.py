@@ -211,12 +211,25 @@ def test_attn_qkv_width():
 
 
 def qkv_call(M=1, h=128, nh=8, nkv=2, d=32, t=2, k=0, act=BF16, w=BF16, x=P, ldx=None, wq=P * 2, ldw=None,
-             s=None, out=P * 8, ldq=None):
+             s=None, out=P * 8, ldq=None, ws=None, wsb=0):
     lib = _lib.load()
     n_loc = lib.tp_attn_qkv_width(nh, nkv, d, t) if t > 0 else 16
     n_loc = max(int(n_loc), 16)
     return lib.tp_attn_qkv_forward(M, h, nh, nkv, d, t, k, act, w, x, ldx if ldx is not None else h, wq,
-                                   ldw if ldw is not None else h, s, out, ldq if ldq is not None else n_loc, None)
+                                   ldw if ldw is not None else h, s, out, ldq if ldq is not None else n_loc,
+                                   ws, wsb, None)
+
+
+def test_attn_qkv_workspace_bytes():
+    lib = _lib.load()
+    # 70B TP=8 decode: the 1280-wide output over h = 8192 is split along h
+    for M in (1, 8, 32, 64):
+        b = lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16)
+        assert b > 0 and b % 256 == 0 and b % (M * 1280 * 4) == 0
+    assert lib.tp_attn_qkv_workspace_bytes(4096, 8192, 64, 8, 128, 8, BF16, BF16) == 0   # prefill tiles
+    assert lib.tp_attn_qkv_workspace_bytes(16, 256, 8, 2, 32, 4, F32, F32) == 0          # fp32 path
+    assert lib.tp_attn_qkv_workspace_bytes(1, 8192, 64, 8, 128, 3, BF16, BF16) == 0      # invalid split
+    assert lib.tp_attn_qkv_workspace_bytes(0, 8192, 64, 8, 128, 8, BF16, BF16) == 0
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -240,9 +253,18 @@ def qkv_call(M=1, h=128, nh=8, nkv=2, d=32, t=2, k=0, act=BF16, w=BF16, x=P, ldx
     (dict(ldw=132), _lib.TP_ERR_UNSUPPORTED),
     (dict(out=P * 2 + 64), _lib.TP_ERR_INVALID_ARG),   # output overlaps the weight
     (dict(out=P), _lib.TP_ERR_INVALID_ARG),            # output overlaps x
+    (dict(M=64, h=8192, nh=64, nkv=8, d=128, t=8, wq=P * 1024, out=P * 4096), _lib.TP_ERR_WORKSPACE),
+    (dict(M=64, h=8192, nh=64, nkv=8, d=128, t=8, wq=P * 1024, out=P * 4096, ws=P * 8192, wsb=256),
+     _lib.TP_ERR_WORKSPACE),                           # too small
+    (dict(M=64, h=8192, nh=64, nkv=8, d=128, t=8, wq=P * 1024, out=P * 4096, ws=P * 8192 + 16, wsb=1 << 26),
+     _lib.TP_ERR_UNSUPPORTED),                         # workspace not 256-aligned
+    (dict(M=64, h=8192, nh=64, nkv=8, d=128, t=8, wq=P * 1024, out=P * 4096, ws=P * 1024, wsb=1 << 26),
+     _lib.TP_ERR_INVALID_ARG),                         # workspace overlaps the weight
 ])
 def test_attn_qkv_rejects(kw, status):
     lib = _lib.load()
+    # every case must fail validation: a valid one would launch on fake addresses
+    assert status != _lib.TP_OK
     assert qkv_call(**kw) == status
     assert lib.tp_last_error() not in (b"", None)
 

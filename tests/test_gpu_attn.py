@@ -85,12 +85,20 @@ QKV_CASES = [
     (3, 1024, 8, 2, 64, 2, "e4m3fn"),
     (40, 320, 8, 2, 64, 2, "e4m3fn"),     # fp8 register-batch path
     (257, 1024, 8, 2, 64, 2, "e4m3fn"),
+    (4, 4096, 8, 2, 64, 2, "bf16"),       # narrow output, long h: h split in 4 ranges
+    (2, 8192, 4, 4, 32, 4, "bf16"),       # n_loc = 96: h split in 8 ranges
+    (40, 4096, 8, 2, 64, 2, "bf16"),      # activation-staged kernels, h split in 8 ranges
+    (16, 4096, 8, 2, 64, 2, "e4m3fn"),    # fp8, h split in 2 ranges
+    (64, 2048, 4, 4, 32, 4, "bf16"),      # n_loc = 96, h split in 4 ranges
 ]
 
 
 @pytest.mark.parametrize("M,h,nh,nkv,d,t,w", QKV_CASES)
 def test_qkv_shapes(M, h, nh, nkv, d, t, w):
-    print("qkv M=%d h=%d heads=%d/%d d=%d t=%d w=%s" % (M, h, nh, nkv, d, t, w), flush=True)
+    print("qkv M=%d h=%d heads=%d/%d d=%d t=%d w=%s workspace=%d" % (
+        M, h, nh, nkv, d, t, w, tp.attn_qkv_workspace_bytes(M, h, nh, nkv, d, t, torch.bfloat16,
+                                                            torch.float8_e4m3fn if w == "e4m3fn" else torch.bfloat16)),
+        flush=True)
     n_loc, _ = workloads.attn_widths(nh, nkv, d, t)
     ws = workloads.make_attn_weights(61, h, n_loc, 64, 1, w, 0.05, weight_set=M)
     x = workloads.make_x(61, M, h, "bf16", weight_set=M)
@@ -218,3 +226,26 @@ def test_prepared_calls_in_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(cq.out.view(torch.int16), eager_q.view(torch.int16))
         assert torch.equal(cp.partial.view(torch.int32), eager_p.view(torch.int32))
+
+
+def test_split_workspace_reuse_and_dirty_contents():
+    """One workspace serves calls of different sizes; what it holds on entry
+    does not change the result (the split sums overwrite it)."""
+    h, nh, nkv, d, t = 8192, 64, 8, 128, 8
+    n_loc, _ = workloads.attn_widths(nh, nkv, d, t)
+    ws = workloads.make_attn_weights(65, h, n_loc, 64, 0, "bf16", 0.02)
+    wq = to_device(ws["w_qkv"], "bf16")
+    need = max(tp.attn_qkv_workspace_bytes(M, h, nh, nkv, d, t) for M in (1, 8, 64))
+    assert need > 0
+    scratch = tp.alloc_workspace(need, "cuda")
+    for M in (64, 1, 8):
+        x = to_device(workloads.make_x(65, M, h, "bf16", weight_set=M), "bf16")
+        kw = dict(n_heads=nh, n_kv_heads=nkv, head_dim=d, t=t, k=0)
+        scratch.fill_(0x7F)                      # fp32 words of 3.4e38
+        a = tp.attn_qkv_forward(x, wq, workspace=scratch, **kw)
+        scratch.fill_(0)
+        b = tp.attn_qkv_forward(x, wq, workspace=scratch, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), M
+        ref = oracle.linear_from_storage(workloads.make_x(65, M, h, "bf16", weight_set=M), "bf16", ws["w_qkv"], "bf16")
+        assert oracle.rms_normalised_max_error(_out_f64(a), ref) <= TOL_BF16
