@@ -56,7 +56,8 @@ extern "C" {
 typedef enum {
   TP_F32 = 0,         /* IEEE binary32                                       */
   TP_BF16 = 1,        /* bfloat16 (upper half of binary32)                   */
-  TP_FP8_E4M3FN = 2   /* OCP FP8 E4M3 (bias 7, max 448, no inf); weights only */
+  TP_FP8_E4M3FN = 2,  /* OCP FP8 E4M3 (bias 7, max 448, no inf); weights only */
+  TP_INT8 = 3         /* two's-complement int8 code; weights only            */
 } tp_dtype;
 
 typedef enum {
@@ -88,7 +89,12 @@ size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
  *            on it.
  *   act_dtype  dtype of X and of the intermediate A: TP_BF16 or TP_F32.
  *   w_dtype    dtype of the three weight shards.  Supported pairs:
- *              (TP_BF16, TP_BF16), (TP_BF16, TP_FP8_E4M3FN), (TP_F32, TP_F32).
+ *              (TP_BF16, TP_BF16), (TP_BF16, TP_FP8_E4M3FN),
+ *              (TP_BF16, TP_INT8), (TP_F32, TP_F32).  The one-byte formats
+ *              are weight-only quantisation ("Build a model sharding system
+ *              ...", the planner's bytes per parameter for fp8 and int8):
+ *              the codes are widened to bf16 exactly in the kernels and the
+ *              activations stay bf16.
  *   x        M x h, leading dimension ldx >= h.
  *   w_gate, w_up   I_s x h each ((out, in) layout: row j is intermediate
  *            channel k*I_s + j of the full matrix), leading dimension
@@ -99,9 +105,9 @@ size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
  *            the full h x I_full matrix passes the pointer to column k*I_s
  *            and ldw_down = I_full.
  *   s_gate, s_up, s_down   fp32 per-output-channel scales, required for
- *            TP_FP8_E4M3FN weights (lengths I_s, I_s, h; the dequantised
- *            weight is code value * scale of its row) and must be NULL
- *            otherwise.
+ *            one-byte weights (TP_FP8_E4M3FN, TP_INT8; lengths I_s, I_s, h;
+ *            the dequantised weight is code value * scale of its row) and
+ *            must be NULL otherwise.
  *   partial  M x h fp32 output, leading dimension ldp >= h; overwritten.
  *            Must not overlap any input or the workspace.
  *   workspace, workspace_bytes   device scratch of at least
@@ -111,7 +117,7 @@ size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
  *   stream   hipStream_t or NULL.
  *
  * Requirements beyond validity (else TP_ERR_UNSUPPORTED): with bf16
- * activations (bf16 or fp8 weights) h % 64 == 0 and I_s % 64 == 0, all tensor
+ * activations (bf16 or one-byte weights) h % 64 == 0 and I_s % 64 == 0, all tensor
  * pointers 16-byte aligned and every row 16-byte aligned (leading dimension
  * times element size a multiple of 16 bytes), scales 4-byte aligned; with
  * fp32 activations and weights any h and I_s, 4-byte alignment.  The
@@ -244,7 +250,7 @@ int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
  *              == 0; else TP_ERR_INVALID_ARG.
  *   t, k       TP degree (1..64), rank index (validated; selects no data).
  *   act_dtype, w_dtype   as tp_mlp_shard_forward: (bf16, bf16),
- *              (bf16, fp8 e4m3fn), (fp32, fp32).
+ *              (bf16, fp8 e4m3fn), (bf16, int8), (fp32, fp32).
  *   x          M x h, leading dimension ldx >= h.
  *   w_qkv      n_loc x h ((out, in) layout), leading dimension ldw >= h: the
  *              rank's rows in the order [its q_loc query heads | its kv_loc
@@ -252,7 +258,7 @@ int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
  *              heads in their global order.  Rank k holds query heads
  *              [k*q_loc, (k+1)*q_loc) and key/value heads [k*kv_loc,
  *              (k+1)*kv_loc), or, replicated, head k / (t / n_kv_heads).
- *   s_qkv      fp8 only: n_loc fp32 per-row scales (weight = code * scale of
+ *   s_qkv      one-byte weights only: n_loc fp32 per-row scales (weight = code * scale of
  *              its row); NULL otherwise.
  *   qkv        M x n_loc output in the activation dtype, leading dimension
  *              ldq >= n_loc, same column order as w_qkv's rows; overwritten;
@@ -297,7 +303,7 @@ size_t tp_attn_qkv_workspace_bytes(int64_t M, int64_t h, int64_t n_heads, int64_
  *              h x n_heads*head_dim matrix), leading dimension ldw >= K.  A
  *              caller holding the full matrix passes the pointer to column
  *              k*K and ldw = n_heads*head_dim.
- *   s_o        fp8 only: h fp32 per-row scales; NULL otherwise.
+ *   s_o        one-byte weights only: h fp32 per-row scales; NULL otherwise.
  *   partial    M x h fp32, leading dimension ldp >= h; overwritten; must not
  *              overlap an input.
  *

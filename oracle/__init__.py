@@ -44,7 +44,7 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 format tables).  No function is "parity unpinned".
 """
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64, E4M3FN_MAX
+from .formats import bf16_bits_to_f64, e4m3fn_to_f64, int8_to_f64, E4M3FN_MAX
 from .attn import (
     local_heads,
     head_rows,
@@ -75,6 +75,7 @@ __all__ = [
     "linear_from_storage",
     "bf16_bits_to_f64",
     "e4m3fn_to_f64",
+    "int8_to_f64",
     "E4M3FN_MAX",
     "silu",
     "mlp_full",

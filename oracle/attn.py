@@ -33,7 +33,7 @@ No blocking or reordering beyond the definition: one library matmul each.
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64
+from .formats import bf16_bits_to_f64, e4m3fn_to_f64, int8_to_f64
 
 
 def local_heads(n_heads, n_kv_heads, t, k):
@@ -88,16 +88,19 @@ def _decode(arr, dtype):
         return a.astype(np.float64)
     if dtype == "e4m3fn":
         return e4m3fn_to_f64(arr)
+    if dtype == "int8":
+        return int8_to_f64(arr)
     raise ValueError("unknown storage dtype %r" % (dtype,))
 
 
 def linear_from_storage(a, a_dtype, w, w_dtype, s=None):
-    """a W^T in float64 from the raw storage the library receives; for e4m3fn
-    weights row n of W is dequantised as code * s[n] (exact in float64)."""
+    """a W^T in float64 from the raw storage the library receives; for one-byte
+    weights (e4m3fn, int8) row n of W is dequantised as code * s[n] (exact in
+    float64)."""
     af = _decode(a, a_dtype)
     wf = _decode(w, w_dtype)
-    if w_dtype == "e4m3fn":
+    if w_dtype in ("e4m3fn", "int8"):
         if s is None:
-            raise ValueError("e4m3fn weights need per-row scales")
+            raise ValueError("one-byte weights need per-row scales")
         wf = wf * np.asarray(s, dtype=np.float64)[:, None]
     return linear(af, wf)

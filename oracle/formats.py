@@ -13,6 +13,10 @@ TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
   per parameter (shard planner, "The Shard Planner" section of the
   scalablesystem.dev page); the OCP E4M3 variant is the reading used here.
 
+* int8 weight codes: two's complement, the byte b read as b for b < 128 and
+  b - 256 otherwise (the planner's "int8" at one byte per parameter on the
+  same page).
+
 The e4m3 table is built from that definition with a direct loop over the 256
 codes; it does not use any library fp8 type.
 """
@@ -49,6 +53,15 @@ _E4M3FN_TABLE = np.array([_e4m3fn_value(c) for c in range(256)], dtype=np.float6
 def e4m3fn_table():
     """The 256 code values, index = code (a copy)."""
     return _E4M3FN_TABLE.copy()
+
+
+def int8_to_f64(codes):
+    """Decode an array of int8 codes stored as uint8 bytes to float64."""
+    c = np.asarray(codes)
+    if c.dtype != np.uint8:
+        raise TypeError("int8 storage must be uint8 bytes")
+    v = c.astype(np.int64)
+    return np.where(v >= 128, v - 256, v).astype(np.float64)
 
 
 def e4m3fn_to_f64(codes):

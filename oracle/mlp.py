@@ -26,7 +26,7 @@ an elementwise SiLU and product, one more matmul.
 
 import numpy as np
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64
+from .formats import bf16_bits_to_f64, e4m3fn_to_f64, int8_to_f64
 
 
 def silu(z):
@@ -127,15 +127,20 @@ def _decode(arr, dtype):
         return a.astype(np.float64)
     if dtype == "e4m3fn":
         return e4m3fn_to_f64(arr)
+    if dtype == "int8":
+        return int8_to_f64(arr)
     raise ValueError("unknown storage dtype %r" % (dtype,))
+
+
+SCALED_FORMATS = ("e4m3fn", "int8")
 
 
 def rank_partial_from_storage(x, x_dtype, w_gate, w_up, w_down, w_dtype,
                               s_gate=None, s_up=None, s_down=None):
     """P_k in float64 from the raw storage the library receives.
 
-    For e4m3fn weights the reference weights are the dequantised values
-    q * s with s the fp32 scale of the output channel: s_gate[j] / s_up[j]
+    For one-byte weights (e4m3fn, int8) the reference weights are the
+    dequantised values q * s with s the fp32 scale of the output channel: s_gate[j] / s_up[j]
     multiply row j of the gate / up shard, s_down[n] multiplies row n of the
     down shard.  The product of an e4m3 value and an fp32 scale is exact in
     float64.
@@ -144,9 +149,9 @@ def rank_partial_from_storage(x, x_dtype, w_gate, w_up, w_down, w_dtype,
     wg = _decode(w_gate, w_dtype)
     wu = _decode(w_up, w_dtype)
     wd = _decode(w_down, w_dtype)
-    if w_dtype == "e4m3fn":
+    if w_dtype in SCALED_FORMATS:
         if s_gate is None or s_up is None or s_down is None:
-            raise ValueError("e4m3fn weights need per-channel scales")
+            raise ValueError("one-byte weights need per-channel scales")
         wg = wg * np.asarray(s_gate, dtype=np.float64)[:, None]
         wu = wu * np.asarray(s_up, dtype=np.float64)[:, None]
         wd = wd * np.asarray(s_down, dtype=np.float64)[:, None]

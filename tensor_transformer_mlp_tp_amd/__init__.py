@@ -20,7 +20,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, EXPORTED_SYMBOLS,  # noqa: F401
+from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, TP_INT8, EXPORTED_SYMBOLS,  # noqa: F401
                    LIB_PATH, load)
 
 __all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
@@ -46,7 +46,9 @@ def _w_code(dt):
         return TP_F32
     if dt in (torch.float8_e4m3fn, torch.uint8):
         return TP_FP8_E4M3FN
-    raise TypeError("weights must be bfloat16, float32 or float8_e4m3fn (uint8 codes), got %s" % dt)
+    if dt == torch.int8:
+        return TP_INT8
+    raise TypeError("weights must be bfloat16, float32, float8_e4m3fn (uint8 codes) or int8, got %s" % dt)
 
 
 def _check_matrix(name, t, device):
@@ -104,8 +106,9 @@ def shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_do
     """Rank k's fp32 partial P_k (M x h) of the TP-MLP; see ``include/tp_mlp.h``.
 
     x: (M, h) bf16 or fp32.  w_gate, w_up: (I_s, h); w_down: (h, I_s), in the
-    (out, in) layout, bf16 / fp32 / float8_e4m3fn (or uint8 codes).  For fp8
-    weights s_gate, s_up (I_s) and s_down (h) are the fp32 per-row scales.
+    (out, in) layout, bf16 / fp32 / float8_e4m3fn (or uint8 codes) / int8.  For
+    one-byte weights s_gate, s_up (I_s) and s_down (h) are the fp32 per-row
+    scales.
     ``partial`` (M, h) fp32 and ``workspace`` (uint8, >= workspace_bytes) may be
     passed to avoid allocation.  Work is enqueued on ``stream`` (default: the
     current stream) and the call returns without waiting.

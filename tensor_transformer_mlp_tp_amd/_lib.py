@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # (used when comparing launch-shape variants).
 LIB_PATH = os.environ.get("TP_MLP_LIB") or os.path.join(PKG, "libtp_mlp.so")
 
-TP_F32, TP_BF16, TP_FP8_E4M3FN = 0, 1, 2
+TP_F32, TP_BF16, TP_FP8_E4M3FN, TP_INT8 = 0, 1, 2, 3
 TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_WORKSPACE, TP_ERR_HIP = 0, 1, 2, 3, 4
 
 EXPORTED_SYMBOLS = (

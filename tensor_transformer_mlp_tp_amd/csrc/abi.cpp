@@ -43,8 +43,27 @@ int elem_bytes(int32_t dt) {
     case TP_F32: return 4;
     case TP_BF16: return 2;
     case TP_FP8_E4M3FN: return 1;
+    case TP_INT8: return 1;
     default: return 0;
   }
+}
+
+// One-byte weight formats (fp32 scale per output row) and the kernels' code.
+bool scaled_weights(int32_t w) { return w == TP_FP8_E4M3FN || w == TP_INT8; }
+
+int weight_format(int32_t w) {
+  return w == TP_FP8_E4M3FN ? tpmlp::kWeightE4M3 : w == TP_INT8 ? tpmlp::kWeightI8 : tpmlp::kWeightWide;
+}
+
+// Supported (activation, weight) pairs; fills an error message otherwise.
+tp_status check_pair(int32_t act, int32_t w) {
+  if (elem_bytes(act) == 0 || elem_bytes(w) == 0)
+    return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act, w);
+  if (act == TP_FP8_E4M3FN || act == TP_INT8)
+    return fail(TP_ERR_UNSUPPORTED, "one-byte activations are not supported");
+  const bool ok = (act == TP_BF16 && (w == TP_BF16 || scaled_weights(w))) || (act == TP_F32 && w == TP_F32);
+  if (!ok) return fail(TP_ERR_UNSUPPORTED, "unsupported dtype pair (act=%d, w=%d)", act, w);
+  return TP_OK;
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -77,17 +96,15 @@ tp_status check_shapes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
   if (k < 0 || k >= t) return fail(TP_ERR_INVALID_ARG, "k must be in [0, t) (got k=%d, t=%d)", k, t);
   if (I_full % t != 0)
     return fail(TP_ERR_INVALID_ARG, "I_full (%lld) must be divisible by t (%d)", (long long)I_full, t);
-  if (elem_bytes(act) == 0 || elem_bytes(w) == 0)
-    return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act, w);
-  if (act == TP_FP8_E4M3FN) return fail(TP_ERR_UNSUPPORTED, "fp8 activations are not supported");
-  const bool ok_pair = (act == TP_BF16 && (w == TP_BF16 || w == TP_FP8_E4M3FN)) ||
-                       (act == TP_F32 && w == TP_F32);
-  if (!ok_pair) return fail(TP_ERR_UNSUPPORTED, "unsupported dtype pair (act=%d, w=%d)", act, w);
+  {
+    const tp_status st = check_pair(act, w);
+    if (st != TP_OK) return st;
+  }
   const int64_t I_s = I_full / t;
   if (M > kMaxDim || h > kMaxDim || I_s > kMaxDim)
     return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
   if (act == TP_BF16 && (h % 64 != 0 || I_s % 64 != 0))
-    return fail(TP_ERR_UNSUPPORTED, "bf16/fp8 paths need h %% 64 == 0 and I_s %% 64 == 0 (h=%lld, I_s=%lld)",
+    return fail(TP_ERR_UNSUPPORTED, "bf16 paths need h %% 64 == 0 and I_s %% 64 == 0 (h=%lld, I_s=%lld)",
                 (long long)h, (long long)I_s);
   return TP_OK;
 }
@@ -164,11 +181,11 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
     return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
   for (int b = 0; b < nb; ++b)
     if (!x_blocks[b]) return fail(TP_ERR_INVALID_ARG, "null activation pointer (block %d)", b);
-  const bool fp8 = w_dtype == TP_FP8_E4M3FN;
+  const bool fp8 = scaled_weights(w_dtype);   // one-byte weights with row scales
   if (fp8 && (!s_gate || !s_up || !s_down))
-    return fail(TP_ERR_INVALID_ARG, "fp8 weights need s_gate, s_up and s_down");
+    return fail(TP_ERR_INVALID_ARG, "one-byte weights need s_gate, s_up and s_down");
   if (!fp8 && (s_gate || s_up || s_down))
-    return fail(TP_ERR_INVALID_ARG, "scales are only accepted with fp8 weights");
+    return fail(TP_ERR_INVALID_ARG, "scales are only accepted with one-byte weights");
   if (ldx < h || ldw_gu < h || ldw_down < I_s || ldp < h)
     return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length "
                 "(ldx=%lld ldw_gu=%lld ldw_down=%lld ldp=%lld)", (long long)ldx, (long long)ldw_gu,
@@ -230,7 +247,7 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
   a.ldp = ldp;
   a.a = workspace;
   a.lda = I_s;
-  a.fp8 = fp8;
+  a.wb = weight_format(w_dtype);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (act_dtype == TP_F32)
@@ -340,27 +357,25 @@ bool attn_local_heads(int64_t n_heads, int64_t n_kv_heads, int32_t t, int64_t* q
 // Split-K scratch the projection needs (bytes, before rounding).
 int64_t linear_workspace_need(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype) {
   if (act_dtype != TP_BF16 || M > tpmlp::kDecodeMaxM) return 0;
-  return tpmlp::rowgemm_decode_workspace_bytes((int)M, (int)N, (int)K, w_dtype == TP_FP8_E4M3FN);
+  return tpmlp::rowgemm_decode_workspace_bytes((int)M, (int)N, (int)K, weight_format(w_dtype));
 }
 
 tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype, const void* a,
                       int64_t lda, const void* w, int64_t ldw, const float* s, void* out, int64_t ldo,
                       bool out_f32, void* workspace, size_t workspace_bytes, bool has_workspace,
                       int kind_decode, int kind_prefill, int kind_f32, void* stream) {
-  if (elem_bytes(act_dtype) == 0 || elem_bytes(w_dtype) == 0)
-    return fail(TP_ERR_INVALID_ARG, "unknown dtype code (act=%d, w=%d)", act_dtype, w_dtype);
-  if (act_dtype == TP_FP8_E4M3FN) return fail(TP_ERR_UNSUPPORTED, "fp8 activations are not supported");
-  const bool ok_pair = (act_dtype == TP_BF16 && (w_dtype == TP_BF16 || w_dtype == TP_FP8_E4M3FN)) ||
-                       (act_dtype == TP_F32 && w_dtype == TP_F32);
-  if (!ok_pair) return fail(TP_ERR_UNSUPPORTED, "unsupported dtype pair (act=%d, w=%d)", act_dtype, w_dtype);
+  {
+    const tp_status st = check_pair(act_dtype, w_dtype);
+    if (st != TP_OK) return st;
+  }
   if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
   if (act_dtype == TP_BF16 && (K % 64 != 0 || N % 16 != 0))
-    return fail(TP_ERR_UNSUPPORTED, "bf16/fp8 paths need K %% 64 == 0 and N %% 16 == 0 (K=%lld, N=%lld)",
+    return fail(TP_ERR_UNSUPPORTED, "bf16 paths need K %% 64 == 0 and N %% 16 == 0 (K=%lld, N=%lld)",
                 (long long)K, (long long)N);
   if (!a || !w || !out) return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
-  const bool fp8 = w_dtype == TP_FP8_E4M3FN;
-  if (fp8 && !s) return fail(TP_ERR_INVALID_ARG, "fp8 weights need their scales");
-  if (!fp8 && s) return fail(TP_ERR_INVALID_ARG, "scales are only accepted with fp8 weights");
+  const bool fp8 = scaled_weights(w_dtype);   // one-byte weights with row scales
+  if (fp8 && !s) return fail(TP_ERR_INVALID_ARG, "one-byte weights need their scales");
+  if (!fp8 && s) return fail(TP_ERR_INVALID_ARG, "scales are only accepted with one-byte weights");
   if (lda < K || ldw < K || ldo < N)
     return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length (lda=%lld ldw=%lld ldo=%lld)",
                 (long long)lda, (long long)ldw, (long long)ldo);
@@ -403,7 +418,7 @@ tp_status linear_impl(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_
   g.out = out;
   g.ldo = ldo;
   g.out_bf16 = act_dtype == TP_BF16 && !out_f32;
-  g.fp8 = fp8;
+  g.wb = weight_format(w_dtype);
   g.ws = need > 0 ? static_cast<float*>(workspace) : nullptr;
   g.kind_decode = kind_decode;
   g.kind_prefill = kind_prefill;

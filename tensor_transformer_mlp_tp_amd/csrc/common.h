@@ -65,6 +65,32 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
+// Eight int8 codes (two dwords) -> eight bf16, exact: an int8 value has at
+// most 8 significant bits.  Each byte is biased to unsigned (xor 0x80),
+// converted to fp32 (exact), unbiased by an exact fp32 subtraction, and the
+// bf16 is the upper half of the fp32 word (exact, the low half is zero).
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t u, int sh) {
+  const float f0 = (float)((u >> sh) & 0xffu) - 128.0f;
+  const float f1 = (float)((u >> (sh + 8)) & 0xffu) - 128.0f;
+  return __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 i8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  const uint32_t a = lo ^ 0x80808080u, b = hi ^ 0x80808080u;
+  const u32x4 r = {i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 16), i8pair_to_bf16x2(b, 0),
+                   i8pair_to_bf16x2(b, 16)};
+  return as_bf16x8(r);
+}
+
+// Eight one-byte weight codes of format WB (kWeightE4M3 or kWeightI8) -> bf16.
+template <int WB>
+__device__ __forceinline__ bf16x8 byte8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  if constexpr (WB == kWeightI8)
+    return i8x8_to_bf16x8(lo, hi);
+  else
+    return fp8x8_to_bf16x8(lo, hi);
+}
+
 // Four consecutive outputs at element index idx of `out`: fp32, or bf16
 // rounded to nearest even (OBF).
 template <bool OBF>

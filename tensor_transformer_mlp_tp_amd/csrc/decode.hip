@@ -49,9 +49,9 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 // A batch of U consecutive k-steps held in registers.  A step is 32 k (bf16
 // weights) or 64 k (fp8 weights): one 16-byte weight load per lane per row
 // block, plus the matching activation fragments.
-template <int NT, int RB, int U, bool FP8>
+template <int NT, int RB, int U, int WB>
 struct Batch {
-  static constexpr int XJ = FP8 ? 2 : 1;
+  static constexpr int XJ = WB ? 2 : 1;
   u32x4 wf[U][RB];
   u32x4 xf[U][NT][XJ];
 };
@@ -59,12 +59,12 @@ struct Batch {
 // Issue the loads of the batch starting at step s.  Steps at or past s_end
 // (only in the last, partial batch) re-read step s_end - 1, which is valid
 // memory; their products are skipped in mac_batch.
-template <int NT, int RB, int U, bool FP8>
-__device__ __forceinline__ void load_batch(Batch<NT, RB, U, FP8>& bt, const uint8_t* const (&wrow)[RB],
+template <int NT, int RB, int U, int WB>
+__device__ __forceinline__ void load_batch(Batch<NT, RB, U, WB>& bt, const uint8_t* const (&wrow)[RB],
                                            const uint16_t* const (&xrow)[NT], int s, int s_end, int grp) {
-  constexpr int KSTEP = FP8 ? 64 : 32;
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int XJ = FP8 ? 2 : 1;
+  constexpr int KSTEP = WB ? 64 : 32;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int XJ = WB ? 2 : 1;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t st = min(s + u, s_end - 1);
@@ -79,23 +79,23 @@ __device__ __forceinline__ void load_batch(Batch<NT, RB, U, FP8>& bt, const uint
 
 // MFMAs of the first n (<= U) steps of a loaded batch.  Token rows past M
 // were loaded from a clamped row and are zeroed here.
-template <int NT, int RB, int U, bool FP8>
-__device__ __forceinline__ void mac_batch(f32x4 (&acc)[RB][NT], const Batch<NT, RB, U, FP8>& bt,
+template <int NT, int RB, int U, int WB>
+__device__ __forceinline__ void mac_batch(f32x4 (&acc)[RB][NT], const Batch<NT, RB, U, WB>& bt,
                                           const bool (&xok)[NT], int n) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (u >= n) break;  // wave-uniform
-    bf16x8 xv[NT][FP8 ? 2 : 1];
+    bf16x8 xv[NT][WB ? 2 : 1];
 #pragma unroll
     for (int b = 0; b < NT; ++b)
 #pragma unroll
-      for (int j = 0; j < (FP8 ? 2 : 1); ++j) xv[b][j] = as_bf16x8(xok[b] ? bt.xf[u][b][j] : zero);
+      for (int j = 0; j < (WB ? 2 : 1); ++j) xv[b][j] = as_bf16x8(xok[b] ? bt.xf[u][b][j] : zero);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      if constexpr (FP8) {
-        const bf16x8 lo = fp8x8_to_bf16x8(bt.wf[u][r][0], bt.wf[u][r][1]);
-        const bf16x8 hi = fp8x8_to_bf16x8(bt.wf[u][r][2], bt.wf[u][r][3]);
+      if constexpr (WB) {
+        const bf16x8 lo = byte8_to_bf16x8<WB>(bt.wf[u][r][0], bt.wf[u][r][1]);
+        const bf16x8 hi = byte8_to_bf16x8<WB>(bt.wf[u][r][2], bt.wf[u][r][3]);
 #pragma unroll
         for (int b = 0; b < NT; ++b) {
           acc[r][b] = mfma16(lo, xv[b][0], acc[r][b]);
@@ -112,12 +112,12 @@ __device__ __forceinline__ void mac_batch(f32x4 (&acc)[RB][NT], const Batch<NT, 
 
 // Steps [s_beg, s_end) with two register batches in flight: the loads of
 // batch i+1 are issued before the MFMAs of batch i.
-template <int NT, int RB, int U, bool FP8>
+template <int NT, int RB, int U, int WB>
 __device__ __forceinline__ void mac_range(f32x4 (&acc)[RB][NT], const uint8_t* const (&wrow)[RB],
                                           const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
                                           int s_beg, int s_end, int grp) {
   if (s_beg >= s_end) return;
-  Batch<NT, RB, U, FP8> b0, b1;
+  Batch<NT, RB, U, WB> b0, b1;
   int s = s_beg;
   load_batch(b0, wrow, xrow, s, s_end, grp);
   while (true) {
@@ -160,14 +160,14 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[RB][NT], int wave, int
   }
 }
 
-template <int NT, int RB, int WAVES, int UNROLL, bool FP8>
+template <int NT, int RB, int WAVES, int UNROLL, int WB>
 __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
     int M, int h, int I_s, const XRows xr,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
     const float* __restrict__ sg, const float* __restrict__ su,
     uint16_t* __restrict__ a_out, int64_t lda) {
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KSTEP = FP8 ? 64 : 32;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int KSTEP = WB ? 64 : 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row16 = lane & 15;
@@ -197,7 +197,7 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mac_range<NT, RB, UNROLL, FP8>(acc, wrow, xrow, xok, s_beg, s_end, grp);
+  mac_range<NT, RB, UNROLL, WB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
 
   reduce_waves<NT, RB, WAVES>(acc, wave, lane, [&](int r, int b, f32x4 v) {
     f32x4 o;
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float g = v[i], u = o[i];
-          if constexpr (FP8) {
+          if constexpr (WB) {
             g *= sg[ch + i];
             u *= su[ch + i];
           }
@@ -225,13 +225,13 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
 }
 
 // out (M x N) = a_in (M x K) * wd^T, wd N x K; fp32 or bf16 (OBF) output.
-template <int NT, int RB, int WAVES, int UNROLL, bool FP8, bool OBF>
+template <int NT, int RB, int WAVES, int UNROLL, int WB, bool OBF>
 __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
     void* __restrict__ p, int64_t ldp) {
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KSTEP = FP8 ? 64 : 32;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int KSTEP = WB ? 64 : 32;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int row16 = lane & 15;
@@ -261,13 +261,13 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mac_range<NT, RB, UNROLL, FP8>(acc, wrow, xrow, xok, s_beg, s_end, grp);
+  mac_range<NT, RB, UNROLL, WB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
 
   reduce_waves<NT, RB, WAVES>(acc, wave, lane, [&](int r, int b, f32x4 v) {
     const int f = n0 + 16 * r + 4 * grp;  // features f .. f+3
     const int tok = b * 16 + row16;
     if (tok < M && f < h) {
-      if constexpr (FP8) {
+      if constexpr (WB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
       }
@@ -335,13 +335,13 @@ __device__ __forceinline__ void wait_slot_peeled(int j) {
 // lane's source for direct-load instruction i of block rb in slot 0 (row
 // 4i + lane/16, pre-swizzled chunk); slot j adds j*256 bytes.  xrow/xok:
 // activation rows of the NT token blocks.
-template <int NT, int RB, bool FP8, int S>
+template <int NT, int RB, int WB, int S>
 __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                             const uint8_t* const (&dsrc)[RB][4],
                                             const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
                                             int j_beg, int nsl, int jstep, int lane) {
-  constexpr int STEPS = FP8 ? 8 : 4;          // MFMA k-steps (32 k) per slot
-  constexpr int KS = FP8 ? 256 : 128;         // k per slot
+  constexpr int STEPS = WB ? 8 : 4;          // MFMA k-steps (32 k) per slot
+  constexpr int KS = WB ? 256 : 128;         // k per slot
   constexpr int XL = STEPS * NT;              // activation loads per slot
   constexpr int D = 4 * RB;                   // direct loads per slot
   constexpr int SLOT = RB * 4096;             // bytes per slot
@@ -360,7 +360,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
     for (int b = 0; b < NT; ++b)
 #pragma unroll
       for (int st = 0; st < STEPS; ++st) {
-        const int ko = FP8 ? (64 * (st >> 1) + 16 * g + 8 * (st & 1)) : (32 * st + 8 * g);
+        const int ko = WB ? (64 * (st >> 1) + 16 * g + 8 * (st & 1)) : (32 * st + 8 * g);
         xf[st][b] = *reinterpret_cast<const u32x4*>(xrow[b] + (int64_t)j * KS + ko);
       }
   };
@@ -370,12 +370,12 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
     for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        if constexpr (FP8) {
+        if constexpr (WB) {
           if ((st & 1) == 0) {
             const int q = 4 * (st >> 1) + g;
             const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
-            const bf16x8 w0 = fp8x8_to_bf16x8(v[0], v[1]);
-            const bf16x8 w1 = fp8x8_to_bf16x8(v[2], v[3]);
+            const bf16x8 w0 = byte8_to_bf16x8<WB>(v[0], v[1]);
+            const bf16x8 w1 = byte8_to_bf16x8<WB>(v[2], v[3]);
 #pragma unroll
             for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w0, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[rb][b]);
 #pragma unroll
@@ -437,16 +437,16 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
 // with more than 16 tokens that doubled line traffic, not the weight stream,
 // is what bounds the kernel.  xsrc[b][i]: this lane's source for activation
 // load i of token block b in slot 0; slot j adds j * 2*KS bytes.
-template <int NT, int RB, bool FP8, int S>
+template <int NT, int RB, int WB, int S>
 __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                                const uint8_t* const (&dsrc)[RB][4],
-                                               const uint8_t* const (&xsrc)[NT][FP8 ? 8 : 4],
+                                               const uint8_t* const (&xsrc)[NT][WB ? 8 : 4],
                                                const bool (&xok)[NT], int j_beg, int nsl, int jstep,
                                                int lane) {
-  constexpr int STEPS = FP8 ? 8 : 4;          // MFMA k-steps (32 k) per slot
-  constexpr int KS = FP8 ? 256 : 128;         // k per slot
+  constexpr int STEPS = WB ? 8 : 4;          // MFMA k-steps (32 k) per slot
+  constexpr int KS = WB ? 256 : 128;         // k per slot
   constexpr int XROWB = 2 * KS;               // activation bytes per row per slot
-  constexpr int XI = FP8 ? 8 : 4;             // activation loads per token block
+  constexpr int XI = WB ? 8 : 4;             // activation loads per token block
   constexpr int XBLK = 16 * XROWB;
   constexpr int D = 4 * RB + NT * XI;         // direct loads per slot
   constexpr int SLOT = RB * 4096 + NT * XBLK; // bytes per slot
@@ -471,16 +471,16 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
       u32x4 xf[NT];
-      const int xc = FP8 ? (8 * (st >> 1) + 2 * g + (st & 1)) : (4 * st + g);
+      const int xc = WB ? (8 * (st >> 1) + 2 * g + (st & 1)) : (4 * st + g);
 #pragma unroll
       for (int b = 0; b < NT; ++b) xf[b] = *reinterpret_cast<const u32x4*>(xl + b * XBLK + ((xc ^ r) * 16));
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         bf16x8 w;
-        if constexpr (FP8) {
+        if constexpr (WB) {
           const int q = 4 * (st >> 1) + g;
           const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
-          w = (st & 1) ? fp8x8_to_bf16x8(v[2], v[3]) : fp8x8_to_bf16x8(v[0], v[1]);
+          w = (st & 1) ? byte8_to_bf16x8<WB>(v[2], v[3]) : byte8_to_bf16x8<WB>(v[0], v[1]);
         } else {
           const int q = 4 * st + g;
           w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16)));
@@ -506,14 +506,14 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
 // Activation direct-load sources of this lane: token block b, load i covers
 // rows i*RPI + lane/LPR of the block (LPR lanes per row), logical chunk
 // (lane % LPR) ^ row.
-template <bool FP8, int NT, typename XPtr>
-__device__ __forceinline__ void stream_x_sources(const uint8_t* (&xsrc)[NT][FP8 ? 8 : 4], int lane, XPtr xptr) {
-  constexpr int LPR = FP8 ? 32 : 16;
+template <int WB, int NT, typename XPtr>
+__device__ __forceinline__ void stream_x_sources(const uint8_t* (&xsrc)[NT][WB ? 8 : 4], int lane, XPtr xptr) {
+  constexpr int LPR = WB ? 32 : 16;
   constexpr int RPI = 64 / LPR;
 #pragma unroll
   for (int b = 0; b < NT; ++b)
 #pragma unroll
-    for (int i = 0; i < (FP8 ? 8 : 4); ++i) {
+    for (int i = 0; i < (WB ? 8 : 4); ++i) {
       const int row = i * RPI + lane / LPR;
       const int c = (lane % LPR) ^ row;
       xsrc[b][i] = reinterpret_cast<const uint8_t*>(xptr(b * 16 + row)) + c * 16;
@@ -565,25 +565,25 @@ __device__ __forceinline__ void wave_slots(int nslots, int wave, int& j_beg, int
 // Ring geometry of a streaming kernel: slot bytes and ring depth.  With the
 // activations in the ring (XD) the slots are larger, so those kernels run two
 // waves per workgroup with three slots each.
-template <int NT, int RB, bool FP8, bool XD>
+template <int NT, int RB, int WB, bool XD>
 struct StreamShape {
   static constexpr int WV = XD ? 2 : kSWaves;
-  static constexpr int SLOT = RB * 4096 + (XD ? NT * 16 * 2 * (FP8 ? 256 : 128) : 0);
+  static constexpr int SLOT = RB * 4096 + (XD ? NT * 16 * 2 * (WB ? 256 : 128) : 0);
   static constexpr int S = XD ? (WV * 3 * SLOT <= 160 * 1024 ? 3 : 2) : kSlots;
   static constexpr int RING = WV * S * SLOT;
   static_assert(WV * RB * NT * 1024 <= RING, "the cross-wave sums fit the ring");
   static_assert(RING <= 160 * 1024, "LDS");
 };
 
-template <int NT, int RB, bool FP8, bool XD>
-__global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateup_stream_kernel(
+template <int NT, int RB, int WB, bool XD>
+__global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup_stream_kernel(
     int M, int h, int I_s, const XRows xr,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
     const float* __restrict__ sg, const float* __restrict__ su,
     uint16_t* __restrict__ a_out, int64_t lda) {
-  using SS = StreamShape<NT, RB, FP8, XD>;
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KS = FP8 ? 256 : 128;
+  using SS = StreamShape<NT, RB, WB, XD>;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int KS = WB ? 256 : 128;
   __shared__ __attribute__((aligned(1024))) uint8_t ring_all[SS::RING];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -609,14 +609,14 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
     for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint8_t* ring = ring_all + wave * SS::S * SS::SLOT;
   if constexpr (XD) {
-    const uint8_t* xsrc[NT][FP8 ? 8 : 4];
-    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return x_row<uint16_t>(xr, min(tok, M - 1)); });
-    stream_rows_xd<NT, RB, FP8, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    const uint8_t* xsrc[NT][WB ? 8 : 4];
+    stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return x_row<uint16_t>(xr, min(tok, M - 1)); });
+    stream_rows_xd<NT, RB, WB, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = x_row<uint16_t>(xr, min(b * 16 + row16, M - 1));
-    stream_rows<NT, RB, FP8, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -632,7 +632,7 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float gv = v[i], uv = o[i];
-          if constexpr (FP8) {
+          if constexpr (WB) {
             gv *= sg[ch + i];
             uv *= su[ch + i];
           }
@@ -650,14 +650,14 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void gateu
 // seg_out[y] (M x h, dense); splitk_finish_kernel adds the nseg ranges in
 // order.  Skinny outputs (few 16-row blocks, long K) need it to keep enough
 // loads in flight across the chip.
-template <int NT, int RB, bool FP8, bool XD, bool OBF>
-__global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_stream_kernel(
+template <int NT, int RB, int WB, bool XD, bool OBF>
+__global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
     void* __restrict__ p, int64_t ldp, int nseg, float* __restrict__ seg_out) {
-  using SS = StreamShape<NT, RB, FP8, XD>;
-  constexpr int EB = FP8 ? 1 : 2;
-  constexpr int KS = FP8 ? 256 : 128;
+  using SS = StreamShape<NT, RB, WB, XD>;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int KS = WB ? 256 : 128;
   __shared__ __attribute__((aligned(1024))) uint8_t ring_all[SS::RING];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -685,14 +685,14 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
     for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   uint8_t* ring = ring_all + wave * SS::S * SS::SLOT;
   if constexpr (XD) {
-    const uint8_t* xsrc[NT][FP8 ? 8 : 4];
-    stream_x_sources<FP8, NT>(xsrc, lane, [&](int tok) { return a_in + (int64_t)min(tok, M - 1) * lda; });
-    stream_rows_xd<NT, RB, FP8, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    const uint8_t* xsrc[NT][WB ? 8 : 4];
+    stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return a_in + (int64_t)min(tok, M - 1) * lda; });
+    stream_rows_xd<NT, RB, WB, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = a_in + (int64_t)min(b * 16 + row16, M - 1) * lda;
-    stream_rows<NT, RB, FP8, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -704,7 +704,7 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
         store_out4<false>(seg_out, ((int64_t)seg * M + tok) * h + f, v);
         return;
       }
-      if constexpr (FP8) {
+      if constexpr (WB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
       }
@@ -715,7 +715,7 @@ __global__ __launch_bounds__((StreamShape<NT, RB, FP8, XD>::WV * 64)) void down_
 
 // out = (((seg[0] + seg[1]) + ...) + seg[nseg-1]) (* row scale), four
 // outputs per thread (N % 4 == 0, so a group never crosses a row).
-template <bool FP8, bool OBF>
+template <int WB, bool OBF>
 __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int nseg, const float* __restrict__ seg,
                                                             const float* __restrict__ s, void* __restrict__ out,
                                                             int64_t ldo) {
@@ -726,7 +726,7 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
   const int tok = (int)(e / N), f = (int)(e % N);
   f32x4 v = *reinterpret_cast<const f32x4*>(seg + e);
   for (int q = 1; q < nseg; ++q) v = v + *reinterpret_cast<const f32x4*>(seg + q * total + e);
-  if constexpr (FP8) {
+  if constexpr (WB) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] *= s[f + i];
   }
@@ -743,21 +743,21 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
 constexpr int kWaves = TPMLP_DECODE_WAVES;
 constexpr int kUnroll = TPMLP_DECODE_UNROLL;
 
-template <int NT, bool FP8>
+template <int NT, int WB>
 hipError_t gateup_v1(const ShardArgs& a, hipStream_t stream) {
   // Row blocks per workgroup: with more token blocks, two weight blocks share
   // each activation fragment load.  Batches shrink as fragments per step grow.
   constexpr int RB = NT >= 3 ? 2 : 1;
-  constexpr int UN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
-  return launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB, kWaves, UN, FP8>,
+  constexpr int UN = WB ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
+  return launch(K_GATEUP_DECODE, gateup_decode_kernel<NT, RB, kWaves, UN, WB>,
                 dim3((a.I_s + 8 * RB - 1) / (8 * RB)), dim3(kWaves * 64), 0, stream, a.M, a.h, a.I_s, a.x,
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
 }
 
-template <int NT, bool FP8, bool OBF>
+template <int NT, int WB, bool OBF>
 hipError_t rowgemm_v1(const RowGemm& g, hipStream_t stream) {
-  constexpr int UN = FP8 ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
-  return launch(g.kind_decode, down_decode_kernel<NT, 1, kWaves, UN, FP8, OBF>, dim3((g.N + 15) / 16),
+  constexpr int UN = WB ? (NT >= 3 ? kUnroll / 4 : kUnroll / 2) : (NT >= 3 ? kUnroll / 2 : kUnroll);
+  return launch(g.kind_decode, down_decode_kernel<NT, 1, kWaves, UN, WB, OBF>, dim3((g.N + 15) / 16),
                 dim3(kWaves * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a, g.lda,
                 (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo);
 }
@@ -780,20 +780,20 @@ hipError_t rowgemm_v1(const RowGemm& g, hipStream_t stream) {
 // (most workgroups).  More tokens: RB row blocks per wave share each
 // activation fragment, and the activations come through the ring (where its
 // slots fit the LDS: fp8 weights have twice the k per slot).
-template <int NT, bool FP8>
-constexpr bool kStreamXD = TPMLP_DECODE_XD && NT >= 2 && (!FP8 || NT == 2);
+template <int NT, int WB>
+constexpr bool kStreamXD = TPMLP_DECODE_XD && NT >= 2 && (!WB || NT == 2);
 
-template <int NT, bool FP8>
+template <int NT, int WB>
 hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
-  constexpr bool XD = kStreamXD<NT, FP8>;
-  constexpr int RB = NT == 1 ? 1 : (XD && FP8 ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
-  return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, FP8, XD>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
-                dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, a.x,
+  constexpr bool XD = kStreamXD<NT, WB>;
+  constexpr int RB = NT == 1 ? 1 : (XD && WB ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
+  return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
+                dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, a.x,
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
 }
 
-template <int NT, bool FP8>
-constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, FP8> && FP8 ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
+template <int NT, int WB>
+constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
 
 // K split of a streaming row GEMM.  A narrow output (few 16-row blocks, e.g.
 // a rank's QKV projection: 80 blocks for 1280 rows) keeps too few loads in
@@ -807,28 +807,28 @@ constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, FP8> && FP8 ? TPMLP_DECODE_R
 #define TPMLP_SPLIT_TARGET_WAVES 1024
 #endif
 
-template <int NT, bool FP8>
+template <int NT, int WB>
 int stream_splits(int N, int K) {
-  constexpr int RB = kRowRB<NT, FP8>;
-  constexpr int WV = StreamShape<NT, RB, FP8, kStreamXD<NT, FP8>>::WV;
+  constexpr int RB = kRowRB<NT, WB>;
+  constexpr int WV = StreamShape<NT, RB, WB, kStreamXD<NT, WB>>::WV;
   const int blocks = (N + 16 * RB - 1) / (16 * RB);
   const int want = (TPMLP_SPLIT_TARGET_WAVES + blocks * WV - 1) / (blocks * WV);
-  const int cap = K / (FP8 ? 256 : 128) / (2 * WV);
+  const int cap = K / (WB ? 256 : 128) / (2 * WV);
   return max(1, min(want, cap));
 }
 
-template <int NT, bool FP8, bool OBF>
+template <int NT, int WB, bool OBF>
 hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
-  constexpr bool XD = kStreamXD<NT, FP8>;
-  constexpr int RB = kRowRB<NT, FP8>;
-  const int nseg = g.ws ? stream_splits<NT, FP8>(g.N, g.K) : 1;
+  constexpr bool XD = kStreamXD<NT, WB>;
+  constexpr int RB = kRowRB<NT, WB>;
+  const int nseg = g.ws ? stream_splits<NT, WB>(g.N, g.K) : 1;
   const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg);
-  hipError_t e = launch(g.kind_decode, down_stream_kernel<NT, RB, FP8, XD, OBF>, grid,
-                        dim3(StreamShape<NT, RB, FP8, XD>::WV * 64), 0, stream, g.M, g.N, g.K,
+  hipError_t e = launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF>, grid,
+                        dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, g.M, g.N, g.K,
                         (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
   if (e != hipSuccess || nseg == 1) return e;
   const int64_t groups = (int64_t)g.M * g.N / 4;
-  return launch(K_SPLITK_FINISH, splitk_finish_kernel<FP8, OBF>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
+  return launch(K_SPLITK_FINISH, splitk_finish_kernel<WB, OBF>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
                 0, stream, g.M, g.N, nseg, (const float*)g.ws, g.s, g.out, g.ldo);
 }
 
@@ -839,58 +839,84 @@ hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
 // The streaming kernels move whole 16-row x 256-byte slots along K: they need
 // K to be a multiple of 128 (bf16) / 256 (fp8) k-values; other shapes use the
 // register-batch kernels, which step 32 / 64 k-values at a time.
-template <bool FP8>
+template <int WB>
 constexpr bool streams(int K) {
-  return TPMLP_DECODE_V2 && K % (FP8 ? 256 : 128) == 0;
+  return TPMLP_DECODE_V2 && K % (WB ? 256 : 128) == 0;
 }
 
-template <bool FP8>
+template <int WB>
 hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
-  const bool st = streams<FP8>(a.h);
+  const bool st = streams<WB>(a.h);
   switch ((a.M + 15) / 16) {
-    case 1: return st ? gateup_stream<1, FP8>(a, stream) : gateup_v1<1, FP8>(a, stream);
-    case 2: return st ? gateup_stream<2, FP8>(a, stream) : gateup_v1<2, FP8>(a, stream);
-    case 3: return st ? gateup_stream<3, FP8>(a, stream) : gateup_v1<3, FP8>(a, stream);
-    case 4: return st ? gateup_stream<4, FP8>(a, stream) : gateup_v1<4, FP8>(a, stream);
+    case 1: return st ? gateup_stream<1, WB>(a, stream) : gateup_v1<1, WB>(a, stream);
+    case 2: return st ? gateup_stream<2, WB>(a, stream) : gateup_v1<2, WB>(a, stream);
+    case 3: return st ? gateup_stream<3, WB>(a, stream) : gateup_v1<3, WB>(a, stream);
+    case 4: return st ? gateup_stream<4, WB>(a, stream) : gateup_v1<4, WB>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-template <bool FP8, bool OBF>
+template <int WB, bool OBF>
 hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
-  const bool st = streams<FP8>(g.K);
+  const bool st = streams<WB>(g.K);
   switch ((g.M + 15) / 16) {
-    case 1: return st ? rowgemm_stream<1, FP8, OBF>(g, stream) : rowgemm_v1<1, FP8, OBF>(g, stream);
-    case 2: return st ? rowgemm_stream<2, FP8, OBF>(g, stream) : rowgemm_v1<2, FP8, OBF>(g, stream);
-    case 3: return st ? rowgemm_stream<3, FP8, OBF>(g, stream) : rowgemm_v1<3, FP8, OBF>(g, stream);
-    case 4: return st ? rowgemm_stream<4, FP8, OBF>(g, stream) : rowgemm_v1<4, FP8, OBF>(g, stream);
+    case 1: return st ? rowgemm_stream<1, WB, OBF>(g, stream) : rowgemm_v1<1, WB, OBF>(g, stream);
+    case 2: return st ? rowgemm_stream<2, WB, OBF>(g, stream) : rowgemm_v1<2, WB, OBF>(g, stream);
+    case 3: return st ? rowgemm_stream<3, WB, OBF>(g, stream) : rowgemm_v1<3, WB, OBF>(g, stream);
+    case 4: return st ? rowgemm_stream<4, WB, OBF>(g, stream) : rowgemm_v1<4, WB, OBF>(g, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, bool fp8) {
-  if (M < 1 || M > kDecodeMaxM) return 0;
+namespace {
+
+template <int WB>
+int64_t workspace_bytes_wb(int M, int N, int K) {
   int nseg = 1;
-  if (fp8 ? streams<true>(K) : streams<false>(K)) {
+  if (streams<WB>(K)) {
     switch ((M + 15) / 16) {
-      case 1: nseg = fp8 ? stream_splits<1, true>(N, K) : stream_splits<1, false>(N, K); break;
-      case 2: nseg = fp8 ? stream_splits<2, true>(N, K) : stream_splits<2, false>(N, K); break;
-      case 3: nseg = fp8 ? stream_splits<3, true>(N, K) : stream_splits<3, false>(N, K); break;
-      default: nseg = fp8 ? stream_splits<4, true>(N, K) : stream_splits<4, false>(N, K); break;
+      case 1: nseg = stream_splits<1, WB>(N, K); break;
+      case 2: nseg = stream_splits<2, WB>(N, K); break;
+      case 3: nseg = stream_splits<3, WB>(N, K); break;
+      default: nseg = stream_splits<4, WB>(N, K); break;
     }
   }
   return nseg > 1 ? (int64_t)nseg * M * N * 4 : 0;
 }
 
+template <int WB>
+hipError_t rowgemm_wb(const RowGemm& g, hipStream_t stream) {
+  return g.out_bf16 ? run_rowgemm<WB, true>(g, stream) : run_rowgemm<WB, false>(g, stream);
+}
+
+}  // namespace
+
+int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {
+  if (M < 1 || M > kDecodeMaxM) return 0;
+  switch (wb) {
+    case kWeightE4M3: return workspace_bytes_wb<kWeightE4M3>(M, N, K);
+    case kWeightI8: return workspace_bytes_wb<kWeightI8>(M, N, K);
+    default: return workspace_bytes_wb<kWeightWide>(M, N, K);
+  }
+}
+
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
-  if (g.fp8) return g.out_bf16 ? run_rowgemm<true, true>(g, stream) : run_rowgemm<true, false>(g, stream);
-  return g.out_bf16 ? run_rowgemm<false, true>(g, stream) : run_rowgemm<false, false>(g, stream);
+  switch (g.wb) {
+    case kWeightE4M3: return rowgemm_wb<kWeightE4M3>(g, stream);
+    case kWeightI8: return rowgemm_wb<kWeightI8>(g, stream);
+    default: return rowgemm_wb<kWeightWide>(g, stream);
+  }
 }
 
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream) {
-  hipError_t e = a.fp8 ? run_gateup<true>(a, stream) : run_gateup<false>(a, stream);
+  hipError_t e;
+  switch (a.wb) {
+    case kWeightE4M3: e = run_gateup<kWeightE4M3>(a, stream); break;
+    case kWeightI8: e = run_gateup<kWeightI8>(a, stream); break;
+    default: e = run_gateup<kWeightWide>(a, stream); break;
+  }
   if (e != hipSuccess) return e;
   return launch_rowgemm_decode(down_of(a), stream);
 }

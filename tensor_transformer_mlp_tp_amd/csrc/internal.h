@@ -27,6 +27,12 @@ enum KernelKind : int {
 
 constexpr int kMaxPartials = 64;
 
+// Weight storage formats of the bf16-activation kernels: 2-byte bf16, or one
+// byte per weight with an fp32 scale per output row (e4m3fn codes or int8).
+constexpr int kWeightWide = 0;
+constexpr int kWeightE4M3 = 1;
+constexpr int kWeightI8 = 2;
+
 struct PartialPtrs {
   const float* p[kMaxPartials];
 };
@@ -69,7 +75,7 @@ struct ShardArgs {
   int64_t ldp;
   void* a;                  // workspace: M x I_s intermediate
   int64_t lda;
-  bool fp8;                 // weights are e4m3fn codes
+  int wb;                   // weight format: kWeightWide / kWeightE4M3 / kWeightI8
 };
 
 // out (M x N) = A (M x K) * W^T with W (N x K, (out, in) layout), fp32
@@ -85,7 +91,7 @@ struct RowGemm {
   void* out;                // M x N
   int64_t ldo;
   bool out_bf16;            // else fp32
-  bool fp8;
+  int wb;                   // weight format (kWeight*)
   float* ws;                // split-K scratch (null: no split), 16-byte aligned
   int kind_decode, kind_prefill, kind_f32;  // timing kinds of the three paths
 };
@@ -102,7 +108,7 @@ inline RowGemm down_of(const ShardArgs& s) {
   g.a = s.a; g.lda = s.lda;
   g.w = s.wd; g.ldw = s.ldw_down; g.s = s.sd;
   g.out = s.p; g.ldo = s.ldp;
-  g.out_bf16 = false; g.fp8 = s.fp8; g.ws = nullptr;
+  g.out_bf16 = false; g.wb = s.wb; g.ws = nullptr;
   g.kind_decode = K_DOWN_DECODE; g.kind_prefill = K_DOWN_PREFILL; g.kind_f32 = K_DOWN_F32;
   return g;
 }
@@ -112,7 +118,7 @@ hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
 // Split-K scratch bytes launch_rowgemm_decode uses for this shape (0: none).
-int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, bool fp8);
+int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
 hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
 

@@ -135,7 +135,7 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   return TileCoord{first_m + i % gsize, i / gsize};
 }
 
-template <bool SWIGLU, bool FP8, int BK, int NS, int WV, bool OBF>
+template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   constexpr int WN = WV / 2;                   // waves across the weight rows (2 across tokens)
   constexpr int CB = BN / WN / 32;             // 32-row weight blocks per wave
   constexpr int TB = BM / 2 / 32;              // 32-token blocks per wave
-  constexpr int EB = FP8 ? 1 : 2;              // weight bytes per element
+  constexpr int EB = WB ? 1 : 2;              // weight bytes per element
   constexpr int KSUB = BK / 16;                // MFMA sub-steps per stage
   constexpr int XROWB = BK * 2;                // bytes per LDS activation row
   constexpr int WROWB = BK * EB;               // bytes per LDS weight row
@@ -258,12 +258,12 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   u32x4 wq[CB];
   auto read_w = [&](const uint8_t* sw, int kk, int cb, bf16x8 (&wf)[CB]) {
     const int r = wrow[cb];
-    if constexpr (FP8) {
+    if constexpr (WB) {
       if ((kk & 1) == 0) {
         wq[cb] = lds_read16(sw + r * WROWB + (((kk + g) ^ swz<WROWB>(r)) * 16));
-        wf[cb] = fp8x8_to_bf16x8(wq[cb][0], wq[cb][1]);
+        wf[cb] = byte8_to_bf16x8<WB>(wq[cb][0], wq[cb][1]);
       } else {
-        wf[cb] = fp8x8_to_bf16x8(wq[cb][2], wq[cb][3]);
+        wf[cb] = byte8_to_bf16x8<WB>(wq[cb][2], wq[cb][3]);
       }
     } else {
       const int ch = 2 * kk + g;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   };
   auto read_x = [&](const uint8_t* sx, int kk, int tb, bf16x8 (&xf)[TB]) {
     const int r = xrow[tb];
-    const int ch = FP8 ? (4 * (kk >> 1) + 2 * g + (kk & 1)) : (2 * kk + g);
+    const int ch = WB ? (4 * (kk >> 1) + 2 * g + (kk & 1)) : (2 * kk + g);
     xf[tb] = as_bf16x8(lds_read16(sx + r * XROWB + ((ch ^ swz<XROWB>(r)) * 16)));
   };
   // Read order = order of first use by the sub-step's MFMAs (cb-major):
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
       // scheduling: direct loads of stage kt+NS-1, fragments of sub-step 0,
       // then each sub-step's MFMAs with the next sub-step's reads threaded in
       // (fp8 odd sub-steps read activations only)
-      constexpr int NMF = CB * TB, NRD = CB + TB, NRX = FP8 ? TB : CB + TB;
+      constexpr int NMF = CB * TB, NRD = CB + TB, NRX = WB ? TB : CB + TB;
       __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
       sched_substep<NRX, NMF>();
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         const int ch = n0 + wn * (BN / 2 / WN) + cb * 32 + 8 * j + 4 * g;  // channels ch .. ch+3
         if (ch >= N) continue;
         float sgv[4] = {1.f, 1.f, 1.f, 1.f}, suv[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (FP8) {
+        if constexpr (WB) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             sgv[i] = s0[ch + i];
@@ -364,7 +364,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float gv = acc[cb][tb][4 * j + i], uv = acc[cb + CB / 2][tb][4 * j + i];
-            if constexpr (FP8) {
+            if constexpr (WB) {
               gv *= sgv[i];
               uv *= suv[i];
             }
@@ -383,7 +383,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         const int f = n0 + wn * (BN / WN) + cb * 32 + 8 * j + 4 * g;  // features f .. f+3
         if (f >= N) continue;
         float sv[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (FP8) {
+        if constexpr (WB) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv[i] = s0[f + i];
         }
@@ -418,20 +418,20 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 
 constexpr int kBK = TPMLP_PREFILL_BK;
 constexpr int kWV = TPMLP_PREFILL_WAVES;
-template <bool FP8>
-constexpr int kNS = FP8 ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
+template <int WB>
+constexpr int kNS = WB ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
 
-template <bool FP8>
+template <int WB>
 hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
-  return launch(K_GATEUP_PREFILL, gemm_kernel<true, FP8, kBK, kNS<FP8>, kWV, false>,
+  return launch(K_GATEUP_PREFILL, gemm_kernel<true, WB, kBK, kNS<WB>, kWV, false>,
                 dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, a.x,
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m,
                 tiles_n);
 }
 
-template <bool FP8, bool OBF>
+template <int WB, bool OBF>
 hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   const int tiles_m = (g.M + BM - 1) / BM;
   const int tiles_n = (g.N + BN - 1) / BN;
@@ -440,7 +440,7 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   ar.nb = 1;
   ar.rows = g.M;
   ar.ld = g.lda;
-  return launch(g.kind_prefill, gemm_kernel<false, FP8, kBK, kNS<FP8>, kWV, OBF>,
+  return launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF>,
                 dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
                 (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr, g.out, g.ldo,
                 tiles_m, tiles_n);
@@ -449,12 +449,23 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
-  if (g.fp8) return g.out_bf16 ? run_rowgemm<true, true>(g, stream) : run_rowgemm<true, false>(g, stream);
-  return g.out_bf16 ? run_rowgemm<false, true>(g, stream) : run_rowgemm<false, false>(g, stream);
+  switch (g.wb) {
+    case kWeightE4M3:
+      return g.out_bf16 ? run_rowgemm<kWeightE4M3, true>(g, stream) : run_rowgemm<kWeightE4M3, false>(g, stream);
+    case kWeightI8:
+      return g.out_bf16 ? run_rowgemm<kWeightI8, true>(g, stream) : run_rowgemm<kWeightI8, false>(g, stream);
+    default:
+      return g.out_bf16 ? run_rowgemm<kWeightWide, true>(g, stream) : run_rowgemm<kWeightWide, false>(g, stream);
+  }
 }
 
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
-  hipError_t e = a.fp8 ? run_gateup<true>(a, stream) : run_gateup<false>(a, stream);
+  hipError_t e;
+  switch (a.wb) {
+    case kWeightE4M3: e = run_gateup<kWeightE4M3>(a, stream); break;
+    case kWeightI8: e = run_gateup<kWeightI8>(a, stream); break;
+    default: e = run_gateup<kWeightWide>(a, stream); break;
+  }
   if (e != hipSuccess) return e;
   return launch_rowgemm_prefill(down_of(a), stream);
 }

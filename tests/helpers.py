@@ -12,6 +12,8 @@ import workloads
 
 TOL_BF16 = 2e-2   # max |out - ref| / rms(ref), bf16 activations and weights (and fp32)
 TOL_FP8 = 6e-2    # same metric, fp8 e4m3fn weights (reference: dequantised weights)
+TOL_INT8 = 2e-2   # int8 weights: the reference is the dequantised weights, and the
+                  # kernels widen the codes to bf16 exactly, so only the bf16 bound applies
 
 
 def to_device(arr, dtype, device="cuda"):
@@ -22,6 +24,8 @@ def to_device(arr, dtype, device="cuda"):
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
     if dtype == "e4m3fn":
         return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8)).view(torch.float8_e4m3fn).to(device)
+    if dtype == "int8":
+        return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.uint8)).view(torch.int8).to(device)
     raise ValueError(dtype)
 
 

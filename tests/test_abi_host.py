@@ -65,6 +65,9 @@ def test_workspace_bytes():
     assert lib.tp_mlp_workspace_bytes(0, 8192, 28672, 8, BF16, BF16) == 0
     assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 8, F32, BF16) == 0        # unsupported pair
     assert lib.tp_mlp_workspace_bytes(1, 100, 28672, 8, BF16, BF16) == 0        # h % 64
+    assert lib.tp_mlp_workspace_bytes(3, 64, 128, 2, BF16, _lib.TP_INT8) == 512
+    assert lib.tp_mlp_workspace_bytes(3, 64, 128, 2, _lib.TP_INT8, _lib.TP_INT8) == 0
+    assert lib.tp_mlp_workspace_bytes(3, 64, 128, 2, BF16, 9) == 0              # unknown code
 
 
 P = 0x10000  # a 256-byte aligned fake address; never dereferenced (every call fails validation)
@@ -96,6 +99,9 @@ def fwd(M=1, h=128, I=256, t=2, k=0, act=BF16, w=BF16, x=P, wg=P * 2, wu=P * 3, 
     (dict(act=F32, w=BF16), _lib.TP_ERR_UNSUPPORTED),
     (dict(act=FP8, w=FP8), _lib.TP_ERR_UNSUPPORTED),
     (dict(w=FP8), _lib.TP_ERR_INVALID_ARG),                 # fp8 without scales
+    (dict(w=_lib.TP_INT8), _lib.TP_ERR_INVALID_ARG),        # int8 without scales
+    (dict(act=_lib.TP_INT8, w=_lib.TP_INT8), _lib.TP_ERR_UNSUPPORTED),
+    (dict(act=F32, w=_lib.TP_INT8), _lib.TP_ERR_UNSUPPORTED),
     (dict(sg=P, su=P, sd=P), _lib.TP_ERR_INVALID_ARG),      # scales with bf16 weights
     (dict(ldx=64), _lib.TP_ERR_INVALID_ARG),                # ld < row length
     (dict(ldd=64), _lib.TP_ERR_INVALID_ARG),
@@ -245,6 +251,7 @@ def test_attn_qkv_workspace_bytes():
     (dict(w=FP8), _lib.TP_ERR_INVALID_ARG),         # fp8 without scales
     (dict(s=P * 4), _lib.TP_ERR_INVALID_ARG),       # scales with bf16 weights
     (dict(act=F32, w=BF16), _lib.TP_ERR_UNSUPPORTED),
+    (dict(w=_lib.TP_INT8), _lib.TP_ERR_INVALID_ARG),  # int8 without scales
     (dict(h=96), _lib.TP_ERR_UNSUPPORTED),          # h % 64
     (dict(d=36), _lib.TP_ERR_UNSUPPORTED),          # n_loc = 216, not a multiple of 16
     (dict(ldx=64), _lib.TP_ERR_INVALID_ARG),

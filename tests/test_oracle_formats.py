@@ -125,3 +125,55 @@ def test_quantise_rows_roundtrip_bound():
     # an all-zero row gets scale 1 and zero codes
     q0, s0 = workloads.quantise_rows_e4m3fn(np.zeros((2, 8), np.float32))
     assert np.all(s0 == 1.0) and np.all(oracle.e4m3fn_to_f64(q0) == 0.0)
+
+
+# ----------------------------------------------------------------- int8
+
+def test_int8_golden_codes():
+    for code, want in read_golden("int8_codes.txt"):
+        got = oracle.int8_to_f64(np.array([int(code, 16)], dtype=np.uint8))[0]
+        assert got == float(want), code
+
+
+def test_int8_matches_numpy_view_for_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    assert np.array_equal(oracle.int8_to_f64(codes), codes.view(np.int8).astype(np.float64))
+    with pytest.raises(TypeError):
+        oracle.int8_to_f64(codes.view(np.int8))
+
+
+def test_int8_quantiser_is_nearest_even_and_symmetric():
+    rng = np.random.Generator(np.random.PCG64(12))
+    w = rng.normal(0, 0.02, (16, 300)).astype(np.float32)
+    w[3, 7] = 0.0
+    w[5] = 0.0                                   # all-zero row
+    q, s = workloads.quantise_rows_int8(w)
+    assert q.dtype == np.uint8 and s.dtype == np.float32
+    v = oracle.int8_to_f64(q)
+    assert np.all(np.abs(v) <= 127)
+    assert s[5] == 1.0 and np.all(v[5] == 0)
+    for r in range(16):
+        if r == 5:
+            continue
+        # the row's largest magnitude maps to +-127
+        assert np.max(np.abs(v[r])) == 127
+        scaled = (w[r] / s[r]).astype(np.float32).astype(np.float64)
+        for j in range(300):
+            cands = np.arange(-127, 128, dtype=np.float64)
+            d = np.abs(cands - scaled[j])
+            best = cands[d == d.min()]
+            want = best[0] if len(best) == 1 else best[(best % 2) == 0][0]
+            assert v[r, j] == want, (r, j)
+    # crafted ties: 0.5 -> 0, 1.5 -> 2, 2.5 -> 2, -2.5 -> -2 (scale 1 from amax 127)
+    t = np.array([[127.0, 0.5, 1.5, 2.5, -2.5, -0.5]], np.float32)
+    qt, st = workloads.quantise_rows_int8(t)
+    assert st[0] == 1.0
+    assert oracle.int8_to_f64(qt)[0].tolist() == [127.0, 0.0, 2.0, 2.0, -2.0, -0.0]
+
+
+def test_int8_roundtrip_bound():
+    w = workloads.draw_f32(98, (32, 512), 0.02)
+    q, s = workloads.quantise_rows_int8(w)
+    deq = oracle.int8_to_f64(q) * s.astype(np.float64)[:, None]
+    err = np.abs(deq - w.astype(np.float64))
+    assert np.all(err <= 0.5 * s[:, None].astype(np.float64) * (1 + 1e-6))

@@ -53,6 +53,9 @@ CONFIGS = {
     4: dict(name="llama70b_tp4_fp8", desc="70B-shaped TP=4 rank, fp8 e4m3 weights",
             M=(32, 2048), h=8192, I=28672, t=4, act="bf16", w="e4m3fn",
             std_x=1.0, std_gu=0.02, std_down=0.02, reduce_n=None),
+    9: dict(name="llama70b_tp2_int8", desc="70B-shaped TP=2 rank, int8 weights (W8A16)",
+            M=(1, 8, 2048), h=8192, I=28672, t=2, act="bf16", w="int8",
+            std_x=1.0, std_gu=0.02, std_down=0.02, reduce_n=None),
     5: dict(name="llama405b_tp8_prefill", desc="405B-shaped TP=8 rank prefill",
             M=(8192,), h=16384, I=53248, t=8, act="bf16", w="bf16",
             std_x=1.0, std_gu=0.01, std_down=0.01, reduce_n=8192 * 16384),
@@ -185,6 +188,23 @@ def quantise_rows_e4m3fn(w):
     return f32_to_e4m3fn(scaled), s
 
 
+INT8_MAX = np.float32(127.0)
+
+
+def quantise_rows_int8(w):
+    """Per-row symmetric int8 quantisation of an (out, in) float32 matrix:
+    s = float32(amax / 127) (1 for an all-zero row), q = round-half-even of
+    float32(w / s) clamped to [-127, 127].  Returns (codes as uint8 bytes,
+    scales float32)."""
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.max(np.abs(w), axis=1)
+    s = (amax / INT8_MAX).astype(np.float32)
+    s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
+    scaled = (w / s[:, None]).astype(np.float32)
+    q = np.clip(np.rint(scaled), -127, 127).astype(np.int8)
+    return q.view(np.uint8), s
+
+
 def to_storage(w32, dtype):
     """float32 draws -> storage dict for the given dtype."""
     if dtype == "f32":
@@ -193,6 +213,9 @@ def to_storage(w32, dtype):
         return dict(data=f32_to_bf16_bits(w32), scale=None)
     if dtype == "e4m3fn":
         q, s = quantise_rows_e4m3fn(w32)
+        return dict(data=q, scale=s)
+    if dtype == "int8":
+        q, s = quantise_rows_int8(w32)
         return dict(data=q, scale=s)
     raise ValueError("unknown dtype %r" % (dtype,))
 
@@ -276,7 +299,8 @@ def make_attn_full_weights(config_id, h, n_heads, n_kv_heads, head_dim, dtype, s
 # accounting (algorithmic bytes and FLOPs; no arithmetic of the method)
 # ---------------------------------------------------------------------------
 
-BYTES = {"f32": 4, "bf16": 2, "e4m3fn": 1}
+BYTES = {"f32": 4, "bf16": 2, "e4m3fn": 1, "int8": 1}
+SCALED = ("e4m3fn", "int8")    # one byte per weight + an fp32 scale per output row
 
 
 def forward_flops(M, h, I_s):
@@ -291,7 +315,7 @@ def forward_bytes(M, h, I_s, act="bf16", w="bf16"):
     not move it.
     """
     b = 3 * h * I_s * BYTES[w] + M * h * BYTES[act] + M * h * 4
-    if w == "e4m3fn":
+    if w in SCALED:
         b += (2 * I_s + h) * 4
     return int(b)
 
@@ -299,7 +323,7 @@ def forward_bytes(M, h, I_s, act="bf16", w="bf16"):
 def gateup_bytes(M, h, I_s, act="bf16", w="bf16"):
     """Algorithmic bytes of the gate/up phase: two weight shards, X, A written."""
     b = 2 * h * I_s * BYTES[w] + M * h * BYTES[act] + M * I_s * BYTES[act]
-    if w == "e4m3fn":
+    if w in SCALED:
         b += 2 * I_s * 4
     return int(b)
 
@@ -307,7 +331,7 @@ def gateup_bytes(M, h, I_s, act="bf16", w="bf16"):
 def down_bytes(M, h, I_s, act="bf16", w="bf16"):
     """Algorithmic bytes of the down phase: down shard, A read, P written."""
     b = h * I_s * BYTES[w] + M * I_s * BYTES[act] + M * h * 4
-    if w == "e4m3fn":
+    if w in SCALED:
         b += h * 4
     return int(b)
 
@@ -323,8 +347,8 @@ def linear_flops(M, N, K):
 
 def linear_bytes(M, N, K, act="bf16", w="bf16", out="bf16"):
     """Algorithmic bytes of one projection: weight, input and output once
-    (+ per-row scales for e4m3fn)."""
+    (+ per-row scales for one-byte weights)."""
     b = N * K * BYTES[w] + M * K * BYTES[act] + M * N * BYTES[out]
-    if w == "e4m3fn":
+    if w in SCALED:
         b += N * 4
     return int(b)
