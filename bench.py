@@ -12,7 +12,9 @@ layers), so the weights come from HBM and not from the 256 MB last-level
 cache.  ``value`` is algorithmic bytes per second over the timed steps.
 
 Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
-(TP=4 fp8 weights: decode M=32 and prefill M=2048), prefill405b (8192 tokens),
+(TP=4 fp8 weights: decode M=32 and prefill M=2048), int8_70b (TP=2 int8
+weights: decode M=1 and 8, prefill M=2048), w8a8_prefill70b (fp8 activations
+and weights on the fp8 matrix cores, TP=4 at 2048 tokens), prefill405b (8192 tokens),
 reduce70b / reduce405b (the 8-way reduces alone), sp_prefill70b (the
 sequence-parallel form: forward over eight row blocks of X, reduce-scatter),
 attn70b / attn_prefill70b (the same rank's attention-block projections: QKV,
@@ -64,7 +66,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--workload", default="decode70b",
                     choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
-                             "sp_prefill70b", "attn70b", "attn_prefill70b", "copy"])
+                             "sp_prefill70b", "attn70b", "attn_prefill70b", "int8_70b", "w8a8_prefill70b",
+                             "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     return ap.parse_args()
@@ -76,6 +79,7 @@ KERNEL_SOURCES = {
     "partial_reduce": ("reduce.hip", "common.h", "internal.h"),
     "qkv_decode": ("decode.hip", "common.h", "internal.h"),
     "qkv_prefill": ("prefill.hip", "common.h", "internal.h"),
+    "gateup_w8a8": ("prefill.hip", "common.h", "internal.h"),
 }
 
 
@@ -119,6 +123,8 @@ def to_dev(arr, dt):
         return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).cuda()
     if dt == "e4m3fn":
         return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.float8_e4m3fn).cuda()
+    if dt == "int8":
+        return torch.from_numpy(np.ascontiguousarray(arr)).view(torch.int8).cuda()
     return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).cuda()
 
 
@@ -146,7 +152,7 @@ class Phase:
         self.x = to_dev(self.x_host, act)
         self.partial = torch.empty((M, h), dtype=torch.float32, device="cuda")
         nbytes = tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16,
-                                    torch.float8_e4m3fn if w == "e4m3fn" else torch.bfloat16)
+                                    {"e4m3fn": torch.float8_e4m3fn, "int8": torch.int8}.get(w, torch.bfloat16))
         self.ws = tp.alloc_workspace(nbytes, "cuda")
         self.with_reduce = with_reduce
         if with_reduce:
@@ -394,48 +400,118 @@ def bench_prefill(tp, args, cfg_id, M, label):
     return out
 
 
-def bench_fp8(tp, args):
-    import torch
-    c = workloads.CONFIGS[4]
-    h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
-    sets, host0 = device_weights(4, h, I_s, "e4m3fn", c["std_gu"], c["std_down"], args.weight_sets)
-    dec = Phase(tp, 4, 32, h, I_s, t, "bf16", "e4m3fn", False)
-    pre = Phase(tp, 4, 2048, h, I_s, t, "bf16", "e4m3fn", False)
+W_LABEL = {"e4m3fn": "fp8 e4m3fn", "int8": "int8"}
+
+
+def bench_quant(tp, args, cfg_id):
+    """One-byte weights with fp32 row scales (W8A16): the decode phases of the
+    configuration (value: algorithmic GB/s) and its prefill size (reported
+    beside it)."""
+    c = workloads.CONFIGS[cfg_id]
+    h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
+    dec_Ms, pre_M = list(c["M"][:-1]), c["M"][-1]
+    # enough weight sets that a step's weights come from HBM (>= 3 x 256 MB)
+    n_sets = max(2, min(args.weight_sets, (768 << 20) // (3 * h * I_s) + 1))
+    sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
+    decs = [Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, False) for M in dec_Ms]
+    pre = Phase(tp, cfg_id, pre_M, h, I_s, t, "bf16", w, False)
+
+    def step(i):
+        for ph in decs:
+            ph.run(sets[i % len(sets)])
+
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
-    el_d, prof_d = timed(tp, lambda i: dec.run(sets[i % len(sets)]), steps, warmup, ["gateup_decode"])
-    prof_d.update({k: v for k, v in breakdown(tp, lambda i: dec.run(sets[i % len(sets)]), steps,
-                                              warmup + steps).items() if k != "gateup_decode"})
-    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), max(10, steps // 10), 3, ["gateup_prefill", "down_prefill"])
-    dec_bytes = dec.bytes()
+    el_d, prof_d = timed(tp, step, steps, warmup, ["gateup_decode"])
+    prof_d.update({k: v for k, v in breakdown(tp, step, steps, warmup + steps).items() if k != "gateup_decode"})
+    p_steps = max(10, steps // 10)
+    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), p_steps, 3, ["gateup_prefill", "down_prefill"])
+    dec_bytes = sum(ph.bytes() for ph in decs)
     dec_gbs = dec_bytes * steps / el_d / 1e9
-    pre_tf = pre.flops() * max(10, steps // 10) / el_p / 1e12
+    pre_tf = pre.flops() * p_steps / el_p / 1e12
     gu_ms, gu_n = prof_d["gateup_decode"]
-    gu_gbs = workloads.gateup_bytes(32, h, I_s, "bf16", "e4m3fn") * gu_n / (gu_ms * 1e-3) / 1e9
+    gu_gbs = steps * sum(workloads.gateup_bytes(M, h, I_s, "bf16", w) for M in dec_Ms) / (gu_ms * 1e-3) / 1e9
     pgu_ms, pgu_n = prof_p["gateup_prefill"]
-    pgu_tf = 4 * 2048 * h * I_s * pgu_n / (pgu_ms * 1e-3) / 1e12
+    pgu_tf = 4 * pre_M * h * I_s * pgu_n / (pgu_ms * 1e-3) / 1e12
     out = dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
-                ms_per_step=round(1e3 * el_d / steps, 5), higher_is_better=True, scaling="weak",
-                vs_baseline=None, dtype="bf16 (fp8 e4m3fn weights)", data="synthetic",
-                config={"workload": "70B-shaped TP=4 rank, fp8 e4m3fn weights + fp32 row scales: decode M=32 "
-                                    "(value) and prefill M=2048", "h": h, "I_s": I_s, "t": t,
-                        "weight_sets": len(sets)},
-                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                          "traffic": recorded_traffic("gateup_decode", "fp8_70b"), "kernel": "gateup_decode"},
-                prefill={"M": 2048, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
-                         "gateup_TFLOPs": round(pgu_tf, 1), "kernels": {k: {"avg_us": 1e3 * v[0] / v[1]}
-                                                                       for k, v in prof_p.items()}},
-                kernels={k: {"avg_us": 1e3 * v[0] / v[1]} for k, v in prof_d.items()})
+               ms_per_step=round(1e3 * el_d / steps, 5), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="bf16 (%s weights)" % W_LABEL[w], data="synthetic",
+               config={"workload": "70B-shaped TP=%d rank, %s weights + fp32 row scales: decode M=%s (value) "
+                                   "and prefill M=%d" % (t, W_LABEL[w], ", ".join(map(str, dec_Ms)), pre_M),
+                       "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
+               roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                         "traffic": recorded_traffic("gateup_decode", args.workload), "kernel": "gateup_decode"},
+               prefill={"M": pre_M, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
+                        "gateup_TFLOPs": round(pgu_tf, 1), "kernels": {k: {"avg_us": 1e3 * v[0] / v[1]}
+                                                                      for k, v in prof_p.items()}},
+               kernels={k: {"avg_us": 1e3 * v[0] / v[1]} for k, v in prof_d.items()})
     if not args.no_cpu_baseline:
         import oracle
 
         def once():
-            oracle.rank_partial_from_storage(dec.x_host, "bf16", host0["w_gate"], host0["w_up"], host0["w_down"],
-                                             "e4m3fn", host0["s_gate"], host0["s_up"], host0["s_down"])
+            for ph in decs:
+                oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
+                                                 host0["w_down"], w, host0["s_gate"], host0["s_up"],
+                                                 host0["s_down"])
         log("timing the CPU oracle")
         out["cpu_baseline"] = cpu_baseline(once, dec_bytes / 1e9, "GB/s",
-                                           "one M=32 rank partial from the fp8 weight bytes and scales "
-                                           "(the decode value's unit of work), repeated >= 10 s")
+                                           "one decode step's rank partials (M=%s) from the %s weight bytes "
+                                           "and scales, repeated >= 10 s" % (", ".join(map(str, dec_Ms)),
+                                                                             W_LABEL[w]))
+    return out
+
+
+FP8_PEAK_TFLOPS = 5000.0
+
+
+def bench_w8a8(tp, args):
+    """fp8 x fp8 forward of the 70B-shaped TP=4 rank at 2048 tokens (the fp8
+    weight configuration's prefill size): per-token quantisation of X, gate/up
+    on the fp8 matrix cores, quantisation of A, down."""
+    import torch
+    import oracle
+    cfg_id, M = 4, 2048
+    c = workloads.CONFIGS[cfg_id]
+    h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
+    sets, host0 = device_weights(cfg_id, h, I_s, "e4m3fn", c["std_gu"], c["std_down"], 1)
+    x_host = workloads.make_x(cfg_id, M, h, "bf16")
+    x = to_dev(x_host, "bf16")
+    w = sets[0]
+    call = tp.prepare_shard_forward_w8a8(x, w["w_gate"], w["w_up"], w["w_down"], t=t, k=0, s_gate=w["s_gate"],
+                                         s_up=w["s_up"], s_down=w["s_down"])
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    elapsed, prof_gu = timed(tp, lambda i: call(), steps, warmup, ["gateup_w8a8"])
+    prof = breakdown(tp, lambda i: call(), steps, warmup + steps)
+    prof["gateup_w8a8"] = prof_gu["gateup_w8a8"]
+    flops = workloads.forward_flops(M, h, I_s)
+    value = flops * steps / elapsed / 1e12
+    gu_ms, gu_n = prof["gateup_w8a8"]
+    gu_tf = 4 * M * h * I_s * gu_n / (gu_ms * 1e-3) / 1e12
+    dn_ms, dn_n = prof["down_w8a8"]
+    dn_tf = 2 * M * h * I_s * dn_n / (dn_ms * 1e-3) / 1e12
+    out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
+               ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="fp8 e4m3fn x e4m3fn (per-token activation scales, row weight scales)",
+               data="synthetic",
+               config={"workload": "70B-shaped TP=4 rank W8A8 forward at M=2048 (h=8192, I_s=7168): quantise X, "
+                                   "gate/up + SwiGLU, quantise A, down to the fp32 partial", "M": M, "h": h,
+                       "I_s": I_s, "t": t},
+               roofline={"bound": "mfma", "achieved": round(gu_tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gu_tf / FP8_PEAK_TFLOPS, 4),
+                         "traffic": recorded_traffic("gateup_w8a8", "w8a8_prefill70b"), "kernel": "gateup_w8a8",
+                         "per_launch_flop": 4 * M * h * I_s},
+               kernels={k: {"launches": v[1], "avg_us": 1e3 * v[0] / v[1]} for k, v in prof.items()},
+               gemm_TFLOPs={"gateup_w8a8": round(gu_tf, 1), "down_w8a8": round(dn_tf, 1)})
+    if not args.no_cpu_baseline:
+        rows = np.arange(0, M, M // 16)
+
+        def once():
+            oracle.rank_partial_w8a8_from_storage(x_host[rows], host0["w_gate"], host0["w_up"], host0["w_down"],
+                                                  host0["s_gate"], host0["s_up"], host0["s_down"])
+        log("timing the CPU oracle")
+        out["cpu_baseline"] = cpu_baseline(once, workloads.forward_flops(len(rows), h, I_s) / 1e12, "TFLOP/s",
+                                           "W8A8 rank partial for %d of the %d token rows (quantisation and "
+                                           "decoding included), repeated >= 10 s" % (len(rows), M))
     return out
 
 
@@ -790,7 +866,11 @@ def main():
         out = bench_prefill(tp, args, 5, 8192, "405B-shaped TP=8 rank prefill, M=8192, h=16384, I_s=6656, "
                                                "bf16, forward + 8-way fp32 partial reduce of 8192x16384")
     elif args.workload == "fp8_70b":
-        out = bench_fp8(tp, args)
+        out = bench_quant(tp, args, 4)
+    elif args.workload == "int8_70b":
+        out = bench_quant(tp, args, 9)
+    elif args.workload == "w8a8_prefill70b":
+        out = bench_w8a8(tp, args)
     elif args.workload == "reduce70b":
         out = bench_reduce(tp, args, 3)
     elif args.workload == "copy":

@@ -207,6 +207,59 @@ tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_t t, in
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * fp8 x fp8 (W8A8) forward.  The pages' fp8 mode is one byte per weight
+ * ("Build a model sharding system for serving 70B+ parameter models",
+ * scalablesystem.dev, the shard planner); quantising the activations too
+ * puts both GEMM operands on gfx950's fp8 matrix instructions (twice the
+ * bf16 rate) and changes the numerics.  Activation rows are quantised per
+ * token:
+ *
+ *   s_m = amax_m / 448 (fp32; 1 for an all-zero row),
+ *   q[m][j] = e4m3fn(x[m][j] / s_m)   (fp32 quotient, nearest code, ties to
+ *                                      even, magnitudes >= 448 saturate)
+ *
+ * and the rank forward becomes: Xq, s_x = quant(X); G, U = (Xq Wq^T) * s_x *
+ * s_w (fp32 accumulation); A = SiLU(G) (.) U rounded to bf16; Aq, s_a =
+ * quant(A); P_k = (Aq W_down_q^T) * s_a * s_down.  It runs on the MFMA GEMM
+ * kernels for every M (meant for prefill; at decode sizes the fp8-weight
+ * tp_mlp_shard_forward reads the same weight bytes).
+ * ---------------------------------------------------------------------- */
+
+/*
+ * Workspace bytes of tp_mlp_shard_forward_w8a8 (0 if the arguments are
+ * invalid): A in bf16, the codes of X and A, and their per-token scales.
+ */
+size_t tp_mlp_w8a8_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t);
+
+/*
+ * Rank k's partial with fp8 activations and fp8 (e4m3fn) weights.  Arguments
+ * as tp_mlp_shard_forward with act_dtype = TP_BF16 (x is bf16) and w_dtype =
+ * TP_FP8_E4M3FN (scales required); contiguous X only.  Requires h % 128 == 0
+ * and I_s % 128 == 0 (else TP_ERR_UNSUPPORTED), 16-byte aligned pointers and
+ * rows, a 256-byte aligned workspace of tp_mlp_w8a8_workspace_bytes(...)
+ * bytes whose contents on entry are ignored.  Deterministic.
+ */
+tp_status tp_mlp_shard_forward_w8a8(int64_t M, int64_t h, int64_t I_full,
+                                    int32_t t, int32_t k,
+                                    const void* x, int64_t ldx,
+                                    const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                    const void* w_down, int64_t ldw_down,
+                                    const float* s_gate, const float* s_up,
+                                    const float* s_down,
+                                    float* partial, int64_t ldp,
+                                    void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * The per-token quantisation above on its own: rows x cols bf16 (leading
+ * dimension ldx, rows 16-byte aligned) -> e4m3fn codes (leading dimension
+ * ldq bytes, rows 8-byte aligned) and one fp32 scale per row.  cols % 8 == 0
+ * (else TP_ERR_UNSUPPORTED); rows == 0 is a no-op.  Buffers must not overlap.
+ */
+tp_status tp_quantize_rows_e4m3(int64_t rows, int64_t cols, const void* x, int64_t ldx,
+                                void* codes, int64_t ldq, float* scales, void* stream);
+
+/* ------------------------------------------------------------------------
  * Attention-block projections of one rank.  "Build a model sharding system
  * for serving 70B+ parameter models" (scalablesystem.dev), section "The
  * Tensor-Parallel Shard Group", class TPAttentionBlock: the QKV projection is

@@ -33,6 +33,8 @@ Sources (the web pages this build follows):
   Dropout": under sequence parallelism the all-reduce becomes a
   reduce-scatter (rank k keeps the reduced rows of its sequence slice) and
   the next column-parallel projection reads the all-gathered sequence.
+* ``oracle/w8a8.py``: the fp8 x fp8 forward (per-token activation codes;
+  steps and their order in that file's docstring).
 * ``oracle/attn.py``: the attention block's projections under the same split
   (TPAttentionBlock of the scalablesystem.dev section above; heads per rank
   in section 12.2.1 of the arunshar.com chapter; grouped-query KV heads split
@@ -44,7 +46,9 @@ Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 format tables).  No function is "parity unpinned".
 """
 
-from .formats import bf16_bits_to_f64, e4m3fn_to_f64, int8_to_f64, E4M3FN_MAX
+from .formats import (bf16_bits_to_f64, e4m3fn_to_f64, int8_to_f64, e4m3fn_encode, bf16_round_bits,
+                      E4M3FN_MAX)
+from .w8a8 import quantise_rows_e4m3, dequantise_rows, rank_partial_w8a8_from_storage
 from .attn import (
     local_heads,
     head_rows,
@@ -76,6 +80,11 @@ __all__ = [
     "bf16_bits_to_f64",
     "e4m3fn_to_f64",
     "int8_to_f64",
+    "e4m3fn_encode",
+    "bf16_round_bits",
+    "quantise_rows_e4m3",
+    "dequantise_rows",
+    "rank_partial_w8a8_from_storage",
     "E4M3FN_MAX",
     "silu",
     "mlp_full",

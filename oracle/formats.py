@@ -64,6 +64,38 @@ def int8_to_f64(codes):
     return np.where(v >= 128, v - 256, v).astype(np.float64)
 
 
+def e4m3fn_encode(v):
+    """float32 values -> e4m3fn codes (uint8): the nearest finite code, ties to
+    the even code (even mantissa), magnitudes of 448 and above saturating to
+    448 (code 0x7E), the sign bit copied (so -0.0 -> 0x80).  Nearest is found
+    by bisection in the increasing table of the non-negative codes 0x00-0x7E;
+    every table value and midpoint is exact in float64."""
+    v = np.asarray(v, dtype=np.float32)
+    if np.isnan(v).any():
+        raise ValueError("NaN has no code here")
+    mags = _E4M3FN_TABLE[:0x7F]                      # codes 0x00 .. 0x7E, increasing
+    a = np.abs(v.astype(np.float64))
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, 0x7E)   # mags[hi-1] < a <= mags[hi] (inside the range)
+    lo = hi - 1
+    dlo = a - mags[lo]
+    dhi = mags[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a >= 448.0, 0x7E, code)
+    code = np.where(a == 0.0, 0, code)
+    sign = np.signbit(v).astype(np.int64) << 7
+    return (code.astype(np.int64) | sign).astype(np.uint8)
+
+
+def bf16_round_bits(v):
+    """float32 values -> bf16 bit patterns (uint16), round to nearest even:
+    the upper 16 bits of the binary32 word after adding half a bf16 unit
+    (0x7FFF plus the kept low bit, for ties to even).  Finite inputs."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    u = v.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
 def e4m3fn_to_f64(codes):
     """Decode an array of e4m3fn codes (uint8) to float64, exactly."""
     c = np.asarray(codes)

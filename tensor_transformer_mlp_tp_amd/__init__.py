@@ -25,7 +25,8 @@ from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, TP_INT8, EXPORTED_SY
 
 __all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
            "shard_forward_sp", "prepare_shard_forward_sp", "partial_reduce_scatter",
-           "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_workspace_bytes", "attn_qkv_forward", "prepare_attn_qkv_forward",
+           "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_workspace_bytes", "attn_qkv_forward",
+           "w8a8_workspace_bytes", "shard_forward_w8a8", "prepare_shard_forward_w8a8", "quantize_rows_e4m3", "prepare_attn_qkv_forward",
            "attn_out_forward", "prepare_attn_out_forward", "profile_reserve",
            "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "kernel_kinds",
            "TPError", "load"]
@@ -269,6 +270,75 @@ def prepare_partial_reduce_scatter(partials, k, out=None, stream=None):
                         (list(partials), out))
     call.out = out
     return call
+
+
+def w8a8_workspace_bytes(M, h, I_full, t):
+    """Bytes of device workspace ``shard_forward_w8a8`` needs (0 if invalid)."""
+    return int(_lib.load().tp_mlp_w8a8_workspace_bytes(int(M), int(h), int(I_full), int(t)))
+
+
+def shard_forward_w8a8(x, w_gate, w_up, w_down, *, t, k, s_gate, s_up, s_down, partial=None, workspace=None,
+                       stream=None):
+    """Rank k's fp32 partial with per-token fp8 activations and fp8 weights
+    (``include/tp_mlp.h``: tp_mlp_shard_forward_w8a8).  x: (M, h) bf16;
+    weights float8_e4m3fn (or uint8 codes) with fp32 row scales."""
+    call = prepare_shard_forward_w8a8(x, w_gate, w_up, w_down, t=t, k=k, s_gate=s_gate, s_up=s_up,
+                                      s_down=s_down, partial=partial, workspace=workspace, stream=stream)
+    call()
+    return call.partial
+
+
+def prepare_shard_forward_w8a8(x, w_gate, w_up, w_down, *, t, k, s_gate, s_up, s_down, partial=None,
+                               workspace=None, stream=None):
+    """Marshal a shard_forward_w8a8 once; returns a PreparedCall (``partial``)."""
+    device = x.device
+    _check_matrix("x", x, device)
+    for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_matrix(name, m, device)
+        if _w_code(m.dtype) != TP_FP8_E4M3FN:
+            raise TypeError("%s must hold e4m3fn codes" % name)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    for sc in (s_gate, s_up, s_down):
+        _check_scales(sc, device)
+    M, h = x.shape
+    I_s = w_gate.shape[0]
+    I_full = I_s * int(t)
+    if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
+        raise ValueError("shard shapes must be w_gate/w_up (I_s, h) and w_down (h, I_s)")
+    if w_gate.stride(0) != w_up.stride(0):
+        raise ValueError("w_gate and w_up must share a leading dimension")
+    if partial is None:
+        partial = torch.empty((M, h), dtype=torch.float32, device=device)
+    need = w8a8_workspace_bytes(M, h, I_full, t)
+    if workspace is None:
+        workspace = alloc_workspace(max(need, 1), device)
+    lib = _lib.load()
+    args = (M, h, I_full, int(t), int(k), _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+            _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(partial),
+            partial.stride(0), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_of(device, stream))
+    call = PreparedCall(lib.tp_mlp_shard_forward_w8a8, args,
+                        (x, w_gate, w_up, w_down, s_gate, s_up, s_down, partial, workspace))
+    call.partial = partial
+    return call
+
+
+def quantize_rows_e4m3(x, codes=None, scales=None, stream=None):
+    """Per-row e4m3fn codes (uint8, same shape) and fp32 scales of a bf16
+    matrix (``include/tp_mlp.h``: tp_quantize_rows_e4m3)."""
+    device = x.device
+    _check_matrix("x", x, device)
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=device)
+    if scales is None:
+        scales = torch.empty((rows,), dtype=torch.float32, device=device)
+    _lib.check(_lib.load().tp_quantize_rows_e4m3(rows, cols, _ptr(x), x.stride(0), _ptr(codes), codes.stride(0),
+                                                 _ptr(scales), _stream_of(device, stream)))
+    return codes, scales
 
 
 def attn_qkv_width(n_heads, n_kv_heads, head_dim, t):

@@ -24,6 +24,9 @@ EXPORTED_SYMBOLS = (
     "tp_partial_reduce",
     "tp_mlp_shard_forward_sp",
     "tp_partial_reduce_scatter",
+    "tp_mlp_w8a8_workspace_bytes",
+    "tp_mlp_shard_forward_w8a8",
+    "tp_quantize_rows_e4m3",
     "tp_attn_qkv_width",
     "tp_attn_qkv_forward",
     "tp_attn_qkv_workspace_bytes",
@@ -74,6 +77,14 @@ def load():
     lib.tp_mlp_shard_forward_sp.restype = c_i32
     lib.tp_partial_reduce_scatter.argtypes = [c_i64, c_i64, c_i32, c_i32, ctypes.POINTER(vp), vp, vp]
     lib.tp_partial_reduce_scatter.restype = c_i32
+    lib.tp_mlp_w8a8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32]
+    lib.tp_mlp_w8a8_workspace_bytes.restype = ctypes.c_size_t
+    lib.tp_mlp_shard_forward_w8a8.argtypes = [
+        c_i64, c_i64, c_i64, c_i32, c_i32,
+        vp, c_i64, vp, vp, c_i64, vp, c_i64, vp, vp, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
+    lib.tp_mlp_shard_forward_w8a8.restype = c_i32
+    lib.tp_quantize_rows_e4m3.argtypes = [c_i64, c_i64, vp, c_i64, vp, c_i64, vp, vp]
+    lib.tp_quantize_rows_e4m3.restype = c_i32
     lib.tp_attn_qkv_width.argtypes = [c_i64, c_i64, c_i64, c_i32]
     lib.tp_attn_qkv_width.restype = c_i64
     lib.tp_attn_qkv_forward.argtypes = [

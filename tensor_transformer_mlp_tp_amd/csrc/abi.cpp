@@ -127,7 +127,8 @@ size_t g_prof_used = 0;
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
     "partial_reduce", "gateup_f32", "down_f32", "qkv_decode", "qkv_prefill",
-    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish"};
+    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish", "quant_rows",
+    "gateup_w8a8", "down_w8a8"};
 
 // Appends one start/stop event pair to the timing pool.
 bool prof_grow() {
@@ -329,6 +330,123 @@ TP_API tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_
     shifted[j] = partials[j] + (int64_t)k * n;
   }
   return tp_partial_reduce(n, t, shifted, out, stream);
+}
+
+// ------------------------------------------------------------ fp8 x fp8
+
+namespace {
+
+struct W8A8Layout {
+  int64_t a, xq, sx, aq, sa, total;   // byte offsets in the workspace
+};
+
+W8A8Layout w8a8_layout(int64_t M, int64_t h, int64_t I_s) {
+  W8A8Layout l;
+  l.a = 0;
+  l.xq = l.a + round_up(M * I_s * 2, 256);
+  l.sx = l.xq + round_up(M * h, 256);
+  l.aq = l.sx + round_up(M * 4, 256);
+  l.sa = l.aq + round_up(M * I_s, 256);
+  l.total = l.sa + round_up(M * 4, 256);
+  return l;
+}
+
+tp_status check_w8a8(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k) {
+  tp_status st = check_shapes(M, h, I_full, t, k, TP_BF16, TP_FP8_E4M3FN);
+  if (st != TP_OK) return st;
+  if (h % 128 != 0 || (I_full / t) % 128 != 0)
+    return fail(TP_ERR_UNSUPPORTED, "the fp8 x fp8 forward needs h %% 128 == 0 and I_s %% 128 == 0");
+  return TP_OK;
+}
+
+}  // namespace
+
+TP_API size_t tp_mlp_w8a8_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t) {
+  if (check_w8a8(M, h, I_full, t, 0) != TP_OK) return 0;
+  return (size_t)w8a8_layout(M, h, I_full / t).total;
+}
+
+TP_API tp_status tp_mlp_shard_forward_w8a8(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                           const void* x, int64_t ldx, const void* w_gate, const void* w_up,
+                                           int64_t ldw_gu, const void* w_down, int64_t ldw_down,
+                                           const float* s_gate, const float* s_up, const float* s_down,
+                                           float* partial, int64_t ldp, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  tp_status st = check_w8a8(M, h, I_full, t, k);
+  if (st != TP_OK) return st;
+  const int64_t I_s = I_full / t;
+  if (!x || !w_gate || !w_up || !w_down || !partial) return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  if (!s_gate || !s_up || !s_down) return fail(TP_ERR_INVALID_ARG, "e4m3fn weights need s_gate, s_up and s_down");
+  if (ldx < h || ldw_gu < h || ldw_down < I_s || ldp < h)
+    return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length");
+  const W8A8Layout l = w8a8_layout(M, h, I_s);
+  if (!workspace || (int64_t)workspace_bytes < l.total)
+    return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)l.total,
+                (unsigned long long)workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(partial, 16))
+    return fail(TP_ERR_UNSUPPORTED, "tensor pointers must be 16-byte aligned");
+  if ((ldx * 2) % 16 || ldw_gu % 16 || ldw_down % 16 || (ldp * 4) % 16)
+    return fail(TP_ERR_UNSUPPORTED, "rows must start 16-byte aligned (leading dimensions)");
+  if (!aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4))
+    return fail(TP_ERR_UNSUPPORTED, "scale pointers must be 4-byte aligned");
+  const Extent ep = extent(partial, M, h, ldp, 4);
+  const Extent ew{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)l.total};
+  const Extent ins[5] = {extent(w_gate, I_s, h, ldw_gu, 1), extent(w_up, I_s, h, ldw_gu, 1),
+                         extent(w_down, h, I_s, ldw_down, 1), extent(x, M, h, ldx, 2), ew};
+  for (const Extent& e : ins)
+    if (overlap(ep, e)) return fail(TP_ERR_INVALID_ARG, "partial overlaps an input or the workspace");
+  for (int i = 0; i < 4; ++i)
+    if (overlap(ew, ins[i])) return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input");
+
+  uint8_t* wsb = static_cast<uint8_t*>(workspace);
+  tpmlp::ShardArgs a;
+  a.M = (int)M;
+  a.h = (int)h;
+  a.I_s = (int)I_s;
+  a.x = tpmlp::XRows{};
+  a.x.p[0] = x;
+  a.x.nb = 1;
+  a.x.rows = (int)M;
+  a.x.ld = ldx;
+  a.wg = w_gate;
+  a.wu = w_up;
+  a.ldw_gu = ldw_gu;
+  a.wd = w_down;
+  a.ldw_down = ldw_down;
+  a.sg = s_gate;
+  a.su = s_up;
+  a.sd = s_down;
+  a.p = partial;
+  a.ldp = ldp;
+  a.a = wsb + l.a;
+  a.lda = I_s;
+  a.wb = tpmlp::kWeightE4M3;
+  tpmlp::W8A8Bufs b;
+  b.xq = wsb + l.xq;
+  b.sx = reinterpret_cast<float*>(wsb + l.sx);
+  b.aq = wsb + l.aq;
+  b.sa = reinterpret_cast<float*>(wsb + l.sa);
+  return from_hip(tpmlp::launch_forward_w8a8(a, b, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
+}
+
+TP_API tp_status tp_quantize_rows_e4m3(int64_t rows, int64_t cols, const void* x, int64_t ldx, void* codes,
+                                       int64_t ldq, float* scales, void* stream) {
+  if (rows < 0 || cols < 1) return fail(TP_ERR_INVALID_ARG, "rows must be >= 0 and cols >= 1");
+  if (rows == 0) return TP_OK;
+  if (rows > kMaxDim || cols > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "dimension above 2^30");
+  if (!x || !codes || !scales) return fail(TP_ERR_INVALID_ARG, "null pointer");
+  if (ldx < cols || ldq < cols) return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length");
+  if (cols % 8 != 0) return fail(TP_ERR_UNSUPPORTED, "cols must be a multiple of 8");
+  if (!aligned(x, 16) || (ldx * 2) % 16 || !aligned(codes, 8) || ldq % 8 || !aligned(scales, 4))
+    return fail(TP_ERR_UNSUPPORTED, "x rows must be 16-byte aligned, code rows 8-byte aligned");
+  const Extent ex = extent(x, rows, cols, ldx, 2), eq = extent(codes, rows, cols, ldq, 1),
+               es = extent(scales, 1, rows, rows, 4);
+  if (overlap(ex, eq) || overlap(ex, es) || overlap(eq, es))
+    return fail(TP_ERR_INVALID_ARG, "buffers overlap");
+  return from_hip(tpmlp::launch_quant_rows((int)rows, (int)cols, x, ldx, codes, ldq, scales,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  "kernel launch");
 }
 
 // ------------------------------------------------------------ attention

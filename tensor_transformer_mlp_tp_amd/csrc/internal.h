@@ -22,7 +22,10 @@ enum KernelKind : int {
   K_QKV_F32 = 11,
   K_OPROJ_F32 = 12,
   K_SPLITK_FINISH = 13,
-  K_NUM_KINDS = 14
+  K_QUANT_ROWS = 14,
+  K_GATEUP_W8A8 = 15,
+  K_DOWN_W8A8 = 16,
+  K_NUM_KINDS = 17
 };
 
 constexpr int kMaxPartials = 64;
@@ -113,6 +116,15 @@ inline RowGemm down_of(const ShardArgs& s) {
   return g;
 }
 
+// Scratch of the fp8 x fp8 forward beyond A (a.a): the activations' e4m3fn
+// codes and per-token scales, and the same for A.
+struct W8A8Bufs {
+  void* xq;                 // M x h codes
+  float* sx;                // M
+  void* aq;                 // M x I_s codes
+  float* sa;                // M
+};
+
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
@@ -121,5 +133,10 @@ hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
 hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
+// rows x K bf16 -> e4m3fn codes (ldq bytes per row) and one fp32 scale per row.
+hipError_t launch_quant_rows(int M, int K, const void* x, int64_t ldx, void* q, int64_t ldq, float* scales,
+                             hipStream_t stream);
+// The fp8 x fp8 forward (contiguous X, e4m3fn weights with row scales).
+hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_t stream);
 
 }  // namespace tpmlp

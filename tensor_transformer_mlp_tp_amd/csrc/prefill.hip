@@ -49,6 +49,8 @@
 // folded so that every XCD receives a contiguous run of tiles, and the run is
 // walked in groups of four M-tiles, which keeps the activation and weight
 // panels of concurrently running workgroups inside one L2.
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -67,6 +69,18 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // (l / 32); it receives D[8*(i/4) + 4*(l/32) + i%4][l % 32], i = 0..15.
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+// 32x32x64 e4m3 x e4m3 MFMA (unit block scales): D(32x32) += A(32x64) *
+// B(64x32).  Lane l supplies 32 k values of row (l % 32) of A and of column
+// (l % 32) of B; A and B must use the same lane/byte -> k assignment (any
+// assignment gives the same sums).  D's layout is that of mfma32.  The
+// hardware's sums are not exact fp32 (a probe with random codes agreed with
+// the fp64 dot products to about 2^-13 of the sum of the magnitudes).
+__device__ __forceinline__ f32x16 mfma32x64_f8(v8i a, v8i b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
 __device__ __forceinline__ void load_lds16(const void* gsrc, void* lds_dst) {
@@ -135,20 +149,25 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   return TileCoord{first_m + i % gsize, i / gsize};
 }
 
-template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF>
+// A8: the activations are e4m3fn codes too (W8A8): one byte per element in
+// LDS, 32x32x64 fp8 MFMAs (twice the bf16 rate), and the per-token scales sx
+// applied in the epilogue with the weight row scales.
+template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF, bool A8>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
-    const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
-    int64_t ld_out, int tiles_m, int tiles_n) {
-  static_assert(BK == 32 || BK == 64, "stage depth");
+    const float* __restrict__ s0, const float* __restrict__ s1, const float* __restrict__ sx,
+    void* __restrict__ out, int64_t ld_out, int tiles_m, int tiles_n) {
+  static_assert(A8 ? (BK == 128 && WB == kWeightE4M3) : (BK == 32 || BK == 64), "stage depth");
   static_assert(WV == 4 || WV == 8, "waves per workgroup");
+  using XT = typename std::conditional<A8, uint8_t, uint16_t>::type;
   constexpr int WN = WV / 2;                   // waves across the weight rows (2 across tokens)
   constexpr int CB = BN / WN / 32;             // 32-row weight blocks per wave
   constexpr int TB = BM / 2 / 32;              // 32-token blocks per wave
   constexpr int EB = WB ? 1 : 2;              // weight bytes per element
-  constexpr int KSUB = BK / 16;                // MFMA sub-steps per stage
-  constexpr int XROWB = BK * 2;                // bytes per LDS activation row
+  constexpr int XE = A8 ? 1 : 2;               // activation bytes per element
+  constexpr int KSUB = BK / (A8 ? 64 : 16);    // MFMA sub-steps per stage
+  constexpr int XROWB = BK * XE;               // bytes per LDS activation row
   constexpr int WROWB = BK * EB;               // bytes per LDS weight row
   constexpr int XBYTES = BM * XROWB;
   constexpr int WBYTES = BN * WROWB;
@@ -182,7 +201,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     const int row = (wave * XINST + i) * XRPI + lane / XCH;
     const int c = (lane % XCH) ^ swz<XROWB>(row);
     const int tok = min(m0 + row, M - 1);
-    xsrc[i] = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, tok)) + c * 16;
+    xsrc[i] = reinterpret_cast<const uint8_t*>(x_row<XT>(xr, tok)) + c * 16;
   }
   const uint8_t* wsrc[WINST];
 #pragma unroll
@@ -207,7 +226,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // flight one k-tile before its own loads, which find the lines in L2.
   // (with 8 waves the upper 256 threads touch the same lines again)
   const int trow = tid & 255;
-  const uint8_t* tx = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, min(m0 + trow, M - 1)));
+  const uint8_t* tx = reinterpret_cast<const uint8_t*>(x_row<XT>(xr, min(m0 + trow, M - 1)));
   const uint8_t* tw;
   if constexpr (SWIGLU)
     tw = (trow < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (trow & (BN / 2 - 1)), N - 1) * ldw * EB;
@@ -215,7 +234,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     tw = w0 + (int64_t)min(n0 + trow, N - 1) * ldw * EB;
   uint8_t* tdst = lds + NS * SBYTES + wave * 512;
   auto touch_stage = [&](int kt) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tx + (int64_t)kt * BK * 2),
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tx + (int64_t)kt * BK * XE),
                                      (__attribute__((address_space(3))) void*)tdst, 4, 0, 0);
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tw + (int64_t)kt * BK * EB),
                                      (__attribute__((address_space(3))) void*)(tdst + 256), 4, 0, 0);
@@ -224,7 +243,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     uint8_t* xdst = lds + buf * SBYTES + wave * XINST * 1024;
     uint8_t* wdst = lds + buf * SBYTES + XBYTES + wave * WINST * 1024;
 #pragma unroll
-    for (int i = 0; i < XINST; ++i) load_lds16(xsrc[i] + (int64_t)kt * BK * 2, xdst + i * 1024);
+    for (int i = 0; i < XINST; ++i) load_lds16(xsrc[i] + (int64_t)kt * BK * XE, xdst + i * 1024);
 #pragma unroll
     for (int i = 0; i < WINST; ++i) load_lds16(wsrc[i] + (int64_t)kt * BK * EB, wdst + i * 1024);
   };
@@ -311,6 +330,45 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
       touch_stage(min(kt + NS, KT - 1));
       const uint8_t* sx = lds + buf * SBYTES;
       const uint8_t* sw = sx + XBYTES;
+      if constexpr (A8) {
+        // 64 k per MFMA: lane group g takes bytes [32g, 32g+32) of the
+        // sub-step's 64 k of its weight row and of its token row (the same k
+        // order on both sides is all the dot product needs)
+        v8i wf[2][CB], xf[2][TB];
+        auto read8 = [&](const uint8_t* base, int rowb_sel, int r, int kk) {
+          const int c0 = 4 * kk + 2 * g;
+          u32x4 lo, hi;
+          if (rowb_sel == 0) {
+            lo = lds_read16(base + r * XROWB + ((c0 ^ swz<XROWB>(r)) * 16));
+            hi = lds_read16(base + r * XROWB + (((c0 + 1) ^ swz<XROWB>(r)) * 16));
+          } else {
+            lo = lds_read16(base + r * WROWB + ((c0 ^ swz<WROWB>(r)) * 16));
+            hi = lds_read16(base + r * WROWB + (((c0 + 1) ^ swz<WROWB>(r)) * 16));
+          }
+          return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        };
+        auto frags8 = [&](int kk, v8i (&w_)[CB], v8i (&x_)[TB]) {
+          w_[0] = read8(sw, 1, wrow[0], kk);
+  #pragma unroll
+          for (int tb = 0; tb < TB; ++tb) x_[tb] = read8(sx, 0, xrow[tb], kk);
+  #pragma unroll
+          for (int cb = 1; cb < CB; ++cb) w_[cb] = read8(sw, 1, wrow[cb], kk);
+        };
+        frags8(0, wf[0], xf[0]);
+  #pragma unroll
+        for (int kk = 0; kk < KSUB; ++kk) {
+          if (kk + 1 < KSUB) frags8(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+  #pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32x64_f8(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+        }
+        constexpr int NMF = CB * TB, NRD = 2 * (CB + TB);
+        __builtin_amdgcn_sched_group_barrier(0x020, LPS + 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+        sched_substep<NRD, NMF>();
+        __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      } else {
       bf16x8 wf[2][CB], xf[2][TB];
       read_frags(sx, sw, 0, wf[0], xf[0]);
   #pragma unroll
@@ -333,6 +391,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         sched_substep<NRX, NMF>();
       }
       __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      }
       buf = buf == NS - 1 ? 0 : buf + 1;
     }
 }
@@ -360,6 +419,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         for (int tb = 0; tb < TB; ++tb) {
           const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
           if (tok >= M) continue;
+          const float st = A8 ? sx[tok] : 1.f;
           float a[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -367,6 +427,10 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
             if constexpr (WB) {
               gv *= sgv[i];
               uv *= suv[i];
+            }
+            if constexpr (A8) {
+              gv *= st;
+              uv *= st;
             }
             a[i] = silu(gv) * uv;
           }
@@ -394,6 +458,11 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
           f32x4 v;
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
+          if constexpr (A8) {
+            const float st = sx[tok];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= st;
+          }
           store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
         }
       }
@@ -425,10 +494,10 @@ template <int WB>
 hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
   const int tiles_m = (a.M + BM - 1) / BM;
   const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
-  return launch(K_GATEUP_PREFILL, gemm_kernel<true, WB, kBK, kNS<WB>, kWV, false>,
+  return launch(K_GATEUP_PREFILL, gemm_kernel<true, WB, kBK, kNS<WB>, kWV, false, false>,
                 dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, a.x,
-                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, a.a, a.lda, tiles_m,
-                tiles_n);
+                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (const float*)nullptr, a.a,
+                a.lda, tiles_m, tiles_n);
 }
 
 template <int WB, bool OBF>
@@ -440,10 +509,10 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   ar.nb = 1;
   ar.rows = g.M;
   ar.ld = g.lda;
-  return launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF>,
+  return launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF, false>,
                 dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
-                (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr, g.out, g.ldo,
-                tiles_m, tiles_n);
+                (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr,
+                (const float*)nullptr, g.out, g.ldo, tiles_m, tiles_n);
 }
 
 }  // namespace
@@ -457,6 +526,34 @@ hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
     default:
       return g.out_bf16 ? run_rowgemm<kWeightWide, true>(g, stream) : run_rowgemm<kWeightWide, false>(g, stream);
   }
+}
+
+hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_t stream) {
+  constexpr int WB = kWeightE4M3;
+  const int tiles_m = (a.M + BM - 1) / BM;
+  hipError_t e = launch_quant_rows(a.M, a.h, a.x.p[0], a.x.ld, b.xq, a.h, b.sx, stream);
+  if (e != hipSuccess) return e;
+  XRows xr{};
+  xr.p[0] = b.xq;
+  xr.nb = 1;
+  xr.rows = a.M;
+  xr.ld = a.h;
+  const int tn_gu = (a.I_s + BN / 2 - 1) / (BN / 2);
+  e = launch(K_GATEUP_W8A8, gemm_kernel<true, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_gu)),
+             dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, xr, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu,
+             a.sg, a.su, (const float*)b.sx, a.a, a.lda, tiles_m, tn_gu);
+  if (e != hipSuccess) return e;
+  e = launch_quant_rows(a.M, a.I_s, a.a, a.lda, b.aq, a.I_s, b.sa, stream);
+  if (e != hipSuccess) return e;
+  XRows ar{};
+  ar.p[0] = b.aq;
+  ar.nb = 1;
+  ar.rows = a.M;
+  ar.ld = a.I_s;
+  const int tn_dn = (a.h + BN - 1) / BN;
+  return launch(K_DOWN_W8A8, gemm_kernel<false, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_dn)),
+                dim3(kWV * 64), 0, stream, a.M, a.h, a.I_s, ar, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
+                a.ldw_down, a.sd, (const float*)nullptr, (const float*)b.sa, (void*)a.p, a.ldp, tiles_m, tn_dn);
 }
 
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
