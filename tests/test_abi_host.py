@@ -300,3 +300,58 @@ def oproj_call(M=1, h=128, nh=8, d=32, t=2, k=0, act=BF16, w=BF16, a=P, lda=None
 ])
 def test_attn_out_rejects(kw, status):
     assert oproj_call(**kw) == status
+
+
+# ------------------------------------------------------------- W8A8
+
+def w8a8_call(M=256, h=128, I=256, t=2, k=0, x=P, wg=P * 2, wu=P * 3, wd=P * 4, sg=P * 5, su=P * 5 + 1024,
+              sd=P * 5 + 2048, p=P * 8, ws=P * 16, wsb=1 << 22, ldx=None):
+    lib = _lib.load()
+    I_s = I // t if t else 1
+    return lib.tp_mlp_shard_forward_w8a8(M, h, I, t, k, x, ldx if ldx is not None else h, wg, wu, h, wd, I_s,
+                                         sg, su, sd, p, h, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=192), _lib.TP_ERR_UNSUPPORTED),            # h % 128
+    (dict(I=2 * 192), _lib.TP_ERR_UNSUPPORTED),        # I_s % 128
+    (dict(I=255), _lib.TP_ERR_INVALID_ARG),
+    (dict(k=2), _lib.TP_ERR_INVALID_ARG),
+    (dict(sg=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(x=None), _lib.TP_ERR_INVALID_ARG),
+    (dict(wsb=100), _lib.TP_ERR_WORKSPACE),
+    (dict(ws=P * 16 + 16), _lib.TP_ERR_UNSUPPORTED),
+    (dict(x=P + 2), _lib.TP_ERR_UNSUPPORTED),
+    (dict(ldx=64), _lib.TP_ERR_INVALID_ARG),
+    (dict(p=P * 2), _lib.TP_ERR_INVALID_ARG),          # partial overlaps a weight
+    (dict(ws=P), _lib.TP_ERR_INVALID_ARG),             # workspace overlaps x
+])
+def test_w8a8_rejects(kw, status):
+    assert status != _lib.TP_OK
+    assert w8a8_call(**kw) == status
+
+
+def test_w8a8_workspace_bytes():
+    lib = _lib.load()
+    # A bf16 + X codes + scales + A codes + scales, each rounded to 256 bytes
+    M, h, I_s = 4096, 8192, 7168
+    want = M * I_s * 2 + M * h + M * 4 + M * I_s + M * 4
+    assert lib.tp_mlp_w8a8_workspace_bytes(M, h, I_s * 4, 4) == want
+    assert lib.tp_mlp_w8a8_workspace_bytes(M, 192, 1024, 4) == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    ((4, 12, P, 12, P * 2, 16, P * 3), _lib.TP_ERR_UNSUPPORTED),    # cols % 8
+    ((4, 16, P, 8, P * 2, 16, P * 3), _lib.TP_ERR_INVALID_ARG),     # ldx < cols
+    ((4, 16, None, 16, P * 2, 16, P * 3), _lib.TP_ERR_INVALID_ARG),
+    ((4, 16, P + 2, 16, P * 2, 16, P * 3), _lib.TP_ERR_UNSUPPORTED),
+    ((4, 16, P, 16, P + 8, 16, P * 3), _lib.TP_ERR_INVALID_ARG),    # codes overlap x
+    ((-1, 16, P, 16, P * 2, 16, P * 3), _lib.TP_ERR_INVALID_ARG),
+])
+def test_quantize_rows_rejects(args, status):
+    lib = _lib.load()
+    assert lib.tp_quantize_rows_e4m3(*args, None) == status
+
+
+def test_quantize_rows_empty_is_noop():
+    assert _lib.load().tp_quantize_rows_e4m3(0, 16, None, 16, None, 16, None, None) == _lib.TP_OK
