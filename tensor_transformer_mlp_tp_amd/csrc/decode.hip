@@ -775,6 +775,14 @@ hipError_t rowgemm_v1(const RowGemm& g, hipStream_t stream) {
 #ifndef TPMLP_DECODE_XD
 #define TPMLP_DECODE_XD 1
 #endif
+// One-byte weights put 256 k in a slot, so up to 16 tokens their activation
+// fragments per weight byte are twice bf16's; two row blocks per wave share
+// them in gate/up (measured: fp8 M = 8 32.0 -> 26.0 us, int8 59.9 -> 55.4 us
+// at the 70B TP = 4 / TP = 2 shards; the down projection, with a quarter of
+// the rows, kept one).
+#ifndef TPMLP_DECODE_RB_NT1_BYTE
+#define TPMLP_DECODE_RB_NT1_BYTE 2
+#endif
 
 // Up to 16 tokens: one 16-row block per wave, activations from registers
 // (most workgroups).  More tokens: RB row blocks per wave share each
@@ -786,7 +794,8 @@ constexpr bool kStreamXD = TPMLP_DECODE_XD && NT >= 2 && (!WB || NT == 2);
 template <int NT, int WB>
 hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
-  constexpr int RB = NT == 1 ? 1 : (XD && WB ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
+  constexpr int RB = NT == 1 ? (WB ? TPMLP_DECODE_RB_NT1_BYTE : 1)
+                             : (XD && WB ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
   return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
                 dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, a.x,
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
