@@ -474,7 +474,8 @@ bool attn_local_heads(int64_t n_heads, int64_t n_kv_heads, int32_t t, int64_t* q
 // (out_f32 forces fp32).
 // Split-K scratch the projection needs (bytes, before rounding).
 int64_t linear_workspace_need(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype) {
-  if (act_dtype != TP_BF16 || M > tpmlp::kDecodeMaxM) return 0;
+  if (act_dtype != TP_BF16) return 0;
+  if (M > tpmlp::kDecodeMaxM) return tpmlp::rowgemm_prefill_workspace_bytes((int)M, (int)N, (int)K);
   return tpmlp::rowgemm_decode_workspace_bytes((int)M, (int)N, (int)K, weight_format(w_dtype));
 }
 

@@ -902,6 +902,20 @@ hipError_t rowgemm_wb(const RowGemm& g, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,
+                                int wb, bool obf, hipStream_t stream) {
+  const dim3 grid((unsigned)(((int64_t)M * N / 4 + 255) / 256));
+  if (wb)   // one-byte weights: the row scale is applied after the sum
+    return obf ? launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightE4M3, true>, grid, dim3(256), 0, stream, M, N,
+                        nseg, ws, s, out, ldo)
+               : launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightE4M3, false>, grid, dim3(256), 0, stream, M,
+                        N, nseg, ws, s, out, ldo);
+  return obf ? launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightWide, true>, grid, dim3(256), 0, stream, M, N,
+                      nseg, ws, s, out, ldo)
+             : launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightWide, false>, grid, dim3(256), 0, stream, M, N,
+                      nseg, ws, s, out, ldo);
+}
+
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {
   if (M < 1 || M > kDecodeMaxM) return 0;
   switch (wb) {

@@ -131,6 +131,12 @@ hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
 // Split-K scratch bytes launch_rowgemm_decode uses for this shape (0: none).
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb);
+// Split-K scratch bytes launch_rowgemm_prefill uses for this shape (0: none).
+int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K);
+// out = ordered sum of the nseg split sums in ws (nseg x M x N fp32), times
+// the row scales for one-byte weights (wb != 0), fp32 or bf16 (obf).
+hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,
+                                int wb, bool obf, hipStream_t stream);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
 hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
 // rows x K bf16 -> e4m3fn codes (ldq bytes per row) and one fp32 scale per row.

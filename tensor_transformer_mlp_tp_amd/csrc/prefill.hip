@@ -157,7 +157,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
     const float* __restrict__ s0, const float* __restrict__ s1, const float* __restrict__ sx,
-    void* __restrict__ out, int64_t ld_out, int tiles_m, int tiles_n) {
+    void* __restrict__ out, int64_t ld_out, int tiles_m, int tiles_n, int nseg, float* __restrict__ seg_out) {
   static_assert(A8 ? (BK == 128 && WB == kWeightE4M3) : (BK == 32 || BK == 64), "stage depth");
   static_assert(WV == 4 || WV == 8, "waves per workgroup");
   using XT = typename std::conditional<A8, uint8_t, uint16_t>::type;
@@ -312,22 +312,27 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // so the body stays one basic block with a fixed load count; the
   // scheduling groups thread the fragment reads of sub-step 1 between the
   // MFMAs of sub-step 0.
+  // K range of this workgroup: all of K, or with nseg > 1 (narrow outputs,
+  // too few tiles for the chip) the blockIdx.y-th of nseg contiguous ranges,
+  // whose raw sums go to seg_out for a finishing kernel.
   const int KT = K / BK;
+  const int seg = blockIdx.y;
+  const int kt0 = (int)((int64_t)seg * KT / nseg), kt1 = (int)((int64_t)(seg + 1) * KT / nseg);
   {
   #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
-      issue_stage(min(s, KT - 1), s);
-      touch_stage(min(s + 1, KT - 1));
+      issue_stage(min(kt0 + s, kt1 - 1), s);
+      touch_stage(min(kt0 + s + 1, kt1 - 1));
     }
     int buf = 0;
-    for (int kt = 0; kt < KT; ++kt) {
+    for (int kt = kt0; kt < kt1; ++kt) {
       // this wave's loads of stage kt have landed (younger: the touch issued
       // with them and NS-2 later iterations' loads + touches)
       wait_vmcnt<2 + (NS - 2) * (LPS + 2)>();
       lds_barrier();                  // ... and every wave's; stage kt-1 is no longer read
       const int nbuf = buf == 0 ? NS - 1 : buf - 1;   // (kt + NS - 1) % NS
-      issue_stage(min(kt + NS - 1, KT - 1), nbuf);
-      touch_stage(min(kt + NS, KT - 1));
+      issue_stage(min(kt + NS - 1, kt1 - 1), nbuf);
+      touch_stage(min(kt + NS, kt1 - 1));
       const uint8_t* sx = lds + buf * SBYTES;
       const uint8_t* sw = sx + XBYTES;
       if constexpr (A8) {
@@ -456,6 +461,12 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
           const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
           if (tok >= M) continue;
           f32x4 v;
+          if (nseg > 1) {   // raw sums of this K range
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i];
+            store_out4<false>(seg_out, ((int64_t)seg * M + tok) * N + f, v);
+            continue;
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
           if constexpr (A8) {
@@ -497,7 +508,20 @@ hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
   return launch(K_GATEUP_PREFILL, gemm_kernel<true, WB, kBK, kNS<WB>, kWV, false, false>,
                 dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, a.x,
                 (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (const float*)nullptr, a.a,
-                a.lda, tiles_m, tiles_n);
+                a.lda, tiles_m, tiles_n, 1, (float*)nullptr);
+}
+
+// K ranges of a prefill row GEMM: an output with fewer tiles than CUs (a
+// rank's QKV projection: 80 tiles at 4096 tokens) splits K until the chip is
+// covered, keeping at least 16 k-tiles per range.
+#ifndef TPMLP_PREFILL_SPLIT_TILES
+#define TPMLP_PREFILL_SPLIT_TILES 256
+#endif
+int prefill_splits(int M, int N, int K) {
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  if (tiles >= TPMLP_PREFILL_SPLIT_TILES) return 1;
+  const int want = (TPMLP_PREFILL_SPLIT_TILES + tiles - 1) / tiles;
+  return max(1, min(want, K / kBK / 16));
 }
 
 template <int WB, bool OBF>
@@ -509,13 +533,21 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   ar.nb = 1;
   ar.rows = g.M;
   ar.ld = g.lda;
-  return launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF, false>,
-                dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
-                (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr,
-                (const float*)nullptr, g.out, g.ldo, tiles_m, tiles_n);
+  const int nseg = g.ws ? prefill_splits(g.M, g.N, g.K) : 1;
+  hipError_t e = launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF, false>,
+                        dim3((unsigned)(tiles_m * tiles_n), nseg), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
+                        (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr,
+                        (const float*)nullptr, g.out, g.ldo, tiles_m, tiles_n, nseg, g.ws);
+  if (e != hipSuccess || nseg == 1) return e;
+  return launch_splitk_finish(g.M, g.N, nseg, g.ws, g.s, g.out, g.ldo, g.wb, OBF, stream);
 }
 
 }  // namespace
+
+int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K) {
+  const int nseg = prefill_splits(M, N, K);
+  return nseg > 1 ? (int64_t)nseg * M * N * 4 : 0;
+}
 
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
   switch (g.wb) {
@@ -541,7 +573,7 @@ hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_
   const int tn_gu = (a.I_s + BN / 2 - 1) / (BN / 2);
   e = launch(K_GATEUP_W8A8, gemm_kernel<true, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_gu)),
              dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, xr, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu,
-             a.sg, a.su, (const float*)b.sx, a.a, a.lda, tiles_m, tn_gu);
+             a.sg, a.su, (const float*)b.sx, a.a, a.lda, tiles_m, tn_gu, 1, (float*)nullptr);
   if (e != hipSuccess) return e;
   e = launch_quant_rows(a.M, a.I_s, a.a, a.lda, b.aq, a.I_s, b.sa, stream);
   if (e != hipSuccess) return e;
@@ -553,7 +585,8 @@ hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_
   const int tn_dn = (a.h + BN - 1) / BN;
   return launch(K_DOWN_W8A8, gemm_kernel<false, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_dn)),
                 dim3(kWV * 64), 0, stream, a.M, a.h, a.I_s, ar, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
-                a.ldw_down, a.sd, (const float*)nullptr, (const float*)b.sa, (void*)a.p, a.ldp, tiles_m, tn_dn);
+                a.ldw_down, a.sd, (const float*)nullptr, (const float*)b.sa, (void*)a.p, a.ldp, tiles_m, tn_dn, 1,
+                (float*)nullptr);
 }
 
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {

@@ -232,7 +232,8 @@ def test_attn_qkv_workspace_bytes():
     for M in (1, 8, 32, 64):
         b = lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16)
         assert b > 0 and b % 256 == 0 and b % (M * 1280 * 4) == 0
-    assert lib.tp_attn_qkv_workspace_bytes(4096, 8192, 64, 8, 128, 8, BF16, BF16) == 0   # prefill tiles
+    # prefill: 80 tiles of 256 x 256 for 4096 tokens, K split in 4 ranges
+    assert lib.tp_attn_qkv_workspace_bytes(4096, 8192, 64, 8, 128, 8, BF16, BF16) == 4 * 4096 * 1280 * 4
     assert lib.tp_attn_qkv_workspace_bytes(16, 256, 8, 2, 32, 4, F32, F32) == 0          # fp32 path
     assert lib.tp_attn_qkv_workspace_bytes(1, 8192, 64, 8, 128, 3, BF16, BF16) == 0      # invalid split
     assert lib.tp_attn_qkv_workspace_bytes(0, 8192, 64, 8, 128, 8, BF16, BF16) == 0

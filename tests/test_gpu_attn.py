@@ -80,7 +80,9 @@ QKV_CASES = [
     (17, 512, 8, 8, 64, 4, "bf16"),
     (33, 320, 8, 2, 64, 4, "bf16"),       # h % 128 != 0: register-batch kernels; KV replicated
     (64, 1024, 16, 4, 32, 2, "bf16"),
-    (300, 512, 8, 2, 64, 2, "bf16"),      # prefill, ragged M and N tiles
+    (300, 512, 8, 2, 64, 2, "bf16"),      # prefill, ragged M and N tiles (K too short to split)
+    (1000, 4096, 8, 2, 64, 2, "bf16"),    # prefill, 8 tiles: K split in 4 ranges
+    (130, 2048, 16, 4, 64, 4, "e4m3fn"),  # prefill with fp8 weights, K split in 2: the row scale after the sum
     (520, 384, 12, 4, 64, 4, "bf16"),
     (3, 1024, 8, 2, 64, 2, "e4m3fn"),
     (40, 320, 8, 2, 64, 2, "e4m3fn"),     # fp8 register-batch path
