@@ -848,7 +848,7 @@ def bench_copy(tp, args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the TP exchange "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the TP exchange "
               "across GPUs is design-only); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch

@@ -12,7 +12,7 @@ arithmetic.
 Everything is computed in float64 with numpy from the exact bytes the GPU
 receives (bf16 bit patterns, fp32 values, OCP e4m3fn codes plus fp32 scales).
 
-Sources (the web pages this build follows):
+Sources (the web pages the oracle follows):
 
 * "Build a model sharding system for serving 70B+ parameter models"
   (scalablesystem.dev), section "The Tensor-Parallel Shard Group": the
