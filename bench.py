@@ -161,7 +161,9 @@ class Phase:
 
         self.calls = {}
 
-    def run(self, wset):
+    def run(self, wset, time_fwd=None):
+        """time_fwd: (library, kind mask) to event-time this call's forward
+        launches of those kinds only."""
         # arguments are marshalled once per weight set; the loop only re-issues the C calls
         key = id(wset)
         if key not in self.calls:
@@ -173,7 +175,12 @@ class Phase:
                                                  out=self.partial.view(-1)) if self.with_reduce else None
             self.calls[key] = (fwd, red)
         fwd, red = self.calls[key]
-        fwd()
+        if time_fwd is not None:
+            time_fwd[0].tp_profile_enable(time_fwd[1])
+            fwd()
+            time_fwd[0].tp_profile_enable(0)
+        else:
+            fwd()
         if red is not None:
             red()
 
@@ -278,15 +285,26 @@ def bench_decode70b(tp, args):
     log("generating %d weight sets of the 70B TP=8 shard" % args.weight_sets)
     sets, host0 = device_weights(2, h, I_s, "bf16", c["std_gu"], c["std_down"], args.weight_sets)
     phases = [Phase(tp, 2, M, h, I_s, t, "bf16", "bf16", True) for M in c["M"]]
+    # An event-timed launch costs the host ~25 us against ~3 us for a plain
+    # one; timing the gate/up launch of all three phases made the step
+    # host-bound (144 us against 130 us untimed).  Step i times the gate/up
+    # launch of phase i % 3 only, so each M is sampled on a third of the steps.
+    lib = tp.load()
+    gmask = 1 << tp.kernel_kinds().index("gateup_decode")
 
     def step(i):
+        wset = sets[i % len(sets)]
+        for idx, ph in enumerate(phases):
+            ph.run(wset, (lib, gmask) if i % len(phases) == idx else None)
+
+    def step_plain(i):
         wset = sets[i % len(sets)]
         for ph in phases:
             ph.run(wset)
 
-    steps, warmup = args.steps or 400, args.warmup if args.warmup is not None else 40
-    elapsed, prof = timed(tp, step, steps, warmup, ["gateup_decode"])
-    prof_all = breakdown(tp, step, steps, warmup + steps)
+    steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
+    elapsed, prof = timed(tp, step, steps, warmup, [])
+    prof_all = breakdown(tp, step_plain, steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
     value = step_bytes * steps / elapsed / 1e9
     gu_bytes = steps * sum(workloads.gateup_bytes(ph.M, h, I_s) for ph in phases)
@@ -298,7 +316,11 @@ def bench_decode70b(tp, args):
         kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
                       "GBps": b / (ms * 1e-3) / 1e9 if ms > 0 else None}
     ms, cnt = prof["gateup_decode"]
-    achieved = gu_bytes / (ms * 1e-3) / 1e9
+    assert cnt == steps
+    timed_bytes = sum(workloads.gateup_bytes(ph.M, h, I_s) * sum(1 for i in range(warmup, warmup + steps)
+                                                                   if i % len(phases) == idx)
+                      for idx, ph in enumerate(phases))
+    achieved = timed_bytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
