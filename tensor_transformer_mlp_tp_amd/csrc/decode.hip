@@ -25,11 +25,17 @@
 // waves split I_s, same fixed-order LDS reduction, fp32 partial written once
 // (the row-parallel partial of "The Tensor-Parallel Shard Group").
 //
-// fp8 weights (OCP e4m3fn): each lane's 16-byte load carries 16 codes of one
-// row = two MFMA k-groups; they are widened to bf16 in registers (exact) and
-// the per-output-channel fp32 scale is applied to the fp32 sums.  The
-// activations are read with the same k order, so the dot products are exact
-// reorderings of the definition.
+// One-byte weights (OCP e4m3fn or int8 codes): each lane's 16-byte load
+// carries 16 codes of one row = two MFMA k-groups; they are widened to bf16 in
+// registers (exact) and the per-output-channel fp32 scale is applied to the
+// fp32 sums.  The activations are read with the same k order, so the dot
+// products are exact reorderings of the definition.
+//
+// The down kernels are generic row GEMMs, out = a * W^T with W in the
+// (out, in) layout (RowGemm): they also run the attention block's
+// projections, with fp32 or bf16 output, and for narrow outputs (too few row
+// blocks to cover the chip) split K over a second grid dimension, with an
+// ordered finishing sum.
 
 #include "common.h"
 #include "internal.h"
