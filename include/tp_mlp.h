@@ -72,7 +72,11 @@ typedef enum {
 /*
  * Workspace bytes tp_mlp_shard_forward needs for these arguments (0 if the
  * arguments are invalid).  The workspace holds the intermediate activation A
- * (M x I_s, in the activation dtype) plus alignment padding.
+ * (M x I_s, in the activation dtype) plus alignment padding, and for a bf16
+ * prefill (M > 64) whose output tiles do not fill whole rounds of the 256
+ * CUs the stream-K scratch of the two GEMMs: arrival counters and one fp32
+ * 256 x 256 tile per piece of the tiles cut along K (at most 256 pieces,
+ * 64 MiB).
  */
 size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                               int32_t act_dtype, int32_t w_dtype);
@@ -227,7 +231,8 @@ tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_t t, in
 
 /*
  * Workspace bytes of tp_mlp_shard_forward_w8a8 (0 if the arguments are
- * invalid): A in bf16, the codes of X and A, and their per-token scales.
+ * invalid): A in bf16, the codes of X and A, their per-token scales, and
+ * the GEMMs' stream-K scratch as for tp_mlp_shard_forward.
  */
 size_t tp_mlp_w8a8_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t);
 
@@ -320,14 +325,17 @@ int64_t tp_attn_qkv_width(int64_t n_heads, int64_t n_kv_heads, int64_t head_dim,
  *              tp_attn_qkv_workspace_bytes(...) bytes, 256-byte aligned, not
  *              overlapping any argument; may be NULL when that size is 0.
  *              It holds fp32 sums over ranges of h when the projection is
- *              split along h across workgroups (a narrow output: few rows of
- *              W to spread over the chip).  Contents on entry are ignored;
- *              concurrent calls must not share it.
+ *              split along h across workgroups: decode with a narrow output
+ *              (few rows of W to spread over the chip), prefill with output
+ *              tiles that do not fill whole rounds of the CUs (stream-K
+ *              pieces and their arrival counters).  Contents on entry are
+ *              ignored; concurrent calls must not share it.
  *
  * Requirements (else TP_ERR_UNSUPPORTED): with bf16 activations h % 64 == 0
  * and n_loc % 16 == 0, pointers and rows 16-byte aligned, scales 4-byte
  * aligned; with fp32, 4-byte alignment.  Deterministic: the split and the
- * order of the partial sums depend on the shape only.
+ * order of the partial sums depend on the shape only (not on which workgroup
+ * finishes first).
  */
 tp_status tp_attn_qkv_forward(int64_t M, int64_t h, int64_t n_heads, int64_t n_kv_heads,
                               int64_t head_dim, int32_t t, int32_t k,

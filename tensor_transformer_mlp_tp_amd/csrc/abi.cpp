@@ -109,8 +109,14 @@ tp_status check_shapes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
   return TP_OK;
 }
 
-int64_t workspace_need(int64_t M, int64_t I_s, int32_t act) {
-  return round_up(M * I_s * elem_bytes(act), 256);
+// The forward's workspace: A (M x I_s, the activation dtype), then for a
+// bf16 prefill the two GEMMs' stream-K scratch.
+int64_t workspace_a_bytes(int64_t M, int64_t I_s, int32_t act) { return round_up(M * I_s * elem_bytes(act), 256); }
+
+int64_t workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t act) {
+  const int64_t sk = act == TP_BF16 && M > tpmlp::kDecodeMaxM
+                         ? tpmlp::forward_prefill_sk_bytes((int)M, (int)h, (int)I_s, false) : 0;
+  return workspace_a_bytes(M, I_s, act) + round_up(sk, 256);
 }
 
 // ------------------------------------------------------------------ timing
@@ -128,7 +134,7 @@ const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
     "partial_reduce", "gateup_f32", "down_f32", "qkv_decode", "qkv_prefill",
     "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish", "quant_rows",
-    "gateup_w8a8", "down_w8a8"};
+    "gateup_w8a8", "down_w8a8", "sk_clear"};
 
 // Appends one start/stop event pair to the timing pool.
 bool prof_grow() {
@@ -162,7 +168,7 @@ void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop) {
 TP_API size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                                      int32_t act_dtype, int32_t w_dtype) {
   if (check_shapes(M, h, I_full, t, 0, act_dtype, w_dtype) != TP_OK) return 0;
-  return (size_t)workspace_need(M, I_full / t, act_dtype);
+  return (size_t)workspace_need(M, h, I_full / t, act_dtype);
 }
 
 namespace {
@@ -191,7 +197,7 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
     return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length "
                 "(ldx=%lld ldw_gu=%lld ldw_down=%lld ldp=%lld)", (long long)ldx, (long long)ldw_gu,
                 (long long)ldw_down, (long long)ldp);
-  const int64_t need = workspace_need(M, I_s, act_dtype);
+  const int64_t need = workspace_need(M, h, I_s, act_dtype);
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
                 (unsigned long long)workspace_bytes);
@@ -249,6 +255,8 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
   a.a = workspace;
   a.lda = I_s;
   a.wb = weight_format(w_dtype);
+  a.sk = need > workspace_a_bytes(M, I_s, act_dtype)
+             ? static_cast<uint8_t*>(workspace) + workspace_a_bytes(M, I_s, act_dtype) : nullptr;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (act_dtype == TP_F32)
@@ -337,7 +345,7 @@ TP_API tp_status tp_partial_reduce_scatter(int64_t rows, int64_t row_len, int32_
 namespace {
 
 struct W8A8Layout {
-  int64_t a, xq, sx, aq, sa, total;   // byte offsets in the workspace
+  int64_t a, xq, sx, aq, sa, sk, total;   // byte offsets in the workspace
 };
 
 W8A8Layout w8a8_layout(int64_t M, int64_t h, int64_t I_s) {
@@ -347,7 +355,8 @@ W8A8Layout w8a8_layout(int64_t M, int64_t h, int64_t I_s) {
   l.sx = l.xq + round_up(M * h, 256);
   l.aq = l.sx + round_up(M * 4, 256);
   l.sa = l.aq + round_up(M * I_s, 256);
-  l.total = l.sa + round_up(M * 4, 256);
+  l.sk = l.sa + round_up(M * 4, 256);
+  l.total = l.sk + round_up(tpmlp::forward_prefill_sk_bytes((int)M, (int)h, (int)I_s, true), 256);
   return l;
 }
 
@@ -422,6 +431,7 @@ TP_API tp_status tp_mlp_shard_forward_w8a8(int64_t M, int64_t h, int64_t I_full,
   a.a = wsb + l.a;
   a.lda = I_s;
   a.wb = tpmlp::kWeightE4M3;
+  a.sk = l.total > l.sk ? wsb + l.sk : nullptr;
   tpmlp::W8A8Bufs b;
   b.xq = wsb + l.xq;
   b.sx = reinterpret_cast<float*>(wsb + l.sx);
@@ -472,7 +482,8 @@ bool attn_local_heads(int64_t n_heads, int64_t n_kv_heads, int32_t t, int64_t* q
 // Checks and launch shared by the attention projections:
 // out (M x N) = a (M x K) * w^T, w N x K, out in the activation dtype
 // (out_f32 forces fp32).
-// Split-K scratch the projection needs (bytes, before rounding).
+// Scratch the projection needs (bytes, before rounding): split-K sums for
+// decode, stream-K counters and partial tiles for prefill.
 int64_t linear_workspace_need(int64_t M, int64_t N, int64_t K, int32_t act_dtype, int32_t w_dtype) {
   if (act_dtype != TP_BF16) return 0;
   if (M > tpmlp::kDecodeMaxM) return tpmlp::rowgemm_prefill_workspace_bytes((int)M, (int)N, (int)K);

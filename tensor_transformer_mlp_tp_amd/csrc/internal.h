@@ -25,7 +25,8 @@ enum KernelKind : int {
   K_QUANT_ROWS = 14,
   K_GATEUP_W8A8 = 15,
   K_DOWN_W8A8 = 16,
-  K_NUM_KINDS = 17
+  K_SK_CLEAR = 17,
+  K_NUM_KINDS = 18
 };
 
 constexpr int kMaxPartials = 64;
@@ -79,6 +80,7 @@ struct ShardArgs {
   void* a;                  // workspace: M x I_s intermediate
   int64_t lda;
   int wb;                   // weight format: kWeightWide / kWeightE4M3 / kWeightI8
+  void* sk;                 // prefill stream-K scratch (forward_prefill_sk_bytes), or null
 };
 
 // out (M x N) = A (M x K) * W^T with W (N x K, (out, in) layout), fp32
@@ -95,7 +97,7 @@ struct RowGemm {
   int64_t ldo;
   bool out_bf16;            // else fp32
   int wb;                   // weight format (kWeight*)
-  float* ws;                // split-K scratch (null: no split), 16-byte aligned
+  float* ws;                // decode: split-K sums; prefill: stream-K scratch (null: neither), 256-byte aligned
   int kind_decode, kind_prefill, kind_f32;  // timing kinds of the three paths
 };
 
@@ -131,8 +133,11 @@ hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);
 // Split-K scratch bytes launch_rowgemm_decode uses for this shape (0: none).
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb);
-// Split-K scratch bytes launch_rowgemm_prefill uses for this shape (0: none).
+// Stream-K scratch bytes launch_rowgemm_prefill uses for this shape (0: none).
 int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K);
+// Stream-K scratch of a prefill forward's two GEMMs (they run one after the
+// other and share it); a8: the fp8 x fp8 forward.
+int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8);
 // out = ordered sum of the nseg split sums in ws (nseg x M x N fp32), times
 // the row scales for one-byte weights (wb != 0), fp32 or bf16 (obf).
 hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,

@@ -49,6 +49,10 @@
 // folded so that every XCD receives a contiguous run of tiles, and the run is
 // walked in groups of four M-tiles, which keeps the activation and weight
 // panels of concurrently running workgroups inside one L2.
+//
+// When the tiles do not fill whole rounds of the 256 CUs, the tiles of the
+// last round are cut along K into pieces that together fill one round
+// (stream-K; SkTail below), their fp32 sums added in a fixed order.
 #include <type_traits>
 
 #include "common.h"
@@ -136,11 +140,16 @@ struct TileCoord {
   int tm, tn;
 };
 
-__device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles_n) {
-  const int nb = tiles_m * tiles_n;
-  const int xcd = b & 7, local = b >> 3;
-  const int q = nb >> 3, r = nb & 7;
-  const int L = xcd * q + min(xcd, r) + local;
+// Permutation of [0, n) for workgroup ids: id j runs on XCD j % 8, and the
+// ids of one XCD receive a contiguous run of indices.
+__device__ __forceinline__ int xcd_fold(int j, int n) {
+  const int xcd = j & 7, local = j >> 3;
+  const int q = n >> 3, r = n & 7;
+  return xcd * q + min(xcd, r) + local;
+}
+
+// Tile of linear index L, walked in groups of GROUP_M M-tiles.
+__device__ __forceinline__ TileCoord tile_coord(int L, int tiles_m, int tiles_n) {
   const int per_group = GROUP_M * tiles_n;
   const int group = L / per_group;
   const int first_m = group * GROUP_M;
@@ -148,6 +157,22 @@ __device__ __forceinline__ TileCoord tile_of_block(int b, int tiles_m, int tiles
   const int i = L - group * per_group;
   return TileCoord{first_m + i % gsize, i / gsize};
 }
+
+// Stream-K tail.  One workgroup fills a CU (LDS), so the tiles run in rounds
+// of one per CU, and a last round of rem tiles costs as much as a full one
+// while the other CUs idle.  Instead, the first nfull = tiles - rem tiles are
+// computed whole (workgroups 0 .. nfull-1) and each of the rem tail tiles is
+// cut along K into d pieces of KT / d k-tiles, one workgroup each.  A piece
+// stores its raw fp32 sums in its slot of `part`, then counts itself in its
+// tile's arrival counter; the piece that arrives last adds the tile's d
+// slots in k order (the same sum whichever piece arrives last) and writes the
+// tile through the ordinary epilogue.  No workgroup waits for another.
+struct SkTail {
+  float* part;   // rem * d slots of BM * BN floats, slot = tail tile * d + piece
+  int* cnt;      // one arrival counter per tail tile, zero at launch
+  int nfull;     // tiles computed whole
+  int d;         // pieces per tail tile; 0: no tail split
+};
 
 // A8: the activations are e4m3fn codes too (W8A8): one byte per element in
 // LDS, 32x32x64 fp8 MFMAs (twice the bf16 rate), and the per-token scales sx
@@ -157,7 +182,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
     const float* __restrict__ s0, const float* __restrict__ s1, const float* __restrict__ sx,
-    void* __restrict__ out, int64_t ld_out, int tiles_m, int tiles_n, int nseg, float* __restrict__ seg_out) {
+    void* __restrict__ out, int64_t ld_out, int tiles_m, int tiles_n, const SkTail sk) {
   static_assert(A8 ? (BK == 128 && WB == kWeightE4M3) : (BK == 32 || BK == 64), "stage depth");
   static_assert(WV == 4 || WV == 8, "waves per workgroup");
   using XT = typename std::conditional<A8, uint8_t, uint16_t>::type;
@@ -182,6 +207,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   constexpr int WCH = WROWB / 16;
 
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + WV * 512];
+  __shared__ int sk_arrived;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -189,7 +215,26 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   const int r32 = lane & 31, g = lane >> 5;
   const int wm = wave / WN, wn = wave % WN;
 
-  const TileCoord tc = tile_of_block(blockIdx.x, tiles_m, tiles_n);
+  // ---- this workgroup's tile and k-tiles kt0 .. kt1-1: a whole tile, or one
+  // piece of a tail tile (tail >= 0; see SkTail)
+  const int KT = K / BK;
+  const int blk = blockIdx.x;
+  int L, kt0 = 0, kt1 = KT, tail = -1, piece = 0;
+  if (sk.d > 0 && blk >= sk.nfull) {
+    // piece-major: the workgroups running together on an XCD hold the same
+    // k-range of neighbouring tiles, which share panels in its L2 as whole
+    // tiles do
+    const int rem = tiles_m * tiles_n - sk.nfull;
+    const int j = xcd_fold(blk - sk.nfull, rem * sk.d);
+    piece = j / rem;
+    tail = j - piece * rem;
+    kt0 = piece * KT / sk.d;
+    kt1 = (piece + 1) * KT / sk.d;
+    L = sk.nfull + tail;
+  } else {
+    L = xcd_fold(blk, sk.d > 0 ? sk.nfull : tiles_m * tiles_n);
+  }
+  const TileCoord tc = tile_coord(L, tiles_m, tiles_n);
   const int m0 = tc.tm * BM;
   const int n0 = tc.tn * TILE_N;
 
@@ -312,12 +357,6 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // so the body stays one basic block with a fixed load count; the
   // scheduling groups thread the fragment reads of sub-step 1 between the
   // MFMAs of sub-step 0.
-  // K range of this workgroup: all of K, or with nseg > 1 (narrow outputs,
-  // too few tiles for the chip) the blockIdx.y-th of nseg contiguous ranges,
-  // whose raw sums go to seg_out for a finishing kernel.
-  const int KT = K / BK;
-  const int seg = blockIdx.y;
-  const int kt0 = (int)((int64_t)seg * KT / nseg), kt1 = (int)((int64_t)(seg + 1) * KT / nseg);
   {
   #pragma unroll
     for (int s = 0; s < NS - 1; ++s) {
@@ -402,6 +441,81 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 }
   __builtin_amdgcn_s_waitcnt(0);  // no direct load is left in flight at exit
 
+  // ---- a piece of a tail tile: publish the raw sums and count the arrival;
+  // the last piece to arrive adds the tile's pieces in k order.  The slots
+  // are stored and loaded with device-scope (sc1) accesses, which pass the
+  // caches that are not coherent across XCDs; with the stores complete
+  // (vmcnt 0) before the counter's increment and the loads issued after the
+  // increment's result is known, no L2 write-back or invalidation is needed
+  // (a device-scope fence does both to the whole XCD's L2, and the GEMM's
+  // panel reuse goes with it).
+  if (tail >= 0) {
+    constexpr int NT = WV * 64;
+    constexpr int SLOT = BM * BN * 4;     // bytes per slot
+    constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
+    // raw buffer over this tile's d slots (word 3 of a gfx9 buffer descriptor:
+    // 32-bit data format, no swizzle); offsets past d * SLOT read zero
+    const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+        sk.part + (int64_t)tail * sk.d * (BM * BN), 0, sk.d * SLOT, 0x00020000);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * qd + i];
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
+                                                 piece * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0,
+                                                 kDeviceScope);
+        }
+    __builtin_amdgcn_s_waitcnt(0);        // this piece's slot stores are complete
+    __syncthreads();
+    if (tid == 0) sk_arrived = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (sk_arrived != sk.d - 1) return;   // another piece writes the tile
+    // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
+    // slot are loaded together (one memory round trip per slot and block)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      f32x4 sum[TB * 4], v[TB * 4];
+      auto own = [&](f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
+      };
+      auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            dst[tb * 4 + qd] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
+      };
+      if (piece == 0) own(sum);
+      else load(0, sum);
+      for (int p = 1; p < sk.d; ++p) {
+        if (p == piece) own(v);
+        else load(p, v);
+#pragma unroll
+        for (int e = 0; e < TB * 4; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
+      }
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
+    }
+  }
+
   // ---- epilogue.  Lane holds, per block, rows 8j + 4g + (0..3) (j = 0..3)
   // of weight-row block cb for token column r32 of block tb.
   if constexpr (SWIGLU) {
@@ -461,12 +575,6 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
           const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
           if (tok >= M) continue;
           f32x4 v;
-          if (nseg > 1) {   // raw sums of this K range
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i];
-            store_out4<false>(seg_out, ((int64_t)seg * M + tok) * N + f, v);
-            continue;
-          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
           if constexpr (A8) {
@@ -501,52 +609,111 @@ constexpr int kWV = TPMLP_PREFILL_WAVES;
 template <int WB>
 constexpr int kNS = WB ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
 
-template <int WB>
-hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
-  const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.I_s + BN / 2 - 1) / (BN / 2);
-  return launch(K_GATEUP_PREFILL, gemm_kernel<true, WB, kBK, kNS<WB>, kWV, false, false>,
-                dim3((unsigned)(tiles_m * tiles_n)), dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, a.x,
-                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (const float*)nullptr, a.a,
-                a.lda, tiles_m, tiles_n, 1, (float*)nullptr);
+// Stream-K plan (see SkTail), sized for MI355X's 256 CUs with one workgroup
+// per CU.  The pieces run as one round (rem * d <= 256): measured, further
+// rounds of pieces lose their gain to the slot stores and arrivals of every
+// round.  d minimises a piece's time, ceil(KT / d) k-tiles plus
+// kSkSlotCost k-tiles for each other slot its final sum may read, and the
+// tail stays whole unless that saves an eighth of the plain last round (KT
+// k-tiles); pieces hold at least kSkMinQ k-tiles.
+constexpr int kSkCUs = 256;
+constexpr int kSkMinQ = 16;
+constexpr int kSkSlotCost = 4;
+
+struct SkPlan {
+  int nfull = 0, rem = 0, d = 0;
+  int64_t cnt_bytes = 0, bytes = 0;   // counters; counters + slots
+};
+
+SkPlan sk_plan(int tiles, int KT) {
+  SkPlan p;
+  const int rem = tiles % kSkCUs;
+  if (rem == 0) return p;
+  int best_d = 1;
+  int best = KT - KT / 8 + 1;   // a split must cost at most 7/8 of the plain round
+  for (int d = 2; d <= KT / kSkMinQ && rem * d <= kSkCUs; ++d) {
+    const int cost = (KT + d - 1) / d + kSkSlotCost * (d - 1);
+    if (cost < best) {
+      best = cost;
+      best_d = d;
+    }
+  }
+  if (best_d == 1) return p;
+  p.nfull = tiles - rem;
+  p.rem = rem;
+  p.d = best_d;
+  p.cnt_bytes = ((int64_t)rem * 4 + 255) / 256 * 256;
+  p.bytes = p.cnt_bytes + (int64_t)rem * best_d * BM * BN * 4;
+  return p;
 }
 
-// K ranges of a prefill row GEMM: an output with fewer tiles than CUs (a
-// rank's QKV projection: 80 tiles at 4096 tokens) splits K until the chip is
-// covered, keeping at least 16 k-tiles per range.
-#ifndef TPMLP_PREFILL_SPLIT_TILES
-#define TPMLP_PREFILL_SPLIT_TILES 256
-#endif
-int prefill_splits(int M, int N, int K) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  if (tiles >= TPMLP_PREFILL_SPLIT_TILES) return 1;
-  const int want = (TPMLP_PREFILL_SPLIT_TILES + tiles - 1) / tiles;
-  return max(1, min(want, K / kBK / 16));
+int gemm_tiles(bool swiglu, int M, int N) {
+  const int tn = swiglu ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
+  return ((M + BM - 1) / BM) * tn;
+}
+
+__global__ void sk_clear_kernel(int* __restrict__ cnt, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = 0;
+}
+
+// One GEMM launch: out = epilogue(rows of W (N of them; gate/up: N channels,
+// 2N weight rows) times the activation rows).  skws: stream-K scratch of
+// sk_plan(...).bytes, or null for whole tiles only.
+template <bool SWIGLU, int WB, int BK, int NS, bool OBF, bool A8>
+hipError_t run_gemm(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
+                    const float* s0, const float* s1, const float* sx, void* out, int64_t ldo, void* skws,
+                    hipStream_t stream) {
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = gemm_tiles(SWIGLU, M, N);
+  SkTail sk{};
+  unsigned grid = (unsigned)tiles;
+  const SkPlan p = skws ? sk_plan(tiles, K / BK) : SkPlan{};
+  if (p.d) {
+    sk.cnt = static_cast<int*>(skws);
+    sk.part = reinterpret_cast<float*>(static_cast<uint8_t*>(skws) + p.cnt_bytes);
+    sk.nfull = p.nfull;
+    sk.d = p.d;
+    grid = (unsigned)(p.nfull + p.rem * p.d);
+    const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
+    if (e != hipSuccess) return e;
+  }
+  return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8>, dim3(grid), dim3(kWV * 64), 0, stream, M, N, K,
+                xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
+}
+
+XRows single_rows(const void* p, int M, int64_t ld) {
+  XRows r{};
+  r.p[0] = p;
+  r.nb = 1;
+  r.rows = M;
+  r.ld = ld;
+  return r;
+}
+
+template <int WB>
+hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
+  return run_gemm<true, WB, kBK, kNS<WB>, false, false>(K_GATEUP_PREFILL, a.M, a.I_s, a.h, a.x, a.wg, a.wu,
+                                                         a.ldw_gu, a.sg, a.su, nullptr, a.a, a.lda, a.sk, stream);
 }
 
 template <int WB, bool OBF>
 hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
-  const int tiles_m = (g.M + BM - 1) / BM;
-  const int tiles_n = (g.N + BN - 1) / BN;
-  XRows ar{};
-  ar.p[0] = g.a;
-  ar.nb = 1;
-  ar.rows = g.M;
-  ar.ld = g.lda;
-  const int nseg = g.ws ? prefill_splits(g.M, g.N, g.K) : 1;
-  hipError_t e = launch(g.kind_prefill, gemm_kernel<false, WB, kBK, kNS<WB>, kWV, OBF, false>,
-                        dim3((unsigned)(tiles_m * tiles_n), nseg), dim3(kWV * 64), 0, stream, g.M, g.N, g.K, ar,
-                        (const uint8_t*)g.w, (const uint8_t*)nullptr, g.ldw, g.s, (const float*)nullptr,
-                        (const float*)nullptr, g.out, g.ldo, tiles_m, tiles_n, nseg, g.ws);
-  if (e != hipSuccess || nseg == 1) return e;
-  return launch_splitk_finish(g.M, g.N, nseg, g.ws, g.s, g.out, g.ldo, g.wb, OBF, stream);
+  return run_gemm<false, WB, kBK, kNS<WB>, OBF, false>(g.kind_prefill, g.M, g.N, g.K, single_rows(g.a, g.M, g.lda),
+                                                        g.w, nullptr, g.ldw, g.s, nullptr, nullptr, g.out, g.ldo,
+                                                        g.ws, stream);
+}
+
+int64_t sk_bytes(bool swiglu, int M, int N, int K, int BK) {
+  return sk_plan(gemm_tiles(swiglu, M, N), K / BK).bytes;
 }
 
 }  // namespace
 
-int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K) {
-  const int nseg = prefill_splits(M, N, K);
-  return nseg > 1 ? (int64_t)nseg * M * N * 4 : 0;
+int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K) { return sk_bytes(false, M, N, K, kBK); }
+
+int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8) {
+  const int bk = a8 ? 128 : kBK;
+  return max(sk_bytes(true, M, I_s, h, bk), sk_bytes(false, M, h, I_s, bk));
 }
 
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
@@ -562,31 +729,15 @@ hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
 
 hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_t stream) {
   constexpr int WB = kWeightE4M3;
-  const int tiles_m = (a.M + BM - 1) / BM;
   hipError_t e = launch_quant_rows(a.M, a.h, a.x.p[0], a.x.ld, b.xq, a.h, b.sx, stream);
   if (e != hipSuccess) return e;
-  XRows xr{};
-  xr.p[0] = b.xq;
-  xr.nb = 1;
-  xr.rows = a.M;
-  xr.ld = a.h;
-  const int tn_gu = (a.I_s + BN / 2 - 1) / (BN / 2);
-  e = launch(K_GATEUP_W8A8, gemm_kernel<true, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_gu)),
-             dim3(kWV * 64), 0, stream, a.M, a.I_s, a.h, xr, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu,
-             a.sg, a.su, (const float*)b.sx, a.a, a.lda, tiles_m, tn_gu, 1, (float*)nullptr);
+  e = run_gemm<true, WB, 128, 2, false, true>(K_GATEUP_W8A8, a.M, a.I_s, a.h, single_rows(b.xq, a.M, a.h), a.wg,
+                                              a.wu, a.ldw_gu, a.sg, a.su, b.sx, a.a, a.lda, a.sk, stream);
   if (e != hipSuccess) return e;
   e = launch_quant_rows(a.M, a.I_s, a.a, a.lda, b.aq, a.I_s, b.sa, stream);
   if (e != hipSuccess) return e;
-  XRows ar{};
-  ar.p[0] = b.aq;
-  ar.nb = 1;
-  ar.rows = a.M;
-  ar.ld = a.I_s;
-  const int tn_dn = (a.h + BN - 1) / BN;
-  return launch(K_DOWN_W8A8, gemm_kernel<false, WB, 128, 2, kWV, false, true>, dim3((unsigned)(tiles_m * tn_dn)),
-                dim3(kWV * 64), 0, stream, a.M, a.h, a.I_s, ar, (const uint8_t*)a.wd, (const uint8_t*)nullptr,
-                a.ldw_down, a.sd, (const float*)nullptr, (const float*)b.sa, (void*)a.p, a.ldp, tiles_m, tn_dn, 1,
-                (float*)nullptr);
+  return run_gemm<false, WB, 128, 2, false, true>(K_DOWN_W8A8, a.M, a.h, a.I_s, single_rows(b.aq, a.M, a.I_s), a.wd,
+                                                  nullptr, a.ldw_down, a.sd, nullptr, b.sa, a.p, a.ldp, a.sk, stream);
 }
 
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
@@ -597,7 +748,9 @@ hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
     default: e = run_gateup<kWeightWide>(a, stream); break;
   }
   if (e != hipSuccess) return e;
-  return launch_rowgemm_prefill(down_of(a), stream);
+  RowGemm g = down_of(a);
+  g.ws = static_cast<float*>(a.sk);
+  return launch_rowgemm_prefill(g, stream);
 }
 
 }  // namespace tpmlp

@@ -53,6 +53,9 @@ def test_status_strings_and_kinds():
 BF16, F32, FP8 = _lib.TP_BF16, _lib.TP_F32, _lib.TP_FP8_E4M3FN
 
 
+SLOT = 256 * 256 * 4   # one stream-K piece's fp32 sums of a 256 x 256 tile
+
+
 def test_workspace_bytes():
     lib = _lib.load()
     # A = M x I_s bf16, rounded up to 256 bytes
@@ -60,6 +63,17 @@ def test_workspace_bytes():
     assert lib.tp_mlp_workspace_bytes(3, 64, 128, 2, BF16, FP8) == 512          # 3*64*2 = 384 -> 512
     assert lib.tp_mlp_workspace_bytes(5, 64, 128, 2, BF16, BF16) == 768         # 5*64*2 = 640 -> 768
     assert lib.tp_mlp_workspace_bytes(16, 256, 1024, 4, F32, F32) == 16 * 256 * 4
+    # bf16 prefill adds the stream-K scratch of its GEMMs (pieces in one round of 256 CUs).
+    # 405B TP=8 at 8192 tokens: gate/up 32 x 52 = 1664 tiles, the last 128 in 2 pieces of 128
+    # k-tiles (counters: 512 bytes); down 32 x 64 = 2048 tiles, whole rounds
+    assert lib.tp_mlp_workspace_bytes(8192, 16384, 53248, 8, BF16, BF16) == 8192 * 6656 * 2 + 512 + 256 * SLOT
+    # 70B TP=8 at 4096 tokens: 448 gate/up tiles, 192 past the first round (2 pieces each would
+    # take two rounds); at 2048 tokens 224 tiles (one round, a split saves under an eighth of it)
+    assert lib.tp_mlp_workspace_bytes(4096, 8192, 28672, 8, BF16, BF16) == 4096 * 3584 * 2
+    assert lib.tp_mlp_workspace_bytes(2048, 8192, 28672, 8, BF16, BF16) == 2048 * 3584 * 2
+    # just above the decode range: 28 gate/up tiles of 128 k-tiles cut in 5 pieces (counters: 256
+    # bytes); the larger of the two GEMMs' scratch
+    assert lib.tp_mlp_workspace_bytes(65, 8192, 28672, 8, BF16, BF16) == 65 * 3584 * 2 + 256 + 140 * SLOT
     # invalid arguments give 0
     assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 5, BF16, BF16) == 0       # I % t
     assert lib.tp_mlp_workspace_bytes(0, 8192, 28672, 8, BF16, BF16) == 0
@@ -232,8 +246,10 @@ def test_attn_qkv_workspace_bytes():
     for M in (1, 8, 32, 64):
         b = lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16)
         assert b > 0 and b % 256 == 0 and b % (M * 1280 * 4) == 0
-    # prefill: 80 tiles of 256 x 256 for 4096 tokens, K split in 4 ranges
-    assert lib.tp_attn_qkv_workspace_bytes(4096, 8192, 64, 8, 128, 8, BF16, BF16) == 4 * 4096 * 1280 * 4
+    # prefill: 80 tiles of 256 x 256 for 4096 tokens, fewer than the 256 CUs: every tile is cut
+    # along K into 3 stream-K pieces (128 k-tiles of 64), each with a 256 x 256 fp32 slot, plus
+    # 80 arrival counters rounded to 512 bytes
+    assert lib.tp_attn_qkv_workspace_bytes(4096, 8192, 64, 8, 128, 8, BF16, BF16) == 512 + 240 * SLOT
     assert lib.tp_attn_qkv_workspace_bytes(16, 256, 8, 2, 32, 4, F32, F32) == 0          # fp32 path
     assert lib.tp_attn_qkv_workspace_bytes(1, 8192, 64, 8, 128, 3, BF16, BF16) == 0      # invalid split
     assert lib.tp_attn_qkv_workspace_bytes(0, 8192, 64, 8, 128, 8, BF16, BF16) == 0
@@ -334,9 +350,10 @@ def test_w8a8_rejects(kw, status):
 
 def test_w8a8_workspace_bytes():
     lib = _lib.load()
-    # A bf16 + X codes + scales + A codes + scales, each rounded to 256 bytes
+    # A bf16 + X codes + scales + A codes + scales, each rounded to 256 bytes, then the stream-K
+    # scratch: gate/up has 16 x 56 = 896 tiles of 64 k-tiles (128 wide), the last 128 cut in 2
     M, h, I_s = 4096, 8192, 7168
-    want = M * I_s * 2 + M * h + M * 4 + M * I_s + M * 4
+    want = M * I_s * 2 + M * h + M * 4 + M * I_s + M * 4 + 512 + 256 * SLOT
     assert lib.tp_mlp_w8a8_workspace_bytes(M, h, I_s * 4, 4) == want
     assert lib.tp_mlp_w8a8_workspace_bytes(M, 192, 1024, 4) == 0
 

@@ -81,8 +81,8 @@ QKV_CASES = [
     (33, 320, 8, 2, 64, 4, "bf16"),       # h % 128 != 0: register-batch kernels; KV replicated
     (64, 1024, 16, 4, 32, 2, "bf16"),
     (300, 512, 8, 2, 64, 2, "bf16"),      # prefill, ragged M and N tiles (K too short to split)
-    (1000, 4096, 8, 2, 64, 2, "bf16"),    # prefill, 8 tiles: K split in 4 ranges
-    (130, 2048, 16, 4, 64, 4, "e4m3fn"),  # prefill with fp8 weights, K split in 2: the row scale after the sum
+    (1000, 4096, 8, 2, 64, 2, "bf16"),    # prefill, 8 tiles, each cut along K in 4 stream-K pieces
+    (130, 2048, 16, 4, 64, 4, "e4m3fn"),  # prefill with fp8 weights, 2 tiles in 2 pieces: the row scale after the sum
     (520, 384, 12, 4, 64, 4, "bf16"),
     (3, 1024, 8, 2, 64, 2, "e4m3fn"),
     (40, 320, 8, 2, 64, 2, "e4m3fn"),     # fp8 register-batch path
@@ -232,15 +232,16 @@ def test_prepared_calls_in_a_graph():
 
 def test_split_workspace_reuse_and_dirty_contents():
     """One workspace serves calls of different sizes; what it holds on entry
-    does not change the result (the split sums overwrite it)."""
+    does not change the result (decode: the split sums overwrite it; prefill:
+    the stream-K counters are cleared by the call)."""
     h, nh, nkv, d, t = 8192, 64, 8, 128, 8
     n_loc, _ = workloads.attn_widths(nh, nkv, d, t)
     ws = workloads.make_attn_weights(65, h, n_loc, 64, 0, "bf16", 0.02)
     wq = to_device(ws["w_qkv"], "bf16")
-    need = max(tp.attn_qkv_workspace_bytes(M, h, nh, nkv, d, t) for M in (1, 8, 64))
+    need = max(tp.attn_qkv_workspace_bytes(M, h, nh, nkv, d, t) for M in (1, 8, 64, 1000))
     assert need > 0
     scratch = tp.alloc_workspace(need, "cuda")
-    for M in (64, 1, 8):
+    for M in (64, 1, 1000, 8):
         x = to_device(workloads.make_x(65, M, h, "bf16", weight_set=M), "bf16")
         kw = dict(n_heads=nh, n_kv_heads=nkv, head_dim=d, t=t, k=0)
         scratch.fill_(0x7F)                      # fp32 words of 3.4e38

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 import tensor_transformer_mlp_tp_amd as tp
-from helpers import TOL_BF16, TOL_FP8, make_case, upload_case, oracle_partial, to_device
+from helpers import TOL_BF16, TOL_FP8, TOL_INT8, make_case, upload_case, oracle_partial, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +205,56 @@ def test_config4_fp8_prefill_full():
 
 def test_config5_prefill_full():
     _full_prefill(5, 8192)
+
+
+# ------------------------------------------------------------ stream-K tail of the prefill GEMMs
+
+@pytest.mark.parametrize("M,h,I_s", [
+    (300, 2112, 2112),   # both GEMMs: every tile cut along K in 2 uneven pieces (33 k-tiles); ragged tiles
+    (65, 8192, 448),     # gate/up: 4 tiles (the last ragged) cut in 5 pieces; down whole
+    (600, 1024, 4096),   # down: 12 tiles in 4 pieces; gate/up whole
+])
+@pytest.mark.parametrize("w", ["bf16", "e4m3fn", "int8"])
+def test_stream_k_tail(M, h, I_s, w):
+    """Tiles cut along K: the last piece to arrive adds the pieces' fp32 slots
+    in k order.  The arrival counters live in the workspace, whose contents
+    on entry must not matter, and the result must not depend on which piece
+    arrives last (bit-identical over calls)."""
+    t = 2
+    print("stream-K M=%d h=%d I_s=%d w=%s" % (M, h, I_s, w), flush=True)
+    x, ws = make_case(45, M, h, I_s, "bf16", w, 0.05, 0.05, weight_set=M)
+    d = upload_case(x, ws, "bf16", w)
+    nbytes = tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16, d["w_gate"].dtype)
+    assert nbytes > M * I_s * 2 + 256      # the stream-K scratch is part of it
+    scratch = tp.alloc_workspace(nbytes, "cuda")
+    outs = []
+    for fill in (0x7F, 0x00, 0xFF):
+        scratch.fill_(fill)
+        outs.append(tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0, s_gate=d["s_gate"],
+                                     s_up=d["s_up"], s_down=d["s_down"], workspace=scratch))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    tol = {"bf16": TOL_BF16, "e4m3fn": TOL_FP8, "int8": TOL_INT8}[w]
+    check(outs[0].cpu().numpy(), oracle_partial(x, ws, "bf16", w), tol, "stream-K M=%d %s" % (M, w))
+
+
+def test_stream_k_tail_after_whole_rounds():
+    """More tiles than CUs: gate/up has 17 x 16 = 272 tiles, 256 computed whole
+    and the 16 of the last (ragged) M-tile cut in 2 pieces; checked on sampled
+    rows, a dozen of them in that M-tile."""
+    M, h, I_s, t = 4300, 2048, 2048, 2
+    print("stream-K after whole rounds M=%d" % M, flush=True)
+    x, ws = make_case(46, M, h, I_s, "bf16", "bf16", 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", "bf16")
+    p = run_forward(d, t, 0)
+    rng = np.random.Generator(np.random.PCG64(46))
+    rows = np.unique(np.concatenate([rng.choice(4096, 30, replace=False), 4096 + rng.choice(M - 4096, 12, replace=False),
+                                     [0, 4095, 4096, M - 1]]))
+    got = p[torch.from_numpy(rows).cuda()].cpu().numpy()
+    check(got, oracle_partial(x, ws, "bf16", "bf16", rows=rows), TOL_BF16, "M=%d (%d sampled rows)" % (M, len(rows)))
+    p2 = run_forward(d, t, 0)
+    assert torch.equal(p.view(torch.int32), p2.view(torch.int32))
 
 
 # ------------------------------------------------------------ streaming decode path, several slots per wave
