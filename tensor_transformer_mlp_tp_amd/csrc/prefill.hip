@@ -177,7 +177,11 @@ struct SkTail {
 // A8: the activations are e4m3fn codes too (W8A8): one byte per element in
 // LDS, 32x32x64 fp8 MFMAs (twice the bf16 rate), and the per-token scales sx
 // applied in the epilogue with the weight row scales.
-template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF, bool A8>
+// SK: the launch has a stream-K tail (sk.d > 0).  Launches without one use
+// the SK = false instance, which has no tail code: with it, the compiler
+// moves all accumulators out of AGPRs ahead of the tail branch and spills,
+// which slows every tile's epilogue.
+template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF, bool A8, bool SK>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
@@ -206,8 +210,11 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   constexpr int XCH = XROWB / 16;              // 16-byte chunks per row
   constexpr int WCH = WROWB / 16;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + WV * 512];
-  __shared__ int sk_arrived;
+  // Stages, the L2 touch scratch and the stream-K arrival flag in one LDS
+  // object: with a second __shared__ object the compiler no longer tells the
+  // direct-to-LDS destinations from the fragment reads and drains the load
+  // ring (vmcnt(0)) before every k-tile's reads.
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * SBYTES + WV * 512 + (SK ? 16 : 0)];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,7 +227,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   const int KT = K / BK;
   const int blk = blockIdx.x;
   int L, kt0 = 0, kt1 = KT, tail = -1, piece = 0;
-  if (sk.d > 0 && blk >= sk.nfull) {
+  if (SK && blk >= sk.nfull) {
     // piece-major: the workgroups running together on an XCD hold the same
     // k-range of neighbouring tiles, which share panels in its L2 as whole
     // tiles do
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     kt1 = (piece + 1) * KT / sk.d;
     L = sk.nfull + tail;
   } else {
-    L = xcd_fold(blk, sk.d > 0 ? sk.nfull : tiles_m * tiles_n);
+    L = xcd_fold(blk, SK ? sk.nfull : tiles_m * tiles_n);
   }
   const TileCoord tc = tile_coord(L, tiles_m, tiles_n);
   const int m0 = tc.tm * BM;
@@ -449,7 +456,8 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // increment's result is known, no L2 write-back or invalidation is needed
   // (a device-scope fence does both to the whole XCD's L2, and the GEMM's
   // panel reuse goes with it).
-  if (tail >= 0) {
+  if (SK && tail >= 0) {
+    int& sk_arrived = *reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512);
     constexpr int NT = WV * 64;
     constexpr int SLOT = BM * BN * 4;     // bytes per slot
     constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
@@ -677,8 +685,12 @@ hipError_t run_gemm(int kind, int M, int N, int K, const XRows& xr, const void* 
     const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
     if (e != hipSuccess) return e;
   }
-  return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8>, dim3(grid), dim3(kWV * 64), 0, stream, M, N, K,
-                xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
+  if (p.d)
+    return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8, true>, dim3(grid), dim3(kWV * 64), 0, stream, M,
+                  N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m,
+                  sk);
+  return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8, false>, dim3(grid), dim3(kWV * 64), 0, stream, M, N,
+                K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
 }
 
 XRows single_rows(const void* p, int M, int64_t ld) {
