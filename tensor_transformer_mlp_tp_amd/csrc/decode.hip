@@ -730,8 +730,18 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
   const int64_t e = 4 * g;
   if (e >= total) return;
   const int tok = (int)(e / N), f = (int)(e % N);
-  f32x4 v = *reinterpret_cast<const f32x4*>(seg + e);
-  for (int q = 1; q < nseg; ++q) v = v + *reinterpret_cast<const f32x4*>(seg + q * total + e);
+  auto at = [&](int q) { return *reinterpret_cast<const f32x4*>(seg + q * total + e); };
+  // the same left fold over the ranges, with eight loads in flight at a time
+  f32x4 v = at(0);
+  int q = 1;
+  for (; q + 8 <= nseg; q += 8) {
+    f32x4 t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[j] = at(q + j);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v = v + t[j];
+  }
+  for (; q < nseg; ++q) v = v + at(q);
   if constexpr (WB) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] *= s[f + i];
@@ -810,6 +820,18 @@ hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
 template <int NT, int WB>
 constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
 
+// A narrow row GEMM that splits K (below) runs three 16-row blocks per wave
+// on the bf16 activation-staged path instead of two: each staged activation
+// fragment serves 48 rows, and the split keeps the workgroup count up.
+// Measured on the 70B TP = 8 QKV projection (1280 rows): M = 64 17.3 ->
+// 13.4 us, M = 32 13.0 -> 10.7 us; the wide outputs (MLP, o_proj) are
+// faster with two.
+#ifndef TPMLP_DECODE_RB_SPLIT
+#define TPMLP_DECODE_RB_SPLIT 3
+#endif
+template <int NT, int WB>
+constexpr int kRowRBSplit = kStreamXD<NT, WB> && !WB ? TPMLP_DECODE_RB_SPLIT : kRowRB<NT, WB>;
+
 // K split of a streaming row GEMM.  A narrow output (few 16-row blocks, e.g.
 // a rank's QKV projection: 80 blocks for 1280 rows) keeps too few loads in
 // flight across the chip; its K slots are then split into nseg contiguous
@@ -822,9 +844,8 @@ constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? TPMLP_DECODE_RB_
 #define TPMLP_SPLIT_TARGET_WAVES 1024
 #endif
 
-template <int NT, int WB>
+template <int NT, int WB, int RB = kRowRBSplit<NT, WB>>
 int stream_splits(int N, int K) {
-  constexpr int RB = kRowRB<NT, WB>;
   constexpr int WV = StreamShape<NT, RB, WB, kStreamXD<NT, WB>>::WV;
   const int blocks = (N + 16 * RB - 1) / (16 * RB);
   const int want = (TPMLP_SPLIT_TARGET_WAVES + blocks * WV - 1) / (blocks * WV);
@@ -832,16 +853,24 @@ int stream_splits(int N, int K) {
   return max(1, min(want, cap));
 }
 
+template <int NT, int RB, int WB, bool OBF>
+hipError_t rowgemm_stream_launch(const RowGemm& g, int nseg, hipStream_t stream) {
+  constexpr bool XD = kStreamXD<NT, WB>;
+  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg);
+  return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF>, grid,
+                dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a, g.lda,
+                (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
+}
+
 template <int NT, int WB, bool OBF>
 hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
-  constexpr bool XD = kStreamXD<NT, WB>;
-  constexpr int RB = kRowRB<NT, WB>;
+  // nseg is planned for kRowRBSplit row blocks per wave; when it comes out 1
+  // the output is wide enough for kRowRB without a split (kRowRB's larger
+  // block count would not split either).
   const int nseg = g.ws ? stream_splits<NT, WB>(g.N, g.K) : 1;
-  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg);
-  hipError_t e = launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF>, grid,
-                        dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, g.M, g.N, g.K,
-                        (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
-  if (e != hipSuccess || nseg == 1) return e;
+  if (nseg == 1) return rowgemm_stream_launch<NT, kRowRB<NT, WB>, WB, OBF>(g, 1, stream);
+  hipError_t e = rowgemm_stream_launch<NT, kRowRBSplit<NT, WB>, WB, OBF>(g, nseg, stream);
+  if (e != hipSuccess) return e;
   const int64_t groups = (int64_t)g.M * g.N / 4;
   return launch(K_SPLITK_FINISH, splitk_finish_kernel<WB, OBF>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
                 0, stream, g.M, g.N, nseg, (const float*)g.ws, g.s, g.out, g.ldo);
