@@ -36,6 +36,7 @@ def _blocks(xdev, t, pad=0):
     (48, 8, 320, 192, "bf16"),      # decode shapes off the streaming grid (register-batch kernels)
     (520, 8, 320, 192, "bf16"),     # prefill, 65-row blocks: block edges inside MFMA tiles
     (1024, 4, 512, 384, "e4m3fn"),
+    (520, 8, 2112, 2112, "bf16"),   # prefill with stream-K tails in both GEMMs (every tile in 2 pieces)
 ])
 def test_forward_sp_matches_gathered(M, t, h, I_s, w):
     print("forward_sp M=%d t=%d h=%d I_s=%d w=%s" % (M, t, h, I_s, w), flush=True)

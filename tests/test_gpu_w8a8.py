@@ -104,6 +104,7 @@ def _w8a8_errors(x, ws, M, h, I_s, t, rows=None):
     (256, 512, 384),
     (300, 1024, 640),
     (1024, 2048, 1536),
+    (300, 4096, 2048),     # gate/up tiles cut along K in 2 stream-K pieces (32 k-tiles of 128)
 ])
 def test_w8a8_forward_shapes(M, h, I_s):
     x, ws = make_case(93, M, h, I_s, "bf16", "e4m3fn", 0.05, 0.05, weight_set=M)
