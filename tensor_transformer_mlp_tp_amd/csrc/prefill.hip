@@ -456,71 +456,73 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // increment's result is known, no L2 write-back or invalidation is needed
   // (a device-scope fence does both to the whole XCD's L2, and the GEMM's
   // panel reuse goes with it).
-  if (SK && tail >= 0) {
-    int& sk_arrived = *reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512);
-    constexpr int NT = WV * 64;
-    constexpr int SLOT = BM * BN * 4;     // bytes per slot
-    constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
-    // raw buffer over this tile's d slots (word 3 of a gfx9 buffer descriptor:
-    // 32-bit data format, no swizzle); offsets past d * SLOT read zero
-    const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
-        sk.part + (int64_t)tail * sk.d * (BM * BN), 0, sk.d * SLOT, 0x00020000);
+  if constexpr (SK) {
+    if (tail >= 0) {
+      int& sk_arrived = *reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512);
+      constexpr int NT = WV * 64;
+      constexpr int SLOT = BM * BN * 4;     // bytes per slot
+      constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
+      // raw buffer over this tile's d slots (word 3 of a gfx9 buffer descriptor:
+      // 32-bit data format, no swizzle); offsets past d * SLOT read zero
+      const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+          sk.part + (int64_t)tail * sk.d * (BM * BN), 0, sk.d * SLOT, 0x00020000);
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-          f32x4 v;
+          for (int qd = 0; qd < 4; ++qd) {
+            f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * qd + i];
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
-                                                 piece * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0,
-                                                 kDeviceScope);
+            for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * qd + i];
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
+                                                   piece * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0,
+                                                   kDeviceScope);
+          }
+      __builtin_amdgcn_s_waitcnt(0);        // this piece's slot stores are complete
+      __syncthreads();
+      if (tid == 0) sk_arrived = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (sk_arrived != sk.d - 1) return;   // another piece writes the tile
+      // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
+      // slot are loaded together (one memory round trip per slot and block)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        f32x4 sum[TB * 4], v[TB * 4];
+        auto own = [&](f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
+        };
+        auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd)
+              dst[tb * 4 + qd] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                             slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
+        };
+        if (piece == 0) own(sum);
+        else load(0, sum);
+        for (int p = 1; p < sk.d; ++p) {
+          if (p == piece) own(v);
+          else load(p, v);
+#pragma unroll
+          for (int e = 0; e < TB * 4; ++e)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
         }
-    __builtin_amdgcn_s_waitcnt(0);        // this piece's slot stores are complete
-    __syncthreads();
-    if (tid == 0) sk_arrived = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (sk_arrived != sk.d - 1) return;   // another piece writes the tile
-    // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
-    // slot are loaded together (one memory round trip per slot and block)
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      f32x4 sum[TB * 4], v[TB * 4];
-      auto own = [&](f32x4 (&dst)[TB * 4]) {
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
           for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
-      };
-      auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-            dst[tb * 4 + qd] = __builtin_bit_cast(
-                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                           slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
-      };
-      if (piece == 0) own(sum);
-      else load(0, sum);
-      for (int p = 1; p < sk.d; ++p) {
-        if (p == piece) own(v);
-        else load(p, v);
-#pragma unroll
-        for (int e = 0; e < TB * 4; ++e)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
+            for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
       }
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
     }
   }
 
