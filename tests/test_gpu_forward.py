@@ -277,6 +277,35 @@ def test_stream_decode_shapes(M, w):
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
 
 
+def test_prefill_stream_k_in_a_graph():
+    """A prefill forward whose GEMMs have stream-K tails, captured in a HIP
+    graph: the arrival counters are cleared by a kernel inside the graph, so
+    every replay (with eager work and a dirtied workspace in between) must
+    equal the eager result bit for bit."""
+    M, h, I_s, t = 300, 2112, 2112, 2
+    x, ws = make_case(48, M, h, I_s, "bf16", "bf16", 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", "bf16")
+    ref = run_forward(d, t, 0).clone()
+    scratch = tp.alloc_workspace(tp.workspace_bytes(M, h, I_s * t, t), "cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        call = tp.prepare_shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0, workspace=scratch)
+        call()   # warm-up outside capture
+        s.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            call()
+    for i in range(4):
+        scratch.fill_(0x7F if i % 2 else 0xFF)          # counters and slots hold garbage
+        call.partial.zero_()
+        other = run_forward(d, t, 1)                     # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(call.partial.view(torch.int32), ref.view(torch.int32)), i
+        assert torch.equal(other.view(torch.int32), ref.view(torch.int32)), i   # k does not change P's value
+
+
 def test_decode_many_calls_and_graph():
     # many calls on two streams in turn, then a captured graph replayed
     M, h, I_s = 8, 512, 512
