@@ -235,8 +235,8 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     const int j = xcd_fold(blk - sk.nfull, rem * sk.d);
     piece = j / rem;
     tail = j - piece * rem;
-    kt0 = piece * KT / sk.d;
-    kt1 = (piece + 1) * KT / sk.d;
+    kt0 = (int)((int64_t)piece * KT / sk.d);
+    kt1 = (int)((int64_t)(piece + 1) * KT / sk.d);
     L = sk.nfull + tail;
   } else {
     L = xcd_fold(blk, SK ? sk.nfull : tiles_m * tiles_n);
