@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libtp_mlp.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["abi.cpp", "reduce.hip", "decode.hip", "prefill.hip", "fp32.hip", "quant.hip"]
+SOURCES = ["abi.cpp", "reduce.hip", "decode.hip", "prefill.hip", "fp32.hip", "quant.hip", "gemv.hip"]
 
 ARCH = "gfx950"
 

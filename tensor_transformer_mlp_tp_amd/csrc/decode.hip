@@ -951,8 +951,19 @@ hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const f
                       nseg, ws, s, out, ldo);
 }
 
+// A narrow row GEMM that the matrix-core stream would split along K (the
+// QKV projection) goes, at up to kGemvMaxM tokens with bf16 weights, to the
+// row-streaming VALU kernel of gemv.hip: no split and no finishing kernel.
+// TPMLP_GEMV=0 keeps the matrix-core streams for every decode shape.
+#ifndef TPMLP_GEMV
+#define TPMLP_GEMV 1
+#endif
+static bool use_gemv(int M, int N, int K, int wb) {
+  return TPMLP_GEMV && gemv_supported(M, K, wb) && stream_splits<1, kWeightWide>(N, K) > 1;
+}
+
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {
-  if (M < 1 || M > kDecodeMaxM) return 0;
+  if (M < 1 || M > kDecodeMaxM || use_gemv(M, N, K, wb)) return 0;
   switch (wb) {
     case kWeightE4M3: return workspace_bytes_wb<kWeightE4M3>(M, N, K);
     case kWeightI8: return workspace_bytes_wb<kWeightI8>(M, N, K);
@@ -961,6 +972,7 @@ int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {
 }
 
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
+  if (use_gemv(g.M, g.N, g.K, g.wb)) return launch_rowgemm_gemv(g, stream);
   switch (g.wb) {
     case kWeightE4M3: return rowgemm_wb<kWeightE4M3>(g, stream);
     case kWeightI8: return rowgemm_wb<kWeightI8>(g, stream);

@@ -103,6 +103,8 @@ struct RowGemm {
 
 // Largest M served by the weight-streaming (decode) kernels.
 constexpr int kDecodeMaxM = 64;
+// Largest M served by the row-streaming VALU kernel (gemv.hip), bf16 weights.
+constexpr int kGemvMaxM = 2;
 
 hipError_t launch_partial_reduce(const PartialPtrs& ptrs, int t, float* out, int64_t n,
                                  hipStream_t stream);
@@ -143,6 +145,10 @@ int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8);
 hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,
                                 int wb, bool obf, hipStream_t stream);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
+// Row-streaming VALU row GEMM (M <= kGemvMaxM, bf16 weights, K a multiple of
+// 512 up to 16384): whether it can take this shape, and the launch.
+bool gemv_supported(int M, int K, int wb);
+hipError_t launch_rowgemm_gemv(const RowGemm& g, hipStream_t stream);
 hipError_t launch_rowgemm_f32(const RowGemm& g, hipStream_t stream);
 // rows x K bf16 -> e4m3fn codes (ldq bytes per row) and one fp32 scale per row.
 hipError_t launch_quant_rows(int M, int K, const void* x, int64_t ldx, void* q, int64_t ldq, float* scales,

@@ -242,10 +242,15 @@ def qkv_call(M=1, h=128, nh=8, nkv=2, d=32, t=2, k=0, act=BF16, w=BF16, x=P, ldx
 
 def test_attn_qkv_workspace_bytes():
     lib = _lib.load()
-    # 70B TP=8 decode: the 1280-wide output over h = 8192 is split along h
-    for M in (1, 8, 32, 64):
+    # 70B TP=8 decode: at one or two tokens the row-streaming kernel needs no scratch; above,
+    # the 1280-wide output over h = 8192 is split along h
+    for M in (1, 2):
+        assert lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16) == 0
+    for M in (3, 8, 32, 64):
         b = lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16)
         assert b > 0 and b % 256 == 0 and b % (M * 1280 * 4) == 0
+    # fp8 weights keep the split at M = 1
+    assert lib.tp_attn_qkv_workspace_bytes(1, 8192, 64, 8, 128, 8, BF16, FP8) > 0
     # prefill: 80 tiles of 256 x 256 for 4096 tokens, fewer than the 256 CUs: every tile is cut
     # along K into 3 stream-K pieces (128 k-tiles of 64), each with a 256 x 256 fp32 slot, plus
     # 80 arrival counters rounded to 512 bytes

@@ -92,6 +92,9 @@ QKV_CASES = [
     (40, 4096, 8, 2, 64, 2, "bf16"),      # activation-staged kernels, h split in 8 ranges
     (16, 4096, 8, 2, 64, 2, "e4m3fn"),    # fp8, h split in 2 ranges
     (64, 2048, 4, 4, 32, 4, "bf16"),      # n_loc = 96, h split in 4 ranges
+    (1, 4096, 8, 2, 64, 2, "bf16"),       # one or two tokens, a narrow output the streams would split:
+    (2, 16384, 32, 8, 128, 4, "bf16"),    # the row-streaming kernel (whole rows per wave, no split);
+    (1, 2048, 16, 4, 64, 4, "bf16"),      # K = 16384 is its largest
 ]
 
 
