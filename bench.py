@@ -77,7 +77,7 @@ KERNEL_SOURCES = {
     "gateup_decode": ("decode.hip", "common.h", "internal.h"),
     "gateup_prefill": ("prefill.hip", "common.h", "internal.h"),
     "partial_reduce": ("reduce.hip", "common.h", "internal.h"),
-    "qkv_decode": ("decode.hip", "common.h", "internal.h"),
+    "qkv_decode": ("decode.hip", "gemv.hip", "common.h", "internal.h"),
     "qkv_prefill": ("prefill.hip", "common.h", "internal.h"),
     "gateup_w8a8": ("prefill.hip", "common.h", "internal.h"),
 }
