@@ -14,9 +14,9 @@
 // wide outputs and for the MLP the matrix-core streams are as fast or
 // faster; they stay there.)
 //
-// The activations of the M tokens (M x K bf16; a second row of zeros when M
-// = 1 with MT = 2) are copied into LDS once per workgroup; per chunk each
-// lane reads its 16 bytes of every token from there.  A row's sum is finished
+// The activations of the M tokens (M x K bf16) are copied into LDS once per
+// workgroup; per chunk each lane reads its 16 bytes of every token from
+// there.  A row's sum is finished
 // with a butterfly over the wave's 64 lanes (every lane ends with the same
 // bits, the order fixed: the result is deterministic) and written by the
 // lanes of the tokens.
