@@ -124,6 +124,8 @@ def fwd(M=1, h=128, I=256, t=2, k=0, act=BF16, w=BF16, x=P, wg=P * 2, wu=P * 3, 
     (dict(I=2 * 96), _lib.TP_ERR_UNSUPPORTED),              # I_s % 64
     (dict(wsb=10), _lib.TP_ERR_WORKSPACE),
     (dict(ws=None), _lib.TP_ERR_WORKSPACE),
+    (dict(M=300, h=2112, I=4224, wsb=300 * 2112 * 2), _lib.TP_ERR_WORKSPACE),   # A only: the prefill's
+                                                                                # stream-K scratch is missing
     (dict(x=P + 2), _lib.TP_ERR_UNSUPPORTED),               # misaligned
     (dict(ldx=132), _lib.TP_ERR_UNSUPPORTED),               # rows not 16-byte aligned
     (dict(ws=P * 16 + 16), _lib.TP_ERR_UNSUPPORTED),        # workspace not 256-aligned
