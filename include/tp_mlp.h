@@ -73,10 +73,10 @@ typedef enum {
  * Workspace bytes tp_mlp_shard_forward needs for these arguments (0 if the
  * arguments are invalid).  The workspace holds the intermediate activation A
  * (M x I_s, in the activation dtype) plus alignment padding, and for a bf16
- * prefill (M > 64) whose output tiles do not fill whole rounds of the 256
- * CUs the stream-K scratch of the two GEMMs: arrival counters and one fp32
- * 256 x 256 tile per piece of the tiles cut along K (at most 256 pieces,
- * 64 MiB).
+ * prefill (M > 64; M > 32 with one-byte weights) whose output tiles do not
+ * fill whole rounds of the 256 CUs the stream-K scratch of the two GEMMs:
+ * arrival counters and one fp32 tile (256 weight rows by 64, 128 or 256
+ * tokens) per piece of the tiles cut along K (at most 256 pieces, 64 MiB).
  */
 size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                               int32_t act_dtype, int32_t w_dtype);

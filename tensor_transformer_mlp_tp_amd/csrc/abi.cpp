@@ -113,8 +113,8 @@ tp_status check_shapes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
 // bf16 prefill the two GEMMs' stream-K scratch.
 int64_t workspace_a_bytes(int64_t M, int64_t I_s, int32_t act) { return round_up(M * I_s * elem_bytes(act), 256); }
 
-int64_t workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t act) {
-  const int64_t sk = act == TP_BF16 && M > tpmlp::kDecodeMaxM
+int64_t workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t act, int32_t w) {
+  const int64_t sk = act == TP_BF16 && M > tpmlp::forward_decode_max_m(weight_format(w))
                          ? tpmlp::forward_prefill_sk_bytes((int)M, (int)h, (int)I_s, false) : 0;
   return workspace_a_bytes(M, I_s, act) + round_up(sk, 256);
 }
@@ -168,7 +168,7 @@ void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop) {
 TP_API size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                                      int32_t act_dtype, int32_t w_dtype) {
   if (check_shapes(M, h, I_full, t, 0, act_dtype, w_dtype) != TP_OK) return 0;
-  return (size_t)workspace_need(M, h, I_full / t, act_dtype);
+  return (size_t)workspace_need(M, h, I_full / t, act_dtype, w_dtype);
 }
 
 namespace {
@@ -197,7 +197,7 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
     return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length "
                 "(ldx=%lld ldw_gu=%lld ldw_down=%lld ldp=%lld)", (long long)ldx, (long long)ldw_gu,
                 (long long)ldw_down, (long long)ldp);
-  const int64_t need = workspace_need(M, h, I_s, act_dtype);
+  const int64_t need = workspace_need(M, h, I_s, act_dtype, w_dtype);
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
                 (unsigned long long)workspace_bytes);
@@ -261,7 +261,7 @@ tp_status forward_impl(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
   hipError_t e;
   if (act_dtype == TP_F32)
     e = tpmlp::launch_forward_f32(a, s);
-  else if (M <= tpmlp::kDecodeMaxM)
+  else if (M <= tpmlp::forward_decode_max_m(a.wb))
     e = tpmlp::launch_forward_decode(a, s);
   else
     e = tpmlp::launch_forward_prefill(a, s);

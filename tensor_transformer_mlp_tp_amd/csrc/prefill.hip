@@ -12,10 +12,12 @@
 //             partial).
 //
 // Both compute C^T = W * act^T with K-contiguous operands (the (out, in)
-// weight layout and row-major activations): 256 x 256 output tiles, four
-// waves in a 2 x 2 grid with a 128 x 128 sub-tile each, built from 32x32x16
-// bf16 MFMAs (the full-rate bf16 matrix instruction on gfx950; 4 x 4 blocks =
-// 256 fp32 accumulators per lane, held in AGPRs).
+// weight layout and row-major activations): output tiles of 256 weight rows
+// by 256 tokens, four waves in a 2 x 2 grid with a 128 x 128 sub-tile each,
+// built from 32x32x16 bf16 MFMAs (the full-rate bf16 matrix instruction on
+// gfx950; 4 x 4 blocks = 256 fp32 accumulators per lane, held in AGPRs).
+// With a few hundred tokens the tiles are 128 or 64 tokens high, the four
+// waves side by side across the weight rows (tile_bm).
 //
 // Global -> LDS: direct-to-LDS 16-byte loads (global_load_lds_dwordx4) into a
 // ring of NS stages of BK k-values; a stage's loads are issued NS-1 k-tiles
@@ -62,7 +64,6 @@ namespace tpmlp {
 
 namespace {
 
-constexpr int BM = 256;      // tokens per tile
 constexpr int BN = 256;      // weight rows per tile
 constexpr int GROUP_M = 4;
 
@@ -126,14 +127,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // Scheduling groups for one sub-step: its NMF MFMAs with NDS fragment reads
 // of the next sub-step threaded one after each of the first NDS MFMAs.
+// (More reads than MFMAs: the rest follow the last MFMA.)
 template <int NDS, int NMF>
 __device__ __forceinline__ void sched_substep() {
+  constexpr int P = NDS < NMF ? NDS : NMF;
 #pragma unroll
-  for (int i = 0; i < NDS; ++i) {
+  for (int i = 0; i < P; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NMF - NDS, 0);
+  if constexpr (NMF > P) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P, 0);
+  if constexpr (NDS > P) __builtin_amdgcn_sched_group_barrier(0x100, NDS - P, 0);
 }
 
 struct TileCoord {
@@ -181,7 +185,7 @@ struct SkTail {
 // the SK = false instance, which has no tail code: with it, the compiler
 // moves all accumulators out of AGPRs ahead of the tail branch and spills,
 // which slows every tile's epilogue.
-template <bool SWIGLU, int WB, int BK, int NS, int WV, bool OBF, bool A8, bool SK>
+template <bool SWIGLU, int WB, int BK, int NS, int WV, int BM, bool OBF, bool A8, bool SK>
 __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
     int M, int N, int K, const XRows xr,
     const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1, int64_t ldw,
@@ -190,9 +194,12 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   static_assert(A8 ? (BK == 128 && WB == kWeightE4M3) : (BK == 32 || BK == 64), "stage depth");
   static_assert(WV == 4 || WV == 8, "waves per workgroup");
   using XT = typename std::conditional<A8, uint8_t, uint16_t>::type;
-  constexpr int WN = WV / 2;                   // waves across the weight rows (2 across tokens)
+  static_assert(BM == 64 || BM == 128 || BM == 256, "tokens per tile");
+  constexpr int WM = BM == 256 ? 2 : 1;        // waves across the tokens
+  constexpr int WN = WV / WM;                  // waves across the weight rows
   constexpr int CB = BN / WN / 32;             // 32-row weight blocks per wave
-  constexpr int TB = BM / 2 / 32;              // 32-token blocks per wave
+  constexpr int TB = BM / WM / 32;             // 32-token blocks per wave
+  static_assert(CB >= 1 && (!SWIGLU || CB % 2 == 0), "weight blocks per wave");
   constexpr int EB = WB ? 1 : 2;              // weight bytes per element
   constexpr int XE = A8 ? 1 : 2;               // activation bytes per element
   constexpr int KSUB = BK / (A8 ? 64 : 16);    // MFMA sub-steps per stage
@@ -278,7 +285,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
   // flight one k-tile before its own loads, which find the lines in L2.
   // (with 8 waves the upper 256 threads touch the same lines again)
   const int trow = tid & 255;
-  const uint8_t* tx = reinterpret_cast<const uint8_t*>(x_row<XT>(xr, min(m0 + trow, M - 1)));
+  const uint8_t* tx = reinterpret_cast<const uint8_t*>(x_row<XT>(xr, min(m0 + (tid & (BM - 1)), M - 1)));
   const uint8_t* tw;
   if constexpr (SWIGLU)
     tw = (trow < BN / 2 ? w0 : w1) + (int64_t)min(n0 + (trow & (BN / 2 - 1)), N - 1) * ldw * EB;
@@ -311,7 +318,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
       wrow[cb] = wn * (BN / WN) + cb * 32 + r32;
   }
 #pragma unroll
-  for (int tb = 0; tb < TB; ++tb) xrow[tb] = wm * (BM / 2) + tb * 32 + r32;
+  for (int tb = 0; tb < TB; ++tb) xrow[tb] = wm * (BM / WM) + tb * 32 + r32;
 
   f32x16 acc[CB][TB];
 #pragma unroll
@@ -546,7 +553,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-          const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
+          const int tok = m0 + wm * (BM / WM) + tb * 32 + r32;
           if (tok >= M) continue;
           const float st = A8 ? sx[tok] : 1.f;
           float a[4];
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-          const int tok = m0 + wm * (BM / 2) + tb * 32 + r32;
+          const int tok = m0 + wm * (BM / WM) + tb * 32 + r32;
           if (tok >= M) continue;
           f32x4 v;
 #pragma unroll
@@ -635,7 +642,7 @@ struct SkPlan {
   int64_t cnt_bytes = 0, bytes = 0;   // counters; counters + slots
 };
 
-SkPlan sk_plan(int tiles, int KT) {
+SkPlan sk_plan(int tiles, int KT, int bm) {
   SkPlan p;
   const int rem = tiles % kSkCUs;
   if (rem == 0) return p;
@@ -653,13 +660,49 @@ SkPlan sk_plan(int tiles, int KT) {
   p.rem = rem;
   p.d = best_d;
   p.cnt_bytes = ((int64_t)rem * 4 + 255) / 256 * 256;
-  p.bytes = p.cnt_bytes + (int64_t)rem * best_d * BM * BN * 4;
+  p.bytes = p.cnt_bytes + (int64_t)rem * best_d * bm * BN * 4;
   return p;
 }
 
-int gemm_tiles(bool swiglu, int M, int N) {
-  const int tn = swiglu ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN;
-  return ((M + BM - 1) / BM) * tn;
+int tiles_n_of(bool swiglu, int N) { return swiglu ? (N + BN / 2 - 1) / (BN / 2) : (N + BN - 1) / BN; }
+
+int gemm_tiles(bool swiglu, int M, int N, int bm) { return ((M + bm - 1) / bm) * tiles_n_of(swiglu, N); }
+
+// Tokens per tile (64, 128 or 256) for M tokens, tiles_n tile columns and
+// KT k-tiles.  A tile costs its CU the same time whatever share of its rows
+// holds tokens, so at a few hundred tokens the 256-token tiles are mostly
+// padding, and too few of them to fill the chip; the smaller tiles (all
+// waves across the weight rows) waste less but read more LDS per MFMA.  When
+// the 256-token tiles fill three quarters of a round of the CUs or more they
+// are kept; otherwise the height with the least modelled time (whole rounds
+// of kSkCUs tiles plus the stream-K tail) is taken, the taller one on a tie,
+// with a k-tile of a 64- or 128-token tile costing 0.34 or 0.52 of a
+// 256-token one (fitted to gate/up and down timings of the 70B shard, bf16
+// and fp8 weights, 65 to 2048 tokens: the chosen height's time is 0.6 % above
+// the best one's on average, 14 % at most).
+#ifndef TPMLP_PREFILL_FORCE_BM
+#define TPMLP_PREFILL_FORCE_BM 0
+#endif
+int tile_bm(int M, int tiles_n, int KT) {
+  if (TPMLP_PREFILL_FORCE_BM) return TPMLP_PREFILL_FORCE_BM;
+  if ((int64_t)((M + 255) / 256) * tiles_n * 4 >= kSkCUs * 3) return 256;
+  constexpr int kHeights[3] = {256, 128, 64};
+  constexpr int kCost[3] = {100, 52, 34};   // per k-tile, relative
+  int best_bm = 256;
+  int64_t best = -1;
+  for (int i = 0; i < 3; ++i) {
+    const int bm = kHeights[i];
+    const int tiles = ((M + bm - 1) / bm) * tiles_n;
+    const SkPlan p = sk_plan(tiles, KT, bm);
+    const int64_t tail =
+        tiles % kSkCUs == 0 ? 0 : p.d ? (KT + p.d - 1) / p.d + kSkSlotCost * (p.d - 1) : (int64_t)KT;
+    const int64_t cost = kCost[i] * ((int64_t)(tiles / kSkCUs) * KT + tail);
+    if (best < 0 || cost < best) {
+      best = cost;
+      best_bm = bm;
+    }
+  }
+  return best_bm;
 }
 
 __global__ void sk_clear_kernel(int* __restrict__ cnt, int n) {
@@ -669,15 +712,15 @@ __global__ void sk_clear_kernel(int* __restrict__ cnt, int n) {
 // One GEMM launch: out = epilogue(rows of W (N of them; gate/up: N channels,
 // 2N weight rows) times the activation rows).  skws: stream-K scratch of
 // sk_plan(...).bytes, or null for whole tiles only.
-template <bool SWIGLU, int WB, int BK, int NS, bool OBF, bool A8>
-hipError_t run_gemm(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
-                    const float* s0, const float* s1, const float* sx, void* out, int64_t ldo, void* skws,
-                    hipStream_t stream) {
+template <bool SWIGLU, int WB, int BK, int NS, int BM, bool OBF, bool A8>
+hipError_t run_gemm_bm(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
+                       const float* s0, const float* s1, const float* sx, void* out, int64_t ldo, void* skws,
+                       hipStream_t stream) {
   const int tiles_m = (M + BM - 1) / BM;
-  const int tiles = gemm_tiles(SWIGLU, M, N);
+  const int tiles = gemm_tiles(SWIGLU, M, N, BM);
   SkTail sk{};
   unsigned grid = (unsigned)tiles;
-  const SkPlan p = skws ? sk_plan(tiles, K / BK) : SkPlan{};
+  const SkPlan p = skws ? sk_plan(tiles, K / BK, BM) : SkPlan{};
   if (p.d) {
     sk.cnt = static_cast<int*>(skws);
     sk.part = reinterpret_cast<float*>(static_cast<uint8_t*>(skws) + p.cnt_bytes);
@@ -688,11 +731,29 @@ hipError_t run_gemm(int kind, int M, int N, int K, const XRows& xr, const void* 
     if (e != hipSuccess) return e;
   }
   if (p.d)
-    return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8, true>, dim3(grid), dim3(kWV * 64), 0, stream, M,
+    return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, BM, OBF, A8, true>, dim3(grid), dim3(kWV * 64), 0, stream, M,
                   N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m,
                   sk);
-  return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, OBF, A8, false>, dim3(grid), dim3(kWV * 64), 0, stream, M, N,
+  return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, BM, OBF, A8, false>, dim3(grid), dim3(kWV * 64), 0, stream, M, N,
                 K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
+}
+
+// One GEMM launch with the tile height for M tokens.
+template <bool SWIGLU, int WB, int BK, int NS, bool OBF, bool A8>
+hipError_t run_gemm(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
+                    const float* s0, const float* s1, const float* sx, void* out, int64_t ldo, void* skws,
+                    hipStream_t stream) {
+  switch (tile_bm(M, tiles_n_of(SWIGLU, N), K / BK)) {
+    case 64:
+      return run_gemm_bm<SWIGLU, WB, BK, NS, 64, OBF, A8>(kind, M, N, K, xr, w0, w1, ldw, s0, s1, sx, out, ldo, skws,
+                                                         stream);
+    case 128:
+      return run_gemm_bm<SWIGLU, WB, BK, NS, 128, OBF, A8>(kind, M, N, K, xr, w0, w1, ldw, s0, s1, sx, out, ldo, skws,
+                                                          stream);
+    default:
+      return run_gemm_bm<SWIGLU, WB, BK, NS, 256, OBF, A8>(kind, M, N, K, xr, w0, w1, ldw, s0, s1, sx, out, ldo, skws,
+                                                          stream);
+  }
 }
 
 XRows single_rows(const void* p, int M, int64_t ld) {
@@ -718,7 +779,8 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
 }
 
 int64_t sk_bytes(bool swiglu, int M, int N, int K, int BK) {
-  return sk_plan(gemm_tiles(swiglu, M, N), K / BK).bytes;
+  const int bm = tile_bm(M, tiles_n_of(swiglu, N), K / BK);
+  return sk_plan(gemm_tiles(swiglu, M, N, bm), K / BK, bm).bytes;
 }
 
 }  // namespace

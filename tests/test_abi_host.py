@@ -54,6 +54,8 @@ BF16, F32, FP8 = _lib.TP_BF16, _lib.TP_F32, _lib.TP_FP8_E4M3FN
 
 
 SLOT = 256 * 256 * 4   # one stream-K piece's fp32 sums of a 256 x 256 tile
+SLOT64 = 64 * 256 * 4  # ... of a 64-token tile
+SLOT128 = 128 * 256 * 4
 
 
 def test_workspace_bytes():
@@ -71,9 +73,18 @@ def test_workspace_bytes():
     # take two rounds); at 2048 tokens 224 tiles (one round, a split saves under an eighth of it)
     assert lib.tp_mlp_workspace_bytes(4096, 8192, 28672, 8, BF16, BF16) == 4096 * 3584 * 2
     assert lib.tp_mlp_workspace_bytes(2048, 8192, 28672, 8, BF16, BF16) == 2048 * 3584 * 2
-    # just above the decode range: 28 gate/up tiles of 128 k-tiles cut in 5 pieces (counters: 256
-    # bytes); the larger of the two GEMMs' scratch
-    assert lib.tp_mlp_workspace_bytes(65, 8192, 28672, 8, BF16, BF16) == 65 * 3584 * 2 + 256 + 140 * SLOT
+    # just above the decode range the tiles are 64 tokens high: 2 x 28 gate/up tiles of 128
+    # k-tiles cut in 4 pieces (counters: 256 bytes), the larger of the two GEMMs' scratch
+    assert lib.tp_mlp_workspace_bytes(65, 8192, 28672, 8, BF16, BF16) == 65 * 3584 * 2 + 256 + 224 * SLOT64
+    # one-byte weights leave the decode kernels above 32 tokens: at 48, 28 gate/up tiles in 5
+    # pieces; bf16 weights stay on them (A only)
+    assert lib.tp_mlp_workspace_bytes(48, 8192, 28672, 8, BF16, FP8) == 48 * 3584 * 2 + 256 + 140 * SLOT64
+    assert lib.tp_mlp_workspace_bytes(48, 8192, 28672, 8, BF16, _lib.TP_INT8) == 48 * 3584 * 2 + 256 + 140 * SLOT64
+    assert lib.tp_mlp_workspace_bytes(32, 8192, 28672, 8, BF16, FP8) == 32 * 3584 * 2
+    assert lib.tp_mlp_workspace_bytes(48, 8192, 28672, 8, BF16, BF16) == 48 * 3584 * 2
+    # 600 tokens, h = I_s = 2048: gate/up in 128-token tiles (5 x 16, 2 pieces each: counters 512
+    # bytes, slots of 128 x 256 fp32), down in 64-token tiles (10 x 8, 2 pieces each)
+    assert lib.tp_mlp_workspace_bytes(600, 2048, 4096, 2, BF16, BF16) == 600 * 2048 * 2 + 512 + 160 * SLOT128
     # invalid arguments give 0
     assert lib.tp_mlp_workspace_bytes(1, 8192, 28672, 5, BF16, BF16) == 0       # I % t
     assert lib.tp_mlp_workspace_bytes(0, 8192, 28672, 8, BF16, BF16) == 0

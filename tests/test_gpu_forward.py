@@ -69,7 +69,7 @@ PREFILL_M = [65, 200, 256, 257, 300, 513]
 
 
 @pytest.mark.parametrize("M", DECODE_M + PREFILL_M)
-@pytest.mark.parametrize("w", ["bf16", "e4m3fn"])
+@pytest.mark.parametrize("w", ["bf16", "e4m3fn", "int8"])
 def test_small_shapes(M, w):
     # h = 320 (256-wide down tiles: 1 full + a ragged one), I_s = 192 (128-channel
     # gate/up tiles: 1 full + a ragged one)
@@ -78,7 +78,8 @@ def test_small_shapes(M, w):
     x, ws = make_case(40, M, h, I_s, "bf16", w, 0.05, 0.05, k=k, weight_set=M)
     d = upload_case(x, ws, "bf16", w)
     p = run_forward(d, t, k).cpu().numpy()
-    check(p, oracle_partial(x, ws, "bf16", w), TOL_FP8 if w == "e4m3fn" else TOL_BF16, "M=%d %s" % (M, w))
+    tol = {"bf16": TOL_BF16, "e4m3fn": TOL_FP8, "int8": TOL_INT8}[w]
+    check(p, oracle_partial(x, ws, "bf16", w), tol, "M=%d %s" % (M, w))
 
 
 @pytest.mark.parametrize("M", [1, 64, 300])
@@ -213,6 +214,7 @@ def test_config5_prefill_full():
     (300, 2112, 2112),   # both GEMMs: every tile cut along K in 2 uneven pieces (33 k-tiles); ragged tiles
     (65, 8192, 448),     # gate/up: 4 tiles (the last ragged) cut in 5 pieces; down whole
     (600, 1024, 4096),   # down: 12 tiles in 4 pieces; gate/up whole
+    (600, 2048, 2048),   # gate/up: 128-token tiles (5 x 16) in 2 pieces; down: 64-token tiles in 2 pieces
 ])
 @pytest.mark.parametrize("w", ["bf16", "e4m3fn", "int8"])
 def test_stream_k_tail(M, h, I_s, w):
