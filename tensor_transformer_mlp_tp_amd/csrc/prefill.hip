@@ -627,7 +627,8 @@ template <int WB>
 constexpr int kNS = WB ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
 
 // Stream-K plan (see SkTail), sized for MI355X's 256 CUs with one workgroup
-// per CU.  The pieces run as one round (rem * d <= 256): measured, further
+// per CU (the 64-token tiles of one-byte weights, 74 KB of LDS, fit two: the
+// plan is conservative there).  The pieces run as one round (rem * d <= 256): measured, further
 // rounds of pieces lose their gain to the slot stores and arrivals of every
 // round.  d minimises a piece's time, ceil(KT / d) k-tiles plus
 // kSkSlotCost k-tiles for each other slot its final sum may read, and the
