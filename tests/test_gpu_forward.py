@@ -208,6 +208,15 @@ def test_config5_prefill_full():
     _full_prefill(5, 8192)
 
 
+@pytest.mark.parametrize("cfg,M", [
+    (3, 300),    # 70B shard: both GEMMs on 128-token tiles, gate/up tiles in 3 stream-K pieces, down in 2
+    (3, 100),    # ... 64-token tiles (2 x 28 gate/up tiles in 4 pieces)
+    (4, 48),     # fp8 weights above 32 tokens: 64-token prefill tiles instead of the decode kernels
+])
+def test_full_shape_short_tiles(cfg, M):
+    _full_prefill(cfg, M)
+
+
 # ------------------------------------------------------------ stream-K tail of the prefill GEMMs
 
 @pytest.mark.parametrize("M,h,I_s", [
