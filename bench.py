@@ -70,6 +70,8 @@ def parse():
                              "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
+    ap.add_argument("--row-major", action="store_true",
+                    help="decode70b: read the weights in the (out, in) layout instead of packed for the decode kernels")
     return ap.parse_args()
 
 
@@ -167,9 +169,14 @@ class Phase:
         # arguments are marshalled once per weight set; the loop only re-issues the C calls
         key = id(wset)
         if key not in self.calls:
-            fwd = self.tp.prepare_shard_forward(self.x, wset["w_gate"], wset["w_up"], wset["w_down"], t=self.t,
-                                                k=0, s_gate=wset["s_gate"], s_up=wset["s_up"],
-                                                s_down=wset["s_down"], partial=self.partial, workspace=self.ws)
+            if wset.get("packed") is not None:
+                fwd = self.tp.prepare_shard_forward_packed(self.x, wset["packed"], k=0, s_gate=wset["s_gate"],
+                                                           s_up=wset["s_up"], s_down=wset["s_down"],
+                                                           partial=self.partial, workspace=self.ws)
+            else:
+                fwd = self.tp.prepare_shard_forward(self.x, wset["w_gate"], wset["w_up"], wset["w_down"],
+                                                    t=self.t, k=0, s_gate=wset["s_gate"], s_up=wset["s_up"],
+                                                    s_down=wset["s_down"], partial=self.partial, workspace=self.ws)
             # in place into the rank's own partial, as the all-reduce does
             red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others,
                                                  out=self.partial.view(-1)) if self.with_reduce else None
@@ -284,6 +291,10 @@ def bench_decode70b(tp, args):
     h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
     log("generating %d weight sets of the 70B TP=8 shard" % args.weight_sets)
     sets, host0 = device_weights(2, h, I_s, "bf16", c["std_gu"], c["std_down"], args.weight_sets)
+    if not args.row_major:
+        # the decode kernels' packed weight layout, written once per weight set
+        for d in sets:
+            d["packed"] = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
     phases = [Phase(tp, 2, M, h, I_s, t, "bf16", "bf16", True) for M in c["M"]]
     # An event-timed launch costs the host ~25 us against ~3 us for a plain
     # one; timing the gate/up launch of all three phases made the step
@@ -343,9 +354,10 @@ def bench_decode70b(tp, args):
     out = dict(metric=METRIC, value=round(value, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * elapsed / steps, 5), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16", data="synthetic",
-               config={"workload": "70B-shaped TP=8 rank decode (h=8192, I_s=3584, bf16 weights) at "
+               config={"workload": "70B-shaped TP=8 rank decode (h=8192, I_s=3584, bf16 weights%s) at "
                                    "M=1, 8 and 64 tokens, each forward followed by the 8-way fp32 "
-                                   "partial reduce",
+                                   "partial reduce" % (", (out, in) layout" if args.row_major else
+                                                       ", packed for the decode kernels"),
                        "M": list(c["M"]), "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
                roofline=roof,
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),

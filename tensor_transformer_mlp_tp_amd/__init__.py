@@ -200,6 +200,87 @@ def _prepare_forward(xs, sp, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, p
     return call
 
 
+class PackedWeights:
+    """A rank's three weight matrices packed for the decode kernels
+    (``tp_mlp_pack_weights``): ``data`` (uint8 on the weights' device) plus
+    the shapes and dtype code it was packed for."""
+
+    def __init__(self, data, h, I_s, t, w_code):
+        self.data, self.h, self.I_s, self.t, self.w_code = data, h, I_s, t, w_code
+
+
+def packed_weights_bytes(h, I_full, t, w_dtype=torch.bfloat16):
+    return int(_lib.load().tp_mlp_packed_weights_bytes(h, I_full, t, _w_code(w_dtype)))
+
+
+def pack_weights(w_gate, w_up, w_down, *, t, out=None, stream=None):
+    """Pack one rank's (out, in) weights for ``shard_forward_packed``; the
+    copy runs on the GPU, enqueued on ``stream``."""
+    device = w_gate.device
+    for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_matrix(name, m, device)
+    I_s, h = w_gate.shape
+    wc = _w_code(w_gate.dtype)
+    if _w_code(w_up.dtype) != wc or _w_code(w_down.dtype) != wc:
+        raise TypeError("w_gate, w_up and w_down must share a dtype")
+    if tuple(w_up.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s) or w_gate.stride(0) != w_up.stride(0):
+        raise ValueError("shard shapes must be w_gate/w_up (I_s, h) with one leading dimension and w_down (h, I_s)")
+    lib = _lib.load()
+    need = int(lib.tp_mlp_packed_weights_bytes(h, I_s * int(t), int(t), wc))
+    if need == 0:
+        _lib.check(_lib.TP_ERR_UNSUPPORTED)
+    if out is None:
+        out = alloc_workspace(need, device)
+    _lib.check(lib.tp_mlp_pack_weights(h, I_s * int(t), int(t), wc, _ptr(w_gate), _ptr(w_up), w_gate.stride(0),
+                                       _ptr(w_down), w_down.stride(0), _ptr(out), out.numel() * out.element_size(),
+                                       _stream_of(device, stream)))
+    return PackedWeights(out, h, I_s, int(t), wc)
+
+
+def shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down=None, partial=None, workspace=None,
+                         stream=None):
+    """``shard_forward`` at decode sizes with packed weights (bit-identical
+    partial); x (M, h) bf16."""
+    call = prepare_shard_forward_packed(x, packed, k=k, s_gate=s_gate, s_up=s_up, s_down=s_down, partial=partial,
+                                        workspace=workspace, stream=stream)
+    call()
+    return call.partial
+
+
+def prepare_shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down=None, partial=None,
+                                 workspace=None, stream=None):
+    device = x.device
+    _check_matrix("x", x, device)
+    if packed.data.device != device:
+        raise ValueError("packed weights must be on %s" % device)
+    M, h = x.shape
+    if h != packed.h:
+        raise ValueError("x has %d columns, the weights were packed for h = %d" % (h, packed.h))
+    for s in (s_gate, s_up, s_down):
+        if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
+            raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+    if partial is None:
+        partial = torch.empty((M, h), dtype=torch.float32, device=device)
+    else:
+        _check_matrix("partial", partial, device)
+        if partial.dtype != torch.float32 or tuple(partial.shape) != (M, h):
+            raise ValueError("partial must be float32 of shape (%d, %d)" % (M, h))
+    lib = _lib.load()
+    act = _act_code(x.dtype)
+    I_full = packed.I_s * packed.t
+    need = int(lib.tp_mlp_workspace_bytes(M, h, I_full, packed.t, act, packed.w_code))
+    if workspace is None:
+        workspace = alloc_workspace(max(need, 1), device)
+    elif workspace.device != device:
+        raise ValueError("workspace must be on %s" % device)
+    args = (M, h, I_full, packed.t, int(k), act, packed.w_code, _ptr(x), x.stride(0), _ptr(packed.data),
+            _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(partial), partial.stride(0), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_of(device, stream))
+    call = PreparedCall(lib.tp_mlp_shard_forward_packed, args, (x, packed, s_gate, s_up, s_down, partial, workspace))
+    call.partial = partial
+    return call
+
+
 def partial_reduce(partials, out=None, stream=None):
     """out = (((P_0 + P_1) + P_2) + ...) elementwise in fp32, fixed order.
 

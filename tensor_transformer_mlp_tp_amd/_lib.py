@@ -21,6 +21,9 @@ TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_WORKSPACE, TP_ERR_HIP = 0,
 EXPORTED_SYMBOLS = (
     "tp_mlp_workspace_bytes",
     "tp_mlp_shard_forward",
+    "tp_mlp_packed_weights_bytes",
+    "tp_mlp_pack_weights",
+    "tp_mlp_shard_forward_packed",
     "tp_partial_reduce",
     "tp_mlp_shard_forward_sp",
     "tp_partial_reduce_scatter",
@@ -77,6 +80,13 @@ def load():
     lib.tp_mlp_shard_forward_sp.restype = c_i32
     lib.tp_partial_reduce_scatter.argtypes = [c_i64, c_i64, c_i32, c_i32, ctypes.POINTER(vp), vp, vp]
     lib.tp_partial_reduce_scatter.restype = c_i32
+    lib.tp_mlp_packed_weights_bytes.argtypes = [c_i64, c_i64, c_i32, c_i32]
+    lib.tp_mlp_packed_weights_bytes.restype = ctypes.c_size_t
+    lib.tp_mlp_pack_weights.argtypes = [c_i64, c_i64, c_i32, c_i32, vp, vp, c_i64, vp, c_i64, vp, ctypes.c_size_t, vp]
+    lib.tp_mlp_pack_weights.restype = c_i32
+    lib.tp_mlp_shard_forward_packed.argtypes = [
+        c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, vp, c_i64, vp, vp, vp, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
+    lib.tp_mlp_shard_forward_packed.restype = c_i32
     lib.tp_mlp_w8a8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32]
     lib.tp_mlp_w8a8_workspace_bytes.restype = ctypes.c_size_t
     lib.tp_mlp_shard_forward_w8a8.argtypes = [

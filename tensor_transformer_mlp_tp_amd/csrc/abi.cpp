@@ -282,6 +282,128 @@ TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int3
                       ldw_down, s_gate, s_up, s_down, partial, ldp, workspace, workspace_bytes, stream);
 }
 
+// ------------------------------------------------------------ packed decode weights
+
+namespace {
+
+// Packed size for valid arguments, else 0 with the error message set.
+int64_t packed_need(int64_t h, int64_t I_full, int32_t t, int32_t w_dtype) {
+  if (check_shapes(1, h, I_full, t, 0, TP_BF16, w_dtype) != TP_OK) return 0;
+  const int wb = weight_format(w_dtype);
+  const int64_t I_s = I_full / t;
+  if (!tpmlp::decode_packable((int)h, (int)I_s, wb)) {
+    fail(TP_ERR_UNSUPPORTED, "packed weights need h and I_s multiples of %d (h=%lld, I_s=%lld)", wb ? 256 : 128,
+         (long long)h, (long long)I_s);
+    return 0;
+  }
+  return tpmlp::packed_gateup_bytes((int)h, (int)I_s, wb) + tpmlp::packed_down_bytes((int)h, (int)I_s, wb);
+}
+
+}  // namespace
+
+TP_API size_t tp_mlp_packed_weights_bytes(int64_t h, int64_t I_full, int32_t t, int32_t w_dtype) {
+  return (size_t)packed_need(h, I_full, t, w_dtype);
+}
+
+TP_API tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32_t w_dtype, const void* w_gate,
+                                     const void* w_up, int64_t ldw_gu, const void* w_down, int64_t ldw_down,
+                                     void* packed, size_t packed_bytes, void* stream) {
+  const int64_t need = packed_need(h, I_full, t, w_dtype);
+  if (need == 0) return TP_ERR_UNSUPPORTED;
+  const int64_t I_s = I_full / t;
+  if (!w_gate || !w_up || !w_down || !packed) return fail(TP_ERR_INVALID_ARG, "null pointer");
+  if (ldw_gu < h || ldw_down < I_s)
+    return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length (ldw_gu=%lld ldw_down=%lld)",
+                (long long)ldw_gu, (long long)ldw_down);
+  const int ew = elem_bytes(w_dtype);
+  if (!aligned(w_gate, 16) || !aligned(w_up, 16) || !aligned(w_down, 16) || !aligned(packed, 16) ||
+      (ldw_gu * ew) % 16 || (ldw_down * ew) % 16)
+    return fail(TP_ERR_UNSUPPORTED, "weights, their rows and the packed array must be 16-byte aligned");
+  if ((int64_t)packed_bytes < need)
+    return fail(TP_ERR_INVALID_ARG, "packed array of %lld bytes needed (got %llu)", (long long)need,
+                (unsigned long long)packed_bytes);
+  const Extent ek{reinterpret_cast<uintptr_t>(packed), reinterpret_cast<uintptr_t>(packed) + (uintptr_t)need};
+  if (overlap(ek, extent(w_gate, I_s, h, ldw_gu, ew)) || overlap(ek, extent(w_up, I_s, h, ldw_gu, ew)) ||
+      overlap(ek, extent(w_down, h, I_s, ldw_down, ew)))
+    return fail(TP_ERR_INVALID_ARG, "the packed array overlaps the weights");
+  tpmlp::ShardArgs a{};
+  a.h = (int)h;
+  a.I_s = (int)I_s;
+  a.wg = w_gate;
+  a.wu = w_up;
+  a.ldw_gu = ldw_gu;
+  a.wd = w_down;
+  a.ldw_down = ldw_down;
+  a.wb = weight_format(w_dtype);
+  return from_hip(tpmlp::launch_pack_weights(a, packed, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
+}
+
+TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                             int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
+                                             const void* packed, const float* s_gate, const float* s_up,
+                                             const float* s_down, float* partial, int64_t ldp, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  tp_status st = check_shapes(M, h, I_full, t, k, act_dtype, w_dtype);
+  if (st != TP_OK) return st;
+  if (act_dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "packed weights take bf16 activations");
+  const int wb = weight_format(w_dtype);
+  if (M > tpmlp::forward_decode_max_m(wb))
+    return fail(TP_ERR_UNSUPPORTED, "packed weights serve the decode kernels: M <= %d (got %lld)",
+                tpmlp::forward_decode_max_m(wb), (long long)M);
+  const int64_t pbytes = packed_need(h, I_full, t, w_dtype);
+  if (pbytes == 0) return TP_ERR_UNSUPPORTED;
+  const int64_t I_s = I_full / t;
+  if (!x || !packed || !partial) return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  const bool fp8 = scaled_weights(w_dtype);
+  if (fp8 && (!s_gate || !s_up || !s_down))
+    return fail(TP_ERR_INVALID_ARG, "one-byte weights need s_gate, s_up and s_down");
+  if (!fp8 && (s_gate || s_up || s_down))
+    return fail(TP_ERR_INVALID_ARG, "scales are only accepted with one-byte weights");
+  if (ldx < h || ldp < h)
+    return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length (ldx=%lld ldp=%lld)",
+                (long long)ldx, (long long)ldp);
+  const int64_t need = workspace_need(M, h, I_s, act_dtype, w_dtype);
+  if (!workspace || (int64_t)workspace_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
+                (unsigned long long)workspace_bytes);
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(partial, 16) || (ldx * 2) % 16 || (ldp * 4) % 16)
+    return fail(TP_ERR_UNSUPPORTED, "tensor pointers and rows must be 16-byte aligned");
+  if (fp8 && (!aligned(s_gate, 4) || !aligned(s_up, 4) || !aligned(s_down, 4)))
+    return fail(TP_ERR_UNSUPPORTED, "scale pointers must be 4-byte aligned");
+  if (!aligned(workspace, 256)) return fail(TP_ERR_UNSUPPORTED, "workspace must be 256-byte aligned");
+  const Extent ep = extent(partial, M, h, ldp, 4), ex = extent(x, M, h, ldx, 2);
+  const Extent ek{reinterpret_cast<uintptr_t>(packed), reinterpret_cast<uintptr_t>(packed) + (uintptr_t)pbytes};
+  const Extent ewk{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)need};
+  if (overlap(ep, ex) || overlap(ep, ek) || overlap(ep, ewk))
+    return fail(TP_ERR_INVALID_ARG, "partial overlaps an input or the workspace");
+  if (overlap(ewk, ex) || overlap(ewk, ek)) return fail(TP_ERR_INVALID_ARG, "workspace overlaps an input");
+
+  tpmlp::ShardArgs a{};
+  a.M = (int)M;
+  a.h = (int)h;
+  a.I_s = (int)I_s;
+  a.x.p[0] = x;
+  a.x.nb = 1;
+  a.x.rows = (int)M;
+  a.x.ld = ldx;
+  a.wb = wb;
+  a.packed = true;
+  a.wg = packed;
+  a.wu = nullptr;
+  a.ldw_gu = h;
+  a.wd = static_cast<const uint8_t*>(packed) + tpmlp::packed_gateup_bytes((int)h, (int)I_s, wb);
+  a.ldw_down = I_s;
+  a.sg = s_gate;
+  a.su = s_up;
+  a.sd = s_down;
+  a.p = partial;
+  a.ldp = ldp;
+  a.a = workspace;
+  a.lda = I_s;
+  a.sk = nullptr;
+  return from_hip(tpmlp::launch_forward_decode(a, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
+}
+
 TP_API tp_status tp_mlp_shard_forward_sp(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
                                          int32_t act_dtype, int32_t w_dtype, const void* const* x_blocks,
                                          int64_t ldx, const void* w_gate, const void* w_up, int64_t ldw_gu,

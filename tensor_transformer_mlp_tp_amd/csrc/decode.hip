@@ -339,9 +339,10 @@ __device__ __forceinline__ void wait_slot_peeled(int j) {
 // Stream slots j_beg, j_beg + jstep, ... (nsl of them) of this wave's RB
 // row blocks through its ring and accumulate the MFMAs.  dsrc[rb][i]: this
 // lane's source for direct-load instruction i of block rb in slot 0 (row
-// 4i + lane/16, pre-swizzled chunk); slot j adds j*256 bytes.  xrow/xok:
-// activation rows of the NT token blocks.
-template <int NT, int RB, int WB, int S>
+// 4i + lane/16, pre-swizzled chunk); slot j adds j*JS bytes (256 in the
+// row-major layout, 4096 in the packed one).  xrow/xok: activation rows of
+// the NT token blocks.
+template <int NT, int RB, int WB, int S, int JS>
 __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                             const uint8_t* const (&dsrc)[RB][4],
                                             const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
@@ -359,7 +360,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * 256, dst + rb * 4096 + i * 1024);
+      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * JS, dst + rb * 4096 + i * 1024);
   };
   auto load_x = [&](int j, u32x4 (&xf)[STEPS][NT]) {
 #pragma unroll
@@ -443,7 +444,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
 // with more than 16 tokens that doubled line traffic, not the weight stream,
 // is what bounds the kernel.  xsrc[b][i]: this lane's source for activation
 // load i of token block b in slot 0; slot j adds j * 2*KS bytes.
-template <int NT, int RB, int WB, int S>
+template <int NT, int RB, int WB, int S, int JS>
 __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                                const uint8_t* const (&dsrc)[RB][4],
                                                const uint8_t* const (&xsrc)[NT][WB ? 8 : 4],
@@ -464,7 +465,7 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * 256, dst + rb * 4096 + i * 1024);
+      for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * JS, dst + rb * 4096 + i * 1024);
 #pragma unroll
     for (int b = 0; b < NT; ++b)
 #pragma unroll
@@ -538,6 +539,18 @@ __device__ __forceinline__ void stream_sources(const uint8_t* (&dsrc)[4], int la
   }
 }
 
+// Packed weights (pack_kernel below): slot j of 16-row block blk is the 4 KB
+// at (blk * nslots + j) * 4096, already in the ring's order, so load i of
+// the slot is its i-th kilobyte and lane l takes bytes [16 l, 16 l + 16).
+// (Gate and up rows of a slot kept in two separate regions, 2 KB each, were
+// measured no different.)
+constexpr int kPackJS = 4096;   // bytes between a block's consecutive slots
+__device__ __forceinline__ void packed_sources(const uint8_t* (&dsrc)[4], const uint8_t* packed, int blk,
+                                               int nslots, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) dsrc[i] = packed + (int64_t)blk * nslots * kPackJS + i * 1024 + lane * 16;
+}
+
 // Cross-wave sum for the streaming kernels: like reduce_waves, but through
 // the (no longer needed) ring memory instead of a separate LDS array.
 template <int NT, int RB, int WAVES, typename Epi>
@@ -581,7 +594,8 @@ struct StreamShape {
   static_assert(RING <= 160 * 1024, "LDS");
 };
 
-template <int NT, int RB, int WB, bool XD>
+// PK: wg is the packed gate/up array (wu, ldw unused).
+template <int NT, int RB, int WB, bool XD, bool PK>
 __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup_stream_kernel(
     int M, int h, int I_s, const XRows xr,
     const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu, int64_t ldw,
@@ -598,11 +612,16 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
   // row block rb: rows 0-7 gate channels c0+8rb..+7, rows 8-15 the same channels' up rows
   const uint8_t* dsrc[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-    stream_sources(dsrc[rb], lane, [&](int row) {
-      const int ch = min(c0 + 8 * rb + (row & 7), I_s - 1);
-      return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
-    });
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (PK)
+      packed_sources(dsrc[rb], wg, min(c0 / 8 + rb, (I_s + 7) / 8 - 1), h / KS, lane);
+    else
+      stream_sources(dsrc[rb], lane, [&](int row) {
+        const int ch = min(c0 + 8 * rb + (row & 7), I_s - 1);
+        return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
+      });
+  }
+  constexpr int JS = PK ? kPackJS : 256;
   int j_beg, nsl, jstep;
   wave_slots<SS::WV>(h / KS, wave, j_beg, nsl, jstep);
   bool xok[NT];
@@ -617,12 +636,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
   if constexpr (XD) {
     const uint8_t* xsrc[NT][WB ? 8 : 4];
     stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return x_row<uint16_t>(xr, min(tok, M - 1)); });
-    stream_rows_xd<NT, RB, WB, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    stream_rows_xd<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = x_row<uint16_t>(xr, min(b * 16 + row16, M - 1));
-    stream_rows<NT, RB, WB, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -656,7 +675,8 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
 // seg_out[y] (M x h, dense); splitk_finish_kernel adds the nseg ranges in
 // order.  Skinny outputs (few 16-row blocks, long K) need it to keep enough
 // loads in flight across the chip.
-template <int NT, int RB, int WB, bool XD, bool OBF>
+// PK: wd is the packed array of the N x K weights (ldw unused).
+template <int NT, int RB, int WB, bool XD, bool OBF, bool PK>
 __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
@@ -669,13 +689,18 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_s
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row16 = lane & 15, grp = lane >> 4;
   const int n0 = blockIdx.x * 16 * RB;
+  const int nslots = I_s / KS;
   const uint8_t* dsrc[RB][4];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-    stream_sources(dsrc[rb], lane,
-                   [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
+  for (int rb = 0; rb < RB; ++rb) {
+    if constexpr (PK)
+      packed_sources(dsrc[rb], wd, min(n0 / 16 + rb, (h + 15) / 16 - 1), nslots, lane);
+    else
+      stream_sources(dsrc[rb], lane,
+                     [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
+  }
+  constexpr int JS = PK ? kPackJS : 256;
   int j_beg, nsl, jstep;
-  const int nslots = I_s / KS;
   const int seg = blockIdx.y;
   const int s0 = (int)((int64_t)seg * nslots / nseg);
   const int s1 = (int)((int64_t)(seg + 1) * nslots / nseg);
@@ -693,12 +718,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_s
   if constexpr (XD) {
     const uint8_t* xsrc[NT][WB ? 8 : 4];
     stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return a_in + (int64_t)min(tok, M - 1) * lda; });
-    stream_rows_xd<NT, RB, WB, SS::S>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    stream_rows_xd<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = a_in + (int64_t)min(b * 16 + row16, M - 1) * lda;
-    stream_rows<NT, RB, WB, SS::S>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -812,9 +837,13 @@ hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
   constexpr int RB = NT == 1 ? (WB ? TPMLP_DECODE_RB_NT1_BYTE : 1)
                              : (XD && WB ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
-  return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD>, dim3((a.I_s + 8 * RB - 1) / (8 * RB)),
-                dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, a.M, a.h, a.I_s, a.x,
-                (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+  const dim3 grid((a.I_s + 8 * RB - 1) / (8 * RB)), block(StreamShape<NT, RB, WB, XD>::WV * 64);
+  if (a.packed)
+    return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD, true>, grid, block, 0, stream, a.M, a.h,
+                  a.I_s, a.x, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a,
+                  a.lda);
+  return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD, false>, grid, block, 0, stream, a.M, a.h,
+                a.I_s, a.x, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
 }
 
 template <int NT, int WB>
@@ -856,10 +885,12 @@ int stream_splits(int N, int K) {
 template <int NT, int RB, int WB, bool OBF>
 hipError_t rowgemm_stream_launch(const RowGemm& g, int nseg, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
-  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg);
-  return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF>, grid,
-                dim3(StreamShape<NT, RB, WB, XD>::WV * 64), 0, stream, g.M, g.N, g.K, (const uint16_t*)g.a, g.lda,
-                (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
+  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg), block(StreamShape<NT, RB, WB, XD>::WV * 64);
+  if (g.packed)
+    return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, true>, grid, block, 0, stream, g.M, g.N,
+                  g.K, (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
+  return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, false>, grid, block, 0, stream, g.M, g.N,
+                g.K, (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
 }
 
 template <int NT, int WB, bool OBF>
@@ -891,6 +922,7 @@ constexpr bool streams(int K) {
 template <int WB>
 hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
   const bool st = streams<WB>(a.h);
+  if (a.packed && !st) return hipErrorInvalidValue;   // packed weights are read by the streams only
   switch ((a.M + 15) / 16) {
     case 1: return st ? gateup_stream<1, WB>(a, stream) : gateup_v1<1, WB>(a, stream);
     case 2: return st ? gateup_stream<2, WB>(a, stream) : gateup_v1<2, WB>(a, stream);
@@ -903,6 +935,7 @@ hipError_t run_gateup(const ShardArgs& a, hipStream_t stream) {
 template <int WB, bool OBF>
 hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   const bool st = streams<WB>(g.K);
+  if (g.packed && !st) return hipErrorInvalidValue;
   switch ((g.M + 15) / 16) {
     case 1: return st ? rowgemm_stream<1, WB, OBF>(g, stream) : rowgemm_v1<1, WB, OBF>(g, stream);
     case 2: return st ? rowgemm_stream<2, WB, OBF>(g, stream) : rowgemm_v1<2, WB, OBF>(g, stream);
@@ -972,7 +1005,7 @@ int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {
 }
 
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
-  if (use_gemv(g.M, g.N, g.K, g.wb)) return launch_rowgemm_gemv(g, stream);
+  if (!g.packed && use_gemv(g.M, g.N, g.K, g.wb)) return launch_rowgemm_gemv(g, stream);
   switch (g.wb) {
     case kWeightE4M3: return rowgemm_wb<kWeightE4M3>(g, stream);
     case kWeightI8: return rowgemm_wb<kWeightI8>(g, stream);
@@ -989,6 +1022,68 @@ hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream) {
   }
   if (e != hipSuccess) return e;
   return launch_rowgemm_decode(down_of(a), stream);
+}
+
+// ---------------------------------------------------------------- packed weights
+// The streams read each 16-row block of W slot by slot (256 bytes of each of
+// the 16 rows per slot), which in the (out, in) layout is 16 pieces 16 KB
+// apart (70B shard); a read pattern like that runs at about 4.9 TB/s on
+// MI355X against 6.3 TB/s for the same bytes read in address order.  The
+// packed array stores every slot as the 4 KB the ring holds (rows 4i..4i+3 in
+// the i-th kilobyte, 16-byte chunks XOR-swizzled by row), slot after slot,
+// block after block, so each workgroup streams one contiguous range.  Gate/up
+// blocks hold 8 gate rows then the same 8 channels' up rows; rows past the
+// end repeat the last row, as the row-major streams clamp.  The values and
+// the order of every load into the ring are those of the row-major path.
+
+namespace {
+
+// One thread per 16 bytes of the packed array of nblk blocks x nslots slots;
+// GU: rows 0-7 of a block from w0 (channels 8 blk + r), 8-15 from w1.
+template <bool GU>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
+                                                   int64_t ld_bytes, int nrows, int nslots, int64_t nchunks,
+                                                   uint8_t* __restrict__ out) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (q >= nchunks) return;
+  const int64_t blk = q / ((int64_t)nslots * 256);
+  const int within = (int)(q - blk * nslots * 256);
+  const int j = within >> 8, i = (within >> 6) & 3, lane = within & 63;
+  const int row = 4 * i + (lane >> 4);
+  const int c = (lane & 15) ^ row;
+  const uint8_t* src;
+  if constexpr (GU)
+    src = (row < 8 ? w0 : w1) + min((int64_t)8 * blk + (row & 7), (int64_t)nrows - 1) * ld_bytes;
+  else
+    src = w0 + min((int64_t)16 * blk + row, (int64_t)nrows - 1) * ld_bytes;
+  *reinterpret_cast<u32x4*>(out + q * 16) = *reinterpret_cast<const u32x4*>(src + (int64_t)j * 256 + c * 16);
+}
+
+}  // namespace
+
+bool decode_packable(int h, int I_s, int wb) {
+  const int ks = wb ? 256 : 128;
+  return h % ks == 0 && I_s % ks == 0;
+}
+
+int64_t packed_gateup_bytes(int h, int I_s, int wb) {
+  return (int64_t)((I_s + 7) / 8) * (h / (wb ? 256 : 128)) * 4096;
+}
+
+int64_t packed_down_bytes(int h, int I_s, int wb) {
+  return (int64_t)((h + 15) / 16) * (I_s / (wb ? 256 : 128)) * 4096;
+}
+
+hipError_t launch_pack_weights(const ShardArgs& a, void* packed, hipStream_t stream) {
+  const int eb = a.wb ? 1 : 2, ks = a.wb ? 256 : 128;
+  uint8_t* gu = static_cast<uint8_t*>(packed);
+  uint8_t* dn = gu + packed_gateup_bytes(a.h, a.I_s, a.wb);
+  const int64_t c_gu = packed_gateup_bytes(a.h, a.I_s, a.wb) / 16, c_dn = packed_down_bytes(a.h, a.I_s, a.wb) / 16;
+  hipError_t e = launch(-1, pack_kernel<true>, dim3((unsigned)((c_gu + 255) / 256)), dim3(256), 0, stream,
+                        (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu * eb, a.I_s, a.h / ks, c_gu, gu);
+  if (e != hipSuccess) return e;
+  return launch(-1, pack_kernel<false>, dim3((unsigned)((c_dn + 255) / 256)), dim3(256), 0, stream,
+                (const uint8_t*)a.wd, (const uint8_t*)nullptr, a.ldw_down * eb, a.h, a.I_s / ks, c_dn, dn);
 }
 
 }  // namespace tpmlp

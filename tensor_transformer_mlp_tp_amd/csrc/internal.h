@@ -81,6 +81,7 @@ struct ShardArgs {
   int64_t lda;
   int wb;                   // weight format: kWeightWide / kWeightE4M3 / kWeightI8
   void* sk;                 // prefill stream-K scratch (forward_prefill_sk_bytes), or null
+  bool packed = false;      // decode only: wg = packed gate/up array, wd = packed down array
 };
 
 // out (M x N) = A (M x K) * W^T with W (N x K, (out, in) layout), fp32
@@ -99,7 +100,16 @@ struct RowGemm {
   int wb;                   // weight format (kWeight*)
   float* ws;                // decode: split-K sums; prefill: stream-K scratch (null: neither), 256-byte aligned
   int kind_decode, kind_prefill, kind_f32;  // timing kinds of the three paths
+  bool packed = false;      // decode streams only: w is a packed array
 };
+
+// Packed decode weights (decode.hip): both GEMMs' K a multiple of the
+// streams' slot (128 k bf16, 256 k one-byte); the gate/up array, then the
+// down array; one pass of pack kernels from the (out, in) weights.
+bool decode_packable(int h, int I_s, int wb);
+int64_t packed_gateup_bytes(int h, int I_s, int wb);
+int64_t packed_down_bytes(int h, int I_s, int wb);
+hipError_t launch_pack_weights(const ShardArgs& a, void* packed, hipStream_t stream);
 
 // Largest M served by the weight-streaming (decode) kernels.
 constexpr int kDecodeMaxM = 64;
@@ -120,7 +130,7 @@ inline RowGemm down_of(const ShardArgs& s) {
   g.a = s.a; g.lda = s.lda;
   g.w = s.wd; g.ldw = s.ldw_down; g.s = s.sd;
   g.out = s.p; g.ldo = s.ldp;
-  g.out_bf16 = false; g.wb = s.wb; g.ws = nullptr;
+  g.out_bf16 = false; g.wb = s.wb; g.ws = nullptr; g.packed = s.packed;
   g.kind_decode = K_DOWN_DECODE; g.kind_prefill = K_DOWN_PREFILL; g.kind_f32 = K_DOWN_F32;
   return g;
 }

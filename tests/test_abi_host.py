@@ -391,3 +391,31 @@ def test_quantize_rows_rejects(args, status):
 
 def test_quantize_rows_empty_is_noop():
     assert _lib.load().tp_quantize_rows_e4m3(0, 16, None, 16, None, 16, None, None) == _lib.TP_OK
+
+
+def test_packed_weights_bytes_and_validation():
+    lib = _lib.load()
+    # the three matrices' bytes: 70B TP=8 bf16, TP=4 fp8
+    assert lib.tp_mlp_packed_weights_bytes(8192, 28672, 8, BF16) == 3 * 3584 * 8192 * 2
+    assert lib.tp_mlp_packed_weights_bytes(8192, 28672, 4, FP8) == 3 * 7168 * 8192
+    assert lib.tp_mlp_packed_weights_bytes(512, 1024, 2, _lib.TP_INT8) == 3 * 512 * 512
+    assert lib.tp_mlp_packed_weights_bytes(320, 512, 2, BF16) == 0          # h % 128
+    assert lib.tp_mlp_packed_weights_bytes(512, 768, 2, FP8) == 0           # I_s = 384: % 256
+    assert lib.tp_mlp_packed_weights_bytes(512, 1024, 2, F32) == 0          # fp32 weights
+    # forward: decode sizes and bf16 activations only; checked before any HIP call
+    def fwdp(M=1, h=512, I=1024, t=2, act=BF16, w=BF16, packed=P, sc=None):
+        return lib.tp_mlp_shard_forward_packed(M, h, I, t, 0, act, w, P, h, packed, sc, sc, sc, P * 8, h,
+                                               P * 16, 1 << 20, None)
+    assert fwdp(M=65) == _lib.TP_ERR_UNSUPPORTED
+    assert fwdp(M=33, w=FP8, sc=P) == _lib.TP_ERR_UNSUPPORTED
+    assert fwdp(act=F32, w=F32) == _lib.TP_ERR_UNSUPPORTED
+    assert fwdp(packed=None) == _lib.TP_ERR_INVALID_ARG
+    assert fwdp(w=FP8) == _lib.TP_ERR_INVALID_ARG                            # scales missing
+    assert fwdp(h=320) == _lib.TP_ERR_UNSUPPORTED
+    # pack: null pointers, short leading dimensions, a short array
+    assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, None, P, 512, P, 512, P * 8, 1 << 22, None) == \
+        _lib.TP_ERR_INVALID_ARG
+    assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, P, P * 2, 256, P * 3, 512, P * 8, 1 << 22, None) == \
+        _lib.TP_ERR_INVALID_ARG
+    assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, P, P * 2, 512, P * 3, 512, P * 64, 1024, None) == \
+        _lib.TP_ERR_INVALID_ARG

@@ -1,0 +1,114 @@
+"""Packed decode weights: the layout, and the packed forward against the
+row-major forward (bit-identical) and the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import tensor_transformer_mlp_tp_amd as tp
+from tensor_transformer_mlp_tp_amd import _lib
+from helpers import TOL_BF16, TOL_FP8, TOL_INT8, make_case, upload_case, oracle_partial
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": TOL_BF16, "e4m3fn": TOL_FP8, "int8": TOL_INT8}
+
+
+def host_packed(ws, I_s, h):
+    """The packed array written out from its documented layout: 4 KB slots of
+    16 rows x 256 bytes, rows 4i..4i+3 in kilobyte i, lane l of a kilobyte
+    holding logical 16-byte chunk (l % 16) ^ row of row 4i + l // 16; gate/up
+    blocks of 8 gate then 8 up rows, then down blocks of 16 rows; rows past
+    the end repeat the last one."""
+    def rows_bytes(a):
+        a = np.ascontiguousarray(a)
+        return a.view(np.uint8).reshape(a.shape[0], -1)
+
+    g, u, d = rows_bytes(ws["w_gate"]), rows_bytes(ws["w_up"]), rows_bytes(ws["w_down"])
+    i = np.arange(4)[:, None]
+    lane = np.arange(64)[None, :]
+    row = 4 * i + lane // 16                     # (4, 64)
+    chunk = (lane % 16) ^ row
+
+    def blocks(src_of_row, nblk, nslots):
+        out = np.empty((nblk, nslots, 4, 64, 16), dtype=np.uint8)
+        for b in range(nblk):
+            src = src_of_row(b)                  # (16, row bytes)
+            for j in range(nslots):
+                seg = src[:, j * 256:(j + 1) * 256].reshape(16, 16, 16)
+                out[b, j] = seg[row, chunk]
+        return out.reshape(-1)
+
+    slot_k = 256 // (g.shape[1] // h)            # k-values per 256-byte slot row
+    gu = blocks(lambda b: np.concatenate([g[np.minimum(8 * b + np.arange(8), I_s - 1)],
+                                          u[np.minimum(8 * b + np.arange(8), I_s - 1)]]),
+                (I_s + 7) // 8, h // slot_k)
+    dn = blocks(lambda b: d[np.minimum(16 * b + np.arange(16), h - 1)], (h + 15) // 16, I_s // slot_k)
+    return np.concatenate([gu, dn])
+
+
+@pytest.mark.parametrize("w,h,I_s", [("bf16", 256, 384), ("e4m3fn", 512, 256), ("int8", 256, 512)])
+def test_pack_layout(w, h, I_s):
+    t = 2
+    print("pack layout w=%s h=%d I_s=%d" % (w, h, I_s), flush=True)
+    x, ws = make_case(60, 1, h, I_s, "bf16", w, 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", w)
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    torch.cuda.synchronize()
+    assert pk.data.numel() == tp.packed_weights_bytes(h, I_s * t, t, d["w_gate"].dtype)
+    assert np.array_equal(pk.data.cpu().numpy(), host_packed(ws, I_s, h))
+
+
+CASES = [(M, w) for w in ("bf16", "e4m3fn", "int8") for M in (1, 2, 5, 16, 17, 32, 33, 48, 64)]
+
+
+@pytest.mark.parametrize("M,w", CASES)
+def test_packed_forward_small(M, w):
+    # h = 512, I_s = 512: 64 gate/up blocks, 32 down blocks, 2 to 4 slots per wave
+    h, I_s, t, k = 512, 512, 2, 1
+    print("packed forward M=%d w=%s" % (M, w), flush=True)
+    x, ws = make_case(61, M, h, I_s, "bf16", w, 0.05, 0.05, k=k, weight_set=M)
+    d = upload_case(x, ws, "bf16", w)
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    if w != "bf16" and M > 32:
+        with pytest.raises(_lib.TPError):
+            tp.shard_forward_packed(d["x"], pk, k=k, s_gate=d["s_gate"], s_up=d["s_up"], s_down=d["s_down"])
+        return
+    p = tp.shard_forward_packed(d["x"], pk, k=k, s_gate=d["s_gate"], s_up=d["s_up"], s_down=d["s_down"])
+    ref = tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=k, s_gate=d["s_gate"],
+                           s_up=d["s_up"], s_down=d["s_down"])
+    torch.cuda.synchronize()
+    assert torch.equal(p.view(torch.int32), ref.view(torch.int32))
+    err = oracle.rms_normalised_max_error(p.cpu().numpy(), oracle_partial(x, ws, "bf16", w))
+    print("  err=%.3e" % err, flush=True)
+    assert err <= TOL[w]
+
+
+@pytest.mark.parametrize("M", [1, 8, 64])
+def test_packed_forward_70b(M):
+    """70B TP = 8 shard (h = 8192, I_s = 3584), the decode sizes of the bench."""
+    h, I_s, t = 8192, 3584, 8
+    print("packed forward 70B M=%d" % M, flush=True)
+    x, ws = make_case(2, M, h, I_s, "bf16", "bf16", 0.02, 0.02, weight_set=M)
+    d = upload_case(x, ws, "bf16", "bf16")
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    p = tp.shard_forward_packed(d["x"], pk, k=0)
+    ref = tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0)
+    torch.cuda.synchronize()
+    assert torch.equal(p.view(torch.int32), ref.view(torch.int32))
+    err = oracle.rms_normalised_max_error(p.cpu().numpy(), oracle_partial(x, ws, "bf16", "bf16"))
+    assert err <= TOL_BF16
+
+
+def test_packed_rejects():
+    h, I_s, t = 256, 384, 2
+    x, ws = make_case(62, 65, h, I_s, "bf16", "bf16", 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", "bf16")
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    with pytest.raises(_lib.TPError, match="decode"):
+        tp.shard_forward_packed(d["x"], pk, k=0)          # 65 tokens: not a decode size
+    small = tp.alloc_workspace(1024, "cuda")
+    lib = _lib.load()
+    st = lib.tp_mlp_pack_weights(h, I_s * t, t, _lib.TP_BF16, d["w_gate"].data_ptr(), d["w_up"].data_ptr(), h,
+                                 d["w_down"].data_ptr(), I_s, small.data_ptr(), 1024, None)
+    assert st == _lib.TP_ERR_INVALID_ARG                  # too small
