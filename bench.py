@@ -449,10 +449,14 @@ def bench_quant(tp, args, cfg_id):
     sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
     decs = [Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, False) for M in dec_Ms]
     pre = Phase(tp, cfg_id, pre_M, h, I_s, t, "bf16", w, False)
+    # the decode phases read the weights packed for the decode kernels (the
+    # prefill phase the (out, in) layout)
+    dsets = sets if args.row_major else \
+        [dict(d, packed=tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)) for d in sets]
 
     def step(i):
         for ph in decs:
-            ph.run(sets[i % len(sets)])
+            ph.run(dsets[i % len(dsets)])
 
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
     el_d, prof_d = timed(tp, step, steps, warmup, ["gateup_decode"])
@@ -469,8 +473,10 @@ def bench_quant(tp, args, cfg_id):
     out = dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * el_d / steps, 5), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16 (%s weights)" % W_LABEL[w], data="synthetic",
-               config={"workload": "70B-shaped TP=%d rank, %s weights + fp32 row scales: decode M=%s (value) "
-                                   "and prefill M=%d" % (t, W_LABEL[w], ", ".join(map(str, dec_Ms)), pre_M),
+               config={"workload": "70B-shaped TP=%d rank, %s weights + fp32 row scales: decode M=%s (value%s) "
+                                   "and prefill M=%d" % (t, W_LABEL[w], ", ".join(map(str, dec_Ms)),
+                                                         "" if args.row_major else ", weights packed for the decode "
+                                                         "kernels", pre_M),
                        "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
