@@ -308,6 +308,8 @@ TP_API size_t tp_mlp_packed_weights_bytes(int64_t h, int64_t I_full, int32_t t, 
 TP_API tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32_t w_dtype, const void* w_gate,
                                      const void* w_up, int64_t ldw_gu, const void* w_down, int64_t ldw_down,
                                      void* packed, size_t packed_bytes, void* stream) {
+  const tp_status st = check_shapes(1, h, I_full, t, 0, TP_BF16, w_dtype);
+  if (st != TP_OK) return st;
   const int64_t need = packed_need(h, I_full, t, w_dtype);
   if (need == 0) return TP_ERR_UNSUPPORTED;
   const int64_t I_s = I_full / t;

@@ -412,7 +412,11 @@ def test_packed_weights_bytes_and_validation():
     assert fwdp(packed=None) == _lib.TP_ERR_INVALID_ARG
     assert fwdp(w=FP8) == _lib.TP_ERR_INVALID_ARG                            # scales missing
     assert fwdp(h=320) == _lib.TP_ERR_UNSUPPORTED
-    # pack: null pointers, short leading dimensions, a short array
+    # pack: invalid shapes, null pointers, short leading dimensions, a short array
+    assert lib.tp_mlp_pack_weights(512, 1024, 0, BF16, P, P * 2, 512, P * 3, 512, P * 8, 1 << 22, None) == \
+        _lib.TP_ERR_INVALID_ARG
+    assert lib.tp_mlp_pack_weights(320, 640, 2, BF16, P, P * 2, 320, P * 3, 320, P * 8, 1 << 22, None) == \
+        _lib.TP_ERR_UNSUPPORTED
     assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, None, P, 512, P, 512, P * 8, 1 << 22, None) == \
         _lib.TP_ERR_INVALID_ARG
     assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, P, P * 2, 256, P * 3, 512, P * 8, 1 << 22, None) == \
