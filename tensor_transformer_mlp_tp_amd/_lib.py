@@ -11,9 +11,8 @@ import ctypes
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-# The in-tree library; TP_MLP_LIB may name another build of the same sources
-# (used when comparing launch-shape variants).
-LIB_PATH = os.environ.get("TP_MLP_LIB") or os.path.join(PKG, "libtp_mlp.so")
+# The in-tree library, built from csrc/ by build.py.
+LIB_PATH = os.path.join(PKG, "libtp_mlp.so")
 
 TP_F32, TP_BF16, TP_FP8_E4M3FN, TP_INT8 = 0, 1, 2, 3
 TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_WORKSPACE, TP_ERR_HIP = 0, 1, 2, 3, 4
@@ -85,7 +84,8 @@ def load():
     lib.tp_mlp_pack_weights.argtypes = [c_i64, c_i64, c_i32, c_i32, vp, vp, c_i64, vp, c_i64, vp, ctypes.c_size_t, vp]
     lib.tp_mlp_pack_weights.restype = c_i32
     lib.tp_mlp_shard_forward_packed.argtypes = [
-        c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, vp, c_i64, vp, vp, vp, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
+        c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, vp, c_i64, vp, ctypes.c_size_t, vp, vp, vp, vp, c_i64, vp,
+        ctypes.c_size_t, vp]
     lib.tp_mlp_shard_forward_packed.restype = c_i32
     lib.tp_mlp_w8a8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32]
     lib.tp_mlp_w8a8_workspace_bytes.restype = ctypes.c_size_t

@@ -316,13 +316,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-#ifndef TPMLP_DECODE_SLOTS
-#define TPMLP_DECODE_SLOTS 2
-#endif
-#ifndef TPMLP_DECODE_XPF
-#define TPMLP_DECODE_XPF 1
-#endif
-
 // Wait until slot j's D direct loads have landed.  Per iteration the wave
 // issues XL activation loads and then the D direct loads of a slot S-1
 // ahead; the first S-1 slots were issued up front without activation loads.
@@ -399,7 +392,6 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
   };
 #pragma unroll
   for (int p = 0; p < S - 1; ++p) issue(j_beg + min(p, nsl - 1) * jstep, p);
-#if TPMLP_DECODE_XPF
   // Activation fragments one slot ahead in a second register set: the loads
   // of slot jj+1 (activations and weights) fly while slot jj is computed.
   // Issue order per step: activations of jj+1, then the direct loads of
@@ -419,20 +411,6 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
     step(jj + 1, xb, xa);
   }
   if (jj < nsl) step(jj, xa, xb);
-#else
-  int pos = 0;
-  for (int jj = 0; jj < nsl; ++jj) {
-    wait_slot_peeled<S, XL, D, 0>(jj);
-    const int j = j_beg + jj * jstep;
-    // activation fragments of this slot (from L2; same k order as the weights)
-    u32x4 xf[STEPS][NT];
-    load_x(j, xf);
-    const int npos = pos == 0 ? S - 1 : pos - 1;   // ring slot of j+S-1 (held j-1)
-    issue(j_beg + min(jj + S - 1, nsl - 1) * jstep, npos);
-    compute(pos, xf);
-    pos = pos == S - 1 ? 0 : pos + 1;
-  }
-#endif
   __builtin_amdgcn_s_waitcnt(0);  // the ring's last (duplicate) loads are done before LDS is reused
 }
 
@@ -570,7 +548,7 @@ __device__ __forceinline__ void reduce_waves_ring(f32x4 (&acc)[RB][NT], f32x4* b
   }
 }
 
-constexpr int kSlots = TPMLP_DECODE_SLOTS;
+constexpr int kSlots = 2;   // the register-activation stream's ring (its prefetch assumes two)
 constexpr int kSWaves = 4;
 
 // Slots of this wave: interleaved over the workgroup's WV waves.
@@ -775,14 +753,8 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
 }
 
 // Launch shape (waves per workgroup splitting K; steps per register batch).
-#ifndef TPMLP_DECODE_WAVES
-#define TPMLP_DECODE_WAVES 4
-#endif
-#ifndef TPMLP_DECODE_UNROLL
-#define TPMLP_DECODE_UNROLL 8
-#endif
-constexpr int kWaves = TPMLP_DECODE_WAVES;
-constexpr int kUnroll = TPMLP_DECODE_UNROLL;
+constexpr int kWaves = 4;
+constexpr int kUnroll = 8;
 
 template <int NT, int WB>
 hipError_t gateup_v1(const ShardArgs& a, hipStream_t stream) {
@@ -803,40 +775,30 @@ hipError_t rowgemm_v1(const RowGemm& g, hipStream_t stream) {
                 (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo);
 }
 
-#ifndef TPMLP_DECODE_RB_WIDE
-#define TPMLP_DECODE_RB_WIDE 2
-#endif
-#ifndef TPMLP_DECODE_RB_XD_FP8_GU
-#define TPMLP_DECODE_RB_XD_FP8_GU 4
-#endif
-#ifndef TPMLP_DECODE_RB_XD_FP8_DN
-#define TPMLP_DECODE_RB_XD_FP8_DN 2
-#endif
+// Row blocks per wave of the activation-staged streams: two (bf16 weights),
+// four for the one-byte gate/up and two for the one-byte down projection.
+constexpr int kRbWide = 2;
+constexpr int kRbXdByteGu = 4;
+constexpr int kRbXdByteDn = 2;
 
-#ifndef TPMLP_DECODE_XD
-#define TPMLP_DECODE_XD 1
-#endif
 // One-byte weights put 256 k in a slot, so up to 16 tokens their activation
 // fragments per weight byte are twice bf16's; two row blocks per wave share
 // them in gate/up (measured: fp8 M = 8 32.0 -> 26.0 us, int8 59.9 -> 55.4 us
 // at the 70B TP = 4 / TP = 2 shards; the down projection, with a quarter of
 // the rows, kept one).
-#ifndef TPMLP_DECODE_RB_NT1_BYTE
-#define TPMLP_DECODE_RB_NT1_BYTE 2
-#endif
+constexpr int kRbNt1Byte = 2;
 
 // Up to 16 tokens: one 16-row block per wave, activations from registers
 // (most workgroups).  More tokens: RB row blocks per wave share each
 // activation fragment, and the activations come through the ring (where its
 // slots fit the LDS: fp8 weights have twice the k per slot).
 template <int NT, int WB>
-constexpr bool kStreamXD = TPMLP_DECODE_XD && NT >= 2 && (!WB || NT == 2);
+constexpr bool kStreamXD = NT >= 2 && (!WB || NT == 2);
 
 template <int NT, int WB>
 hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
-  constexpr int RB = NT == 1 ? (WB ? TPMLP_DECODE_RB_NT1_BYTE : 1)
-                             : (XD && WB ? TPMLP_DECODE_RB_XD_FP8_GU : TPMLP_DECODE_RB_WIDE);
+  constexpr int RB = NT == 1 ? (WB ? kRbNt1Byte : 1) : (XD && WB ? kRbXdByteGu : kRbWide);
   const dim3 grid((a.I_s + 8 * RB - 1) / (8 * RB)), block(StreamShape<NT, RB, WB, XD>::WV * 64);
   if (a.packed)
     return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD, true>, grid, block, 0, stream, a.M, a.h,
@@ -847,7 +809,7 @@ hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
 }
 
 template <int NT, int WB>
-constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? TPMLP_DECODE_RB_XD_FP8_DN : TPMLP_DECODE_RB_WIDE);
+constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? kRbXdByteDn : kRbWide);
 
 // A narrow row GEMM that splits K (below) runs three 16-row blocks per wave
 // on the bf16 activation-staged path instead of two: each staged activation
@@ -855,11 +817,8 @@ constexpr int kRowRB = NT == 1 ? 1 : (kStreamXD<NT, WB> && WB ? TPMLP_DECODE_RB_
 // Measured on the 70B TP = 8 QKV projection (1280 rows): M = 64 17.3 ->
 // 13.4 us, M = 32 13.0 -> 10.7 us; the wide outputs (MLP, o_proj) are
 // faster with two.
-#ifndef TPMLP_DECODE_RB_SPLIT
-#define TPMLP_DECODE_RB_SPLIT 3
-#endif
 template <int NT, int WB>
-constexpr int kRowRBSplit = kStreamXD<NT, WB> && !WB ? TPMLP_DECODE_RB_SPLIT : kRowRB<NT, WB>;
+constexpr int kRowRBSplit = kStreamXD<NT, WB> && !WB ? 3 : kRowRB<NT, WB>;
 
 // K split of a streaming row GEMM.  A narrow output (few 16-row blocks, e.g.
 // a rank's QKV projection: 80 blocks for 1280 rows) keeps too few loads in
@@ -869,15 +828,13 @@ constexpr int kRowRBSplit = kStreamXD<NT, WB> && !WB ? TPMLP_DECODE_RB_SPLIT : k
 // keeping at least two slots.  (Sixteen waves per row block instead of a
 // split was measured slower: per-CU streaming rate, not wave count, is the
 // limit.)
-#ifndef TPMLP_SPLIT_TARGET_WAVES
-#define TPMLP_SPLIT_TARGET_WAVES 1024
-#endif
+constexpr int kSplitTargetWaves = 1024;
 
 template <int NT, int WB, int RB = kRowRBSplit<NT, WB>>
 int stream_splits(int N, int K) {
   constexpr int WV = StreamShape<NT, RB, WB, kStreamXD<NT, WB>>::WV;
   const int blocks = (N + 16 * RB - 1) / (16 * RB);
-  const int want = (TPMLP_SPLIT_TARGET_WAVES + blocks * WV - 1) / (blocks * WV);
+  const int want = (kSplitTargetWaves + blocks * WV - 1) / (blocks * WV);
   const int cap = K / (WB ? 256 : 128) / (2 * WV);
   return max(1, min(want, cap));
 }
@@ -907,16 +864,12 @@ hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
                 0, stream, g.M, g.N, nseg, (const float*)g.ws, g.s, g.out, g.ldo);
 }
 
-#ifndef TPMLP_DECODE_V2
-#define TPMLP_DECODE_V2 1
-#endif
-
 // The streaming kernels move whole 16-row x 256-byte slots along K: they need
 // K to be a multiple of 128 (bf16) / 256 (fp8) k-values; other shapes use the
 // register-batch kernels, which step 32 / 64 k-values at a time.
 template <int WB>
 constexpr bool streams(int K) {
-  return TPMLP_DECODE_V2 && K % (WB ? 256 : 128) == 0;
+  return K % (WB ? 256 : 128) == 0;
 }
 
 template <int WB>
@@ -987,12 +940,8 @@ hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const f
 // A narrow row GEMM that the matrix-core stream would split along K (the
 // QKV projection) goes, at up to kGemvMaxM tokens with bf16 weights, to the
 // row-streaming VALU kernel of gemv.hip: no split and no finishing kernel.
-// TPMLP_GEMV=0 keeps the matrix-core streams for every decode shape.
-#ifndef TPMLP_GEMV
-#define TPMLP_GEMV 1
-#endif
 static bool use_gemv(int M, int N, int K, int wb) {
-  return TPMLP_GEMV && gemv_supported(M, K, wb) && stream_splits<1, kWeightWide>(N, K) > 1;
+  return gemv_supported(M, K, wb) && stream_splits<1, kWeightWide>(N, K) > 1;
 }
 
 int64_t rowgemm_decode_workspace_bytes(int M, int N, int K, int wb) {

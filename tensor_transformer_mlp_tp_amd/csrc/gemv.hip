@@ -27,15 +27,9 @@ namespace tpmlp {
 
 namespace {
 
-#ifndef TPMLP_GEMV_WAVES
-#define TPMLP_GEMV_WAVES 8
-#endif
-#ifndef TPMLP_GEMV_UNROLL
-#define TPMLP_GEMV_UNROLL 8
-#endif
-constexpr int kGWaves = TPMLP_GEMV_WAVES;    // waves per workgroup (they share the activations in LDS)
-constexpr int kGChunk = 512;                 // k per load instruction of a wave (1 KB of bf16)
-constexpr int kGUnroll = TPMLP_GEMV_UNROLL;  // load instructions in flight per wave
+constexpr int kGWaves = 8;      // waves per workgroup (they share the activations in LDS)
+constexpr int kGChunk = 512;    // k per load instruction of a wave (1 KB of bf16)
+constexpr int kGUnroll = 8;     // load instructions in flight per wave
 
 // Largest K held in LDS (static: 32 KB per token).
 constexpr int kGKmax = 16384;

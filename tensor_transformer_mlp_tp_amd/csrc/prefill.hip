@@ -178,6 +178,176 @@ struct SkTail {
   int d;         // pieces per tail tile; 0: no tail split
 };
 
+// A tail tile's piece (see SkTail): store this workgroup's raw fp32 sums in
+// its slot and count the arrival; the piece that arrives last adds the tile's
+// d slots in k order into acc and returns true (it writes the tile), every
+// other piece returns false.  NT threads, each holding CB x TB 32x32 blocks;
+// `flag` is an int in LDS.
+template <int CB, int TB, int NT, int BM>
+__device__ __forceinline__ bool sk_handoff(f32x16 (&acc)[CB][TB], const SkTail sk, int tail, int piece, int tid,
+                                           int* flag) {
+  constexpr int SLOT = BM * BN * 4;     // bytes per slot
+  static_assert(CB * TB * 16 * NT * 4 == SLOT, "a slot holds the tile");
+  constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
+  // raw buffer over this tile's d slots (word 3 of a gfx9 buffer descriptor:
+  // 32-bit data format, no swizzle); offsets past d * SLOT read zero
+  const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+      sk.part + (int64_t)tail * sk.d * (BM * BN), 0, sk.d * SLOT, 0x00020000);
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * qd + i];
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
+                                               piece * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0,
+                                               kDeviceScope);
+      }
+  // Ordering.  The LLVM AMDGPU memory model's agent-scope release on
+  // gfx942/gfx950 is "buffer_wbl2 sc1; s_waitcnt vmcnt(0)" before the
+  // atomic, and its acquire "buffer_inv sc1" after it: the write-back pushes
+  // out L2 lines that were written without the agent-scope (sc1) policy and
+  // the invalidate drops lines that later non-sc1 loads could hit.  Every
+  // store and load of the slots here carries sc1 (they go through to the
+  // point of coherence shared by the XCDs), so only the s_waitcnt part of the
+  // release is needed: vmcnt(0) makes each lane's slot stores complete at
+  // agent scope, the workgroup barrier orders all lanes before lane 0's
+  // counter increment, and the last piece's slot loads are issued only after
+  // the increment's returned value is known (a control dependence through the
+  // barrier below).  Dropping the write-back and invalidate keeps the GEMM's
+  // L2 panels: a full fence here measured the tail at half speed.
+  __builtin_amdgcn_s_waitcnt(0);        // this piece's slot stores are complete
+  __syncthreads();
+  if (tid == 0) *flag = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*flag != sk.d - 1) return false;  // another piece writes the tile
+  // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
+  // slot are loaded together (one memory round trip per slot and block)
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    f32x4 sum[TB * 4], v[TB * 4];
+    auto own = [&](f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
+    };
+    auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd)
+          dst[tb * 4 + qd] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
+    };
+    if (piece == 0) own(sum);
+    else load(0, sum);
+    for (int p = 1; p < sk.d; ++p) {
+      if (p == piece) own(v);
+      else load(p, v);
+#pragma unroll
+      for (int e = 0; e < TB * 4; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
+    }
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
+  }
+  return true;
+}
+
+// Epilogue of a wave's CB x TB blocks.  The lane holds, per block, weight
+// rows 8j + 4g + (0..3) (j = 0..3) of block cb for token r32 of block tb.
+// Gate/up (SWIGLU): blocks 0 .. CB/2-1 are gate rows of channels ch0 +
+// 32 cb + ..., blocks CB/2 .. CB-1 the same channels' up rows; A =
+// SiLU(G) * U is written in bf16.  Otherwise rows are output features f0 +
+// 32 cb + ... (fp32, or bf16 with OBF).  Tokens: tok0 + 32 tb + r32.  One-byte
+// weights scale by the row scales s0 (s1: up), fp8 activations by sx.
+template <bool SWIGLU, int WB, bool A8, bool OBF, int CB, int TB>
+__device__ __forceinline__ void store_tile(const f32x16 (&acc)[CB][TB], int M, int N, int ch0, int tok0, int r32, int g,
+                                           const float* __restrict__ s0, const float* __restrict__ s1,
+                                           const float* __restrict__ sx, void* __restrict__ out, int64_t ld_out) {
+  if constexpr (SWIGLU) {
+    uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+    for (int cb = 0; cb < CB / 2; ++cb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ch = ch0 + cb * 32 + 8 * j + 4 * g;  // channels ch .. ch+3
+        if (ch >= N) continue;
+        float sgv[4] = {1.f, 1.f, 1.f, 1.f}, suv[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (WB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sgv[i] = s0[ch + i];
+            suv[i] = s1[ch + i];
+          }
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tok = tok0 + tb * 32 + r32;
+          if (tok >= M) continue;
+          const float st = A8 ? sx[tok] : 1.f;
+          float a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float gv = acc[cb][tb][4 * j + i], uv = acc[cb + CB / 2][tb][4 * j + i];
+            if constexpr (WB) {
+              gv *= sgv[i];
+              uv *= suv[i];
+            }
+            if constexpr (A8) {
+              gv *= st;
+              uv *= st;
+            }
+            a[i] = silu(gv) * uv;
+          }
+          u32x2 packed = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          *reinterpret_cast<u32x2*>(a_out + (int64_t)tok * ld_out + ch) = packed;
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int f = ch0 + cb * 32 + 8 * j + 4 * g;  // features f .. f+3
+        if (f >= N) continue;
+        float sv[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (WB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sv[i] = s0[f + i];
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tok = tok0 + tb * 32 + r32;
+          if (tok >= M) continue;
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
+          if constexpr (A8) {
+            const float st = sx[tok];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= st;
+          }
+          store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
+        }
+      }
+    }
+  }
+}
+
 // A8: the activations are e4m3fn codes too (W8A8): one byte per element in
 // LDS, 32x32x64 fp8 MFMAs (twice the bf16 rate), and the per-token scales sx
 // applied in the epilogue with the weight row scales.
@@ -455,176 +625,23 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 }
   __builtin_amdgcn_s_waitcnt(0);  // no direct load is left in flight at exit
 
-  // ---- a piece of a tail tile: publish the raw sums and count the arrival;
-  // the last piece to arrive adds the tile's pieces in k order.  The slots
-  // are stored and loaded with device-scope (sc1) accesses, which pass the
-  // caches that are not coherent across XCDs; with the stores complete
-  // (vmcnt 0) before the counter's increment and the loads issued after the
-  // increment's result is known, no L2 write-back or invalidation is needed
-  // (a device-scope fence does both to the whole XCD's L2, and the GEMM's
-  // panel reuse goes with it).
+  // ---- a piece of a tail tile: publish the raw sums; the last piece to
+  // arrive adds the tile's pieces in k order and writes the tile
   if constexpr (SK) {
-    if (tail >= 0) {
-      int& sk_arrived = *reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512);
-      constexpr int NT = WV * 64;
-      constexpr int SLOT = BM * BN * 4;     // bytes per slot
-      constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
-      // raw buffer over this tile's d slots (word 3 of a gfx9 buffer descriptor:
-      // 32-bit data format, no swizzle); offsets past d * SLOT read zero
-      const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
-          sk.part + (int64_t)tail * sk.d * (BM * BN), 0, sk.d * SLOT, 0x00020000);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd) {
-            f32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * qd + i];
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
-                                                   piece * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0,
-                                                   kDeviceScope);
-          }
-      __builtin_amdgcn_s_waitcnt(0);        // this piece's slot stores are complete
-      __syncthreads();
-      if (tid == 0) sk_arrived = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-      if (sk_arrived != sk.d - 1) return;   // another piece writes the tile
-      // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
-      // slot are loaded together (one memory round trip per slot and block)
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        f32x4 sum[TB * 4], v[TB * 4];
-        auto own = [&](f32x4 (&dst)[TB * 4]) {
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-              for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
-        };
-        auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int qd = 0; qd < 4; ++qd)
-              dst[tb * 4 + qd] = __builtin_bit_cast(
-                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                             slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
-        };
-        if (piece == 0) own(sum);
-        else load(0, sum);
-        for (int p = 1; p < sk.d; ++p) {
-          if (p == piece) own(v);
-          else load(p, v);
-#pragma unroll
-          for (int e = 0; e < TB * 4; ++e)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
-        }
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-          for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
-      }
-    }
+    if (tail >= 0 &&
+        !sk_handoff<CB, TB, WV * 64, BM>(acc, sk, tail, piece, tid, reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512)))
+      return;
   }
-
-  // ---- epilogue.  Lane holds, per block, rows 8j + 4g + (0..3) (j = 0..3)
-  // of weight-row block cb for token column r32 of block tb.
-  if constexpr (SWIGLU) {
-    uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
-#pragma unroll
-    for (int cb = 0; cb < CB / 2; ++cb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ch = n0 + wn * (BN / 2 / WN) + cb * 32 + 8 * j + 4 * g;  // channels ch .. ch+3
-        if (ch >= N) continue;
-        float sgv[4] = {1.f, 1.f, 1.f, 1.f}, suv[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (WB) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sgv[i] = s0[ch + i];
-            suv[i] = s1[ch + i];
-          }
-        }
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          const int tok = m0 + wm * (BM / WM) + tb * 32 + r32;
-          if (tok >= M) continue;
-          const float st = A8 ? sx[tok] : 1.f;
-          float a[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float gv = acc[cb][tb][4 * j + i], uv = acc[cb + CB / 2][tb][4 * j + i];
-            if constexpr (WB) {
-              gv *= sgv[i];
-              uv *= suv[i];
-            }
-            if constexpr (A8) {
-              gv *= st;
-              uv *= st;
-            }
-            a[i] = silu(gv) * uv;
-          }
-          u32x2 packed = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
-          *reinterpret_cast<u32x2*>(a_out + (int64_t)tok * ld_out + ch) = packed;
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int f = n0 + wn * (BN / WN) + cb * 32 + 8 * j + 4 * g;  // features f .. f+3
-        if (f >= N) continue;
-        float sv[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (WB) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sv[i] = s0[f + i];
-        }
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-          const int tok = m0 + wm * (BM / WM) + tb * 32 + r32;
-          if (tok >= M) continue;
-          f32x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = acc[cb][tb][4 * j + i] * sv[i];
-          if constexpr (A8) {
-            const float st = sx[tok];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] *= st;
-          }
-          store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
-        }
-      }
-    }
-  }
+  store_tile<SWIGLU, WB, A8, OBF, CB, TB>(acc, M, N, n0 + (SWIGLU ? wn * (BN / 2 / WN) : wn * (BN / WN)),
+                                          m0 + wm * (BM / WM), r32, g, s0, s1, sx, out, ld_out);
 }
 
 // Stage shape: bf16 weights use two stages of BK = 64 (128 KB of LDS); fp8
 // weights, with 48 KB stages, fit three.
-#ifndef TPMLP_PREFILL_BK
-#define TPMLP_PREFILL_BK 64
-#endif
-#ifndef TPMLP_PREFILL_NS_BF16
-#define TPMLP_PREFILL_NS_BF16 2
-#endif
-#ifndef TPMLP_PREFILL_NS_FP8
-#define TPMLP_PREFILL_NS_FP8 3
-#endif
-#ifndef TPMLP_PREFILL_WAVES
-#define TPMLP_PREFILL_WAVES 4
-#endif
-
-constexpr int kBK = TPMLP_PREFILL_BK;
-constexpr int kWV = TPMLP_PREFILL_WAVES;
+constexpr int kBK = 64;
+constexpr int kWV = 4;
 template <int WB>
-constexpr int kNS = WB ? TPMLP_PREFILL_NS_FP8 : TPMLP_PREFILL_NS_BF16;
+constexpr int kNS = WB ? 3 : 2;
 
 // Stream-K plan (see SkTail), sized for MI355X's 256 CUs with one workgroup
 // per CU (the 64-token tiles of one-byte weights, 74 KB of LDS, fit two: the
@@ -681,11 +698,7 @@ int gemm_tiles(bool swiglu, int M, int N, int bm) { return ((M + bm - 1) / bm) *
 // 256-token one (fitted to gate/up and down timings of the 70B shard, bf16
 // and fp8 weights, 65 to 2048 tokens: the chosen height's time is 0.6 % above
 // the best one's on average, 14 % at most).
-#ifndef TPMLP_PREFILL_FORCE_BM
-#define TPMLP_PREFILL_FORCE_BM 0
-#endif
 int tile_bm(int M, int tiles_n, int KT) {
-  if (TPMLP_PREFILL_FORCE_BM) return TPMLP_PREFILL_FORCE_BM;
   if ((int64_t)((M + 255) / 256) * tiles_n * 4 >= kSkCUs * 3) return 256;
   constexpr int kHeights[3] = {256, 128, 64};
   constexpr int kCost[3] = {100, 52, 34};   // per k-tile, relative

@@ -18,16 +18,10 @@ namespace {
 // Block shape: 1024 threads for the large (bandwidth-bound) reduces, 256 for
 // small ones (a decode partial of a few hundred KB), where more blocks
 // finish sooner.
-#ifndef TPMLP_REDUCE_THREADS
-#define TPMLP_REDUCE_THREADS 1024
-#endif
-#ifndef TPMLP_REDUCE_UNROLL
-#define TPMLP_REDUCE_UNROLL 1
-#endif
 constexpr int kReduceThreadsSmall = 256;
 constexpr int64_t kReduceSmallN4 = 1 << 20;
-constexpr int kReduceThreads = TPMLP_REDUCE_THREADS;
-constexpr int kReduceUnroll = TPMLP_REDUCE_UNROLL;
+constexpr int kReduceThreads = 1024;
+constexpr int kReduceUnroll = 1;
 
 // Loads are non-temporal: every input byte is read exactly once.  Stores:
 // when the output fits well inside the 256 MB last-level cache, plain stores
