@@ -243,6 +243,11 @@ size_t tp_mlp_w8a8_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t
  * and I_s % 128 == 0 (else TP_ERR_UNSUPPORTED), 16-byte aligned pointers and
  * rows, a 256-byte aligned workspace of tp_mlp_w8a8_workspace_bytes(...)
  * bytes whose contents on entry are ignored.  Deterministic.
+ *
+ * When the work has completed, the workspace holds the forward's
+ * intermediates, each starting at the next multiple of 256 bytes after the
+ * previous one (offset 0 first): A (M x I_s bf16), X's codes (M x h bytes),
+ * X's scales (M fp32), A's codes (M x I_s bytes), A's scales (M fp32).
  */
 tp_status tp_mlp_shard_forward_w8a8(int64_t M, int64_t h, int64_t I_full,
                                     int32_t t, int32_t k,
@@ -467,13 +472,17 @@ tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32_t w_dt
  * tp_mlp_shard_forward with the weights given as a packed array (above)
  * instead of w_gate, w_up, w_down and their leading dimensions; bf16
  * activations only; M at most 64 (32 with one-byte weights), else
- * TP_ERR_UNSUPPORTED.  s_gate, s_up, s_down, partial, the workspace
- * (tp_mlp_workspace_bytes(...) bytes) and the errors are as there; the
- * packed array must not overlap the partial or the workspace.
+ * TP_ERR_UNSUPPORTED.  packed_bytes is the size of the caller's packed
+ * array; fewer than tp_mlp_packed_weights_bytes(h, I_full, t, w_dtype) bytes
+ * (an array packed for other shapes) is TP_ERR_INVALID_ARG.  s_gate, s_up,
+ * s_down, partial, the workspace (tp_mlp_workspace_bytes(...) bytes) and the
+ * errors are as there; the packed array must not overlap the partial or the
+ * workspace.
  */
 tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
                                       int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
-                                      const void* packed, const float* s_gate, const float* s_up,
+                                      const void* packed, size_t packed_bytes,
+                                      const float* s_gate, const float* s_up,
                                       const float* s_down, float* partial, int64_t ldp,
                                       void* workspace, size_t workspace_bytes, void* stream);
 

@@ -167,10 +167,8 @@ def _prepare_forward(xs, sp, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, p
     if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
         raise ValueError("shard shapes must be w_gate/w_up (I_s, h) and w_down (h, I_s); got %s %s %s"
                          % (tuple(w_gate.shape), tuple(w_up.shape), tuple(w_down.shape)))
-    scales = (s_gate, s_up, s_down)
-    for s in scales:
-        if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
-            raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+    for name, s, n in (("s_gate", s_gate, I_s), ("s_up", s_up, I_s), ("s_down", s_down, h)):
+        _check_scales(s, device, n, name)
     if partial is None:
         partial = torch.empty((M, h), dtype=torch.float32, device=device)
     else:
@@ -256,9 +254,8 @@ def prepare_shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down
     M, h = x.shape
     if h != packed.h:
         raise ValueError("x has %d columns, the weights were packed for h = %d" % (h, packed.h))
-    for s in (s_gate, s_up, s_down):
-        if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
-            raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+    for name, s, n in (("s_gate", s_gate, packed.I_s), ("s_up", s_up, packed.I_s), ("s_down", s_down, h)):
+        _check_scales(s, device, n, name)
     if partial is None:
         partial = torch.empty((M, h), dtype=torch.float32, device=device)
     else:
@@ -274,7 +271,7 @@ def prepare_shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down
     elif workspace.device != device:
         raise ValueError("workspace must be on %s" % device)
     args = (M, h, I_full, packed.t, int(k), act, packed.w_code, _ptr(x), x.stride(0), _ptr(packed.data),
-            _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(partial), partial.stride(0), _ptr(workspace),
+            packed.data.numel() * packed.data.element_size(), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(partial), partial.stride(0), _ptr(workspace),
             workspace.numel() * workspace.element_size(), _stream_of(device, stream))
     call = PreparedCall(lib.tp_mlp_shard_forward_packed, args, (x, packed, s_gate, s_up, s_down, partial, workspace))
     call.partial = partial
@@ -380,11 +377,11 @@ def prepare_shard_forward_w8a8(x, w_gate, w_up, w_down, *, t, k, s_gate, s_up, s
             raise TypeError("%s must hold e4m3fn codes" % name)
     if x.dtype != torch.bfloat16:
         raise TypeError("x must be bfloat16")
-    for sc in (s_gate, s_up, s_down):
-        _check_scales(sc, device)
     M, h = x.shape
     I_s = w_gate.shape[0]
     I_full = I_s * int(t)
+    for name, sc, n in (("s_gate", s_gate, I_s), ("s_up", s_up, I_s), ("s_down", s_down, h)):
+        _check_scales(sc, device, n, name)
     if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
         raise ValueError("shard shapes must be w_gate/w_up (I_s, h) and w_down (h, I_s)")
     if w_gate.stride(0) != w_up.stride(0):
@@ -428,9 +425,16 @@ def attn_qkv_width(n_heads, n_kv_heads, head_dim, t):
     return int(_lib.load().tp_attn_qkv_width(int(n_heads), int(n_kv_heads), int(head_dim), int(t)))
 
 
-def _check_scales(s, device):
-    if s is not None and (s.dtype != torch.float32 or s.device != device or not s.is_contiguous()):
-        raise ValueError("scales must be contiguous float32 tensors on %s" % device)
+def _check_scales(s, device, n=None, name="scales"):
+    """A scale vector is a contiguous float32 tensor on `device`; with `n`,
+    it must hold exactly n elements (the C ABI takes no length, and the
+    kernels read one scale per output row)."""
+    if s is None:
+        return
+    if s.dtype != torch.float32 or s.device != device or not s.is_contiguous():
+        raise ValueError("%s must be contiguous float32 tensors on %s" % (name, device))
+    if n is not None and s.numel() != n:
+        raise ValueError("%s must hold %d elements (one per output row), got %d" % (name, n, s.numel()))
 
 
 def attn_qkv_workspace_bytes(M, h, n_heads, n_kv_heads, head_dim, t, act_dtype=torch.bfloat16,
@@ -458,11 +462,11 @@ def prepare_attn_qkv_forward(x, w_qkv, *, n_heads, n_kv_heads, head_dim, t, k, s
     device = x.device
     _check_matrix("x", x, device)
     _check_matrix("w_qkv", w_qkv, device)
-    _check_scales(s_qkv, device)
     M, h = x.shape
     n_loc = attn_qkv_width(n_heads, n_kv_heads, head_dim, t)
     if n_loc < 0:
         raise ValueError("heads (%d query, %d kv) do not split over t = %d" % (n_heads, n_kv_heads, t))
+    _check_scales(s_qkv, device, n_loc, "s_qkv")
     if tuple(w_qkv.shape) != (n_loc, h):
         raise ValueError("w_qkv must be (%d, %d), got %s" % (n_loc, h, tuple(w_qkv.shape)))
     if out is None:
@@ -502,9 +506,9 @@ def prepare_attn_out_forward(attn, w_o, *, n_heads, head_dim, t, k, s_o=None, pa
     device = attn.device
     _check_matrix("attn", attn, device)
     _check_matrix("w_o", w_o, device)
-    _check_scales(s_o, device)
     M, K = attn.shape
     h = w_o.shape[0]
+    _check_scales(s_o, device, h, "s_o")
     if int(n_heads) % int(t) or K != int(n_heads) // int(t) * int(head_dim) or w_o.shape[1] != K:
         raise ValueError("attn (%d, %d) and w_o %s do not match n_heads/t * head_dim = %s"
                          % (M, K, tuple(w_o.shape), int(n_heads) / int(t) * int(head_dim)))

@@ -342,9 +342,9 @@ TP_API tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32
 
 TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
                                              int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
-                                             const void* packed, const float* s_gate, const float* s_up,
-                                             const float* s_down, float* partial, int64_t ldp, void* workspace,
-                                             size_t workspace_bytes, void* stream) {
+                                             const void* packed, size_t packed_bytes, const float* s_gate,
+                                             const float* s_up, const float* s_down, float* partial, int64_t ldp,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
   tp_status st = check_shapes(M, h, I_full, t, k, act_dtype, w_dtype);
   if (st != TP_OK) return st;
   if (act_dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "packed weights take bf16 activations");
@@ -356,6 +356,9 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   if (pbytes == 0) return TP_ERR_UNSUPPORTED;
   const int64_t I_s = I_full / t;
   if (!x || !packed || !partial) return fail(TP_ERR_INVALID_ARG, "null tensor pointer");
+  if ((int64_t)packed_bytes < pbytes)
+    return fail(TP_ERR_INVALID_ARG, "packed array of %lld bytes needed for these shapes (got %llu)",
+                (long long)pbytes, (unsigned long long)packed_bytes);
   const bool fp8 = scaled_weights(w_dtype);
   if (fp8 && (!s_gate || !s_up || !s_down))
     return fail(TP_ERR_INVALID_ARG, "one-byte weights need s_gate, s_up and s_down");

@@ -403,8 +403,8 @@ def test_packed_weights_bytes_and_validation():
     assert lib.tp_mlp_packed_weights_bytes(512, 768, 2, FP8) == 0           # I_s = 384: % 256
     assert lib.tp_mlp_packed_weights_bytes(512, 1024, 2, F32) == 0          # fp32 weights
     # forward: decode sizes and bf16 activations only; checked before any HIP call
-    def fwdp(M=1, h=512, I=1024, t=2, act=BF16, w=BF16, packed=P, sc=None):
-        return lib.tp_mlp_shard_forward_packed(M, h, I, t, 0, act, w, P, h, packed, sc, sc, sc, P * 8, h,
+    def fwdp(M=1, h=512, I=1024, t=2, act=BF16, w=BF16, packed=P, nbytes=1 << 24, sc=None):
+        return lib.tp_mlp_shard_forward_packed(M, h, I, t, 0, act, w, P, h, packed, nbytes, sc, sc, sc, P * 8, h,
                                                P * 16, 1 << 20, None)
     assert fwdp(M=65) == _lib.TP_ERR_UNSUPPORTED
     assert fwdp(M=33, w=FP8, sc=P) == _lib.TP_ERR_UNSUPPORTED
@@ -412,6 +412,8 @@ def test_packed_weights_bytes_and_validation():
     assert fwdp(packed=None) == _lib.TP_ERR_INVALID_ARG
     assert fwdp(w=FP8) == _lib.TP_ERR_INVALID_ARG                            # scales missing
     assert fwdp(h=320) == _lib.TP_ERR_UNSUPPORTED
+    # an array packed for smaller shapes (3 * 512 * 512 bf16 bytes needed)
+    assert fwdp(nbytes=3 * 512 * 512 * 2 - 16) == _lib.TP_ERR_INVALID_ARG
     # pack: invalid shapes, null pointers, short leading dimensions, a short array
     assert lib.tp_mlp_pack_weights(512, 1024, 0, BF16, P, P * 2, 512, P * 3, 512, P * 8, 1 << 22, None) == \
         _lib.TP_ERR_INVALID_ARG
@@ -423,3 +425,56 @@ def test_packed_weights_bytes_and_validation():
         _lib.TP_ERR_INVALID_ARG
     assert lib.tp_mlp_pack_weights(512, 1024, 2, BF16, P, P * 2, 512, P * 3, 512, P * 64, 1024, None) == \
         _lib.TP_ERR_INVALID_ARG
+
+
+# ---- binding: scale vectors must have one element per output row (the C ABI
+# takes no length, so the binding is the only place a short vector is caught)
+
+def _cpu_fp8_shard(M=4, h=256, I_s=128):
+    import torch
+    x = torch.zeros((M, h), dtype=torch.bfloat16)
+    wg = torch.zeros((I_s, h), dtype=torch.float8_e4m3fn)
+    wu = torch.zeros((I_s, h), dtype=torch.float8_e4m3fn)
+    wd = torch.zeros((h, I_s), dtype=torch.float8_e4m3fn)
+    return x, wg, wu, wd
+
+
+@pytest.mark.parametrize("which,n", [("s_gate", 127), ("s_up", 129), ("s_down", 255), ("s_down", 128)])
+def test_binding_rejects_scale_lengths(which, n):
+    import torch
+    import tensor_transformer_mlp_tp_amd as tp
+    x, wg, wu, wd = _cpu_fp8_shard()
+    sc = {"s_gate": torch.ones(128), "s_up": torch.ones(128), "s_down": torch.ones(256)}
+    sc[which] = torch.ones(n)
+    with pytest.raises(ValueError, match=which):
+        tp.prepare_shard_forward(x, wg, wu, wd, t=2, k=0, **sc)
+    with pytest.raises(ValueError, match=which):
+        tp.prepare_shard_forward_w8a8(x, wg, wu, wd, t=2, k=0, **sc)
+
+
+def test_binding_rejects_packed_scale_lengths():
+    import torch
+    import tensor_transformer_mlp_tp_amd as tp
+    x = torch.zeros((4, 512), dtype=torch.bfloat16)
+    pk = tp.PackedWeights(torch.zeros(3 * 512 * 256, dtype=torch.uint8), 512, 256, 2, _lib.TP_FP8_E4M3FN)
+    with pytest.raises(ValueError, match="s_down"):
+        tp.prepare_shard_forward_packed(x, pk, k=0, s_gate=torch.ones(256), s_up=torch.ones(256),
+                                        s_down=torch.ones(256))
+    with pytest.raises(ValueError, match="s_gate"):
+        tp.prepare_shard_forward_packed(x, pk, k=0, s_gate=torch.ones(512), s_up=torch.ones(256),
+                                        s_down=torch.ones(512))
+
+
+def test_binding_rejects_attention_scale_lengths():
+    import torch
+    import tensor_transformer_mlp_tp_amd as tp
+    n_loc = tp.attn_qkv_width(8, 2, 32, 2)          # (4 + 2*1) * 32 = 192
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    w = torch.zeros((n_loc, 256), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="s_qkv"):
+        tp.prepare_attn_qkv_forward(x, w, n_heads=8, n_kv_heads=2, head_dim=32, t=2, k=0,
+                                    s_qkv=torch.ones(n_loc - 1))
+    o = torch.zeros((4, 128), dtype=torch.bfloat16)
+    wo = torch.zeros((256, 128), dtype=torch.float8_e4m3fn)
+    with pytest.raises(ValueError, match="s_o"):
+        tp.prepare_attn_out_forward(o, wo, n_heads=8, head_dim=32, t=2, k=0, s_o=torch.ones(128))
