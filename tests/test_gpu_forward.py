@@ -3,9 +3,9 @@
 Metric: max |P_gpu - P_ref| / rms(P_ref) with the tolerances of the contract
 (2e-2 bf16 and fp32, 6e-2 fp8 weights against the dequantised reference).
 Small shapes span several tiles with ragged tails in M and N and are checked
-element by element; the configurations' full shapes are checked on every
-element (decode) or on sampled token rows (prefill: tokens are independent,
-so the oracle evaluated on a subset of rows is exact for those rows).
+element by element, and so are the configurations at their full sizes
+(decode and prefill: every tile and every stream-K tail tile of the launch
+the benchmark times).
 """
 
 import numpy as np
@@ -171,29 +171,24 @@ def test_config4_fp8_decode_full():
     _full_decode(4, 32)
 
 
-def _sample_rows(M, n=48, seed=0):
-    rng = np.random.Generator(np.random.PCG64(seed))
-    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
-    rows.update([0, M - 1, min(255, M - 1), min(256, M - 1)])
-    return np.array(sorted(rows))
-
-
 def _full_prefill(cfg, M):
+    """Every element of the configuration's prefill partial against the fp64
+    oracle (several seconds of host BLAS at these sizes), then a second call
+    for determinism."""
     c = workloads.CONFIGS[cfg]
     I_s = c["I"] // c["t"]
     print("config %d prefill M=%d" % (cfg, M), flush=True)
     x, ws = make_case(cfg, M, c["h"], I_s, c["act"], c["w"], c["std_gu"], c["std_down"])
     d = upload_case(x, ws, c["act"], c["w"])
     p = run_forward(d, c["t"], 0)
-    rows = _sample_rows(M, seed=cfg)
-    got = p[torch.from_numpy(rows).cuda()].cpu().numpy()
-    tol = TOL_FP8 if c["w"] == "e4m3fn" else TOL_BF16
-    check(got, oracle_partial(x, ws, c["act"], c["w"], rows=rows), tol,
-          "config %d M=%d (%d sampled rows)" % (cfg, M, len(rows)))
-    # every element finite and the whole output deterministic
+    got = p.cpu().numpy()
+    assert np.all(np.isfinite(got))
     p2 = run_forward(d, c["t"], 0)
     assert torch.equal(p.view(torch.int32), p2.view(torch.int32))
-    assert bool(torch.isfinite(p).all())
+    del p2, d
+    tol = TOL_FP8 if c["w"] == "e4m3fn" else TOL_BF16
+    print("config %d prefill M=%d: oracle on all rows" % (cfg, M), flush=True)
+    check(got, oracle_partial(x, ws, c["act"], c["w"]), tol, "config %d M=%d (all elements)" % (cfg, M))
 
 
 def test_config3_prefill_full():
@@ -252,18 +247,13 @@ def test_stream_k_tail(M, h, I_s, w):
 
 def test_stream_k_tail_after_whole_rounds():
     """More tiles than CUs: gate/up has 17 x 16 = 272 tiles, 256 computed whole
-    and the 16 of the last (ragged) M-tile cut in 2 pieces; checked on sampled
-    rows, a dozen of them in that M-tile."""
+    and the 16 of the last (ragged) M-tile cut in 2 pieces; every element."""
     M, h, I_s, t = 4300, 2048, 2048, 2
     print("stream-K after whole rounds M=%d" % M, flush=True)
     x, ws = make_case(46, M, h, I_s, "bf16", "bf16", 0.05, 0.05)
     d = upload_case(x, ws, "bf16", "bf16")
     p = run_forward(d, t, 0)
-    rng = np.random.Generator(np.random.PCG64(46))
-    rows = np.unique(np.concatenate([rng.choice(4096, 30, replace=False), 4096 + rng.choice(M - 4096, 12, replace=False),
-                                     [0, 4095, 4096, M - 1]]))
-    got = p[torch.from_numpy(rows).cuda()].cpu().numpy()
-    check(got, oracle_partial(x, ws, "bf16", "bf16", rows=rows), TOL_BF16, "M=%d (%d sampled rows)" % (M, len(rows)))
+    check(p.cpu().numpy(), oracle_partial(x, ws, "bf16", "bf16"), TOL_BF16, "M=%d (all elements)" % M)
     p2 = run_forward(d, t, 0)
     assert torch.equal(p.view(torch.int32), p2.view(torch.int32))
 

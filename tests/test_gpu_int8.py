@@ -39,17 +39,10 @@ def test_int8_forward_shapes(M, h, I_s):
     assert err <= TOL_INT8, err
 
 
-def _sample_rows(M, n=32):
-    if M <= n:
-        return np.arange(M)
-    r = np.random.Generator(np.random.PCG64(M)).choice(M - 2, n - 2, replace=False) + 1
-    return np.sort(np.concatenate([[0, M - 1], r]))
-
-
 @pytest.mark.parametrize("M", [1, 8, 2048])
 def test_llama70b_tp2_int8(M):
     """70B-shaped TP=2 rank with int8 weights (I_s = 14336): decode and
-    prefill, sampled rows above 32 tokens."""
+    prefill, every element."""
     c = workloads.CONFIGS[9]
     h, I_s = c["h"], c["I"] // c["t"]
     print("int8 70B TP=2 M=%d" % M, flush=True)
@@ -58,8 +51,7 @@ def test_llama70b_tp2_int8(M):
     p = tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=c["t"], k=0, s_gate=d["s_gate"],
                          s_up=d["s_up"], s_down=d["s_down"])
     torch.cuda.synchronize()
-    rows = _sample_rows(M)
-    err = oracle.rms_normalised_max_error(p.cpu().numpy()[rows], oracle_partial(x, ws, "bf16", "int8", rows=rows))
+    err = oracle.rms_normalised_max_error(p.cpu().numpy(), oracle_partial(x, ws, "bf16", "int8"))
     assert err <= TOL_INT8, err
 
 
