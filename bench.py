@@ -2,16 +2,24 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-Prints ONE JSON line.  The default workload is the 70B-shaped TP=8 rank at
-decode: one step runs, for each of M = 1, 8 and 64 tokens, the rank's forward
-(gate/up with fused SwiGLU, down to an fp32 partial) and the 8-way fp32
-partial reduce over that partial and seven resident stand-ins.  Inputs are
-seeded synthetic tensors (``workloads``), resident in HBM before timing.
-Successive steps walk through several distinct weight sets (like successive
-layers), so the weights come from HBM and not from the 256 MB last-level
-cache.  ``value`` is algorithmic bytes per second over the timed steps.
+Prints ONE JSON line.  The default workload carries both halves of the
+metric for the 70B-shaped TP=8 rank:
 
-Other workloads (--workload): prefill70b (4096 tokens, TFLOP/s), fp8_70b
+* decode (``value``, algorithmic GB/s): one step runs, for each of M = 1, 8
+  and 64 tokens, the rank's forward (gate/up with fused SwiGLU, down to an
+  fp32 partial) and the 8-way fp32 partial reduce of that partial with seven
+  other ranks' partials.  Each phase of a step reads its own weight set out
+  of eight or more (like successive layers), and the reduces rotate through
+  four sets of other partials, so the bytes come from HBM and not from the
+  256 MB last-level cache;
+* ``prefill`` (TFLOP/s): M = 4096, the forward and the 8-way reduce of its
+  4096 x 8192 partial (``reduce``: that reduce's own GB/s).
+
+Inputs are seeded synthetic tensors (``workloads``), resident in HBM before
+timing.
+
+Other workloads (--workload): decode70b and prefill70b (the two halves
+alone), fp8_70b
 (TP=4 fp8 weights: decode M=32 and prefill M=2048), int8_70b (TP=2 int8
 weights: decode M=1 and 8, prefill M=2048), w8a8_prefill70b (fp8 activations
 and weights on the fp8 matrix cores, TP=4 at 2048 tokens), prefill405b (8192 tokens),
@@ -64,8 +72,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode70b",
-                    choices=["decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
+    ap.add_argument("--workload", default="default",
+                    choices=["default", "decode70b", "prefill70b", "fp8_70b", "prefill405b", "reduce70b", "reduce405b",
                              "sp_prefill70b", "attn70b", "attn_prefill70b", "int8_70b", "w8a8_prefill70b",
                              "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -147,7 +155,7 @@ def device_weights(cfg_id, h, I_s, w, std_gu, std_down, n_sets):
 class Phase:
     """One forward (+ optional reduce) of a rank at M tokens, buffers preallocated."""
 
-    def __init__(self, tp, cfg_id, M, h, I_s, t, act, w, with_reduce):
+    def __init__(self, tp, cfg_id, M, h, I_s, t, act, w, with_reduce, other_sets=1):
         import torch
         self.tp, self.M, self.h, self.I_s, self.t, self.w = tp, M, h, I_s, t, w
         self.x_host = workloads.make_x(cfg_id, M, h, act)
@@ -157,17 +165,23 @@ class Phase:
                                     {"e4m3fn": torch.float8_e4m3fn, "int8": torch.int8}.get(w, torch.bfloat16))
         self.ws = tp.alloc_workspace(nbytes, "cuda")
         self.with_reduce = with_reduce
+        # the t - 1 other ranks' partials: `other_sets` distinct sets, used in turn
+        self.others = []
         if with_reduce:
-            others = workloads.make_partials(cfg_id, t - 1, M * h, weight_set=M)
-            self.others = [torch.from_numpy(o).cuda() for o in others]
+            for r in range(other_sets):
+                others = workloads.make_partials(cfg_id, t - 1, M * h, weight_set=M + 1000 * r)
+                self.others.append([torch.from_numpy(o).cuda() for o in others])
 
         self.calls = {}
 
-    def run(self, wset, time_fwd=None):
+    def run(self, wset, time_fwd=None, other=0):
         """time_fwd: (library, kind mask) to event-time this call's forward
-        launches of those kinds only."""
-        # arguments are marshalled once per weight set; the loop only re-issues the C calls
-        key = id(wset)
+        launches of those kinds only; other: which set of other partials the
+        reduce reads."""
+        # arguments are marshalled once per (weight set, other-partials set);
+        # the loop only re-issues the C calls
+        other = other % max(1, len(self.others))
+        key = (id(wset), other)
         if key not in self.calls:
             if wset.get("packed") is not None:
                 fwd = self.tp.prepare_shard_forward_packed(self.x, wset["packed"], k=0, s_gate=wset["s_gate"],
@@ -178,7 +192,7 @@ class Phase:
                                                     t=self.t, k=0, s_gate=wset["s_gate"], s_up=wset["s_up"],
                                                     s_down=wset["s_down"], partial=self.partial, workspace=self.ws)
             # in place into the rank's own partial, as the all-reduce does
-            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others,
+            red = self.tp.prepare_partial_reduce([self.partial.view(-1)] + self.others[other],
                                                  out=self.partial.view(-1)) if self.with_reduce else None
             self.calls[key] = (fwd, red)
         fwd, red = self.calls[key]
@@ -285,17 +299,28 @@ def cpu_baseline(fn_once, unit_amount, unit, sample, min_seconds=10.0, max_reps=
 
 # ----------------------------------------------------------------------------- workloads
 
+N_OTHER_SETS = 4   # sets of the other ranks' partials the decode reduces rotate through
+
+
 def bench_decode70b(tp, args):
+    """70B TP=8 decode step: for M = 1, 8 and 64 tokens, the forward and the
+    8-way reduce of its partial.  Each phase of a step reads its own weight
+    set (phase idx of step i: set (3 i + idx) mod n, n >= 8, so a set is read
+    again only after seven others, 1.2 GB, have streamed through the 256 MB
+    last-level cache), and the reduces rotate through N_OTHER_SETS sets of
+    the other ranks' partials."""
     import oracle
     c = workloads.CONFIGS[2]
     h, t, I_s = c["h"], c["t"], c["I"] // c["t"]
-    log("generating %d weight sets of the 70B TP=8 shard" % args.weight_sets)
-    sets, host0 = device_weights(2, h, I_s, "bf16", c["std_gu"], c["std_down"], args.weight_sets)
+    n_sets = max(args.weight_sets, 8)
+    log("generating %d weight sets of the 70B TP=8 shard" % n_sets)
+    sets, host0 = device_weights(2, h, I_s, "bf16", c["std_gu"], c["std_down"], n_sets)
     if not args.row_major:
         # the decode kernels' packed weight layout, written once per weight set
         for d in sets:
             d["packed"] = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
-    phases = [Phase(tp, 2, M, h, I_s, t, "bf16", "bf16", True) for M in c["M"]]
+    phases = [Phase(tp, 2, M, h, I_s, t, "bf16", "bf16", True, other_sets=N_OTHER_SETS) for M in c["M"]]
+    nph = len(phases)
     # An event-timed launch costs the host ~25 us against ~3 us for a plain
     # one; timing the gate/up launch of all three phases made the step
     # host-bound (144 us against 130 us untimed).  Step i times the gate/up
@@ -303,15 +328,16 @@ def bench_decode70b(tp, args):
     lib = tp.load()
     gmask = 1 << tp.kernel_kinds().index("gateup_decode")
 
+    def wset(i, idx):
+        return sets[(nph * i + idx) % len(sets)]
+
     def step(i):
-        wset = sets[i % len(sets)]
         for idx, ph in enumerate(phases):
-            ph.run(wset, (lib, gmask) if i % len(phases) == idx else None)
+            ph.run(wset(i, idx), (lib, gmask) if i % nph == idx else None, other=i)
 
     def step_plain(i):
-        wset = sets[i % len(sets)]
-        for ph in phases:
-            ph.run(wset)
+        for idx, ph in enumerate(phases):
+            ph.run(wset(i, idx), other=i)
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
     elapsed, prof = timed(tp, step, steps, warmup, [])
@@ -324,28 +350,31 @@ def bench_decode70b(tp, args):
     kern = {}
     for name, b in (("gateup_decode", gu_bytes), ("down_decode", dn_bytes), ("partial_reduce", red_bytes)):
         ms, cnt = prof_all.get(name, (0.0, 0))
-        kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
-                      "GBps": b / (ms * 1e-3) / 1e9 if ms > 0 else None}
+        kern[name] = {"launches": cnt, "avg_us": round(1e3 * ms / max(cnt, 1), 3),
+                      "GBps": round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
     ms, cnt = prof["gateup_decode"]
     assert cnt == steps
     timed_bytes = sum(workloads.gateup_bytes(ph.M, h, I_s) * sum(1 for i in range(warmup, warmup + steps)
-                                                                   if i % len(phases) == idx)
+                                                                   if i % nph == idx)
                       for idx, ph in enumerate(phases))
     achieved = timed_bytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
-            "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases}}
+            "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases},
+            "avg_us": round(1e3 * ms / cnt, 3),
+            "source": "HIP events on the gate/up launch of one phase per timed step (phase i mod 3), "
+                      "on the launch stream; achieved = their algorithmic bytes / their summed durations"}
     fwd_time_ms = sum(prof_all[k][0] for k in ("gateup_decode", "down_decode")) / steps
     fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
     # parity sample at full size, outside the timed region: the M=1 forward alone on weight set 0
     # (the step's reduce overwrites the partial in place)
     parity = None
     if not args.no_cpu_baseline:
+        import torch
         ph = phases[0]
         ph.run(sets[0])
-        ph.calls[id(sets[0])][0]()
-        import torch
+        ph.calls[(id(sets[0]), 0)][0]()
         torch.cuda.synchronize()
         ref = oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
                                                host0["w_down"], "bf16")
@@ -358,7 +387,9 @@ def bench_decode70b(tp, args):
                                    "M=1, 8 and 64 tokens, each forward followed by the 8-way fp32 "
                                    "partial reduce" % (", (out, in) layout" if args.row_major else
                                                        ", packed for the decode kernels"),
-                       "M": list(c["M"]), "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
+                       "M": list(c["M"]), "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets),
+                       "weight_set_of_phase": "(3 * step + phase) mod weight_sets",
+                       "other_partial_sets": N_OTHER_SETS},
                roofline=roof,
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
                forward_only={"GBps": round(fwd_bytes / (fwd_time_ms * 1e-3) / 1e9, 1),
@@ -374,7 +405,7 @@ def bench_decode70b(tp, args):
                 p = oracle.rank_partial_from_storage(ph.x_host, "bf16", host0["w_gate"], host0["w_up"],
                                                      host0["w_down"], "bf16")
                 oracle.fold_fp32([p.astype(np.float32).reshape(-1)] + [hp] * (t - 1))
-        log("timing the CPU oracle")
+        log("timing the CPU oracle (decode)")
         out["cpu_baseline"] = cpu_baseline(once, step_bytes / 1e9, "GB/s",
                                            "one full step (M=1, 8, 64 rank partials from the bf16 "
                                            "weight bytes + 8-way fp32 folds), repeated >= 10 s")
@@ -383,10 +414,10 @@ def bench_decode70b(tp, args):
 
 def bench_prefill(tp, args, cfg_id, M, label):
     import oracle
-    import torch
     c = workloads.CONFIGS[cfg_id]
     h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
     n_sets = 1   # compute-bound: weight reuse across tokens dwarfs any cache effect
+    log("generating the %s inputs" % c["name"])
     sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
     ph = Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, c["reduce_n"] is not None)
 
@@ -404,16 +435,30 @@ def bench_prefill(tp, args, cfg_id, M, label):
     gu_tf = (4 * M * h * I_s) * gu_n / (gu_ms * 1e-3) / 1e12
     dn_tf = (2 * M * h * I_s) * dn_n / (dn_ms * 1e-3) / 1e12
     fwd_tf = flops * steps / ((gu_ms + dn_ms) * 1e-3) / 1e12
-    kern = {"gateup_prefill": {"launches": gu_n, "avg_us": 1e3 * gu_ms / gu_n, "TFLOPs": round(gu_tf, 1)},
-            "down_prefill": {"launches": dn_n, "avg_us": 1e3 * dn_ms / dn_n, "TFLOPs": round(dn_tf, 1)}}
+    kern = {"gateup_prefill": {"launches": gu_n, "avg_us": round(1e3 * gu_ms / gu_n, 2), "TFLOPs": round(gu_tf, 1)},
+            "down_prefill": {"launches": dn_n, "avg_us": round(1e3 * dn_ms / dn_n, 2), "TFLOPs": round(dn_tf, 1)}}
+    red = None
     if "partial_reduce" in prof:
         ms, n = prof["partial_reduce"]
-        kern["partial_reduce"] = {"launches": n, "avg_us": 1e3 * ms / n,
-                                  "GBps": round(workloads.reduce_bytes(M * h, t) * n / (ms * 1e-3) / 1e9, 1)}
+        rb = workloads.reduce_bytes(M * h, t)
+        gbs = rb * n / (ms * 1e-3) / 1e9
+        kern["partial_reduce"] = {"launches": n, "avg_us": round(1e3 * ms / n, 2), "GBps": round(gbs, 1)}
+        red = {"value": round(gbs, 1), "unit": "GB/s", "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+               "config": {"workload": "%d-way fp32 partial reduce of %dx%d, in place into the rank's partial "
+                                      "(the reduce of the prefill step)" % (t, M, h), "t": t, "n": M * h},
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "traffic": recorded_traffic("partial_reduce", "reduce70b" if cfg_id == 3 else
+                                                        "reduce405b"),
+                            "kernel": "partial_reduce", "per_launch_bytes": rb,
+                            "avg_us": round(1e3 * ms / n, 2),
+                            "source": "HIP events on every reduce launch of a further pass of the same steps"}}
     roof = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
-            "traffic": recorded_traffic("gateup_prefill", args.workload), "kernel": "gateup_prefill",
-            "per_launch_flop": 4 * M * h * I_s}
+            "traffic": recorded_traffic("gateup_prefill", args.workload if args.workload != "default" else
+                                        "prefill70b"),
+            "kernel": "gateup_prefill", "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
+            "source": "HIP events on every gate/up launch of the timed steps, on the launch stream"}
     out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="bf16", data="synthetic",
@@ -427,11 +472,41 @@ def bench_prefill(tp, args, cfg_id, M, label):
         def once():
             oracle.rank_partial_from_storage(ph.x_host[rows], "bf16", host0["w_gate"], host0["w_up"],
                                              host0["w_down"], w, host0["s_gate"], host0["s_up"], host0["s_down"])
-        log("timing the CPU oracle")
+        log("timing the CPU oracle (prefill)")
         out["cpu_baseline"] = cpu_baseline(once, workloads.forward_flops(len(rows), h, I_s) / 1e12, "TFLOP/s",
                                            "rank partial for %d of the %d token rows (decoding the weight "
                                            "bytes each time), repeated >= 10 s" % (len(rows), M))
+        if red is not None:
+            sub = max(1, (M * h) // 16)
+            hp = [ph.others[0][j][:sub].cpu().numpy() for j in range(t - 1)]
+            hp = [np.random.Generator(np.random.PCG64(7)).standard_normal(sub, dtype=np.float32)] + hp
+            log("timing the CPU oracle (reduce)")
+            red["cpu_baseline"] = cpu_baseline(lambda: oracle.fold_fp32(hp), workloads.reduce_bytes(sub, t) / 1e9,
+                                               "GB/s", "fold of the first %d elements of each of the %d buffers, "
+                                               "repeated >= 10 s" % (sub, t), max_reps=1 << 30)
+    if red is not None:
+        out["reduce"] = red
     return out
+
+
+def bench_default(tp, args):
+    """The metric's two halves in one line: the 70B TP=8 decode step (value,
+    GB/s) and, beside it, the 70B TP=8 prefill step (TFLOP/s: forward + the
+    8-way reduce of its 4096 x 8192 partial) with the reduce's own GB/s."""
+    out = bench_decode70b(tp, args)
+    pre = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL)
+    red = pre.pop("reduce", None)
+    out["prefill"] = {k: pre[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "config", "roofline",
+                                          "forward_only_TFLOPs", "forward_frac_of_bf16_peak", "kernels",
+                                          "cpu_baseline") if k in pre}
+    out["prefill"]["frac_of_bf16_peak"] = round(pre["value"] / BF16_PEAK_TFLOPS, 4)
+    if red is not None:
+        out["reduce"] = red
+    return out
+
+
+PREFILL70B_LABEL = ("70B-shaped TP=8 rank prefill, M=4096, h=8192, I_s=3584, bf16, forward + 8-way fp32 partial "
+                    "reduce of 4096x8192")
 
 
 W_LABEL = {"e4m3fn": "fp8 e4m3fn", "int8": "int8"}
@@ -444,8 +519,8 @@ def bench_quant(tp, args, cfg_id):
     c = workloads.CONFIGS[cfg_id]
     h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
     dec_Ms, pre_M = list(c["M"][:-1]), c["M"][-1]
-    # enough weight sets that a step's weights come from HBM (>= 3 x 256 MB)
-    n_sets = max(2, min(args.weight_sets, (768 << 20) // (3 * h * I_s) + 1))
+    # enough weight sets that a set is read again only after >= 768 MB of others
+    n_sets = max(2, (768 << 20) // (3 * h * I_s * (1 if w != "bf16" else 2)) + 2)
     sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
     decs = [Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, False) for M in dec_Ms]
     pre = Phase(tp, cfg_id, pre_M, h, I_s, t, "bf16", w, False)
@@ -455,8 +530,9 @@ def bench_quant(tp, args, cfg_id):
         [dict(d, packed=tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)) for d in sets]
 
     def step(i):
-        for ph in decs:
-            ph.run(dsets[i % len(dsets)])
+        # each phase of a step reads its own weight set
+        for idx, ph in enumerate(decs):
+            ph.run(dsets[(len(decs) * i + idx) % len(dsets)])
 
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
     el_d, prof_d = timed(tp, step, steps, warmup, ["gateup_decode"])
@@ -583,7 +659,8 @@ def bench_reduce(tp, args, cfg_id):
         sub = max(1, n // 16)
         hp = [p[:sub] for p in parts_host]
         res["cpu_baseline"] = cpu_baseline(lambda: oracle.fold_fp32(hp), workloads.reduce_bytes(sub, t) / 1e9,
-                                           "GB/s", "fold of the first %d elements of each buffer" % sub)
+                                           "GB/s", "fold of the first %d elements of each buffer, repeated "
+                                           ">= 10 s" % sub, max_reps=1 << 30)
     return res
 
 
@@ -743,15 +820,14 @@ def bench_attn_decode(tp, args):
     lib = tp.load()
     qmask = 1 << tp.kernel_kinds().index("qkv_decode")
 
+    # each phase of a step reads its own weight set: phase idx of step i takes set (3 i + idx) mod n
     def step(i):
-        wset = sets[i % len(sets)]
         for idx, ph in enumerate(phases):
-            ph.run(wset, (lib, qmask) if i % 3 == idx else None)
+            ph.run(sets[(3 * i + idx) % len(sets)], (lib, qmask) if i % 3 == idx else None)
 
     def step_plain(i):
-        wset = sets[i % len(sets)]
-        for ph in phases:
-            ph.run(wset)
+        for idx, ph in enumerate(phases):
+            ph.run(sets[(3 * i + idx) % len(sets)])
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
     elapsed, prof = timed(tp, step, steps, warmup, [])
@@ -897,11 +973,12 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     tp.load()
-    if args.workload == "decode70b":
+    if args.workload == "default":
+        out = bench_default(tp, args)
+    elif args.workload == "decode70b":
         out = bench_decode70b(tp, args)
     elif args.workload == "prefill70b":
-        out = bench_prefill(tp, args, 3, 4096, "70B-shaped TP=8 rank prefill, M=4096, h=8192, I_s=3584, "
-                                               "bf16, forward + 8-way fp32 partial reduce of 4096x8192")
+        out = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL)
     elif args.workload == "prefill405b":
         out = bench_prefill(tp, args, 5, 8192, "405B-shaped TP=8 rank prefill, M=8192, h=16384, I_s=6656, "
                                                "bf16, forward + 8-way fp32 partial reduce of 8192x16384")
