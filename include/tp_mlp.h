@@ -144,6 +144,40 @@ tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full,
                                void* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * tp_mlp_shard_forward without its workspace argument.  The forward's
+ * scratch (the intermediate A and, for a prefill with a stream-K tail, its
+ * arrival counters and slots) lives in a static device array of
+ * TP_NOALLOC_SCRATCH_BYTES bytes, one per device the library runs on, held
+ * until the process ends.  The call allocates nothing and calls no
+ * allocating routine (its first call on a device looks up that device's
+ * array address once).  Every call on a device shares the array and it keeps
+ * the last call's contents (the counters are cleared by a kernel of the
+ * call itself): calls that overlap in time on one device (several streams
+ * or host threads) race and give undefined results; calls on one stream are
+ * ordered and safe.  With kernel timing on, only launches with events made
+ * beforehand by tp_profile_reserve are timed.
+ *
+ * Arguments, requirements, errors and results (bit for bit) are those of
+ * tp_mlp_shard_forward.  A forward whose tp_mlp_workspace_bytes(...) is
+ * larger than TP_NOALLOC_SCRATCH_BYTES returns TP_ERR_UNSUPPORTED and
+ * launches nothing (the 70B shard at TP = 8 needs 7 KB per token for A, so a
+ * 4096-token prefill fits).
+ */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+tp_status tp_mlp_shard_forward_noalloc(int64_t M, int64_t h, int64_t I_full,
+                                       int32_t t, int32_t k,
+                                       int32_t act_dtype, int32_t w_dtype,
+                                       const void* x, int64_t ldx,
+                                       const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                       const void* w_down, int64_t ldw_down,
+                                       const float* s_gate, const float* s_up,
+                                       const float* s_down,
+                                       float* partial, int64_t ldp, void* stream);
+
+/*
  * out[i] = (((partials[0][i] + partials[1][i]) + partials[2][i]) + ...)
  *          + partials[t-1][i]   for 0 <= i < n, fp32 round-to-nearest-even,
  * no fused operations and no flush of subnormals: bit-exact against that

@@ -23,7 +23,7 @@ from . import _lib
 from ._lib import (TPError, TP_F32, TP_BF16, TP_FP8_E4M3FN, TP_INT8, EXPORTED_SYMBOLS,  # noqa: F401
                    LIB_PATH, load)
 
-__all__ = ["shard_forward", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
+__all__ = ["shard_forward", "shard_forward_noalloc", "partial_reduce", "prepare_shard_forward", "prepare_partial_reduce",
            "shard_forward_sp", "prepare_shard_forward_sp", "partial_reduce_scatter",
            "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_workspace_bytes", "attn_qkv_forward",
            "w8a8_workspace_bytes", "shard_forward_w8a8", "prepare_shard_forward_w8a8", "quantize_rows_e4m3", "prepare_attn_qkv_forward",
@@ -126,6 +126,38 @@ def prepare_shard_forward(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=No
     (attribute ``partial`` is the output tensor)."""
     return _prepare_forward([x], False, w_gate, w_up, w_down, t, k, s_gate, s_up, s_down, partial, workspace,
                             stream)
+
+
+def shard_forward_noalloc(x, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None, partial,
+                          stream=None):
+    """``shard_forward`` through the allocation-free entry point
+    (``include/tp_mlp.h``: tp_mlp_shard_forward_noalloc): the library's
+    static per-device scratch replaces the workspace, and ``partial`` (M, h)
+    fp32 must be given, so the call allocates nothing.  Calls that overlap in
+    time on one device race on that scratch."""
+    device = x.device
+    _check_matrix("x", x, device)
+    for name, m in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+        _check_matrix(name, m, device)
+    _check_matrix("partial", partial, device)
+    M, h = x.shape
+    I_s = w_gate.shape[0]
+    wc = _w_code(w_gate.dtype)
+    if _w_code(w_up.dtype) != wc or _w_code(w_down.dtype) != wc:
+        raise TypeError("w_gate, w_up and w_down must share a dtype")
+    if tuple(w_up.shape) != (I_s, h) or tuple(w_gate.shape) != (I_s, h) or tuple(w_down.shape) != (h, I_s):
+        raise ValueError("shard shapes must be w_gate/w_up (I_s, h) and w_down (h, I_s)")
+    if w_gate.stride(0) != w_up.stride(0):
+        raise ValueError("w_gate and w_up must share a leading dimension")
+    for name, s, n in (("s_gate", s_gate, I_s), ("s_up", s_up, I_s), ("s_down", s_down, h)):
+        _check_scales(s, device, n, name)
+    if partial.dtype != torch.float32 or tuple(partial.shape) != (M, h):
+        raise ValueError("partial must be float32 of shape (%d, %d)" % (M, h))
+    _lib.check(_lib.load().tp_mlp_shard_forward_noalloc(
+        M, h, I_s * int(t), int(t), int(k), _act_code(x.dtype), wc, _ptr(x), x.stride(0), _ptr(w_gate), _ptr(w_up),
+        w_gate.stride(0), _ptr(w_down), w_down.stride(0), _ptr(s_gate), _ptr(s_up), _ptr(s_down), _ptr(partial),
+        partial.stride(0), _stream_of(device, stream)))
+    return partial
 
 
 def shard_forward_sp(x_blocks, w_gate, w_up, w_down, *, t, k, s_gate=None, s_up=None, s_down=None,

@@ -20,6 +20,7 @@ TP_OK, TP_ERR_INVALID_ARG, TP_ERR_UNSUPPORTED, TP_ERR_WORKSPACE, TP_ERR_HIP = 0,
 EXPORTED_SYMBOLS = (
     "tp_mlp_workspace_bytes",
     "tp_mlp_shard_forward",
+    "tp_mlp_shard_forward_noalloc",
     "tp_mlp_packed_weights_bytes",
     "tp_mlp_pack_weights",
     "tp_mlp_shard_forward_packed",
@@ -71,6 +72,10 @@ def load():
         c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
         vp, c_i64, vp, vp, c_i64, vp, c_i64, vp, vp, vp, vp, c_i64, vp, ctypes.c_size_t, vp]
     lib.tp_mlp_shard_forward.restype = c_i32
+    lib.tp_mlp_shard_forward_noalloc.argtypes = [
+        c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32,
+        vp, c_i64, vp, vp, c_i64, vp, c_i64, vp, vp, vp, vp, c_i64, vp]
+    lib.tp_mlp_shard_forward_noalloc.restype = c_i32
     lib.tp_partial_reduce.argtypes = [c_i64, c_i32, ctypes.POINTER(vp), vp, vp]
     lib.tp_partial_reduce.restype = c_i32
     lib.tp_mlp_shard_forward_sp.argtypes = [

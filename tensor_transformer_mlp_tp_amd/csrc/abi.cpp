@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
@@ -129,6 +130,8 @@ struct ProfRec {
 uint32_t g_prof_mask = 0;   // bit i: time kernels of kind i
 std::vector<ProfRec> g_prof_pool;
 size_t g_prof_used = 0;
+// Set during an allocation-free call: timing then uses reserved events only.
+thread_local bool g_no_alloc = false;
 
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
@@ -156,7 +159,7 @@ void profile_events_for_launch(int kind, hipEvent_t* start, hipEvent_t* stop) {
   *start = nullptr;
   *stop = nullptr;
   if (kind < 0 || kind >= 32 || !((g_prof_mask >> kind) & 1u)) return;
-  if (g_prof_used == g_prof_pool.size() && !prof_grow()) return;
+  if (g_prof_used == g_prof_pool.size() && (g_no_alloc || !prof_grow())) return;
   ProfRec& r = g_prof_pool[g_prof_used++];
   r.kind = kind;
   *start = r.start;
@@ -280,6 +283,68 @@ TP_API tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full, int3
   const void* blocks[1] = {x};
   return forward_impl(M, h, I_full, t, k, act_dtype, w_dtype, blocks, 1, M, ldx, w_gate, w_up, ldw_gu, w_down,
                       ldw_down, s_gate, s_up, s_down, partial, ldp, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------ allocation-free forward
+
+namespace {
+
+// The allocation-free forward's scratch: one array per device (each device
+// that loads the library's code object holds its own copy until the process
+// ends).  In host code `noalloc_scratch` names a host-side stand-in, not the
+// device array: device code reaches the array only through the address
+// hipGetSymbolAddress returns for the current device, kept per device.
+static __device__ __align__(256) uint8_t noalloc_scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+void* g_noalloc_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up on the
+// first call on that device.
+tp_status noalloc_scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(TP_ERR_UNSUPPORTED, "device index %d is not below %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  if (!g_noalloc_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc_scratch));
+    if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress (allocation-free scratch)");
+    if (!p || !aligned(p, 256)) return fail(TP_ERR_HIP, "allocation-free scratch has no 256-byte aligned address");
+    g_noalloc_ptr[dev] = p;
+  }
+  *out = g_noalloc_ptr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+TP_API tp_status tp_mlp_shard_forward_noalloc(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
+                                              int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
+                                              const void* w_gate, const void* w_up, int64_t ldw_gu,
+                                              const void* w_down, int64_t ldw_down, const float* s_gate,
+                                              const float* s_up, const float* s_down, float* partial,
+                                              int64_t ldp, void* stream) {
+  const tp_status st = check_shapes(M, h, I_full, t, k, act_dtype, w_dtype);
+  if (st != TP_OK) return st;
+  const int64_t need = workspace_need(M, h, I_full / t, act_dtype, w_dtype);
+  if (need > (int64_t)TP_NOALLOC_SCRATCH_BYTES)
+    return fail(TP_ERR_UNSUPPORTED, "this forward needs %lld bytes of scratch; the allocation-free entry point "
+                "holds %llu (use tp_mlp_shard_forward with a workspace)", (long long)need,
+                (unsigned long long)TP_NOALLOC_SCRATCH_BYTES);
+  void* scratch = nullptr;
+  const tp_status sp = noalloc_scratch_ptr(&scratch);
+  if (sp != TP_OK) return sp;
+  const void* blocks[1] = {x};
+  g_no_alloc = true;
+  const tp_status r = forward_impl(M, h, I_full, t, k, act_dtype, w_dtype, blocks, 1, M, ldx, w_gate, w_up, ldw_gu,
+                                   w_down, ldw_down, s_gate, s_up, s_down, partial, ldp, scratch,
+                                   TP_NOALLOC_SCRATCH_BYTES, stream);
+  g_no_alloc = false;
+  return r;
 }
 
 // ------------------------------------------------------------ packed decode weights
