@@ -636,6 +636,215 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
                                           m0 + wm * (BM / WM), r32, g, s0, s1, sx, out, ld_out);
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong GEMM: bf16 weights and activations, 256 x 256 tiles, eight waves.
+//
+// What bounds the four-wave kernel above, measured on MI355X: a CU moves
+// global memory into LDS at about 35 bytes per clock for this access pattern
+// (rows of 128 bytes), which a 64-k stage of a 256 x 256 tile (64 KB) needs
+// about 1800 clocks for, close to the 2048 clocks its MFMAs take; and a wave
+// that issues direct-to-LDS loads stalls on them at that rate, issuing no
+// MFMAs meanwhile.  With one wave per SIMD the loads and the MFMAs therefore
+// take turns instead of overlapping.
+//
+// Here two waves share each SIMD, in two groups of four (A: waves 0-3, B:
+// 4-7; a workgroup's waves go to the SIMDs in turn, so each SIMD holds one of
+// each).  Each wave alternates a compute phase (the 32 MFMAs of one 64-k
+// stage, with that stage's fragment reads from LDS threaded between them)
+// and a load phase (issue 8 KB of direct-to-LDS loads), and the groups are
+// one phase apart, so on every SIMD one wave issues MFMAs while the other
+// waits on its loads, and the loads stream continuously.  Workgroup barriers
+// (all eight waves) separate the phases; compute phases run at raised wave
+// priority (s_setprio).
+//
+// Output split: wave q of a group (q = wave % 4) owns 64 weight rows (in a
+// gate/up tile: the gate rows of 32 channels and the same channels' up rows)
+// and its group's 128 tokens (A: tokens 0-127 of the tile, B: 128-255), 2 x 4
+// blocks of 32 x 32 (128 fp32 accumulators per lane).
+//
+// LDS: a ring of five half-stages of 32 KB (160 KB): the activation half X_s
+// (256 token rows x 64 k) of stage s sits in buffer 2s mod 5, its weight half
+// W_s in buffer 2s+1 mod 5.  Group A loads the X halves, group B the W
+// halves.  In phase slots between barriers (slot 0 = the prologue):
+//   slot 2s+1: A computes stage s,  B loads W_{s+1};
+//   slot 2s+2: B computes stage s,  A loads X_{s+2}.
+// A half-stage's buffer was freed at least one slot before its loads are
+// issued, X_s has two slots after its load slot to land and W_s one; each
+// wave waits for its own loads (vmcnt) before the barrier after which they
+// are read.
+template <bool SWIGLU, bool OBF, bool SK>
+__global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, const XRows xr,
+                                                         const uint8_t* __restrict__ w0,
+                                                         const uint8_t* __restrict__ w1, int64_t ldw,
+                                                         void* __restrict__ out, int64_t ld_out, int tiles_m,
+                                                         int tiles_n, const SkTail sk) {
+  constexpr int BM = 256, BK = 64, WV = 8;
+  constexpr int CB = 2, TB = 4;               // 32-row weight blocks, 32-token blocks per wave
+  constexpr int ROWB = BK * 2;                // bytes per LDS row
+  constexpr int HALF = 256 * ROWB;            // one half-stage: 256 rows
+  constexpr int NH = 5;                       // half-stages in the ring
+  constexpr int LPH = HALF / 1024 / 4;        // 1 KB loads per wave per half-stage
+  constexpr int RPI = 1024 / ROWB;            // rows per 1 KB load
+  constexpr int CH = ROWB / 16;               // 16-byte chunks per row
+  constexpr int KSUB = BK / 16;               // MFMA sub-steps per stage
+  constexpr int TILE_N = SWIGLU ? BN / 2 : BN;
+  static_assert(NH * HALF <= 160 * 1024, "LDS");
+  // One LDS object (the stream-K flag reuses its first bytes once the ring
+  // has drained).
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NH * HALF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool grpB = wave >= 4;
+  const int q = wave & 3;
+  const int r32 = lane & 31, g = lane >> 5;
+
+  // ---- tile and k-range (as gemm_kernel)
+  const int KT = K / BK;
+  const int blk = blockIdx.x;
+  int L, kt0 = 0, kt1 = KT, tail = -1, piece = 0;
+  if (SK && blk >= sk.nfull) {
+    const int rem = tiles_m * tiles_n - sk.nfull;
+    const int j = xcd_fold(blk - sk.nfull, rem * sk.d);
+    piece = j / rem;
+    tail = j - piece * rem;
+    kt0 = (int)((int64_t)piece * KT / sk.d);
+    kt1 = (int)((int64_t)(piece + 1) * KT / sk.d);
+    L = sk.nfull + tail;
+  } else {
+    L = xcd_fold(blk, SK ? sk.nfull : tiles_m * tiles_n);
+  }
+  const TileCoord tc = tile_coord(L, tiles_m, tiles_n);
+  const int m0 = tc.tm * BM;
+  const int n0 = tc.tn * TILE_N;
+
+  // ---- this wave's loads: rows q*64 + 8i + lane/8 of its group's half
+  // (A: token rows of X, B: weight rows), 128 bytes each, chunk-swizzled
+  const uint8_t* src[LPH];
+#pragma unroll
+  for (int i = 0; i < LPH; ++i) {
+    const int row = q * (256 / 4) + i * RPI + lane / CH;
+    const int c = (lane % CH) ^ swz<ROWB>(row);
+    if (!grpB) {
+      src[i] = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, min(m0 + row, M - 1))) + c * 16;
+    } else {
+      int ch;
+      const uint8_t* base;
+      if constexpr (SWIGLU) {
+        ch = n0 + (row & (BN / 2 - 1));
+        base = row < BN / 2 ? w0 : w1;
+      } else {
+        ch = n0 + row;
+        base = w0;
+      }
+      src[i] = base + (int64_t)min(ch, N - 1) * ldw * 2 + c * 16;
+    }
+  }
+  // half-stage of stage kt (clamped to the k-range: past its end the last
+  // stage is loaded again, so every load phase issues the same count) into
+  // ring buffer `hb`
+  auto load_half = [&](int kt, int hb) {
+    kt = min(kt, kt1 - 1);
+    uint8_t* dst = lds + hb * HALF + q * (HALF / 4);
+#pragma unroll
+    for (int i = 0; i < LPH; ++i) load_lds16(src[i] + (int64_t)kt * BK * 2, dst + i * 1024);
+  };
+
+  // ---- fragment rows
+  int wrow[CB], xrow[TB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) wrow[cb] = SWIGLU ? cb * (BN / 2) + q * 32 + r32 : q * 64 + cb * 32 + r32;
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) xrow[tb] = (grpB ? 128 : 0) + tb * 32 + r32;
+
+  f32x16 acc[CB][TB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
+
+  auto barrier = [&]() {
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // compute phase of stage kt (ring position s = kt - kt0): fragment reads of
+  // sub-step kk+1 threaded between the MFMAs of sub-step kk
+  auto compute = [&](int s) {
+    const uint8_t* sx = lds + ((2 * s) % NH) * HALF;
+    const uint8_t* sw = lds + ((2 * s + 1) % NH) * HALF;
+    bf16x8 wf[2][CB], xf[2][TB];
+    auto read = [&](int kk, bf16x8 (&w_)[CB], bf16x8 (&x_)[TB]) {
+      const int c = 2 * kk + g;
+      w_[0] = as_bf16x8(lds_read16(sw + wrow[0] * ROWB + ((c ^ swz<ROWB>(wrow[0])) * 16)));
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        x_[tb] = as_bf16x8(lds_read16(sx + xrow[tb] * ROWB + ((c ^ swz<ROWB>(xrow[tb])) * 16)));
+#pragma unroll
+      for (int cb = 1; cb < CB; ++cb)
+        w_[cb] = as_bf16x8(lds_read16(sw + wrow[cb] * ROWB + ((c ^ swz<ROWB>(wrow[cb])) * 16)));
+    };
+    __builtin_amdgcn_s_setprio(1);
+    read(0, wf[0], xf[0]);
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      if (kk + 1 < KSUB) read(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+    }
+    // reads of sub-step 0, then per sub-step its MFMAs with the next
+    // sub-step's reads threaded one after each of the first MFMAs
+    constexpr int NMF = CB * TB, NRD = CB + TB;
+    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+    sched_substep<NRD, NMF>();
+    sched_substep<NRD, NMF>();
+    sched_substep<NRD, NMF>();
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // ---- prologue (slot 0): A loads X_0 and X_1, B loads W_0
+  if (!grpB) {
+    load_half(kt0, 0);
+    load_half(kt0 + 1, 2);
+    wait_vmcnt<LPH>();
+  } else {
+    load_half(kt0, 1);
+    wait_vmcnt<0>();
+  }
+  barrier();
+
+  // slots 1 .. 2S: A computes in the odd ones, B in the even ones
+  const int S = kt1 - kt0;
+  for (int j = 1; j <= 2 * S; ++j) {
+    if (((j & 1) != 0) != grpB) {
+      compute(grpB ? j / 2 - 1 : j / 2);       // stage s: slot 2s+1 (A), 2s+2 (B)
+      if (grpB) wait_vmcnt<0>();                // B: its W_{s+1} has landed
+    } else {
+      // A, slot 2s+2: X_{s+2} into buffer 2s+4; B, slot 2s+1: W_{s+1} into 2s+3
+      const int s = grpB ? j / 2 : j / 2 - 1;
+      load_half(kt0 + s + (grpB ? 1 : 2), (2 * s + (grpB ? 3 : 4)) % NH);
+      if (!grpB) wait_vmcnt<LPH>();             // A: its X_{s+1} has landed
+    }
+    barrier();
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // no direct load is left in flight at exit
+
+  if constexpr (SK) {
+    if (tail >= 0 && !sk_handoff<CB, TB, WV * 64, BM>(acc, sk, tail, piece, tid, reinterpret_cast<int*>(lds)))
+      return;
+  }
+  store_tile<SWIGLU, kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + (SWIGLU ? q * 32 : q * 64),
+                                                     m0 + (grpB ? 128 : 0), r32, g, nullptr, nullptr, nullptr,
+                                                     out, ld_out);
+}
+
 // Stage shape: bf16 weights use two stages of BK = 64 (128 KB of LDS); fp8
 // weights, with 48 KB stages, fit three.
 constexpr int kBK = 64;
@@ -743,6 +952,14 @@ hipError_t run_gemm_bm(int kind, int M, int N, int K, const XRows& xr, const voi
     grid = (unsigned)(p.nfull + p.rem * p.d);
     const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
     if (e != hipSuccess) return e;
+  }
+  if constexpr (BM == 256 && WB == kWeightWide && !A8) {
+    // bf16 x bf16 on 256 x 256 tiles: the eight-wave ping-pong kernel
+    if (p.d)
+      return launch(kind, gemm_pp_kernel<SWIGLU, OBF, true>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
+                    (const uint8_t*)w0, (const uint8_t*)w1, ldw, out, ldo, tiles_m, tiles / tiles_m, sk);
+    return launch(kind, gemm_pp_kernel<SWIGLU, OBF, false>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
+                  (const uint8_t*)w0, (const uint8_t*)w1, ldw, out, ldo, tiles_m, tiles / tiles_m, sk);
   }
   if (p.d)
     return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, BM, OBF, A8, true>, dim3(grid), dim3(kWV * 64), 0, stream, M,

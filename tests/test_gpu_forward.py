@@ -212,6 +212,24 @@ def test_full_shape_short_tiles(cfg, M):
     _full_prefill(cfg, M)
 
 
+# ------------------------------------------------------------ 256 x 256 tiles (enough tiles to fill the chip)
+
+@pytest.mark.parametrize("M,h,I_s", [
+    (2048, 512, 3072),    # gate/up: 8 x 24 = 192 tiles of 256 x 256; down on shorter tiles
+    (2000, 512, 3136),    # gate/up: ragged last M-tile (208 tokens) and last channel tile (64 of 128)
+    (2048, 6144, 256),    # down: 8 x 24 = 192 tiles; K = 256
+    (1900, 6464, 320),    # down: ragged M-tile (108 tokens) and feature tile (64 of 256), K = 320
+])
+def test_full_tiles_ragged(M, h, I_s):
+    print("256x256 tiles M=%d h=%d I_s=%d" % (M, h, I_s), flush=True)
+    x, ws = make_case(49, M, h, I_s, "bf16", "bf16", 0.05, 0.05, weight_set=M)
+    d = upload_case(x, ws, "bf16", "bf16")
+    p = run_forward(d, 2, 0)
+    p2 = run_forward(d, 2, 1)
+    assert torch.equal(p.view(torch.int32), p2.view(torch.int32))
+    check(p.cpu().numpy(), oracle_partial(x, ws, "bf16", "bf16"), TOL_BF16, "256x256 M=%d h=%d I_s=%d" % (M, h, I_s))
+
+
 # ------------------------------------------------------------ stream-K tail of the prefill GEMMs
 
 @pytest.mark.parametrize("M,h,I_s", [
