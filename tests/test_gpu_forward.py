@@ -263,6 +263,30 @@ def test_stream_k_tail(M, h, I_s, w):
     check(outs[0].cpu().numpy(), oracle_partial(x, ws, "bf16", w), tol, "stream-K M=%d %s" % (M, w))
 
 
+def test_stream_k_runs_across_tiles():
+    """256-token tiles past the last whole round cut along K: gate/up has 10 x
+    32 = 320 tiles (64 past the round, each in 4 pieces of 32 of its 128
+    k-tiles) and down 10 x 32 = 320 (64 in 4 pieces of 16 of 64); the last
+    token tile is ragged.  The arrival counters and piece slots live in the
+    workspace, whose contents on entry must not matter, and the result must
+    not depend on which piece arrives last (bit-identical over calls)."""
+    M, h, I_s, t = 2500, 8192, 4096, 2
+    print("stream-K runs M=%d h=%d I_s=%d" % (M, h, I_s), flush=True)
+    x, ws = make_case(50, M, h, I_s, "bf16", "bf16", 0.02, 0.02)
+    d = upload_case(x, ws, "bf16", "bf16")
+    nbytes = tp.workspace_bytes(M, h, I_s * t, t)
+    assert nbytes >= M * I_s * 2 + 256 * 256 * 256 * 4        # counters and 256 piece slots
+    scratch = tp.alloc_workspace(nbytes, "cuda")
+    outs = []
+    for fill in (0x7F, 0x00, 0xFF):
+        scratch.fill_(fill)
+        outs.append(tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0, workspace=scratch))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    check(outs[0].cpu().numpy(), oracle_partial(x, ws, "bf16", "bf16"), TOL_BF16, "stream-K runs (all elements)")
+
+
 def test_stream_k_tail_after_whole_rounds():
     """More tiles than CUs: gate/up has 17 x 16 = 272 tiles, 256 computed whole
     and the 16 of the last (ragged) M-tile cut in 2 pieces; every element."""
