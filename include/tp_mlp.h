@@ -72,11 +72,16 @@ typedef enum {
 /*
  * Workspace bytes tp_mlp_shard_forward needs for these arguments (0 if the
  * arguments are invalid).  The workspace holds the intermediate activation A
- * (M x I_s, in the activation dtype) plus alignment padding, and for a bf16
- * prefill (M > 64; M > 32 with one-byte weights) whose output tiles do not
- * fill whole rounds of the 256 CUs the stream-K scratch of the two GEMMs:
- * arrival counters and one fp32 tile (256 weight rows by 64, 128 or 256
- * tokens) per piece of the tiles cut along K (at most 256 pieces, 64 MiB).
+ * (M x I_s, in the activation dtype) plus alignment padding, and
+ *  - for a bf16 prefill (M > 64; M > 32 with one-byte weights) whose output
+ *    tiles do not fill whole rounds of the 256 CUs, the stream-K scratch of
+ *    the two GEMMs: arrival counters and one fp32 tile (256 weight rows by
+ *    64, 128 or 256 tokens) per piece of the tiles cut along K (at most 256
+ *    pieces, 64 MiB);
+ *  - for a decode forward on the split-K streams (bf16 weights and
+ *    49 <= M <= 64, one-byte weights and 17 <= M <= 32), arrival counters
+ *    and one fp32 slot (128 weight rows by 16 * ceil(M / 16) tokens) per
+ *    tile and K range (about 224 slots, 8 MiB for the 70B shard at TP = 8).
  */
 size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                               int32_t act_dtype, int32_t w_dtype);
@@ -147,10 +152,10 @@ tp_status tp_mlp_shard_forward(int64_t M, int64_t h, int64_t I_full,
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation):
  * tp_mlp_shard_forward without its workspace argument.  The forward's
- * scratch (the intermediate A and, for a prefill with a stream-K tail, its
- * arrival counters and slots) lives in a static device array of
- * TP_NOALLOC_SCRATCH_BYTES bytes, one per device the library runs on, held
- * until the process ends.  The call allocates nothing and calls no
+ * scratch (the intermediate A and, for a prefill with a stream-K tail or a
+ * decode on the split-K streams, their arrival counters and slots) lives in
+ * a static device array of TP_NOALLOC_SCRATCH_BYTES bytes, one per device
+ * the library runs on, held until the process ends.  The call allocates nothing and calls no
  * allocating routine (its first call on a device looks up that device's
  * array address once).  Every call on a device shares the array and it keeps
  * the last call's contents (the counters are cleared by a kernel of the

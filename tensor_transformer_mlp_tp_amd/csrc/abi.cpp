@@ -115,8 +115,11 @@ tp_status check_shapes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t 
 int64_t workspace_a_bytes(int64_t M, int64_t I_s, int32_t act) { return round_up(M * I_s * elem_bytes(act), 256); }
 
 int64_t workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t act, int32_t w) {
-  const int64_t sk = act == TP_BF16 && M > tpmlp::forward_decode_max_m(weight_format(w))
-                         ? tpmlp::forward_prefill_sk_bytes((int)M, (int)h, (int)I_s, false) : 0;
+  const int wb = weight_format(w);
+  const int64_t sk = act != TP_BF16 ? 0
+                     : M > tpmlp::forward_decode_max_m(wb)
+                         ? tpmlp::forward_prefill_sk_bytes((int)M, (int)h, (int)I_s, false)
+                         : tpmlp::forward_decode_sk_bytes((int)M, (int)h, (int)I_s, wb);
   return workspace_a_bytes(M, I_s, act) + round_up(sk, 256);
 }
 
@@ -470,7 +473,8 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   a.ldp = ldp;
   a.a = workspace;
   a.lda = I_s;
-  a.sk = nullptr;
+  a.sk = need > workspace_a_bytes(M, I_s, act_dtype)
+             ? static_cast<uint8_t*>(workspace) + workspace_a_bytes(M, I_s, act_dtype) : nullptr;
   return from_hip(tpmlp::launch_forward_decode(a, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
 }
 

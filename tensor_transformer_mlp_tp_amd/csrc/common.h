@@ -33,6 +33,18 @@ inline hipError_t launch(int kind, void (*kernel)(Params...), dim3 grid, dim3 bl
   return hipGetLastError();
 }
 
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() would also
+// wait for every outstanding global load (vmcnt(0)), which would drain a
+// direct-load ring at each step; the ring's completion is tracked with
+// explicit vmcnt waits instead.
+// Before it, this wave's LDS reads are complete (lgkmcnt(0)); the acquire
+// fence after it keeps later LDS reads below the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // ---------------------------------------------------------------- numerics
 
 // fp32 -> bf16 bits, round to nearest even (inputs here are finite).

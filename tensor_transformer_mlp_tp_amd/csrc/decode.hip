@@ -46,6 +46,19 @@ namespace {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// Packed weights (pack_kernel below) store every 16-row block as a run of
+// 1 KB MFMA A fragments, block after block: fragment st of block blk, at
+// packed_frag(blk, nsteps, st), gives lane l (16 bytes) row l % 16's weight
+// bytes [64 st + 16 (l / 16), +16), i.e. 32 bf16 or 64 one-byte k-values of
+// the 16 rows.  (Interleaving the fragments of groups of 8 blocks, so that
+// a split-K workgroup's 8 blocks read one contiguous range per step, was
+// measured no faster there and a third slower for the one-block rings.)
+constexpr int kPackStep = 1024;           // bytes between a block's consecutive fragments
+constexpr int kPackJS = 4 * kPackStep;    // ... and between its consecutive ring slots (4 fragments)
+__host__ __device__ __forceinline__ int64_t packed_frag(int blk, int nsteps, int st) {
+  return ((int64_t)blk * nsteps + st) * kPackStep;
+}
+
 // Weights are read exactly once per call: non-temporal loads keep them from
 // displacing the activations, which every workgroup re-reads from L2.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
@@ -62,20 +75,20 @@ struct Batch {
   u32x4 xf[U][NT][XJ];
 };
 
-// Issue the loads of the batch starting at step s.  Steps at or past s_end
-// (only in the last, partial batch) re-read step s_end - 1, which is valid
-// memory; their products are skipped in mac_batch.
-template <int NT, int RB, int U, int WB>
+// Issue the loads of the batch starting at step s.  wrow[r]: this lane's
+// weight bytes of step 0 in row block r; step st adds st * JS bytes.  Steps
+// at or past s_end (only in the last, partial batch) re-read step s_end - 1,
+// which is valid memory; their products are skipped in mac_batch.
+template <int NT, int RB, int U, int WB, int JS>
 __device__ __forceinline__ void load_batch(Batch<NT, RB, U, WB>& bt, const uint8_t* const (&wrow)[RB],
                                            const uint16_t* const (&xrow)[NT], int s, int s_end, int grp) {
   constexpr int KSTEP = WB ? 64 : 32;
-  constexpr int EB = WB ? 1 : 2;
   constexpr int XJ = WB ? 2 : 1;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int64_t st = min(s + u, s_end - 1);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) bt.wf[u][r] = ld16_stream(wrow[r] + st * KSTEP * EB + grp * 16);
+    for (int r = 0; r < RB; ++r) bt.wf[u][r] = ld16_stream(wrow[r] + st * JS);
 #pragma unroll
     for (int b = 0; b < NT; ++b)
 #pragma unroll
@@ -118,22 +131,22 @@ __device__ __forceinline__ void mac_batch(f32x4 (&acc)[RB][NT], const Batch<NT, 
 
 // Steps [s_beg, s_end) with two register batches in flight: the loads of
 // batch i+1 are issued before the MFMAs of batch i.
-template <int NT, int RB, int U, int WB>
+template <int NT, int RB, int U, int WB, int JS>
 __device__ __forceinline__ void mac_range(f32x4 (&acc)[RB][NT], const uint8_t* const (&wrow)[RB],
                                           const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
                                           int s_beg, int s_end, int grp) {
   if (s_beg >= s_end) return;
   Batch<NT, RB, U, WB> b0, b1;
   int s = s_beg;
-  load_batch(b0, wrow, xrow, s, s_end, grp);
+  load_batch<NT, RB, U, WB, JS>(b0, wrow, xrow, s, s_end, grp);
   while (true) {
     int nxt = s + U;
-    if (nxt < s_end) load_batch(b1, wrow, xrow, nxt, s_end, grp);
+    if (nxt < s_end) load_batch<NT, RB, U, WB, JS>(b1, wrow, xrow, nxt, s_end, grp);
     mac_batch(acc, b0, xok, s_end - s);
     if (nxt >= s_end) break;
     s = nxt;
     nxt = s + U;
-    if (nxt < s_end) load_batch(b0, wrow, xrow, nxt, s_end, grp);
+    if (nxt < s_end) load_batch<NT, RB, U, WB, JS>(b0, wrow, xrow, nxt, s_end, grp);
     mac_batch(acc, b1, xok, s_end - s);
     if (nxt >= s_end) break;
     s = nxt;
@@ -179,12 +192,13 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   const int row16 = lane & 15;
   const int grp = lane >> 4;
   const int c0 = blockIdx.x * (8 * RB);
+  const int nsteps = h / KSTEP;
 
   const uint8_t* wrow[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int ch = min(c0 + 8 * r + (row16 & 7), I_s - 1);
-    wrow[r] = (row16 < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
+    wrow[r] = (row16 < 8 ? wg : wu) + (int64_t)ch * ldw * EB + grp * 16;
   }
   const uint16_t* xrow[NT];
   bool xok[NT];
@@ -195,7 +209,6 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
     xrow[b] = x_row<uint16_t>(xr, min(tok, M - 1));
   }
 
-  const int nsteps = h / KSTEP;
   const int s_beg = (wave * nsteps) / WAVES;
   const int s_end = ((wave + 1) * nsteps) / WAVES;
   f32x4 acc[RB][NT];
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(WAVES * 64) void gateup_decode_kernel(
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mac_range<NT, RB, UNROLL, WB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
+  mac_range<NT, RB, UNROLL, WB, KSTEP * EB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
 
   reduce_waves<NT, RB, WAVES>(acc, wave, lane, [&](int r, int b, f32x4 v) {
     f32x4 o;
@@ -243,12 +256,13 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   const int row16 = lane & 15;
   const int grp = lane >> 4;
   const int n0 = blockIdx.x * (16 * RB);
+  const int nsteps = I_s / KSTEP;
 
   const uint8_t* wrow[RB];
 #pragma unroll
   for (int r = 0; r < RB; ++r) {
     const int f = min(n0 + 16 * r + row16, h - 1);
-    wrow[r] = wd + (int64_t)f * ldw * EB;
+    wrow[r] = wd + (int64_t)f * ldw * EB + grp * 16;
   }
   const uint16_t* xrow[NT];
   bool xok[NT];
@@ -259,7 +273,6 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
     xrow[b] = a_in + (int64_t)min(tok, M - 1) * lda;
   }
 
-  const int nsteps = I_s / KSTEP;
   const int s_beg = (wave * nsteps) / WAVES;
   const int s_end = ((wave + 1) * nsteps) / WAVES;
   f32x4 acc[RB][NT];
@@ -267,7 +280,7 @@ __global__ __launch_bounds__(WAVES * 64) void down_decode_kernel(
   for (int r = 0; r < RB; ++r)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[r][b] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mac_range<NT, RB, UNROLL, WB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
+  mac_range<NT, RB, UNROLL, WB, KSTEP * EB>(acc, wrow, xrow, xok, s_beg, s_end, grp);
 
   reduce_waves<NT, RB, WAVES>(acc, wave, lane, [&](int r, int b, f32x4 v) {
     const int f = n0 + 16 * r + 4 * grp;  // features f .. f+3
@@ -329,13 +342,23 @@ __device__ __forceinline__ void wait_slot_peeled(int j) {
   }
 }
 
+// Byte offset, within one 16-row block of a ring slot, of row r's 16-byte
+// chunk q (q = 0..15; 16 weight bytes each).  From the (out, in) layout the
+// direct loads carry 4 rows x 256 bytes and the chunks sit XOR-swizzled by
+// row; packed weights (PK) arrive in MFMA fragment order: kilobyte q / 4
+// holds chunk q % 4 of the 16 rows, row r in lane 16 * (q % 4) + r.
+template <bool PK>
+__device__ __forceinline__ int ring_chunk(int r, int q) {
+  return PK ? (q >> 2) * 1024 + ((q & 3) * 16 + r) * 16 : r * 256 + ((q ^ r) * 16);
+}
+
 // Stream slots j_beg, j_beg + jstep, ... (nsl of them) of this wave's RB
 // row blocks through its ring and accumulate the MFMAs.  dsrc[rb][i]: this
 // lane's source for direct-load instruction i of block rb in slot 0 (row
-// 4i + lane/16, pre-swizzled chunk); slot j adds j*JS bytes (256 in the
-// row-major layout, 4096 in the packed one).  xrow/xok: activation rows of
-// the NT token blocks.
-template <int NT, int RB, int WB, int S, int JS>
+// 4i + lane/16, pre-swizzled chunk; packed: kilobyte i of the slot); slot j
+// adds j*JS bytes (256 in the row-major layout, 4096 in the packed one).
+// xrow/xok: activation rows of the NT token blocks.
+template <int NT, int RB, int WB, int S, bool PK>
 __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                             const uint8_t* const (&dsrc)[RB][4],
                                             const uint16_t* const (&xrow)[NT], const bool (&xok)[NT],
@@ -345,6 +368,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
   constexpr int XL = STEPS * NT;              // activation loads per slot
   constexpr int D = 4 * RB;                   // direct loads per slot
   constexpr int SLOT = RB * 4096;             // bytes per slot
+  constexpr int JS = PK ? kPackJS : 256;
   const int r = lane & 15, g = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if (nsl <= 0) return;
@@ -365,7 +389,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
       }
   };
   auto compute = [&](int pos, const u32x4 (&xf)[STEPS][NT]) {
-    const uint8_t* sl = ring + pos * SLOT + r * 256;
+    const uint8_t* sl = ring + pos * SLOT;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
 #pragma unroll
@@ -373,7 +397,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
         if constexpr (WB) {
           if ((st & 1) == 0) {
             const int q = 4 * (st >> 1) + g;
-            const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
+            const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ring_chunk<PK>(r, q));
             const bf16x8 w0 = byte8_to_bf16x8<WB>(v[0], v[1]);
             const bf16x8 w1 = byte8_to_bf16x8<WB>(v[2], v[3]);
 #pragma unroll
@@ -383,7 +407,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
           }
         } else {
           const int q = 4 * st + g;
-          const bf16x8 w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16)));
+          const bf16x8 w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ring_chunk<PK>(r, q)));
 #pragma unroll
           for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w, as_bf16x8(xok[b] ? xf[st][b] : zero), acc[rb][b]);
         }
@@ -422,7 +446,7 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
 // with more than 16 tokens that doubled line traffic, not the weight stream,
 // is what bounds the kernel.  xsrc[b][i]: this lane's source for activation
 // load i of token block b in slot 0; slot j adds j * 2*KS bytes.
-template <int NT, int RB, int WB, int S, int JS>
+template <int NT, int RB, int WB, int S, bool PK>
 __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ring,
                                                const uint8_t* const (&dsrc)[RB][4],
                                                const uint8_t* const (&xsrc)[NT][WB ? 8 : 4],
@@ -435,6 +459,7 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
   constexpr int XBLK = 16 * XROWB;
   constexpr int D = 4 * RB + NT * XI;         // direct loads per slot
   constexpr int SLOT = RB * 4096 + NT * XBLK; // bytes per slot
+  constexpr int JS = PK ? kPackJS : 256;
   const int r = lane & 15, g = lane >> 4;
   const u32x4 zero = {0u, 0u, 0u, 0u};
   if (nsl <= 0) return;
@@ -451,7 +476,7 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
         dma16(xsrc[b][i] + (int64_t)j * XROWB, dst + RB * 4096 + b * XBLK + i * 1024);
   };
   auto compute = [&](int pos) {
-    const uint8_t* sl = ring + pos * SLOT + r * 256;
+    const uint8_t* sl = ring + pos * SLOT;
     const uint8_t* xl = ring + pos * SLOT + RB * 4096 + r * XROWB;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
@@ -464,11 +489,11 @@ __device__ __forceinline__ void stream_rows_xd(f32x4 (&acc)[RB][NT], uint8_t* ri
         bf16x8 w;
         if constexpr (WB) {
           const int q = 4 * (st >> 1) + g;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16));
+          const u32x4 v = *reinterpret_cast<const u32x4*>(sl + rb * 4096 + ring_chunk<PK>(r, q));
           w = (st & 1) ? byte8_to_bf16x8<WB>(v[2], v[3]) : byte8_to_bf16x8<WB>(v[0], v[1]);
         } else {
           const int q = 4 * st + g;
-          w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ((q ^ r) * 16)));
+          w = as_bf16x8(*reinterpret_cast<const u32x4*>(sl + rb * 4096 + ring_chunk<PK>(r, q)));
         }
 #pragma unroll
         for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(w, as_bf16x8(xok[b] ? xf[b] : zero), acc[rb][b]);
@@ -517,16 +542,12 @@ __device__ __forceinline__ void stream_sources(const uint8_t* (&dsrc)[4], int la
   }
 }
 
-// Packed weights (pack_kernel below): slot j of 16-row block blk is the 4 KB
-// at (blk * nslots + j) * 4096, already in the ring's order, so load i of
-// the slot is its i-th kilobyte and lane l takes bytes [16 l, 16 l + 16).
-// (Gate and up rows of a slot kept in two separate regions, 2 KB each, were
-// measured no different.)
-constexpr int kPackJS = 4096;   // bytes between a block's consecutive slots
+// Packed ring sources: load i of slot j of block blk is the block's fragment
+// 4 j + i, lane l taking bytes [16 l, 16 l + 16).
 __device__ __forceinline__ void packed_sources(const uint8_t* (&dsrc)[4], const uint8_t* packed, int blk,
                                                int nslots, int lane) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) dsrc[i] = packed + (int64_t)blk * nslots * kPackJS + i * 1024 + lane * 16;
+  for (int i = 0; i < 4; ++i) dsrc[i] = packed + packed_frag(blk, 4 * nslots, i) + lane * 16;
 }
 
 // Cross-wave sum for the streaming kernels: like reduce_waves, but through
@@ -599,7 +620,6 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
         return (row < 8 ? wg : wu) + (int64_t)ch * ldw * EB;
       });
   }
-  constexpr int JS = PK ? kPackJS : 256;
   int j_beg, nsl, jstep;
   wave_slots<SS::WV>(h / KS, wave, j_beg, nsl, jstep);
   bool xok[NT];
@@ -614,12 +634,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
   if constexpr (XD) {
     const uint8_t* xsrc[NT][WB ? 8 : 4];
     stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return x_row<uint16_t>(xr, min(tok, M - 1)); });
-    stream_rows_xd<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    stream_rows_xd<NT, RB, WB, SS::S, PK>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = x_row<uint16_t>(xr, min(b * 16 + row16, M - 1));
-    stream_rows<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S, PK>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -677,7 +697,6 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_s
       stream_sources(dsrc[rb], lane,
                      [&](int row) { return wd + (int64_t)min(n0 + 16 * rb + row, h - 1) * ldw * EB; });
   }
-  constexpr int JS = PK ? kPackJS : 256;
   int j_beg, nsl, jstep;
   const int seg = blockIdx.y;
   const int s0 = (int)((int64_t)seg * nslots / nseg);
@@ -696,12 +715,12 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_s
   if constexpr (XD) {
     const uint8_t* xsrc[NT][WB ? 8 : 4];
     stream_x_sources<WB, NT>(xsrc, lane, [&](int tok) { return a_in + (int64_t)min(tok, M - 1) * lda; });
-    stream_rows_xd<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
+    stream_rows_xd<NT, RB, WB, SS::S, PK>(acc, ring, dsrc, xsrc, xok, j_beg, nsl, jstep, lane);
   } else {
     const uint16_t* xrow[NT];
 #pragma unroll
     for (int b = 0; b < NT; ++b) xrow[b] = a_in + (int64_t)min(b * 16 + row16, M - 1) * lda;
-    stream_rows<NT, RB, WB, SS::S, JS>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
+    stream_rows<NT, RB, WB, SS::S, PK>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
   reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
@@ -750,6 +769,284 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
     for (int i = 0; i < 4; ++i) v[i] *= s[f + i];
   }
   store_out4<OBF>(out, (int64_t)tok * ldo + f, v);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K streams for 17 to 64 tokens.
+//
+// Above 16 tokens a stream whose workgroups each own a few rows is bound by
+// its activation reads: every workgroup re-reads the activations of its K
+// range, M / R bytes per weight byte for R rows per workgroup (two at 64
+// tokens and 32 rows), and staged through the ring they also take the LDS
+// that would hold weight bytes in flight.  Here a workgroup owns R = 64 * RB
+// rows (four waves of RB 16-row blocks) and one of nseg contiguous K ranges,
+// so the grid still covers the chip while each activation byte serves R
+// rows:
+//  - the activation fragments of a step (16 tokens x 32 k each, in MFMA B
+//    order) are loaded once per workgroup, the four waves sharing the
+//    loads, D - 1 steps ahead into registers, and written to one of two
+//    LDS stages just before the step, where all four waves read them;
+//  - each wave streams its own weight fragments (packed layout: one
+//    contiguous kilobyte per load; (out, in) layout: 16 rows x 64 bytes)
+//    straight into registers, D - 1 steps ahead;
+//  - one barrier per step, between the stage writes and the reads.
+// Every load goes to registers, so the compiler counts them all and places
+// the waits (direct-to-LDS loads would make it wait for all of them before
+// each LDS read).  The step loop is unrolled completely (ranges of at most
+// NSTEP steps): in a loop the wait counting drains every load at the loop
+// head.
+// A step is one weight fragment: 32 k (bf16) or 64 k (one-byte weights).
+//
+// The nseg range sums of a tile meet as in the prefill stream-K tail: each
+// range stores its fp32 sums with agent-scope (sc1) buffer stores, counts
+// itself in the tile's arrival counter, and the range that arrives last adds
+// the nseg sums in range order (the same sum whichever arrives last), sets
+// the counter back to zero and runs the epilogue.  The counters are zeroed
+// by a one-workgroup kernel before the first split GEMM of a call.
+// ---------------------------------------------------------------------------
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+template <int NT, int WB>
+struct SkShape {
+  static constexpr int XJ = WB ? 2 : 1;          // activation fragments per token block and step
+  static constexpr int NF = NT * XJ;             // activation fragments per step
+  static constexpr int AF = (NF + 3) / 4;        // ... loaded by each wave (padded)
+  static constexpr int STAGE = 4 * AF * 1024;    // LDS bytes per stage
+};
+
+// Bytes of one range's fp32 sums of a tile (4 waves x RB x NT fragments).
+template <int NT, int RB>
+constexpr int kSkSlot = 4 * RB * NT * 1024;
+
+// GU: gate/up (N = I_s channels, w0/w1 = W_gate/W_up or the packed array in
+// w0, out = A in bf16 with SiLU(gate) * up applied); else a row GEMM
+// (N output rows, out fp32 or bf16 (OBF)).  s0/s1: row scales of one-byte
+// weights.  part/cnt: split scratch (nseg > 1).  Each of the nseg K ranges
+// is at most NSTEP steps.
+template <int NT, int RB, int WB, int D, int NSTEP, bool PK, bool GU, bool OBF>
+__global__ __launch_bounds__(256) void sk_stream_kernel(
+    int M, int N, int K, const XRows xr, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
+    int64_t ldw, const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
+    int64_t ldo, int nseg, float* __restrict__ part, int* __restrict__ cnt) {
+  using SS = SkShape<NT, WB>;
+  constexpr int XJ = SS::XJ, AF = SS::AF;
+  constexpr int EB = WB ? 1 : 2;
+  constexpr int KSTEP = WB ? 64 : 32;           // k per step
+  constexpr int JS = PK ? kPackStep : 64;       // weight bytes between steps
+  __shared__ __attribute__((aligned(1024))) uint8_t stage_buf[2][SS::STAGE];
+  __shared__ int flag;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int tile = blockIdx.x, seg = blockIdx.y;
+  const int nsteps = K / KSTEP;
+  const int sb = (int)((int64_t)seg * nsteps / nseg);
+  const int n = (int)((int64_t)(seg + 1) * nsteps / nseg) - sb;
+
+  // Weight sources of this wave's blocks at step sb.
+  const int nblk = GU ? (N + 7) / 8 : (N + 15) / 16;
+  const int blk0 = (tile * 4 + wave) * RB;
+  const uint8_t* wsrc[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int blk = min(blk0 + rb, nblk - 1);
+    if constexpr (PK) {
+      wsrc[rb] = w0 + packed_frag(blk, nsteps, sb) + lane * 16;
+    } else if constexpr (GU) {
+      const int ch = min(blk * 8 + (r16 & 7), N - 1);
+      wsrc[rb] = (r16 < 8 ? w0 : w1) + (int64_t)ch * ldw * EB + g * 16 + (int64_t)sb * 64;
+    } else {
+      const int row = min(blk * 16 + r16, N - 1);
+      wsrc[rb] = w0 + (int64_t)row * ldw * EB + g * 16 + (int64_t)sb * 64;
+    }
+  }
+  // Activation fragments this wave loads: f = wave + 4a (token block f / XJ,
+  // part f % XJ); the padding fragments (f >= NF) repeat fragment 0 into
+  // stage positions nobody reads.  Lane l loads token (l % 16) of the block,
+  // which is the MFMA B order.
+  const uint8_t* xsrc[AF];
+#pragma unroll
+  for (int a = 0; a < AF; ++a) {
+    const int f = wave + 4 * a < SS::NF ? wave + 4 * a : 0;
+    const int b = f / XJ, j = f % XJ;
+    const int tok = min(b * 16 + r16, M - 1);
+    const int k0 = sb * KSTEP + (WB ? 16 * g + 8 * j : 8 * g);
+    xsrc[a] = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, tok) + k0);
+  }
+
+  // Steps past the range (j >= n, the pipeline's last D - 1 iterations)
+  // still issue their loads, from the range's last activation fragment (an
+  // L2 hit), into registers no step reads: every path through the unrolled
+  // iterations then issues the same loads, so the compiler's wait counts
+  // need no worst case over the range length.
+  const uint8_t* spare = xsrc[0] + (int64_t)(n - 1) * (2 * KSTEP);
+  auto issue_x = [&](int i, u32x4 (&dst)[AF]) {
+#pragma unroll
+    for (int a = 0; a < AF; ++a) dst[a] = ld16(i < n ? xsrc[a] + (int64_t)i * (2 * KSTEP) : spare);
+  };
+  auto stage_x = [&](int stage, const u32x4 (&src)[AF]) {
+#pragma unroll
+    for (int a = 0; a < AF; ++a)
+      *reinterpret_cast<u32x4*>(stage_buf[stage] + (wave + 4 * a) * 1024 + lane * 16) = src[a];
+  };
+  auto issue_w = [&](int i, u32x4 (&dst)[RB]) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) dst[rb] = ld16_stream(i < n ? wsrc[rb] + (int64_t)i * JS : spare);
+  };
+  f32x4 acc[RB][NT];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) acc[rb][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int stage, const u32x4 (&w)[RB]) {
+    const uint8_t* st = stage_buf[stage] + lane * 16;
+    u32x4 xf[NT][XJ];
+#pragma unroll
+    for (int b = 0; b < NT; ++b)
+#pragma unroll
+      for (int j = 0; j < XJ; ++j) xf[b][j] = *reinterpret_cast<const u32x4*>(st + (b * XJ + j) * 1024);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+      if constexpr (WB) {
+        const bf16x8 lo = byte8_to_bf16x8<WB>(w[rb][0], w[rb][1]);
+        const bf16x8 hi = byte8_to_bf16x8<WB>(w[rb][2], w[rb][3]);
+#pragma unroll
+        for (int b = 0; b < NT; ++b) {
+          acc[rb][b] = mfma16(lo, as_bf16x8(xf[b][0]), acc[rb][b]);
+          acc[rb][b] = mfma16(hi, as_bf16x8(xf[b][1]), acc[rb][b]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < NT; ++b) acc[rb][b] = mfma16(as_bf16x8(w[rb]), as_bf16x8(xf[b][0]), acc[rb][b]);
+      }
+    }
+  };
+
+  // Iteration j (0 <= j < n + D - 1), with i = j - D + 1: once step i is
+  // due, write its activation fragments (registers xv[i % D]) to stage i % 2
+  // (step i - 2 read it; the previous barrier saw every wave finish those
+  // reads), barrier (every wave's fragments are in), and compute it from the
+  // stage and registers wf[i % D]; then issue step j (activations into
+  // xv[j % D], weights into wf[j % D], both last used by step i - 1).
+  // The iterations are unrolled at compile time (static_for; n <= NSTEP):
+  // every stage and register set is a constant, and the compiler's wait
+  // counting stays exact (at the head of a loop it drains every load).
+  u32x4 wf[D][RB], xv[D][AF];
+  static_for<0, NSTEP + D - 1>([&](auto J) {
+    constexpr int j = J, i = j - (D - 1);
+    if constexpr (i >= 0) {
+      if (i < n) {
+        stage_x(i % 2, xv[i % D]);
+        lds_barrier();
+        compute(i % 2, wf[i % D]);
+      }
+    }
+    if constexpr (j < NSTEP) {
+      issue_x(j, xv[j % D]);
+      issue_w(j, wf[j % D]);
+    }
+  });
+
+  if (nseg > 1) {
+    constexpr int SLOT = kSkSlot<NT, RB>;
+    constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
+    const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+        part + (int64_t)tile * nseg * (SLOT / 4), 0, nseg * SLOT, 0x00020000);
+    auto off = [&](int p, int rb, int b) { return p * SLOT + ((wave * RB + rb) * NT + b) * 1024 + lane * 16; };
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int b = 0; b < NT; ++b)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rb][b]), slots, off(seg, rb, b), 0,
+                                               kDeviceScope);
+    // The ordering argument is the prefill stream-K tail's (sk_handoff):
+    // every slot store and load carries sc1, vmcnt(0) completes this range's
+    // stores at agent scope, the barrier orders all lanes before the
+    // counter increment, and the last range's loads depend on its result.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) flag = __hip_atomic_fetch_add(cnt + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (flag != nseg - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(cnt + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Ranges in order, FB at a time with all their loads in flight together
+    // (one memory round trip per FB ranges); this range's own sums in place.
+    constexpr int FB = 2;
+    f32x4 sum[RB][NT];
+    for (int p0 = 0; p0 < nseg; p0 += FB) {
+      f32x4 v[FB][RB][NT];
+#pragma unroll
+      for (int q = 0; q < FB; ++q)
+        if (p0 + q < nseg && p0 + q != seg)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int b = 0; b < NT; ++b)
+              v[q][rb][b] = __builtin_bit_cast(
+                  f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, off(p0 + q, rb, b), 0, kDeviceScope));
+#pragma unroll
+      for (int q = 0; q < FB; ++q) {
+        const int p = p0 + q;
+        if (p < nseg)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int b = 0; b < NT; ++b) {
+              const f32x4 x = p == seg ? acc[rb][b] : v[q][rb][b];
+              sum[rb][b] = p == 0 ? x : sum[rb][b] + x;
+            }
+      }
+    }
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int b = 0; b < NT; ++b) acc[rb][b] = sum[rb][b];
+  }
+
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int b = 0; b < NT; ++b) {
+      f32x4 v = acc[rb][b];
+      const int tok = b * 16 + r16;
+      if constexpr (GU) {
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = __shfl_xor(v[i], 32);
+        const int ch = (blk0 + rb) * 8 + 4 * g;   // four channels ch .. ch+3 (lanes g < 2)
+        if (g < 2 && tok < M && ch < N) {
+          float a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float gv = v[i], uv = o[i];
+            if constexpr (WB) {
+              gv *= s0[ch + i];
+              uv *= s1[ch + i];
+            }
+            a[i] = silu(gv) * uv;
+          }
+          const u32x2 packed = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + (int64_t)tok * ldo + ch) = packed;
+        }
+      } else {
+        const int f = (blk0 + rb) * 16 + 4 * g;   // rows f .. f+3
+        if (tok < M && f < N) {
+          if constexpr (WB) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= s0[f + i];
+          }
+          store_out4<OBF>(out, (int64_t)tok * ldo + f, v);
+        }
+      }
+    }
 }
 
 // Launch shape (waves per workgroup splitting K; steps per register batch).
@@ -898,6 +1195,129 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   }
 }
 
+// Split-K streams: which token counts take them, their shape (RB row
+// blocks per wave, D steps in flight) and their grid: tiles of 64 * RB
+// weight rows, K cut into nseg balanced ranges so that about kSkWgs
+// workgroups run, with ranges of at most 64 steps; the kernel is compiled
+// for ranges of up to 32 and up to 64 steps (nstep).
+//
+// Measured on the 70B TP = 8 shard (whole forward, packed weights, six
+// rotating weight sets): 64 tokens 53.4 -> 48.6 us against the rings, 48
+// tokens 44.7 -> 44.5, 32 tokens 38.5 -> 41.9; fp8 at TP = 4, 32 tokens
+// 52.0 -> 44.5.  So they take bf16 weights at 49-64 tokens and one-byte
+// weights at 17-32.  The workgroup target is one per CU at most: a CU that
+// holds two finishes last (gate/up at 64 tokens: 56 tiles x 4 ranges = 224
+// workgroups 28.3 us, x 5 = 280 workgroups 47.6 us, x 9 = 504 33.6 us),
+// and more ranges cost more range sums (a round trip through memory each)
+// and shorter streams.
+template <int NT, int WB>
+constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
+template <int NT, int WB>
+struct SkPlan {
+  static constexpr int RB = 2;
+  static constexpr int D = 8;
+};
+constexpr int kSkWgs = 224;
+
+struct SkGrid {
+  int tiles, nseg, nstep;
+};
+
+template <int NT, int WB, bool GU>
+SkGrid sk_grid(int N, int K) {
+  using P = SkPlan<NT, WB>;
+  const int rows = 64 * P::RB;
+  const int tiles = GU ? (2 * N + rows - 1) / rows : (N + rows - 1) / rows;
+  const int nsteps = K / (WB ? 64 : 32);
+  int nseg = max(1, (kSkWgs + tiles / 2) / tiles);
+  nseg = min(max(nseg, (nsteps + 63) / 64), nsteps);
+  const int longest = (nsteps + nseg - 1) / nseg;
+  return SkGrid{tiles, nseg, longest <= 32 ? 32 : 64};
+}
+
+template <int NT, int RB>
+int64_t sk_part_bytes(const SkGrid& g) {
+  return g.nseg > 1 ? (int64_t)g.tiles * g.nseg * kSkSlot<NT, RB> : 0;
+}
+
+inline int64_t sk_cnt_bytes(int tiles) { return ((int64_t)tiles * 4 + 255) / 256 * 256; }
+
+// One split-K GEMM.  scratch: arrival counters (zero) then the range slots.
+template <int NT, int WB, bool GU, bool OBF>
+hipError_t sk_launch(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
+                     const float* s0, const float* s1, void* out, int64_t ldo, bool packed, void* scratch,
+                     int cnt_tiles, hipStream_t stream) {
+  using P = SkPlan<NT, WB>;
+  const SkGrid gr = sk_grid<NT, WB, GU>(N, K);
+  int* cnt = static_cast<int*>(scratch);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(scratch) + sk_cnt_bytes(cnt_tiles));
+  const dim3 grid(gr.tiles, gr.nseg), block(256);
+  auto go = [&](auto kern) {
+    return launch(kind, kern, grid, block, 0, stream, M, N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0,
+                  s1, out, ldo, gr.nseg, part, cnt);
+  };
+  if (gr.nstep == 32)
+    return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, true, GU, OBF>)
+                  : go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, false, GU, OBF>);
+  return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, true, GU, OBF>)
+                : go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, false, GU, OBF>);
+}
+
+template <int NT, int WB>
+int64_t forward_sk_bytes(int h, int I_s) {
+  using P = SkPlan<NT, WB>;
+  const SkGrid g1 = sk_grid<NT, WB, true>(I_s, h), g2 = sk_grid<NT, WB, false>(h, I_s);
+  const int64_t part = max(sk_part_bytes<NT, P::RB>(g1), sk_part_bytes<NT, P::RB>(g2));
+  return part ? sk_cnt_bytes(max(g1.tiles, g2.tiles)) + part : 0;
+}
+
+// The forward on the split-K streams: clear the counters, gate/up, down.
+// Both GEMMs use the same counters (each range that finishes a tile sets
+// its counter back to zero) and the same range slots.
+template <int NT, int WB>
+hipError_t forward_sk(const ShardArgs& a, hipStream_t stream) {
+  const SkGrid g1 = sk_grid<NT, WB, true>(a.I_s, a.h), g2 = sk_grid<NT, WB, false>(a.h, a.I_s);
+  const int ct = max(g1.tiles, g2.tiles);
+  if (g1.nseg > 1 || g2.nseg > 1) {
+    const hipError_t e = launch_counter_clear(static_cast<int*>(a.sk), ct, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = sk_launch<NT, WB, true, false>(K_GATEUP_DECODE, a.M, a.I_s, a.h, a.x, a.wg, a.wu, a.ldw_gu, a.sg,
+                                                a.su, a.a, a.lda, a.packed, a.sk, ct, stream);
+  if (e != hipSuccess) return e;
+  XRows ax{};
+  ax.p[0] = a.a;
+  ax.nb = 1;
+  ax.rows = a.M;
+  ax.ld = a.lda;
+  return sk_launch<NT, WB, false, false>(K_DOWN_DECODE, a.M, a.h, a.I_s, ax, a.wd, nullptr, a.ldw_down, a.sd,
+                                         nullptr, a.p, a.ldp, a.packed, a.sk, ct, stream);
+}
+
+// Whether the forward takes the split-K streams (M tokens, weight format
+// wb), and its scratch bytes (0 if it does not or needs none).
+template <int WB>
+int64_t forward_sk_bytes_wb(int M, int h, int I_s) {
+  if (h % (WB ? 64 : 32) || I_s % (WB ? 64 : 32)) return -1;
+  switch ((M + 15) / 16) {
+    case 2: return kSkStream<2, WB> ? forward_sk_bytes<2, WB>(h, I_s) : -1;
+    case 3: return kSkStream<3, WB> ? forward_sk_bytes<3, WB>(h, I_s) : -1;
+    case 4: return kSkStream<4, WB> ? forward_sk_bytes<4, WB>(h, I_s) : -1;
+    default: return -1;
+  }
+}
+
+template <int WB>
+hipError_t forward_sk_wb(const ShardArgs& a, hipStream_t stream) {
+  switch ((a.M + 15) / 16) {
+    case 2: if constexpr (kSkStream<2, WB>) return forward_sk<2, WB>(a, stream); break;
+    case 3: if constexpr (kSkStream<3, WB>) return forward_sk<3, WB>(a, stream); break;
+    case 4: if constexpr (kSkStream<4, WB>) return forward_sk<4, WB>(a, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 namespace {
@@ -962,7 +1382,28 @@ hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream) {
   }
 }
 
+// Split-K scratch of the decode forward (-1: the forward does not take the
+// split-K streams).
+static int64_t forward_sk_need(int M, int h, int I_s, int wb) {
+  if (M < 1 || M > kDecodeMaxM) return -1;
+  switch (wb) {
+    case kWeightE4M3: return forward_sk_bytes_wb<kWeightE4M3>(M, h, I_s);
+    case kWeightI8: return forward_sk_bytes_wb<kWeightI8>(M, h, I_s);
+    default: return forward_sk_bytes_wb<kWeightWide>(M, h, I_s);
+  }
+}
+
+int64_t forward_decode_sk_bytes(int M, int h, int I_s, int wb) { return max((int64_t)0, forward_sk_need(M, h, I_s, wb)); }
+
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream) {
+  const int64_t skb = forward_sk_need(a.M, a.h, a.I_s, a.wb);
+  if (skb >= 0 && (skb == 0 || a.sk)) {
+    switch (a.wb) {
+      case kWeightE4M3: return forward_sk_wb<kWeightE4M3>(a, stream);
+      case kWeightI8: return forward_sk_wb<kWeightI8>(a, stream);
+      default: return forward_sk_wb<kWeightWide>(a, stream);
+    }
+  }
   hipError_t e;
   switch (a.wb) {
     case kWeightE4M3: e = run_gateup<kWeightE4M3>(a, stream); break;
@@ -978,34 +1419,32 @@ hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream) {
 // the 16 rows per slot), which in the (out, in) layout is 16 pieces 16 KB
 // apart (70B shard); a read pattern like that runs at about 4.9 TB/s on
 // MI355X against 6.3 TB/s for the same bytes read in address order.  The
-// packed array stores every slot as the 4 KB the ring holds (rows 4i..4i+3 in
-// the i-th kilobyte, 16-byte chunks XOR-swizzled by row), slot after slot,
-// block after block, so each workgroup streams one contiguous range.  Gate/up
-// blocks hold 8 gate rows then the same 8 channels' up rows; rows past the
-// end repeat the last row, as the row-major streams clamp.  The values and
-// the order of every load into the ring are those of the row-major path.
+// packed array stores every 16-row block as its run of 1 KB MFMA A fragments
+// (packed_frag above), block after block, so each block streams one
+// contiguous range.  Gate/up blocks hold 8 gate rows then the same 8
+// channels' up rows; rows past the end repeat the last row, as the row-major
+// streams clamp.
 
 namespace {
 
-// One thread per 16 bytes of the packed array of nblk blocks x nslots slots;
-// GU: rows 0-7 of a block from w0 (channels 8 blk + r), 8-15 from w1.
+// One thread per 16 bytes of the packed array (blocks x nsteps fragments);
+// GU: rows 0-7 of block blk from w0 (channels 8 blk + r), 8-15 from w1.
 template <bool GU>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
-                                                   int64_t ld_bytes, int nrows, int nslots, int64_t nchunks,
+                                                   int64_t ld_bytes, int nrows, int nsteps, int64_t nchunks,
                                                    uint8_t* __restrict__ out) {
   const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (q >= nchunks) return;
-  const int64_t blk = q / ((int64_t)nslots * 256);
-  const int within = (int)(q - blk * nslots * 256);
-  const int j = within >> 8, i = (within >> 6) & 3, lane = within & 63;
-  const int row = 4 * i + (lane >> 4);
-  const int c = (lane & 15) ^ row;
+  const int64_t blk = q / ((int64_t)nsteps * 64);
+  const int within = (int)(q - blk * nsteps * 64);
+  const int st = within >> 6, lane = within & 63;   // fragment st of the block, lane
+  const int row = lane & 15;
   const uint8_t* src;
   if constexpr (GU)
-    src = (row < 8 ? w0 : w1) + min((int64_t)8 * blk + (row & 7), (int64_t)nrows - 1) * ld_bytes;
+    src = (row < 8 ? w0 : w1) + min(8 * blk + (row & 7), (int64_t)nrows - 1) * ld_bytes;
   else
-    src = w0 + min((int64_t)16 * blk + row, (int64_t)nrows - 1) * ld_bytes;
-  *reinterpret_cast<u32x4*>(out + q * 16) = *reinterpret_cast<const u32x4*>(src + (int64_t)j * 256 + c * 16);
+    src = w0 + min(16 * blk + row, (int64_t)nrows - 1) * ld_bytes;
+  *reinterpret_cast<u32x4*>(out + q * 16) = *reinterpret_cast<const u32x4*>(src + (int64_t)st * 64 + (lane >> 4) * 16);
 }
 
 }  // namespace
@@ -1015,24 +1454,25 @@ bool decode_packable(int h, int I_s, int wb) {
   return h % ks == 0 && I_s % ks == 0;
 }
 
+// One fragment (1 KB) per 64 weight bytes of a block's rows.
 int64_t packed_gateup_bytes(int h, int I_s, int wb) {
-  return (int64_t)((I_s + 7) / 8) * (h / (wb ? 256 : 128)) * 4096;
+  return (int64_t)((I_s + 7) / 8) * (h * (wb ? 1 : 2) / 64) * 1024;
 }
 
 int64_t packed_down_bytes(int h, int I_s, int wb) {
-  return (int64_t)((h + 15) / 16) * (I_s / (wb ? 256 : 128)) * 4096;
+  return (int64_t)((h + 15) / 16) * (I_s * (wb ? 1 : 2) / 64) * 1024;
 }
 
 hipError_t launch_pack_weights(const ShardArgs& a, void* packed, hipStream_t stream) {
-  const int eb = a.wb ? 1 : 2, ks = a.wb ? 256 : 128;
+  const int eb = a.wb ? 1 : 2;
   uint8_t* gu = static_cast<uint8_t*>(packed);
   uint8_t* dn = gu + packed_gateup_bytes(a.h, a.I_s, a.wb);
   const int64_t c_gu = packed_gateup_bytes(a.h, a.I_s, a.wb) / 16, c_dn = packed_down_bytes(a.h, a.I_s, a.wb) / 16;
   hipError_t e = launch(-1, pack_kernel<true>, dim3((unsigned)((c_gu + 255) / 256)), dim3(256), 0, stream,
-                        (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu * eb, a.I_s, a.h / ks, c_gu, gu);
+                        (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu * eb, a.I_s, a.h * eb / 64, c_gu, gu);
   if (e != hipSuccess) return e;
   return launch(-1, pack_kernel<false>, dim3((unsigned)((c_dn + 255) / 256)), dim3(256), 0, stream,
-                (const uint8_t*)a.wd, (const uint8_t*)nullptr, a.ldw_down * eb, a.h, a.I_s / ks, c_dn, dn);
+                (const uint8_t*)a.wd, (const uint8_t*)nullptr, a.ldw_down * eb, a.h, a.I_s * eb / 64, c_dn, dn);
 }
 
 }  // namespace tpmlp

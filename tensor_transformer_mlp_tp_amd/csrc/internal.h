@@ -145,6 +145,10 @@ struct W8A8Bufs {
 };
 
 hipError_t launch_forward_decode(const ShardArgs& a, hipStream_t stream);
+// Split-K scratch of a decode forward (a.sk; 0: none needed).
+int64_t forward_decode_sk_bytes(int M, int h, int I_s, int wb);
+// Zero n arrival counters (one workgroup).
+hipError_t launch_counter_clear(int* cnt, int n, hipStream_t stream);
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_forward_f32(const ShardArgs& a, hipStream_t stream);
 hipError_t launch_rowgemm_decode(const RowGemm& g, hipStream_t stream);

@@ -105,18 +105,6 @@ __device__ __forceinline__ int swz(int row) {
   else return (row >> 3) & 1;  // 32-byte rows
 }
 
-// Workgroup barrier ordering LDS accesses only.  __syncthreads() would also
-// wait for every outstanding global load (vmcnt(0)), which would drain the
-// direct-load ring at each k-tile; the ring's completion is tracked with
-// explicit vmcnt waits instead.
-// Before it, this wave's LDS reads are complete (lgkmcnt(0)); the acquire
-// fence after it keeps later LDS reads below the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // s_waitcnt that waits until at most n vector-memory loads of this wave are
 // outstanding (expcnt and lgkmcnt not waited on).
 template <int N>
@@ -931,6 +919,14 @@ int tile_bm(int M, int tiles_n, int KT) {
 __global__ void sk_clear_kernel(int* __restrict__ cnt, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) cnt[i] = 0;
 }
+
+}  // namespace
+
+hipError_t launch_counter_clear(int* cnt, int n, hipStream_t stream) {
+  return launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, cnt, n);
+}
+
+namespace {
 
 // One GEMM launch: out = epilogue(rows of W (N of them; gate/up: N channels,
 // 2N weight rows) times the activation rows).  skws: stream-K scratch of

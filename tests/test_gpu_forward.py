@@ -320,6 +320,46 @@ def test_stream_decode_shapes(M, w):
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
 
 
+# ------------------------------------------------------------ decode split-K streams
+
+# bf16 weights at 49-64 tokens and one-byte weights at 17-32 take the split-K
+# streams: tiles of 128 weight rows, K cut into ranges whose fp32 sums the
+# last range to arrive adds in order.  (gate/up tiles x ranges, down tiles x
+# ranges; steps of 32 k bf16 / 64 k one-byte.)
+SK_CASES = [
+    (64, 8192, 448, "bf16"),      # 7 x 32 ranges of 8 steps; 64 x 4 ranges of 3-4 steps
+    (57, 1088, 3584, "bf16"),     # 56 x 4 of 8-9; ragged 9 x 25 of 4-5 (1088 rows = 8.5 tiles)
+    (64, 256, 14336, "bf16"),     # 224 whole tiles (no split); 2 x 112 ranges of 4 steps
+    (32, 2048, 1024, "e4m3fn"),   # 16 x 14 of 2-3; 16 x 14 of 1-2
+    (17, 2048, 1024, "int8"),
+]
+
+
+@pytest.mark.parametrize("M,h,I_s,w", SK_CASES)
+def test_decode_split_k(M, h, I_s, w):
+    """Every element against the oracle; the arrival counters and range slots
+    live in the workspace, whose contents on entry must not matter, and the
+    result must not depend on which range arrives last (bit-identical over
+    calls with a dirtied workspace)."""
+    t = 2
+    print("decode split-K M=%d h=%d I_s=%d w=%s" % (M, h, I_s, w), flush=True)
+    x, ws = make_case(62, M, h, I_s, "bf16", w, 0.05, 0.05, weight_set=M)
+    d = upload_case(x, ws, "bf16", w)
+    nbytes = tp.workspace_bytes(M, h, I_s * t, t, w_dtype=d["w_gate"].dtype)
+    assert nbytes > M * I_s * 2     # counters and range slots past A
+    scratch = tp.alloc_workspace(nbytes, "cuda")
+    outs = []
+    for fill in (0x7F, 0x00, 0xFF):
+        scratch.fill_(fill)
+        outs.append(tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0, s_gate=d["s_gate"],
+                                     s_up=d["s_up"], s_down=d["s_down"], workspace=scratch))
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    tol = {"bf16": TOL_BF16, "e4m3fn": TOL_FP8, "int8": TOL_INT8}[w]
+    check(outs[0].cpu().numpy(), oracle_partial(x, ws, "bf16", w), tol, "split-K M=%d %s (all elements)" % (M, w))
+
+
 def test_prefill_stream_k_in_a_graph():
     """A prefill forward whose GEMMs have stream-K tails, captured in a HIP
     graph: the arrival counters are cleared by a kernel inside the graph, so

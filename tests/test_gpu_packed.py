@@ -15,35 +15,30 @@ TOL = {"bf16": TOL_BF16, "e4m3fn": TOL_FP8, "int8": TOL_INT8}
 
 
 def host_packed(ws, I_s, h):
-    """The packed array written out from its documented layout: 4 KB slots of
-    16 rows x 256 bytes, rows 4i..4i+3 in kilobyte i, lane l of a kilobyte
-    holding logical 16-byte chunk (l % 16) ^ row of row 4i + l // 16; gate/up
-    blocks of 8 gate then 8 up rows, then down blocks of 16 rows; rows past
-    the end repeat the last one."""
+    """The packed array written out from its documented layout: each 16-row
+    block is a run of 1 KB MFMA A fragments, fragment st giving lane l the
+    16 bytes [64 st + 16 (l // 16), +16) of row l % 16; gate/up blocks of 8
+    gate then 8 up rows, then down blocks of 16 rows; rows past the end
+    repeat the last one."""
     def rows_bytes(a):
         a = np.ascontiguousarray(a)
         return a.view(np.uint8).reshape(a.shape[0], -1)
 
     g, u, d = rows_bytes(ws["w_gate"]), rows_bytes(ws["w_up"]), rows_bytes(ws["w_down"])
-    i = np.arange(4)[:, None]
-    lane = np.arange(64)[None, :]
-    row = 4 * i + lane // 16                     # (4, 64)
-    chunk = (lane % 16) ^ row
+    lane = np.arange(64)
 
-    def blocks(src_of_row, nblk, nslots):
-        out = np.empty((nblk, nslots, 4, 64, 16), dtype=np.uint8)
+    def blocks(src_of_row, nblk):
+        parts = []
         for b in range(nblk):
             src = src_of_row(b)                  # (16, row bytes)
-            for j in range(nslots):
-                seg = src[:, j * 256:(j + 1) * 256].reshape(16, 16, 16)
-                out[b, j] = seg[row, chunk]
-        return out.reshape(-1)
+            nfrag = src.shape[1] // 64
+            seg = src.reshape(16, nfrag, 4, 16)  # row, fragment, 16-byte chunk, byte
+            parts.append(seg[lane % 16, :, lane // 16, :].transpose(1, 0, 2).reshape(-1))
+        return np.concatenate(parts)
 
-    slot_k = 256 // (g.shape[1] // h)            # k-values per 256-byte slot row
     gu = blocks(lambda b: np.concatenate([g[np.minimum(8 * b + np.arange(8), I_s - 1)],
-                                          u[np.minimum(8 * b + np.arange(8), I_s - 1)]]),
-                (I_s + 7) // 8, h // slot_k)
-    dn = blocks(lambda b: d[np.minimum(16 * b + np.arange(16), h - 1)], (h + 15) // 16, I_s // slot_k)
+                                          u[np.minimum(8 * b + np.arange(8), I_s - 1)]]), (I_s + 7) // 8)
+    dn = blocks(lambda b: d[np.minimum(16 * b + np.arange(16), h - 1)], (h + 15) // 16)
     return np.concatenate([gu, dn])
 
 
