@@ -304,6 +304,8 @@ tp_status tp_mlp_shard_forward_w8a8(int64_t M, int64_t h, int64_t I_full,
  * dimension ldx, rows 16-byte aligned) -> e4m3fn codes (leading dimension
  * ldq bytes, rows 8-byte aligned) and one fp32 scale per row.  cols % 8 == 0
  * (else TP_ERR_UNSUPPORTED); rows == 0 is a no-op.  Buffers must not overlap.
+ * The rows must be finite: a row holding an infinity or a NaN gets
+ * unspecified codes.
  */
 tp_status tp_quantize_rows_e4m3(int64_t rows, int64_t cols, const void* x, int64_t ldx,
                                 void* codes, int64_t ldq, float* scales, void* stream);

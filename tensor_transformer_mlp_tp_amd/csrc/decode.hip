@@ -1049,6 +1049,133 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
     }
 }
 
+// Split-K streams: which token counts take them, their shape (RB row
+// blocks per wave, D steps in flight) and their grid: tiles of 64 * RB
+// weight rows, K cut into nseg balanced ranges so that about kSkWgs
+// workgroups run, with ranges of at most 64 steps; the kernel is compiled
+// for ranges of up to 32 and up to 64 steps (nstep).
+//
+// Measured on the 70B TP = 8 shard (whole forward, packed weights, six
+// rotating weight sets): 64 tokens 53.4 -> 48.6 us against the rings, 48
+// tokens 44.7 -> 44.5, 32 tokens 38.5 -> 41.9; fp8 at TP = 4, 32 tokens
+// 52.0 -> 44.5.  So they take bf16 weights at 49-64 tokens and one-byte
+// weights at 17-32.  The workgroup target is one per CU at most: a CU that
+// holds two finishes last (gate/up at 64 tokens: 56 tiles x 4 ranges = 224
+// workgroups 28.3 us, x 5 = 280 workgroups 47.6 us, x 9 = 504 33.6 us),
+// and more ranges cost more range sums (a round trip through memory each)
+// and shorter streams.  For the same reason they lose on a narrow output
+// such as the attention block's QKV projection (1280 rows: 10 tiles, 22
+// ranges of 11-12 steps): 13.2 us plus a 2 us finishing kernel on the
+// rings against 26.3 us at 64 tokens.
+template <int NT, int WB>
+constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
+
+template <int NT, int WB>
+struct SkPlan {
+  static constexpr int RB = 2;
+  static constexpr int D = 8;
+};
+constexpr int kSkWgs = 224;
+
+struct SkGrid {
+  int tiles, nseg, nstep;
+};
+
+template <int NT, int WB, bool GU>
+SkGrid sk_grid(int N, int K) {
+  using P = SkPlan<NT, WB>;
+  const int rows = 64 * P::RB;
+  const int tiles = GU ? (2 * N + rows - 1) / rows : (N + rows - 1) / rows;
+  const int nsteps = K / (WB ? 64 : 32);
+  int nseg = max(1, (kSkWgs + tiles / 2) / tiles);
+  nseg = min(max(nseg, (nsteps + 63) / 64), nsteps);
+  const int longest = (nsteps + nseg - 1) / nseg;
+  return SkGrid{tiles, nseg, longest <= 32 ? 32 : 64};
+}
+
+template <int NT, int RB>
+int64_t sk_part_bytes(const SkGrid& g) {
+  return g.nseg > 1 ? (int64_t)g.tiles * g.nseg * kSkSlot<NT, RB> : 0;
+}
+
+inline int64_t sk_cnt_bytes(int tiles) { return ((int64_t)tiles * 4 + 255) / 256 * 256; }
+
+// One split-K GEMM.  scratch: arrival counters (zero) then the range slots.
+template <int NT, int WB, bool GU, bool OBF>
+hipError_t sk_launch(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
+                     const float* s0, const float* s1, void* out, int64_t ldo, bool packed, void* scratch,
+                     int cnt_tiles, hipStream_t stream) {
+  using P = SkPlan<NT, WB>;
+  const SkGrid gr = sk_grid<NT, WB, GU>(N, K);
+  int* cnt = static_cast<int*>(scratch);
+  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(scratch) + sk_cnt_bytes(cnt_tiles));
+  const dim3 grid(gr.tiles, gr.nseg), block(256);
+  auto go = [&](auto kern) {
+    return launch(kind, kern, grid, block, 0, stream, M, N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0,
+                  s1, out, ldo, gr.nseg, part, cnt);
+  };
+  if (gr.nstep == 32)
+    return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, true, GU, OBF>)
+                  : go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, false, GU, OBF>);
+  return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, true, GU, OBF>)
+                : go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, false, GU, OBF>);
+}
+
+template <int NT, int WB>
+int64_t forward_sk_bytes(int h, int I_s) {
+  using P = SkPlan<NT, WB>;
+  const SkGrid g1 = sk_grid<NT, WB, true>(I_s, h), g2 = sk_grid<NT, WB, false>(h, I_s);
+  const int64_t part = max(sk_part_bytes<NT, P::RB>(g1), sk_part_bytes<NT, P::RB>(g2));
+  return part ? sk_cnt_bytes(max(g1.tiles, g2.tiles)) + part : 0;
+}
+
+// The forward on the split-K streams: clear the counters, gate/up, down.
+// Both GEMMs use the same counters (each range that finishes a tile sets
+// its counter back to zero) and the same range slots.
+template <int NT, int WB>
+hipError_t forward_sk(const ShardArgs& a, hipStream_t stream) {
+  const SkGrid g1 = sk_grid<NT, WB, true>(a.I_s, a.h), g2 = sk_grid<NT, WB, false>(a.h, a.I_s);
+  const int ct = max(g1.tiles, g2.tiles);
+  if (g1.nseg > 1 || g2.nseg > 1) {
+    const hipError_t e = launch_counter_clear(static_cast<int*>(a.sk), ct, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = sk_launch<NT, WB, true, false>(K_GATEUP_DECODE, a.M, a.I_s, a.h, a.x, a.wg, a.wu, a.ldw_gu, a.sg,
+                                                a.su, a.a, a.lda, a.packed, a.sk, ct, stream);
+  if (e != hipSuccess) return e;
+  XRows ax{};
+  ax.p[0] = a.a;
+  ax.nb = 1;
+  ax.rows = a.M;
+  ax.ld = a.lda;
+  return sk_launch<NT, WB, false, false>(K_DOWN_DECODE, a.M, a.h, a.I_s, ax, a.wd, nullptr, a.ldw_down, a.sd,
+                                         nullptr, a.p, a.ldp, a.packed, a.sk, ct, stream);
+}
+
+// Whether the forward takes the split-K streams (M tokens, weight format
+// wb), and its scratch bytes (0 if it does not or needs none).
+template <int WB>
+int64_t forward_sk_bytes_wb(int M, int h, int I_s) {
+  if (h % (WB ? 64 : 32) || I_s % (WB ? 64 : 32)) return -1;
+  switch ((M + 15) / 16) {
+    case 2: return kSkStream<2, WB> ? forward_sk_bytes<2, WB>(h, I_s) : -1;
+    case 3: return kSkStream<3, WB> ? forward_sk_bytes<3, WB>(h, I_s) : -1;
+    case 4: return kSkStream<4, WB> ? forward_sk_bytes<4, WB>(h, I_s) : -1;
+    default: return -1;
+  }
+}
+
+template <int WB>
+hipError_t forward_sk_wb(const ShardArgs& a, hipStream_t stream) {
+  switch ((a.M + 15) / 16) {
+    case 2: if constexpr (kSkStream<2, WB>) return forward_sk<2, WB>(a, stream); break;
+    case 3: if constexpr (kSkStream<3, WB>) return forward_sk<3, WB>(a, stream); break;
+    case 4: if constexpr (kSkStream<4, WB>) return forward_sk<4, WB>(a, stream); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
 // Launch shape (waves per workgroup splitting K; steps per register batch).
 constexpr int kWaves = 4;
 constexpr int kUnroll = 8;
@@ -1195,145 +1322,26 @@ hipError_t run_rowgemm(const RowGemm& g, hipStream_t stream) {
   }
 }
 
-// Split-K streams: which token counts take them, their shape (RB row
-// blocks per wave, D steps in flight) and their grid: tiles of 64 * RB
-// weight rows, K cut into nseg balanced ranges so that about kSkWgs
-// workgroups run, with ranges of at most 64 steps; the kernel is compiled
-// for ranges of up to 32 and up to 64 steps (nstep).
-//
-// Measured on the 70B TP = 8 shard (whole forward, packed weights, six
-// rotating weight sets): 64 tokens 53.4 -> 48.6 us against the rings, 48
-// tokens 44.7 -> 44.5, 32 tokens 38.5 -> 41.9; fp8 at TP = 4, 32 tokens
-// 52.0 -> 44.5.  So they take bf16 weights at 49-64 tokens and one-byte
-// weights at 17-32.  The workgroup target is one per CU at most: a CU that
-// holds two finishes last (gate/up at 64 tokens: 56 tiles x 4 ranges = 224
-// workgroups 28.3 us, x 5 = 280 workgroups 47.6 us, x 9 = 504 33.6 us),
-// and more ranges cost more range sums (a round trip through memory each)
-// and shorter streams.
-template <int NT, int WB>
-constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
-template <int NT, int WB>
-struct SkPlan {
-  static constexpr int RB = 2;
-  static constexpr int D = 8;
-};
-constexpr int kSkWgs = 224;
-
-struct SkGrid {
-  int tiles, nseg, nstep;
-};
-
-template <int NT, int WB, bool GU>
-SkGrid sk_grid(int N, int K) {
-  using P = SkPlan<NT, WB>;
-  const int rows = 64 * P::RB;
-  const int tiles = GU ? (2 * N + rows - 1) / rows : (N + rows - 1) / rows;
-  const int nsteps = K / (WB ? 64 : 32);
-  int nseg = max(1, (kSkWgs + tiles / 2) / tiles);
-  nseg = min(max(nseg, (nsteps + 63) / 64), nsteps);
-  const int longest = (nsteps + nseg - 1) / nseg;
-  return SkGrid{tiles, nseg, longest <= 32 ? 32 : 64};
-}
-
-template <int NT, int RB>
-int64_t sk_part_bytes(const SkGrid& g) {
-  return g.nseg > 1 ? (int64_t)g.tiles * g.nseg * kSkSlot<NT, RB> : 0;
-}
-
-inline int64_t sk_cnt_bytes(int tiles) { return ((int64_t)tiles * 4 + 255) / 256 * 256; }
-
-// One split-K GEMM.  scratch: arrival counters (zero) then the range slots.
-template <int NT, int WB, bool GU, bool OBF>
-hipError_t sk_launch(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
-                     const float* s0, const float* s1, void* out, int64_t ldo, bool packed, void* scratch,
-                     int cnt_tiles, hipStream_t stream) {
-  using P = SkPlan<NT, WB>;
-  const SkGrid gr = sk_grid<NT, WB, GU>(N, K);
-  int* cnt = static_cast<int*>(scratch);
-  float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(scratch) + sk_cnt_bytes(cnt_tiles));
-  const dim3 grid(gr.tiles, gr.nseg), block(256);
-  auto go = [&](auto kern) {
-    return launch(kind, kern, grid, block, 0, stream, M, N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0,
-                  s1, out, ldo, gr.nseg, part, cnt);
-  };
-  if (gr.nstep == 32)
-    return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, true, GU, OBF>)
-                  : go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, false, GU, OBF>);
-  return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, true, GU, OBF>)
-                : go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, false, GU, OBF>);
-}
-
-template <int NT, int WB>
-int64_t forward_sk_bytes(int h, int I_s) {
-  using P = SkPlan<NT, WB>;
-  const SkGrid g1 = sk_grid<NT, WB, true>(I_s, h), g2 = sk_grid<NT, WB, false>(h, I_s);
-  const int64_t part = max(sk_part_bytes<NT, P::RB>(g1), sk_part_bytes<NT, P::RB>(g2));
-  return part ? sk_cnt_bytes(max(g1.tiles, g2.tiles)) + part : 0;
-}
-
-// The forward on the split-K streams: clear the counters, gate/up, down.
-// Both GEMMs use the same counters (each range that finishes a tile sets
-// its counter back to zero) and the same range slots.
-template <int NT, int WB>
-hipError_t forward_sk(const ShardArgs& a, hipStream_t stream) {
-  const SkGrid g1 = sk_grid<NT, WB, true>(a.I_s, a.h), g2 = sk_grid<NT, WB, false>(a.h, a.I_s);
-  const int ct = max(g1.tiles, g2.tiles);
-  if (g1.nseg > 1 || g2.nseg > 1) {
-    const hipError_t e = launch_counter_clear(static_cast<int*>(a.sk), ct, stream);
-    if (e != hipSuccess) return e;
-  }
-  hipError_t e = sk_launch<NT, WB, true, false>(K_GATEUP_DECODE, a.M, a.I_s, a.h, a.x, a.wg, a.wu, a.ldw_gu, a.sg,
-                                                a.su, a.a, a.lda, a.packed, a.sk, ct, stream);
-  if (e != hipSuccess) return e;
-  XRows ax{};
-  ax.p[0] = a.a;
-  ax.nb = 1;
-  ax.rows = a.M;
-  ax.ld = a.lda;
-  return sk_launch<NT, WB, false, false>(K_DOWN_DECODE, a.M, a.h, a.I_s, ax, a.wd, nullptr, a.ldw_down, a.sd,
-                                         nullptr, a.p, a.ldp, a.packed, a.sk, ct, stream);
-}
-
-// Whether the forward takes the split-K streams (M tokens, weight format
-// wb), and its scratch bytes (0 if it does not or needs none).
-template <int WB>
-int64_t forward_sk_bytes_wb(int M, int h, int I_s) {
-  if (h % (WB ? 64 : 32) || I_s % (WB ? 64 : 32)) return -1;
-  switch ((M + 15) / 16) {
-    case 2: return kSkStream<2, WB> ? forward_sk_bytes<2, WB>(h, I_s) : -1;
-    case 3: return kSkStream<3, WB> ? forward_sk_bytes<3, WB>(h, I_s) : -1;
-    case 4: return kSkStream<4, WB> ? forward_sk_bytes<4, WB>(h, I_s) : -1;
-    default: return -1;
-  }
-}
-
-template <int WB>
-hipError_t forward_sk_wb(const ShardArgs& a, hipStream_t stream) {
-  switch ((a.M + 15) / 16) {
-    case 2: if constexpr (kSkStream<2, WB>) return forward_sk<2, WB>(a, stream); break;
-    case 3: if constexpr (kSkStream<3, WB>) return forward_sk<3, WB>(a, stream); break;
-    case 4: if constexpr (kSkStream<4, WB>) return forward_sk<4, WB>(a, stream); break;
-    default: break;
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 namespace {
 
+template <int NT, int WB>
+int64_t workspace_bytes_nt(int M, int N, int K) {
+  const int nseg = stream_splits<NT, WB>(N, K);
+  if (nseg == 1) return 0;
+  return (int64_t)nseg * M * N * 4;
+}
+
 template <int WB>
 int64_t workspace_bytes_wb(int M, int N, int K) {
-  int nseg = 1;
-  if (streams<WB>(K)) {
-    switch ((M + 15) / 16) {
-      case 1: nseg = stream_splits<1, WB>(N, K); break;
-      case 2: nseg = stream_splits<2, WB>(N, K); break;
-      case 3: nseg = stream_splits<3, WB>(N, K); break;
-      default: nseg = stream_splits<4, WB>(N, K); break;
-    }
+  if (!streams<WB>(K)) return 0;
+  switch ((M + 15) / 16) {
+    case 1: return workspace_bytes_nt<1, WB>(M, N, K);
+    case 2: return workspace_bytes_nt<2, WB>(M, N, K);
+    case 3: return workspace_bytes_nt<3, WB>(M, N, K);
+    default: return workspace_bytes_nt<4, WB>(M, N, K);
   }
-  return nseg > 1 ? (int64_t)nseg * M * N * 4 : 0;
 }
 
 template <int WB>

@@ -42,8 +42,9 @@ def _bf16_dev(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+# rows of 1 to 8 chunks of 8 per thread held in registers, and (20480) the two-pass loop
 @pytest.mark.parametrize("rows,cols,scale", [(1, 8, 1.0), (7, 136, 3.0), (64, 8192, 1.0), (300, 3584, 1e-3),
-                                              (5, 1024, 1e4)])
+                                              (5, 1024, 1e4), (3, 16384, 1.0), (2, 20480, 2.0)])
 def test_quantiser_bit_exact(rows, cols, scale):
     print("quant rows=%d cols=%d" % (rows, cols), flush=True)
     rng = np.random.Generator(np.random.PCG64(rows * 7 + cols))
@@ -55,6 +56,24 @@ def test_quantiser_bit_exact(rows, cols, scale):
     q, s = tp.quantize_rows_e4m3(_bf16_dev(xb))
     torch.cuda.synchronize()
     q_ref, s_ref = oracle.quantise_rows_e4m3(oracle.bf16_bits_to_f64(xb).astype(np.float32))
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+    assert np.array_equal(q.cpu().numpy(), q_ref)
+
+
+def test_quantiser_row_scales_across_the_range():
+    """Rows whose magnitudes run from bf16 subnormals (the scale an fp32
+    subnormal) to 1e37: every code and scale bit-exact."""
+    print("quant scales across the range", flush=True)
+    rng = np.random.Generator(np.random.PCG64(77))
+    rows, cols = 80, 1024
+    exps = np.linspace(-40.0, 37.0, rows)
+    x = (rng.normal(0, 1, (rows, cols)) * 10.0 ** exps[:, None]).astype(np.float32)
+    x[:, 5] = -0.0
+    xb = workloads.f32_to_bf16_bits(x)
+    q, s = tp.quantize_rows_e4m3(_bf16_dev(xb))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quantise_rows_e4m3(oracle.bf16_bits_to_f64(xb).astype(np.float32))
+    assert s_ref[0] < np.finfo(np.float32).tiny        # the first rows' scales are fp32 subnormals
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(q.cpu().numpy(), q_ref)
 
