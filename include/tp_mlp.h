@@ -80,8 +80,9 @@ typedef enum {
  *    pieces, 64 MiB);
  *  - for a decode forward on the split-K streams (bf16 weights and
  *    49 <= M <= 64, one-byte weights and 17 <= M <= 32), arrival counters
- *    and one fp32 slot (128 weight rows by 16 * ceil(M / 16) tokens) per
- *    tile and K range (about 224 slots, 8 MiB for the 70B shard at TP = 8).
+ *    and one fp32 slot (112 or 128 weight rows by 16 * ceil(M / 16)
+ *    tokens) per tile and K range (about 256 slots, 8 MiB for the 70B
+ *    shard at TP = 8).
  */
 size_t tp_mlp_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t,
                               int32_t act_dtype, int32_t w_dtype);

@@ -778,14 +778,14 @@ __global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int ns
 // its activation reads: every workgroup re-reads the activations of its K
 // range, M / R bytes per weight byte for R rows per workgroup (two at 64
 // tokens and 32 rows), and staged through the ring they also take the LDS
-// that would hold weight bytes in flight.  Here a workgroup owns R = 64 * RB
-// rows (four waves of RB 16-row blocks) and one of nseg contiguous K ranges,
+// that would hold weight bytes in flight.  Here a workgroup owns R = 16 W RB
+// rows (W waves of RB 16-row blocks) and one of nseg contiguous K ranges,
 // so the grid still covers the chip while each activation byte serves R
 // rows:
 //  - the activation fragments of a step (16 tokens x 32 k each, in MFMA B
-//    order) are loaded once per workgroup, the four waves sharing the
-//    loads, D - 1 steps ahead into registers, and written to one of two
-//    LDS stages just before the step, where all four waves read them;
+//    order) are loaded once per workgroup, the W waves sharing the loads,
+//    D - 1 steps ahead into registers, and written to one of two LDS
+//    stages just before the step, where all W waves read them;
 //  - each wave streams its own weight fragments (packed layout: one
 //    contiguous kilobyte per load; (out, in) layout: 16 rows x 64 bytes)
 //    straight into registers, D - 1 steps ahead;
@@ -814,29 +814,29 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int NT, int WB>
+template <int NT, int WB, int W>
 struct SkShape {
   static constexpr int XJ = WB ? 2 : 1;          // activation fragments per token block and step
   static constexpr int NF = NT * XJ;             // activation fragments per step
-  static constexpr int AF = (NF + 3) / 4;        // ... loaded by each wave (padded)
-  static constexpr int STAGE = 4 * AF * 1024;    // LDS bytes per stage
+  static constexpr int AF = (NF + W - 1) / W;    // ... loaded by each of the W waves (padded)
+  static constexpr int STAGE = W * AF * 1024;    // LDS bytes per stage
 };
 
-// Bytes of one range's fp32 sums of a tile (4 waves x RB x NT fragments).
-template <int NT, int RB>
-constexpr int kSkSlot = 4 * RB * NT * 1024;
+// Bytes of one range's fp32 sums of a tile (W waves x RB x NT fragments).
+template <int NT, int RB, int W>
+constexpr int kSkSlot = W * RB * NT * 1024;
 
 // GU: gate/up (N = I_s channels, w0/w1 = W_gate/W_up or the packed array in
 // w0, out = A in bf16 with SiLU(gate) * up applied); else a row GEMM
 // (N output rows, out fp32 or bf16 (OBF)).  s0/s1: row scales of one-byte
 // weights.  part/cnt: split scratch (nseg > 1).  Each of the nseg K ranges
 // is at most NSTEP steps.
-template <int NT, int RB, int WB, int D, int NSTEP, bool PK, bool GU, bool OBF>
-__global__ __launch_bounds__(256) void sk_stream_kernel(
+template <int NT, int RB, int W, int WB, int D, int NSTEP, bool PK, bool GU, bool OBF>
+__global__ __launch_bounds__(W * 64) void sk_stream_kernel(
     int M, int N, int K, const XRows xr, const uint8_t* __restrict__ w0, const uint8_t* __restrict__ w1,
     int64_t ldw, const float* __restrict__ s0, const float* __restrict__ s1, void* __restrict__ out,
     int64_t ldo, int nseg, float* __restrict__ part, int* __restrict__ cnt) {
-  using SS = SkShape<NT, WB>;
+  using SS = SkShape<NT, WB, W>;
   constexpr int XJ = SS::XJ, AF = SS::AF;
   constexpr int EB = WB ? 1 : 2;
   constexpr int KSTEP = WB ? 64 : 32;           // k per step
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
 
   // Weight sources of this wave's blocks at step sb.
   const int nblk = GU ? (N + 7) / 8 : (N + 15) / 16;
-  const int blk0 = (tile * 4 + wave) * RB;
+  const int blk0 = (tile * W + wave) * RB;
   const uint8_t* wsrc[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
@@ -868,14 +868,14 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
       wsrc[rb] = w0 + (int64_t)row * ldw * EB + g * 16 + (int64_t)sb * 64;
     }
   }
-  // Activation fragments this wave loads: f = wave + 4a (token block f / XJ,
+  // Activation fragments this wave loads: f = wave + W a (token block f / XJ,
   // part f % XJ); the padding fragments (f >= NF) repeat fragment 0 into
   // stage positions nobody reads.  Lane l loads token (l % 16) of the block,
   // which is the MFMA B order.
   const uint8_t* xsrc[AF];
 #pragma unroll
   for (int a = 0; a < AF; ++a) {
-    const int f = wave + 4 * a < SS::NF ? wave + 4 * a : 0;
+    const int f = wave + W * a < SS::NF ? wave + W * a : 0;
     const int b = f / XJ, j = f % XJ;
     const int tok = min(b * 16 + r16, M - 1);
     const int k0 = sb * KSTEP + (WB ? 16 * g + 8 * j : 8 * g);
@@ -895,7 +895,7 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
   auto stage_x = [&](int stage, const u32x4 (&src)[AF]) {
 #pragma unroll
     for (int a = 0; a < AF; ++a)
-      *reinterpret_cast<u32x4*>(stage_buf[stage] + (wave + 4 * a) * 1024 + lane * 16) = src[a];
+      *reinterpret_cast<u32x4*>(stage_buf[stage] + (wave + W * a) * 1024 + lane * 16) = src[a];
   };
   auto issue_w = [&](int i, u32x4 (&dst)[RB]) {
 #pragma unroll
@@ -936,6 +936,7 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
   // reads), barrier (every wave's fragments are in), and compute it from the
   // stage and registers wf[i % D]; then issue step j (activations into
   // xv[j % D], weights into wf[j % D], both last used by step i - 1).
+  // (Staging two or four steps per barrier measured no faster.)
   // The iterations are unrolled at compile time (static_for; n <= NSTEP):
   // every stage and register set is a constant, and the compiler's wait
   // counting stays exact (at the head of a loop it drains every load).
@@ -956,7 +957,7 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
   });
 
   if (nseg > 1) {
-    constexpr int SLOT = kSkSlot<NT, RB>;
+    constexpr int SLOT = kSkSlot<NT, RB, W>;
     constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
     const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
         part + (int64_t)tile * nseg * (SLOT / 4), 0, nseg * SLOT, 0x00020000);
@@ -1049,8 +1050,8 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
     }
 }
 
-// Split-K streams: which token counts take them, their shape (RB row
-// blocks per wave, D steps in flight) and their grid: tiles of 64 * RB
+// Split-K streams: which token counts take them, their shape (W waves of
+// RB row blocks, D steps in flight) and their grid: tiles of 16 * W * RB
 // weight rows, K cut into nseg balanced ranges so that about kSkWgs
 // workgroups run, with ranges of at most 64 steps; the kernel is compiled
 // for ranges of up to 32 and up to 64 steps (nstep).
@@ -1059,23 +1060,31 @@ __global__ __launch_bounds__(256) void sk_stream_kernel(
 // rotating weight sets): 64 tokens 53.4 -> 48.6 us against the rings, 48
 // tokens 44.7 -> 44.5, 32 tokens 38.5 -> 41.9; fp8 at TP = 4, 32 tokens
 // 52.0 -> 44.5.  So they take bf16 weights at 49-64 tokens and one-byte
-// weights at 17-32.  The workgroup target is one per CU at most: a CU that
-// holds two finishes last (gate/up at 64 tokens: 56 tiles x 4 ranges = 224
-// workgroups 28.3 us, x 5 = 280 workgroups 47.6 us, x 9 = 504 33.6 us),
-// and more ranges cost more range sums (a round trip through memory each)
-// and shorter streams.  For the same reason they lose on a narrow output
+// weights at 17-32.  The workgroup target is one per CU: a CU that holds two
+// finishes last (gate/up at 64 tokens in 128-row tiles: 56 tiles x 4 ranges
+// = 224 workgroups 28.3 us, x 5 = 280 workgroups 47.6 us, x 9 = 504 33.6
+// us; in 112-row tiles, 64 x 4 = 256 workgroups, 29.2 -> 28.3 us on one
+// box against the 128-row tiles), and more ranges
+// cost more range sums (a round trip through memory each) and shorter
+// streams.  Pipelines of 12 or 16 steps instead of 8 measured no faster.  For the same reason they lose on a narrow output
 // such as the attention block's QKV projection (1280 rows: 10 tiles, 22
 // ranges of 11-12 steps): 13.2 us plus a 2 us finishing kernel on the
 // rings against 26.3 us at 64 tokens.
 template <int NT, int WB>
 constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
 
-template <int NT, int WB>
+// Tiles: gate/up seven waves of one 16-row block (112 rows = 56 channels),
+// so the 70B shards' gate/up rows (7168 and 14336) make whole multiples of
+// 64 tiles and their ranges fill the 256 CUs; the down projection four
+// waves of two blocks (128 rows).
+template <int NT, int WB, bool GU>
 struct SkPlan {
-  static constexpr int RB = 2;
+  static constexpr int W = GU ? 7 : 4;
+  static constexpr int RB = GU ? 1 : 2;
   static constexpr int D = 8;
+  static constexpr int ROWS = 16 * W * RB;
 };
-constexpr int kSkWgs = 224;
+constexpr int kSkWgs = 256;
 
 struct SkGrid {
   int tiles, nseg, nstep;
@@ -1083,8 +1092,8 @@ struct SkGrid {
 
 template <int NT, int WB, bool GU>
 SkGrid sk_grid(int N, int K) {
-  using P = SkPlan<NT, WB>;
-  const int rows = 64 * P::RB;
+  using P = SkPlan<NT, WB, GU>;
+  const int rows = P::ROWS;
   const int tiles = GU ? (2 * N + rows - 1) / rows : (N + rows - 1) / rows;
   const int nsteps = K / (WB ? 64 : 32);
   int nseg = max(1, (kSkWgs + tiles / 2) / tiles);
@@ -1093,9 +1102,10 @@ SkGrid sk_grid(int N, int K) {
   return SkGrid{tiles, nseg, longest <= 32 ? 32 : 64};
 }
 
-template <int NT, int RB>
+template <int NT, int WB, bool GU>
 int64_t sk_part_bytes(const SkGrid& g) {
-  return g.nseg > 1 ? (int64_t)g.tiles * g.nseg * kSkSlot<NT, RB> : 0;
+  using P = SkPlan<NT, WB, GU>;
+  return g.nseg > 1 ? (int64_t)g.tiles * g.nseg * kSkSlot<NT, P::RB, P::W> : 0;
 }
 
 inline int64_t sk_cnt_bytes(int tiles) { return ((int64_t)tiles * 4 + 255) / 256 * 256; }
@@ -1105,27 +1115,26 @@ template <int NT, int WB, bool GU, bool OBF>
 hipError_t sk_launch(int kind, int M, int N, int K, const XRows& xr, const void* w0, const void* w1, int64_t ldw,
                      const float* s0, const float* s1, void* out, int64_t ldo, bool packed, void* scratch,
                      int cnt_tiles, hipStream_t stream) {
-  using P = SkPlan<NT, WB>;
+  using P = SkPlan<NT, WB, GU>;
   const SkGrid gr = sk_grid<NT, WB, GU>(N, K);
   int* cnt = static_cast<int*>(scratch);
   float* part = reinterpret_cast<float*>(static_cast<uint8_t*>(scratch) + sk_cnt_bytes(cnt_tiles));
-  const dim3 grid(gr.tiles, gr.nseg), block(256);
+  const dim3 grid(gr.tiles, gr.nseg), block(P::W * 64);
   auto go = [&](auto kern) {
     return launch(kind, kern, grid, block, 0, stream, M, N, K, xr, (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0,
                   s1, out, ldo, gr.nseg, part, cnt);
   };
   if (gr.nstep == 32)
-    return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, true, GU, OBF>)
-                  : go(sk_stream_kernel<NT, P::RB, WB, P::D, 32, false, GU, OBF>);
-  return packed ? go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, true, GU, OBF>)
-                : go(sk_stream_kernel<NT, P::RB, WB, P::D, 64, false, GU, OBF>);
+    return packed ? go(sk_stream_kernel<NT, P::RB, P::W, WB, P::D, 32, true, GU, OBF>)
+                  : go(sk_stream_kernel<NT, P::RB, P::W, WB, P::D, 32, false, GU, OBF>);
+  return packed ? go(sk_stream_kernel<NT, P::RB, P::W, WB, P::D, 64, true, GU, OBF>)
+                : go(sk_stream_kernel<NT, P::RB, P::W, WB, P::D, 64, false, GU, OBF>);
 }
 
 template <int NT, int WB>
 int64_t forward_sk_bytes(int h, int I_s) {
-  using P = SkPlan<NT, WB>;
   const SkGrid g1 = sk_grid<NT, WB, true>(I_s, h), g2 = sk_grid<NT, WB, false>(h, I_s);
-  const int64_t part = max(sk_part_bytes<NT, P::RB>(g1), sk_part_bytes<NT, P::RB>(g2));
+  const int64_t part = max(sk_part_bytes<NT, WB, true>(g1), sk_part_bytes<NT, WB, false>(g2));
   return part ? sk_cnt_bytes(max(g1.tiles, g2.tiles)) + part : 0;
 }
 

@@ -83,14 +83,15 @@ def test_workspace_bytes():
     assert lib.tp_mlp_workspace_bytes(48, 8192, 28672, 8, BF16, BF16) == 48 * 3584 * 2
     assert lib.tp_mlp_workspace_bytes(16, 8192, 28672, 8, BF16, FP8) == 16 * 3584 * 2
     # decode split-K streams (bf16 at 49-64 tokens, one-byte weights at 17-32): arrival counters
-    # (one per tile of 128 weight rows, 256-byte rounded) and a 4 waves x 2 blocks x NT fragments
-    # slot (1 KB each) per tile and K range, the larger of the two GEMMs.  70B TP = 8, 64 tokens:
-    # gate/up 56 tiles x 4 ranges, down 64 tiles x 4 ranges of 32 KB slots
+    # (one per tile, 256-byte rounded) and a slot of fp32 fragments (1 KB each) per tile and K
+    # range, the larger of the two GEMMs: gate/up tiles of 7 waves x 1 block (112 rows), down of
+    # 4 waves x 2 blocks (128 rows).  70B TP = 8, 64 tokens: gate/up 64 tiles x 4 ranges of 28 KB,
+    # down 64 tiles x 4 ranges of 32 KB
     assert lib.tp_mlp_workspace_bytes(64, 8192, 28672, 8, BF16, BF16) == 64 * 3584 * 2 + 256 + 64 * 4 * 32768
-    # fp8 TP = 4, 32 tokens: gate/up 112 tiles x 2 ranges, down 64 tiles x 4 ranges of 16 KB
+    # fp8 TP = 4, 32 tokens: gate/up 128 tiles x 2 ranges of 14 KB, down 64 tiles x 4 ranges of 16 KB
     assert lib.tp_mlp_workspace_bytes(32, 8192, 28672, 4, BF16, FP8) == 32 * 7168 * 2 + 512 + 64 * 4 * 16384
     assert lib.tp_mlp_workspace_bytes(32, 8192, 28672, 4, BF16, _lib.TP_INT8) == 32 * 7168 * 2 + 512 + 64 * 4 * 16384
-    # fp8 TP = 8, 32 tokens: gate/up 56 tiles x 4 ranges, down 64 x 4
+    # fp8 TP = 8, 32 tokens: gate/up 64 tiles x 4 ranges, down 64 x 4
     assert lib.tp_mlp_workspace_bytes(32, 8192, 28672, 8, BF16, FP8) == 32 * 3584 * 2 + 256 + 64 * 4 * 16384
     # 600 tokens, h = I_s = 2048: gate/up in 128-token tiles (5 x 16, 2 pieces each: counters 512
     # bytes, slots of 128 x 256 fp32), down in 64-token tiles (10 x 8, 2 pieces each)

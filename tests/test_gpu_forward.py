@@ -323,14 +323,14 @@ def test_stream_decode_shapes(M, w):
 # ------------------------------------------------------------ decode split-K streams
 
 # bf16 weights at 49-64 tokens and one-byte weights at 17-32 take the split-K
-# streams: tiles of 128 weight rows, K cut into ranges whose fp32 sums the
-# last range to arrive adds in order.  (gate/up tiles x ranges, down tiles x
-# ranges; steps of 32 k bf16 / 64 k one-byte.)
+# streams: tiles of 112 (gate/up) or 128 (down) weight rows, K cut into
+# ranges whose fp32 sums the last range to arrive adds in order.  (gate/up
+# tiles x ranges, down tiles x ranges; steps of 32 k bf16 / 64 k one-byte.)
 SK_CASES = [
-    (64, 8192, 448, "bf16"),      # 7 x 32 ranges of 8 steps; 64 x 4 ranges of 3-4 steps
-    (57, 1088, 3584, "bf16"),     # 56 x 4 of 8-9; ragged 9 x 25 of 4-5 (1088 rows = 8.5 tiles)
-    (64, 256, 14336, "bf16"),     # 224 whole tiles (no split); 2 x 112 ranges of 4 steps
-    (32, 2048, 1024, "e4m3fn"),   # 16 x 14 of 2-3; 16 x 14 of 1-2
+    (64, 8192, 448, "bf16"),      # 8 x 32 ranges of 8 steps; 64 x 4 ranges of 3-4 steps
+    (57, 1088, 3584, "bf16"),     # 64 x 4 of 8-9; ragged 9 x 28 of 4 (1088 rows = 8.5 tiles)
+    (64, 256, 14336, "bf16"),     # 256 whole tiles (no split); 2 x 128 ranges of 3-4 steps
+    (32, 2048, 1024, "e4m3fn"),   # ragged 19 x 13 of 2-3 (2048 rows = 18.3 tiles); 16 x 16 of 1
     (17, 2048, 1024, "int8"),
 ]
 
