@@ -16,7 +16,8 @@ metric for the 70B-shaped TP=8 rank:
   4096 x 8192 partial (``reduce``: that reduce's own GB/s).
 
 Inputs are seeded synthetic tensors (``workloads``), resident in HBM before
-timing.
+timing.  The MFMA-bound workloads warm up for at least 50 ms by default
+(``WARMUP_MS``): the GPU's clocks settle only after about 40 ms of GEMMs.
 
 Other workloads (--workload): decode70b and prefill70b (the two halves
 alone), fp8_70b
@@ -175,9 +176,9 @@ class Phase:
         self.calls = {}
 
     def run(self, wset, time_fwd=None, other=0):
-        """time_fwd: (library, kind mask) to event-time this call's forward
-        launches of those kinds only; other: which set of other partials the
-        reduce reads."""
+        """time_fwd: (library, kind mask) to event-time this call's launches
+        (forward and reduce) of those kinds only; other: which set of other
+        partials the reduce reads."""
         # arguments are marshalled once per (weight set, other-partials set);
         # the loop only re-issues the C calls
         other = other % max(1, len(self.others))
@@ -198,12 +199,11 @@ class Phase:
         fwd, red = self.calls[key]
         if time_fwd is not None:
             time_fwd[0].tp_profile_enable(time_fwd[1])
-            fwd()
-            time_fwd[0].tp_profile_enable(0)
-        else:
-            fwd()
+        fwd()
         if red is not None:
             red()
+        if time_fwd is not None:
+            time_fwd[0].tp_profile_enable(0)
 
     def bytes(self, act="bf16"):
         b = workloads.forward_bytes(self.M, self.h, self.I_s, act, self.w)
@@ -257,6 +257,46 @@ def breakdown(tp, step_fn, steps, first):
     torch.cuda.synchronize()
     tp.profile_enable(False)
     return tp.profile_collect()
+
+
+def timed_phase(i, nph):
+    """The phase of step i whose launches are event-timed, or None: phase
+    i mod P on steps with i mod P < nph, P = max(nph, 3).  At most one phase
+    per step, and with fewer than three phases not every step: an event-timed
+    launch costs the host several plain ones, and a loop of short kernels
+    that turns host-bound starts its kernels on an idle GPU, where the
+    events read high."""
+    period = max(nph, 3)
+    return i % period if i % period < nph else None
+
+
+def breakdown_rotating(tp, run_step, nph, kinds, steps, first):
+    """Per-kind kernel durations of a loop of short kernels, in the timed
+    region's own regime: for each kind, a further `steps` steps in which only
+    that kind's launches in the phase timed_phase(i, nph) are event-timed, as
+    in the timed region.  (Timing every launch makes such a loop host-bound,
+    and its kernels then start on an idle GPU.)
+    run_step(i, sel): runs step i, sel(phase index) giving that phase's
+    (library, kind mask) or None.  Returns {kind: (ms, launches)} of the timed
+    launches and {kind: ms per step} (max(nph, 3) x ms / steps)."""
+    import torch
+    lib = tp.load()
+    names = tp.kernel_kinds()
+    rec, per_step = {}, {}
+    for k in kinds:
+        mask = 1 << names.index(k)
+        torch.cuda.synchronize()
+        tp.profile_collect()
+        tp.profile_reserve(2 * steps + 64)
+        for j in range(steps):
+            i = first + j
+            run_step(i, lambda idx, i=i: (lib, mask) if timed_phase(i, nph) == idx else None)
+        torch.cuda.synchronize()
+        got = tp.profile_collect()
+        if k in got:
+            rec[k] = got[k]
+            per_step[k] = max(nph, 3) * got[k][0] / steps
+    return rec, per_step
 
 
 def cpu_info():
@@ -331,27 +371,31 @@ def bench_decode70b(tp, args):
     def wset(i, idx):
         return sets[(nph * i + idx) % len(sets)]
 
-    def step(i):
+    def run_step(i, sel):
         for idx, ph in enumerate(phases):
-            ph.run(wset(i, idx), (lib, gmask) if i % nph == idx else None, other=i)
+            ph.run(wset(i, idx), sel(idx), other=i)
 
-    def step_plain(i):
-        for idx, ph in enumerate(phases):
-            ph.run(wset(i, idx), other=i)
+    def step(i):
+        run_step(i, lambda idx: (lib, gmask) if i % nph == idx else None)
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
     elapsed, prof = timed(tp, step, steps, warmup, [])
-    prof_all = breakdown(tp, step_plain, steps, warmup + steps)
+    # sk_clear: the one-workgroup clear of the split-K counters (M=64 forward)
+    prof_all, per_step = breakdown_rotating(tp, run_step, nph, ["gateup_decode", "down_decode", "sk_clear",
+                                                                "partial_reduce"], steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
     value = step_bytes * steps / elapsed / 1e9
-    gu_bytes = steps * sum(workloads.gateup_bytes(ph.M, h, I_s) for ph in phases)
-    dn_bytes = steps * sum(workloads.down_bytes(ph.M, h, I_s) for ph in phases)
-    red_bytes = steps * sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)
     kern = {}
-    for name, b in (("gateup_decode", gu_bytes), ("down_decode", dn_bytes), ("partial_reduce", red_bytes)):
-        ms, cnt = prof_all.get(name, (0.0, 0))
-        kern[name] = {"launches": cnt, "avg_us": round(1e3 * ms / max(cnt, 1), 3),
-                      "GBps": round(b / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+    for name, b in (("gateup_decode", sum(workloads.gateup_bytes(ph.M, h, I_s) for ph in phases)),
+                    ("down_decode", sum(workloads.down_bytes(ph.M, h, I_s) for ph in phases)),
+                    ("partial_reduce", sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)),
+                    ("sk_clear", None)):
+        if name not in prof_all:
+            continue
+        ms, cnt = prof_all[name]
+        kern[name] = {"launches": cnt, "avg_us": round(1e3 * ms / max(cnt, 1), 3)}
+        if b is not None:
+            kern[name]["GBps"] = round(b / (per_step[name] * 1e-3) / 1e9, 1)
     ms, cnt = prof["gateup_decode"]
     assert cnt == steps
     timed_bytes = sum(workloads.gateup_bytes(ph.M, h, I_s) * sum(1 for i in range(warmup, warmup + steps)
@@ -365,7 +409,7 @@ def bench_decode70b(tp, args):
             "avg_us": round(1e3 * ms / cnt, 3),
             "source": "HIP events on the gate/up launch of one phase per timed step (phase i mod 3), "
                       "on the launch stream; achieved = their algorithmic bytes / their summed durations"}
-    fwd_time_ms = sum(prof_all[k][0] for k in ("gateup_decode", "down_decode")) / steps
+    fwd_time_ms = sum(per_step[k] for k in ("gateup_decode", "down_decode", "sk_clear") if k in per_step)
     fwd_bytes = sum(workloads.forward_bytes(ph.M, h, I_s) for ph in phases)
     # parity sample at full size, outside the timed region: the M=1 forward alone on weight set 0
     # (the step's reduce overwrites the partial in place)
@@ -394,8 +438,9 @@ def bench_decode70b(tp, args):
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4),
                forward_only={"GBps": round(fwd_bytes / (fwd_time_ms * 1e-3) / 1e9, 1),
                              "us_per_step": round(fwd_time_ms * 1e3, 2)},
-               kernels=kern, kernels_note="kernels and forward_only: a further pass of the same "
-                                          "number of steps with every launch event-timed",
+               kernels=kern, kernels_note="kernels and forward_only: for each kernel kind a further pass of "
+                                          "the same number of steps that event-times that kind's launches "
+                                          "in one phase per step, like the timed region",
                parity_err_M1=parity)
     if not args.no_cpu_baseline:
         host_parts = [np.zeros(ph.M * h, np.float32) for ph in phases]
@@ -412,7 +457,18 @@ def bench_decode70b(tp, args):
     return out
 
 
-def bench_prefill(tp, args, cfg_id, M, label):
+# Untimed warm-up of the MFMA-bound workloads: at the start of a run of long
+# GEMMs the GPU's clocks take about 40 ms to settle (70B prefill gate/up in a
+# kernel trace: 437, 441, 534, 624, ... us, then down to a steady 405-415 us
+# after about 40 steps), so their default warm-up covers at least 50 ms.
+WARMUP_MS = 50.0
+
+
+def warmup_steps(step_ms):
+    return max(5, int(WARMUP_MS / step_ms + 0.999))
+
+
+def bench_prefill(tp, args, cfg_id, M, label, step_ms):
     import oracle
     c = workloads.CONFIGS[cfg_id]
     h, t, I_s, w = c["h"], c["t"], c["I"] // c["t"], c["w"]
@@ -424,7 +480,7 @@ def bench_prefill(tp, args, cfg_id, M, label):
     def step(i):
         ph.run(sets[0])
 
-    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(step_ms)
     elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"])
     prof = breakdown(tp, step, steps, warmup + steps)
     prof["gateup_prefill"] = prof_gu["gateup_prefill"]   # the timed region's own record
@@ -494,7 +550,7 @@ def bench_default(tp, args):
     GB/s) and, beside it, the 70B TP=8 prefill step (TFLOP/s: forward + the
     8-way reduce of its 4096 x 8192 partial) with the reduce's own GB/s."""
     out = bench_decode70b(tp, args)
-    pre = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL)
+    pre = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL, 0.85)
     red = pre.pop("reduce", None)
     out["prefill"] = {k: pre[k] for k in ("value", "unit", "steps", "warmup", "ms_per_step", "config", "roofline",
                                           "forward_only_TFLOPs", "forward_frac_of_bf16_peak", "kernels",
@@ -529,21 +585,33 @@ def bench_quant(tp, args, cfg_id):
     dsets = sets if args.row_major else \
         [dict(d, packed=tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)) for d in sets]
 
-    def step(i):
+    nph = len(decs)
+    lib = tp.load()
+    gmask = 1 << tp.kernel_kinds().index("gateup_decode")
+
+    def run_step(i, sel):
         # each phase of a step reads its own weight set
         for idx, ph in enumerate(decs):
-            ph.run(dsets[(len(decs) * i + idx) % len(dsets)])
+            ph.run(dsets[(nph * i + idx) % len(dsets)], sel(idx))
+
+    def step(i):
+        # the gate/up launch of at most one phase per step is event-timed
+        run_step(i, lambda idx: (lib, gmask) if timed_phase(i, nph) == idx else None)
 
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
-    el_d, prof_d = timed(tp, step, steps, warmup, ["gateup_decode"])
-    prof_d.update({k: v for k, v in breakdown(tp, step, steps, warmup + steps).items() if k != "gateup_decode"})
+    el_d, prof_d = timed(tp, step, steps, warmup, [])
+    rot, _ = breakdown_rotating(tp, run_step, nph, ["down_decode", "sk_clear"], steps, warmup + steps)
+    prof_d.update(rot)
     p_steps = max(10, steps // 10)
-    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), p_steps, 3, ["gateup_prefill", "down_prefill"])
+    el_p, prof_p = timed(tp, lambda i: pre.run(sets[0]), p_steps, warmup_steps(1.5 if w == "int8" else 0.7),
+                         ["gateup_prefill", "down_prefill"])
     dec_bytes = sum(ph.bytes() for ph in decs)
     dec_gbs = dec_bytes * steps / el_d / 1e9
     pre_tf = pre.flops() * p_steps / el_p / 1e12
     gu_ms, gu_n = prof_d["gateup_decode"]
-    gu_gbs = steps * sum(workloads.gateup_bytes(M, h, I_s, "bf16", w) for M in dec_Ms) / (gu_ms * 1e-3) / 1e9
+    timed_gu_bytes = sum(workloads.gateup_bytes(decs[timed_phase(warmup + j, nph)].M, h, I_s, "bf16", w)
+                         for j in range(steps) if timed_phase(warmup + j, nph) is not None)
+    gu_gbs = timed_gu_bytes / (gu_ms * 1e-3) / 1e9
     pgu_ms, pgu_n = prof_p["gateup_prefill"]
     pgu_tf = 4 * pre_M * h * I_s * pgu_n / (pgu_ms * 1e-3) / 1e12
     out = dict(metric=METRIC, value=round(dec_gbs, 1), unit="GB/s", n_gpus=1, steps=steps, warmup=warmup,
@@ -556,7 +624,10 @@ def bench_quant(tp, args, cfg_id):
                        "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": recorded_traffic("gateup_decode", args.workload), "kernel": "gateup_decode"},
+                         "traffic": recorded_traffic("gateup_decode", args.workload), "kernel": "gateup_decode",
+                         "avg_us": round(1e3 * gu_ms / gu_n, 3),
+                         "source": "HIP events on the gate/up launch of phase i mod %d on the timed steps i "
+                                   "with i mod %d < %d" % (max(nph, 3), max(nph, 3), nph)},
                prefill={"M": pre_M, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
                         "gateup_TFLOPs": round(pgu_tf, 1), "kernels": {k: {"avg_us": 1e3 * v[0] / v[1]}
                                                                       for k, v in prof_p.items()}},
@@ -595,7 +666,7 @@ def bench_w8a8(tp, args):
     w = sets[0]
     call = tp.prepare_shard_forward_w8a8(x, w["w_gate"], w["w_up"], w["w_down"], t=t, k=0, s_gate=w["s_gate"],
                                          s_up=w["s_up"], s_down=w["s_down"])
-    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(0.45)
     elapsed, prof_gu = timed(tp, lambda i: call(), steps, warmup, ["gateup_w8a8"])
     prof = breakdown(tp, lambda i: call(), steps, warmup + steps)
     prof["gateup_w8a8"] = prof_gu["gateup_w8a8"]
@@ -615,7 +686,8 @@ def bench_w8a8(tp, args):
                roofline={"bound": "mfma", "achieved": round(gu_tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(gu_tf / FP8_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic("gateup_w8a8", "w8a8_prefill70b"), "kernel": "gateup_w8a8",
-                         "per_launch_flop": 4 * M * h * I_s},
+                         "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
+                         "source": "HIP events on every gate/up launch of the timed steps"},
                kernels={k: {"launches": v[1], "avg_us": 1e3 * v[0] / v[1]} for k, v in prof.items()},
                gemm_TFLOPs={"gateup_w8a8": round(gu_tf, 1), "down_w8a8": round(dn_tf, 1)})
     if not args.no_cpu_baseline:
@@ -654,7 +726,9 @@ def bench_reduce(tp, args, cfg_id):
                                    % (t, n), "t": t, "n": n, "in_place": True},
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": recorded_traffic("partial_reduce", args.workload), "kernel": "partial_reduce"})
+                         "traffic": recorded_traffic("partial_reduce", args.workload), "kernel": "partial_reduce",
+                         "avg_us": round(1e3 * ms / cnt, 2), "source": "HIP events on every reduce launch of the "
+                                                                       "timed steps"})
     if not args.no_cpu_baseline:
         sub = max(1, n // 16)
         hp = [p[:sub] for p in parts_host]
@@ -690,7 +764,7 @@ def bench_sp_prefill(tp, args):
         fwd()
         rs()
 
-    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(0.85)
     elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"])
     prof = breakdown(tp, step, steps, warmup + steps)
     flops = workloads.forward_flops(M, h, I_s)
@@ -746,7 +820,8 @@ class AttnPhase:
         self.calls = {}
 
     def run(self, wset, time_qkv=None):
-        """time_qkv: (library, kind mask) to event-time this call's QKV launch only."""
+        """time_qkv: (library, kind mask) to event-time this call's launches of
+        those kinds only."""
         key = id(wset)
         if key not in self.calls:
             c = self.c
@@ -761,13 +836,12 @@ class AttnPhase:
         q, o, red = self.calls[key]
         if time_qkv is not None:
             time_qkv[0].tp_profile_enable(time_qkv[1])
-            q()
-            time_qkv[0].tp_profile_enable(0)
-        else:
-            q()
+        q()
         o()
         if red is not None:
             red()
+        if time_qkv is not None:
+            time_qkv[0].tp_profile_enable(0)
 
     def qkv_bytes(self, w="bf16"):
         return workloads.linear_bytes(self.M, self.n_loc, self.h, "bf16", w, "bf16")
@@ -821,26 +895,29 @@ def bench_attn_decode(tp, args):
     qmask = 1 << tp.kernel_kinds().index("qkv_decode")
 
     # each phase of a step reads its own weight set: phase idx of step i takes set (3 i + idx) mod n
-    def step(i):
+    def run_step(i, sel):
         for idx, ph in enumerate(phases):
-            ph.run(sets[(3 * i + idx) % len(sets)], (lib, qmask) if i % 3 == idx else None)
+            ph.run(sets[(3 * i + idx) % len(sets)], sel(idx))
 
-    def step_plain(i):
-        for idx, ph in enumerate(phases):
-            ph.run(sets[(3 * i + idx) % len(sets)])
+    def step(i):
+        run_step(i, lambda idx: (lib, qmask) if i % 3 == idx else None)
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
     elapsed, prof = timed(tp, step, steps, warmup, [])
-    prof_all = breakdown(tp, step_plain, steps, warmup + steps)
+    prof_all, per_step = breakdown_rotating(tp, run_step, 3, ["qkv_decode", "oproj_decode", "splitk_finish",
+                                                              "partial_reduce"], steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
     value = step_bytes * steps / elapsed / 1e9
     per = {"qkv_decode": sum(ph.qkv_bytes() for ph in phases), "oproj_decode": sum(ph.oproj_bytes() for ph in phases),
-           "partial_reduce": sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases)}
+           "partial_reduce": sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases), "splitk_finish": None}
     kern = {}
     for name, b in per.items():
-        ms, cnt = prof_all.get(name, (0.0, 0))
-        kern[name] = {"launches": cnt, "avg_us": 1e3 * ms / max(cnt, 1),
-                      "GBps": round(b * steps / (ms * 1e-3) / 1e9, 1) if ms > 0 else None}
+        if name not in prof_all:
+            continue
+        ms, cnt = prof_all[name]
+        kern[name] = {"launches": cnt, "avg_us": round(1e3 * ms / max(cnt, 1), 3)}
+        if b is not None:
+            kern[name]["GBps"] = round(b / (per_step[name] * 1e-3) / 1e9, 1)
     ms, cnt = prof["qkv_decode"]
     # the timed launches: phase idx on the steps i with i % 3 == idx
     timed_bytes = sum(ph.qkv_bytes() * sum(1 for i in range(warmup, warmup + steps) if i % 3 == idx)
@@ -869,9 +946,12 @@ def bench_attn_decode(tp, args):
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("qkv_decode", "attn70b"), "kernel": "qkv_decode",
-                         "per_launch_bytes": {str(ph.M): ph.qkv_bytes() for ph in phases}},
+                         "per_launch_bytes": {str(ph.M): ph.qkv_bytes() for ph in phases},
+                         "avg_us": round(1e3 * ms / cnt, 3),
+                         "source": "HIP events on the QKV launch of one phase per timed step (phase i mod 3)"},
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4), kernels=kern,
-               kernels_note="kernels: a further pass of the same number of steps with every launch event-timed",
+               kernels_note="kernels: for each kernel kind a further pass of the same number of steps that "
+                            "event-times that kind's launches in one phase per step, like the timed region",
                parity_err_M1=parity)
     if not args.no_cpu_baseline:
         hp = [[np.zeros(ph.M * h, np.float32)] * (t - 1) for ph in phases]
@@ -901,7 +981,7 @@ def bench_attn_prefill(tp, args):
     def step(i):
         ph.run(sets[0])
 
-    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else 5
+    steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(0.4)
     elapsed, prof_q = timed(tp, step, steps, warmup, ["qkv_prefill"])
     prof = breakdown(tp, step, steps, warmup + steps)
     prof["qkv_prefill"] = prof_q["qkv_prefill"]
@@ -924,7 +1004,8 @@ def bench_attn_prefill(tp, args):
                roofline={"bound": "mfma", "achieved": q_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(q_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic("qkv_prefill", "attn_prefill70b"), "kernel": "qkv_prefill",
-                         "per_launch_flop": f["qkv_prefill"]},
+                         "per_launch_flop": f["qkv_prefill"], "avg_us": round(kern["qkv_prefill"]["avg_us"], 2),
+                         "source": "HIP events on every QKV launch of the timed steps"},
                kernels=kern)
     if not args.no_cpu_baseline:
         rows = np.arange(0, M, M // 16)
@@ -978,10 +1059,10 @@ def main():
     elif args.workload == "decode70b":
         out = bench_decode70b(tp, args)
     elif args.workload == "prefill70b":
-        out = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL)
+        out = bench_prefill(tp, args, 3, 4096, PREFILL70B_LABEL, 0.85)
     elif args.workload == "prefill405b":
         out = bench_prefill(tp, args, 5, 8192, "405B-shaped TP=8 rank prefill, M=8192, h=16384, I_s=6656, "
-                                               "bf16, forward + 8-way fp32 partial reduce of 8192x16384")
+                                               "bf16, forward + 8-way fp32 partial reduce of 8192x16384", 5.5)
     elif args.workload == "fp8_70b":
         out = bench_quant(tp, args, 4)
     elif args.workload == "int8_70b":

@@ -142,11 +142,14 @@ const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish", "quant_rows",
     "gateup_w8a8", "down_w8a8", "sk_clear"};
 
-// Appends one start/stop event pair to the timing pool.
+// Appends one start/stop event pair to the timing pool.  The events only
+// time launches (read after the caller synchronises), so they skip the
+// system-scope fence on record: its L2 write-back and invalidate would add to
+// the timed interval and slow the launch that follows.
 bool prof_grow() {
   ProfRec r{};
-  if (hipEventCreate(&r.start) != hipSuccess) return false;
-  if (hipEventCreate(&r.stop) != hipSuccess) {
+  if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) return false;
+  if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
     (void)hipEventDestroy(r.start);
     return false;
   }
