@@ -1221,6 +1221,16 @@ constexpr int kRbXdByteDn = 2;
 // the rows, kept one).
 constexpr int kRbNt1Byte = 2;
 
+// bf16 weights, up to 16 tokens: the activation fragments of a slot are
+// M x 256 bytes against 4 KB of weights per row block, so from about 8
+// tokens two row blocks per wave pay for their halved workgroup count.
+// Measured on the 70B TP = 8 shard (whole forward, packed weights): gate/up
+// with two blocks 1 token 33.6 -> 34.2 us, 4: 33.9 -> 34.4, 8: 35.0 -> 34.7,
+// 12: 37.7 -> 35.4, 16: 42.0 -> 36.8; the down projection as well, over
+// that: 12 tokens 35.5 -> 35.4, 16: 36.8 -> 35.8, 8: 34.7 -> 35.2.
+constexpr int kRb2MinMGateUp = 8;
+constexpr int kRb2MinMDown = 13;
+
 // Up to 16 tokens: one 16-row block per wave, activations from registers
 // (most workgroups).  More tokens: RB row blocks per wave share each
 // activation fragment, and the activations come through the ring (where its
@@ -1228,10 +1238,9 @@ constexpr int kRbNt1Byte = 2;
 template <int NT, int WB>
 constexpr bool kStreamXD = NT >= 2 && (!WB || NT == 2);
 
-template <int NT, int WB>
-hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
+template <int NT, int WB, int RB>
+hipError_t gateup_stream_rb(const ShardArgs& a, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
-  constexpr int RB = NT == 1 ? (WB ? kRbNt1Byte : 1) : (XD && WB ? kRbXdByteGu : kRbWide);
   const dim3 grid((a.I_s + 8 * RB - 1) / (8 * RB)), block(StreamShape<NT, RB, WB, XD>::WV * 64);
   if (a.packed)
     return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD, true>, grid, block, 0, stream, a.M, a.h,
@@ -1239,6 +1248,17 @@ hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
                   a.lda);
   return launch(K_GATEUP_DECODE, gateup_stream_kernel<NT, RB, WB, XD, false>, grid, block, 0, stream, a.M, a.h,
                 a.I_s, a.x, (const uint8_t*)a.wg, (const uint8_t*)a.wu, a.ldw_gu, a.sg, a.su, (uint16_t*)a.a, a.lda);
+}
+
+template <int NT, int WB>
+hipError_t gateup_stream(const ShardArgs& a, hipStream_t stream) {
+  if constexpr (NT == 1 && !WB) {
+    if (a.M >= kRb2MinMGateUp) return gateup_stream_rb<1, WB, 2>(a, stream);
+    return gateup_stream_rb<1, WB, 1>(a, stream);
+  } else {
+    constexpr int RB = NT == 1 ? kRbNt1Byte : (kStreamXD<NT, WB> && WB ? kRbXdByteGu : kRbWide);
+    return gateup_stream_rb<NT, WB, RB>(a, stream);
+  }
 }
 
 template <int NT, int WB>
@@ -1289,6 +1309,9 @@ hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
   // the output is wide enough for kRowRB without a split (kRowRB's larger
   // block count would not split either).
   const int nseg = g.ws ? stream_splits<NT, WB>(g.N, g.K) : 1;
+  if constexpr (NT == 1 && !WB) {
+    if (nseg == 1 && g.M >= kRb2MinMDown) return rowgemm_stream_launch<1, 2, WB, OBF>(g, 1, stream);
+  }
   if (nseg == 1) return rowgemm_stream_launch<NT, kRowRB<NT, WB>, WB, OBF>(g, 1, stream);
   hipError_t e = rowgemm_stream_launch<NT, kRowRBSplit<NT, WB>, WB, OBF>(g, nseg, stream);
   if (e != hipSuccess) return e;

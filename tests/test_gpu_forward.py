@@ -302,11 +302,13 @@ def test_stream_k_tail_after_whole_rounds():
 
 # ------------------------------------------------------------ streaming decode path, several slots per wave
 
-@pytest.mark.parametrize("M", [1, 7, 16, 33, 64])
+@pytest.mark.parametrize("M", [1, 7, 8, 12, 13, 16, 33, 64])
 @pytest.mark.parametrize("w", ["bf16", "e4m3fn"])
 def test_stream_decode_shapes(M, w):
     # h and I_s multiples of the slot width (128 bf16 / 256 fp8 k-values) take
-    # the streaming kernels; uneven slot counts per wave, ragged token blocks
+    # the streaming kernels; uneven slot counts per wave, ragged token blocks.
+    # bf16 up to 16 tokens: one row block per wave below 8 tokens (gate/up) /
+    # 13 tokens (down), two from there; the packed layout gives the same bits.
     h, I_s = (512, 640) if w == "bf16" else (1024, 1280)
     print("stream decode M=%d w=%s" % (M, w), flush=True)
     x, ws = make_case(45, M, h, I_s, "bf16", w, 0.05, 0.05, weight_set=M)
@@ -318,6 +320,11 @@ def test_stream_decode_shapes(M, w):
     check(outs[0], ref, TOL_FP8 if w == "e4m3fn" else TOL_BF16, "stream M=%d %s" % (M, w))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
     assert np.array_equal(outs[0].view(np.uint32), outs[2].view(np.uint32))
+    if w == "bf16" or M <= 32:
+        pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=4)
+        pp = tp.shard_forward_packed(d["x"], pk, k=1, s_gate=d["s_gate"], s_up=d["s_up"], s_down=d["s_down"])
+        torch.cuda.synchronize()
+        assert np.array_equal(pp.cpu().numpy().view(np.uint32), outs[0].view(np.uint32))
 
 
 # ------------------------------------------------------------ decode split-K streams
