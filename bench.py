@@ -217,11 +217,12 @@ class Phase:
 
 # ----------------------------------------------------------------------------- timing
 
-def timed(tp, step_fn, steps, warmup, kinds):
+def timed(tp, step_fn, steps, warmup, kinds, dur_kind=None, dur=None):
     """Wall time of `steps` steps after `warmup`, with HIP-event timing of the
     library's launches of the kernel kinds `kinds` only (an event-timed launch
     costs the host several times a plain one, which would otherwise make the
-    loop host-bound)."""
+    loop host-bound).  dur_kind, dur: append the timed steps' durations (ms)
+    of that kind's timed launches, in launch order, to the list dur."""
     import torch
     # warm-up with the same timing on: counts the timed launches of a step, so
     # that every event the timed steps use exists before the clock starts
@@ -241,8 +242,19 @@ def timed(tp, step_fn, steps, warmup, kinds):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     tp.profile_enable(False)
+    if dur_kind is not None:
+        dur.extend(tp.profile_durations(dur_kind))
     prof = tp.profile_collect()
     return elapsed, prof
+
+
+def spread(ms):
+    """Median, 10th and 90th percentile (microseconds) of launch durations in ms."""
+    if not ms:
+        return None
+    v = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median_us": round(float(np.median(v)), 3), "p10_us": round(float(np.percentile(v, 10)), 3),
+            "p90_us": round(float(np.percentile(v, 90)), 3), "launches": int(v.size)}
 
 
 def breakdown(tp, step_fn, steps, first):
@@ -379,7 +391,8 @@ def bench_decode70b(tp, args):
         run_step(i, lambda idx: (lib, gmask) if i % nph == idx else None)
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
-    elapsed, prof = timed(tp, step, steps, warmup, [])
+    gu_dur = []
+    elapsed, prof = timed(tp, step, steps, warmup, [], "gateup_decode", gu_dur)
     # sk_clear: the one-workgroup clear of the split-K counters (M=64 forward)
     prof_all, per_step = breakdown_rotating(tp, run_step, nph, ["gateup_decode", "down_decode", "sk_clear",
                                                                 "partial_reduce"], steps, warmup + steps)
@@ -407,6 +420,8 @@ def bench_decode70b(tp, args):
             "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
             "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases},
             "avg_us": round(1e3 * ms / cnt, 3),
+            "per_M_launch_us": {str(ph.M): spread([d for j, d in enumerate(gu_dur) if (warmup + j) % nph == idx])
+                                for idx, ph in enumerate(phases)},
             "source": "HIP events on the gate/up launch of one phase per timed step (phase i mod 3), "
                       "on the launch stream; achieved = their algorithmic bytes / their summed durations"}
     fwd_time_ms = sum(per_step[k] for k in ("gateup_decode", "down_decode", "sk_clear") if k in per_step)
@@ -481,7 +496,8 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
         ph.run(sets[0])
 
     steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(step_ms)
-    elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"])
+    gu_dur = []
+    elapsed, prof_gu = timed(tp, step, steps, warmup, ["gateup_prefill"], "gateup_prefill", gu_dur)
     prof = breakdown(tp, step, steps, warmup + steps)
     prof["gateup_prefill"] = prof_gu["gateup_prefill"]   # the timed region's own record
     flops = ph.flops()
@@ -514,6 +530,7 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
             "traffic": recorded_traffic("gateup_prefill", args.workload if args.workload != "default" else
                                         "prefill70b"),
             "kernel": "gateup_prefill", "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
+            "launch_us": spread(gu_dur),
             "source": "HIP events on every gate/up launch of the timed steps, on the launch stream"}
     out = dict(metric=METRIC, value=round(value, 1), unit="TFLOP/s", n_gpus=1, steps=steps, warmup=warmup,
                ms_per_step=round(1e3 * elapsed / steps, 4), higher_is_better=True, scaling="weak",
@@ -599,7 +616,8 @@ def bench_quant(tp, args, cfg_id):
         run_step(i, lambda idx: (lib, gmask) if timed_phase(i, nph) == idx else None)
 
     steps, warmup = args.steps or 100, args.warmup if args.warmup is not None else 10
-    el_d, prof_d = timed(tp, step, steps, warmup, [])
+    gu_dur = []
+    el_d, prof_d = timed(tp, step, steps, warmup, [], "gateup_decode", gu_dur)
     rot, _ = breakdown_rotating(tp, run_step, nph, ["down_decode", "sk_clear"], steps, warmup + steps)
     prof_d.update(rot)
     p_steps = max(10, steps // 10)
@@ -625,7 +643,7 @@ def bench_quant(tp, args, cfg_id):
                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("gateup_decode", args.workload), "kernel": "gateup_decode",
-                         "avg_us": round(1e3 * gu_ms / gu_n, 3),
+                         "avg_us": round(1e3 * gu_ms / gu_n, 3), "launch_us": spread(gu_dur),
                          "source": "HIP events on the gate/up launch of phase i mod %d on the timed steps i "
                                    "with i mod %d < %d" % (max(nph, 3), max(nph, 3), nph)},
                prefill={"M": pre_M, "TFLOPs": round(pre_tf, 1), "frac_bf16_peak": round(pre_tf / BF16_PEAK_TFLOPS, 4),
@@ -667,7 +685,8 @@ def bench_w8a8(tp, args):
     call = tp.prepare_shard_forward_w8a8(x, w["w_gate"], w["w_up"], w["w_down"], t=t, k=0, s_gate=w["s_gate"],
                                          s_up=w["s_up"], s_down=w["s_down"])
     steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(0.45)
-    elapsed, prof_gu = timed(tp, lambda i: call(), steps, warmup, ["gateup_w8a8"])
+    gu_dur = []
+    elapsed, prof_gu = timed(tp, lambda i: call(), steps, warmup, ["gateup_w8a8"], "gateup_w8a8", gu_dur)
     prof = breakdown(tp, lambda i: call(), steps, warmup + steps)
     prof["gateup_w8a8"] = prof_gu["gateup_w8a8"]
     flops = workloads.forward_flops(M, h, I_s)
@@ -687,7 +706,7 @@ def bench_w8a8(tp, args):
                          "frac": round(gu_tf / FP8_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic("gateup_w8a8", "w8a8_prefill70b"), "kernel": "gateup_w8a8",
                          "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
-                         "source": "HIP events on every gate/up launch of the timed steps"},
+                         "launch_us": spread(gu_dur), "source": "HIP events on every gate/up launch of the timed steps"},
                kernels={k: {"launches": v[1], "avg_us": 1e3 * v[0] / v[1]} for k, v in prof.items()},
                gemm_TFLOPs={"gateup_w8a8": round(gu_tf, 1), "down_w8a8": round(dn_tf, 1)})
     if not args.no_cpu_baseline:
@@ -714,7 +733,9 @@ def bench_reduce(tp, args, cfg_id):
     # (the values grow step by step; the work and the bytes do not change)
     out = parts[0]
     steps, warmup = args.steps or 50, args.warmup if args.warmup is not None else 5
-    elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup, ["partial_reduce"])
+    red_dur = []
+    elapsed, prof = timed(tp, lambda i: tp.partial_reduce(parts, out=out), steps, warmup, ["partial_reduce"],
+                          "partial_reduce", red_dur)
     b = workloads.reduce_bytes(n, t)
     ms, cnt = prof["partial_reduce"]
     achieved = b * cnt / (ms * 1e-3) / 1e9
@@ -727,8 +748,8 @@ def bench_reduce(tp, args, cfg_id):
                roofline={"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": recorded_traffic("partial_reduce", args.workload), "kernel": "partial_reduce",
-                         "avg_us": round(1e3 * ms / cnt, 2), "source": "HIP events on every reduce launch of the "
-                                                                       "timed steps"})
+                         "avg_us": round(1e3 * ms / cnt, 2), "launch_us": spread(red_dur),
+                         "source": "HIP events on every reduce launch of the timed steps"})
     if not args.no_cpu_baseline:
         sub = max(1, n // 16)
         hp = [p[:sub] for p in parts_host]
@@ -903,7 +924,8 @@ def bench_attn_decode(tp, args):
         run_step(i, lambda idx: (lib, qmask) if i % 3 == idx else None)
 
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
-    elapsed, prof = timed(tp, step, steps, warmup, [])
+    q_dur = []
+    elapsed, prof = timed(tp, step, steps, warmup, [], "qkv_decode", q_dur)
     prof_all, per_step = breakdown_rotating(tp, run_step, 3, ["qkv_decode", "oproj_decode", "splitk_finish",
                                                               "partial_reduce"], steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
@@ -948,6 +970,9 @@ def bench_attn_decode(tp, args):
                          "traffic": recorded_traffic("qkv_decode", "attn70b"), "kernel": "qkv_decode",
                          "per_launch_bytes": {str(ph.M): ph.qkv_bytes() for ph in phases},
                          "avg_us": round(1e3 * ms / cnt, 3),
+                         "per_M_launch_us": {str(ph.M): spread([d for j, d in enumerate(q_dur)
+                                                                if (warmup + j) % 3 == idx])
+                                             for idx, ph in enumerate(phases)},
                          "source": "HIP events on the QKV launch of one phase per timed step (phase i mod 3)"},
                frac_of_hbm_peak=round(value / HBM_PEAK_GBS, 4), kernels=kern,
                kernels_note="kernels: for each kernel kind a further pass of the same number of steps that "
@@ -982,7 +1007,8 @@ def bench_attn_prefill(tp, args):
         ph.run(sets[0])
 
     steps, warmup = args.steps or 30, args.warmup if args.warmup is not None else warmup_steps(0.4)
-    elapsed, prof_q = timed(tp, step, steps, warmup, ["qkv_prefill"])
+    q_dur = []
+    elapsed, prof_q = timed(tp, step, steps, warmup, ["qkv_prefill"], "qkv_prefill", q_dur)
     prof = breakdown(tp, step, steps, warmup + steps)
     prof["qkv_prefill"] = prof_q["qkv_prefill"]
     value = ph.flops() * steps / elapsed / 1e12
@@ -1005,6 +1031,7 @@ def bench_attn_prefill(tp, args):
                          "frac": round(q_tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": recorded_traffic("qkv_prefill", "attn_prefill70b"), "kernel": "qkv_prefill",
                          "per_launch_flop": f["qkv_prefill"], "avg_us": round(kern["qkv_prefill"]["avg_us"], 2),
+                         "launch_us": spread(q_dur),
                          "source": "HIP events on every QKV launch of the timed steps"},
                kernels=kern)
     if not args.no_cpu_baseline:

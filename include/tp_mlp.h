@@ -467,6 +467,15 @@ tp_status tp_profile_reserve(int64_t records);
  */
 tp_status tp_profile_collect(double* total_ms, int64_t* counts, int32_t n_kinds);
 
+/*
+ * Durations in milliseconds of the recorded launches of kernel kind `kind`,
+ * in launch order, without clearing the record (call before
+ * tp_profile_collect): the first min(count, capacity) go to ms (host
+ * memory, may be NULL when capacity is 0) and the count to *n.  Waits for
+ * those launches' events.
+ */
+tp_status tp_profile_durations(int32_t kind, float* ms, int64_t capacity, int64_t* n);
+
 /* ------------------------------------------------------------------------
  * Packed decode weights.
  *

@@ -28,7 +28,7 @@ __all__ = ["shard_forward", "shard_forward_noalloc", "partial_reduce", "prepare_
            "prepare_partial_reduce_scatter", "attn_qkv_width", "attn_qkv_workspace_bytes", "attn_qkv_forward",
            "w8a8_workspace_bytes", "shard_forward_w8a8", "prepare_shard_forward_w8a8", "quantize_rows_e4m3", "prepare_attn_qkv_forward",
            "attn_out_forward", "prepare_attn_out_forward", "profile_reserve",
-           "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "kernel_kinds",
+           "workspace_bytes", "alloc_workspace", "profile_enable", "profile_collect", "profile_durations", "kernel_kinds",
            "TPError", "load"]
 
 
@@ -582,6 +582,19 @@ def profile_enable(on=True, kinds=None):
 def profile_reserve(records):
     """Create timing events for `records` launches ahead of a measured loop."""
     _lib.check(_lib.load().tp_profile_reserve(int(records)))
+
+
+def profile_durations(kind):
+    """Durations in milliseconds of the recorded launches of one kernel kind
+    (a name from kernel_kinds()), in launch order; the record is kept for
+    profile_collect()."""
+    lib = _lib.load()
+    k = kernel_kinds().index(kind)
+    n = ctypes.c_int64(0)
+    _lib.check(lib.tp_profile_durations(k, None, 0, ctypes.byref(n)))
+    buf = (ctypes.c_float * max(n.value, 1))()
+    _lib.check(lib.tp_profile_durations(k, buf, n.value, ctypes.byref(n)))
+    return [float(buf[i]) for i in range(n.value)]
 
 
 def profile_collect():

@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "tp_kernel_kind_name",
     "tp_profile_enable",
     "tp_profile_collect",
+    "tp_profile_durations",
     "tp_profile_reserve",
 )
 
@@ -126,6 +127,8 @@ def load():
     lib.tp_profile_collect.restype = c_i32
     lib.tp_profile_reserve.argtypes = [c_i64]
     lib.tp_profile_reserve.restype = c_i32
+    lib.tp_profile_durations.argtypes = [c_i32, ctypes.POINTER(ctypes.c_float), c_i64, ctypes.POINTER(c_i64)]
+    lib.tp_profile_durations.restype = c_i32
     _lib = lib
     return lib
 

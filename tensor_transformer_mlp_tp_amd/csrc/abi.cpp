@@ -861,6 +861,24 @@ TP_API tp_status tp_profile_reserve(int64_t records) {
   return TP_OK;
 }
 
+TP_API tp_status tp_profile_durations(int32_t kind, float* ms, int64_t capacity, int64_t* n) {
+  if (!n || capacity < 0 || (capacity > 0 && !ms)) return fail(TP_ERR_INVALID_ARG, "bad output arrays");
+  int64_t k = 0;
+  for (size_t i = 0; i < g_prof_used; ++i) {
+    ProfRec& r = g_prof_pool[i];
+    if (r.kind != kind) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return from_hip(e, "hipEventSynchronize");
+    float v = 0.f;
+    e = hipEventElapsedTime(&v, r.start, r.stop);
+    if (e != hipSuccess) return from_hip(e, "hipEventElapsedTime");
+    if (k < capacity) ms[k] = v;
+    ++k;
+  }
+  *n = k;
+  return TP_OK;
+}
+
 TP_API tp_status tp_profile_collect(double* total_ms, int64_t* counts, int32_t n_kinds) {
   if (!total_ms || !counts || n_kinds < 0) return fail(TP_ERR_INVALID_ARG, "bad output arrays");
   for (size_t i = 0; i < g_prof_used; ++i) {
