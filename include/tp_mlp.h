@@ -477,17 +477,23 @@ tp_status tp_profile_collect(double* total_ms, int64_t* counts, int32_t n_kinds)
 tp_status tp_profile_durations(int32_t kind, float* ms, int64_t capacity, int64_t* n);
 
 /* ------------------------------------------------------------------------
- * Packed decode weights.
+ * Packed weights.
  *
- * The same forward as tp_mlp_shard_forward at decode sizes (M <= 64; M <= 32
- * with one-byte weights), reading the rank's three weight matrices from one
- * array in the order the weight-streaming kernels consume them: each
- * workgroup then reads one contiguous range of memory instead of 16 rows
- * side by side (on MI355X the gate/up launches of the 70B shard measured
- * 5 to 14 % shorter).  Packing is a permutation of the weight bytes, done once per weight
- * set on the GPU; the packed forward's partial is bit-identical to
- * tp_mlp_shard_forward's on the same weights.  The projections are those of
- * "The Tensor-Parallel Shard Group" (scalablesystem.dev): the rank's column
+ * The same forward as tp_mlp_shard_forward, reading the rank's three weight
+ * matrices from one array in the order the weight-streaming decode kernels
+ * consume them: each workgroup then reads one contiguous range of memory
+ * instead of 16 rows side by side (on MI355X the gate/up launches of the 70B
+ * shard measured 5 to 14 % shorter).  With bf16 weights the same array also
+ * serves every larger M: MFMA GEMMs on 256-token tiles that load each
+ * packed 1 KB fragment straight into the matrix instruction's operand
+ * registers, so a server keeps one copy of the weights for decode and
+ * prefill.  Packing is a permutation of the weight bytes, done once per
+ * weight set on the GPU.  At decode sizes the packed forward's partial is
+ * bit-identical to tp_mlp_shard_forward's on the same weights; above them
+ * too when both add the products in the same order (256-token tiles with
+ * the same stream-K plan, e.g. 4096 tokens of the 70B TP = 8 shard), and
+ * otherwise within the bf16 tolerance.  The projections are those of "The
+ * Tensor-Parallel Shard Group" (scalablesystem.dev): the rank's column
  * shards of W_gate and W_up and its row shard of W_down.
  *
  * Layout (opaque to callers; for the record): gate/up blocks of 8 channels
@@ -520,15 +526,27 @@ tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32_t w_dt
                               void* packed, size_t packed_bytes, void* stream);
 
 /*
+ * Workspace bytes of tp_mlp_shard_forward_packed for these shapes (bf16
+ * activations): A (M x I_s bf16) plus the split scratch of the decode
+ * streams or, above the decode sizes, the stream-K scratch of the packed
+ * 256-token GEMMs (this can exceed tp_mlp_workspace_bytes for a few hundred
+ * tokens).  0 if the shapes are invalid or the packed forward does not take
+ * them (one-byte weights above 32 tokens).
+ */
+size_t tp_mlp_packed_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t w_dtype);
+
+/*
  * tp_mlp_shard_forward with the weights given as a packed array (above)
  * instead of w_gate, w_up, w_down and their leading dimensions; bf16
- * activations only; M at most 64 (32 with one-byte weights), else
- * TP_ERR_UNSUPPORTED.  packed_bytes is the size of the caller's packed
- * array; fewer than tp_mlp_packed_weights_bytes(h, I_full, t, w_dtype) bytes
- * (an array packed for other shapes) is TP_ERR_INVALID_ARG.  s_gate, s_up,
- * s_down, partial, the workspace (tp_mlp_workspace_bytes(...) bytes) and the
- * errors are as there; the packed array must not overlap the partial or the
- * workspace.
+ * activations only.  Any M >= 1 with bf16 weights; with one-byte weights M
+ * at most 32, else TP_ERR_UNSUPPORTED.  packed_bytes is the size of the
+ * caller's packed array; fewer than tp_mlp_packed_weights_bytes(h, I_full,
+ * t, w_dtype) bytes (an array packed for other shapes) is
+ * TP_ERR_INVALID_ARG.  The workspace needs tp_mlp_packed_workspace_bytes(...)
+ * bytes (TP_ERR_WORKSPACE if smaller); its contents on entry do not matter.
+ * s_gate, s_up, s_down, partial and the other errors are as for
+ * tp_mlp_shard_forward; the packed array must not overlap the partial or
+ * the workspace.
  */
 tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
                                       int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,

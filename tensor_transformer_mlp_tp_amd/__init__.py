@@ -267,10 +267,16 @@ def pack_weights(w_gate, w_up, w_down, *, t, out=None, stream=None):
     return PackedWeights(out, h, I_s, int(t), wc)
 
 
+def packed_workspace_bytes(M, h, I_full, t, w_dtype=torch.bfloat16):
+    """Workspace bytes of ``shard_forward_packed`` (0: shapes the packed forward does not take)."""
+    return int(_lib.load().tp_mlp_packed_workspace_bytes(M, h, I_full, t, _w_code(w_dtype)))
+
+
 def shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down=None, partial=None, workspace=None,
                          stream=None):
-    """``shard_forward`` at decode sizes with packed weights (bit-identical
-    partial); x (M, h) bf16."""
+    """``shard_forward`` with packed weights; x (M, h) bf16.  Decode sizes run
+    the weight-streaming kernels (bit-identical to ``shard_forward``), larger
+    M with bf16 weights the packed-weight MFMA GEMMs."""
     call = prepare_shard_forward_packed(x, packed, k=k, s_gate=s_gate, s_up=s_up, s_down=s_down, partial=partial,
                                         workspace=workspace, stream=stream)
     call()
@@ -297,7 +303,7 @@ def prepare_shard_forward_packed(x, packed, *, k, s_gate=None, s_up=None, s_down
     lib = _lib.load()
     act = _act_code(x.dtype)
     I_full = packed.I_s * packed.t
-    need = int(lib.tp_mlp_workspace_bytes(M, h, I_full, packed.t, act, packed.w_code))
+    need = int(lib.tp_mlp_packed_workspace_bytes(M, h, I_full, packed.t, packed.w_code))
     if workspace is None:
         workspace = alloc_workspace(max(need, 1), device)
     elif workspace.device != device:

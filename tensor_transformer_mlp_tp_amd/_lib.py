@@ -24,6 +24,7 @@ EXPORTED_SYMBOLS = (
     "tp_mlp_packed_weights_bytes",
     "tp_mlp_pack_weights",
     "tp_mlp_shard_forward_packed",
+    "tp_mlp_packed_workspace_bytes",
     "tp_partial_reduce",
     "tp_mlp_shard_forward_sp",
     "tp_partial_reduce_scatter",
@@ -93,6 +94,8 @@ def load():
         c_i64, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, vp, c_i64, vp, ctypes.c_size_t, vp, vp, vp, vp, c_i64, vp,
         ctypes.c_size_t, vp]
     lib.tp_mlp_shard_forward_packed.restype = c_i32
+    lib.tp_mlp_packed_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32, c_i32]
+    lib.tp_mlp_packed_workspace_bytes.restype = ctypes.c_size_t
     lib.tp_mlp_w8a8_workspace_bytes.argtypes = [c_i64, c_i64, c_i64, c_i32]
     lib.tp_mlp_w8a8_workspace_bytes.restype = ctypes.c_size_t
     lib.tp_mlp_shard_forward_w8a8.argtypes = [

@@ -123,6 +123,16 @@ int64_t workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t act, int32_t w
   return workspace_a_bytes(M, I_s, act) + round_up(sk, 256);
 }
 
+// Workspace of the packed forward (bf16 activations): the decode streams'
+// split scratch, or above the decode sizes that of the packed-weight GEMMs.
+int64_t packed_workspace_need(int64_t M, int64_t h, int64_t I_s, int32_t w) {
+  const int wb = weight_format(w);
+  const int64_t sk = M > tpmlp::forward_decode_max_m(wb)
+                         ? tpmlp::forward_prefill_packed_sk_bytes((int)M, (int)h, (int)I_s)
+                         : tpmlp::forward_decode_sk_bytes((int)M, (int)h, (int)I_s, wb);
+  return workspace_a_bytes(M, I_s, TP_BF16) + round_up(sk, 256);
+}
+
 // ------------------------------------------------------------------ timing
 
 struct ProfRec {
@@ -411,6 +421,14 @@ TP_API tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32
   return from_hip(tpmlp::launch_pack_weights(a, packed, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
 }
 
+TP_API size_t tp_mlp_packed_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t w_dtype) {
+  if (check_shapes(M, h, I_full, t, 0, TP_BF16, w_dtype) != TP_OK) return 0;
+  const int wb = weight_format(w_dtype);
+  if (M > tpmlp::forward_decode_max_m(wb) && wb != tpmlp::kWeightWide) return 0;
+  if (packed_need(h, I_full, t, w_dtype) == 0) return 0;
+  return (size_t)packed_workspace_need(M, h, I_full / t, w_dtype);
+}
+
 TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t k,
                                              int32_t act_dtype, int32_t w_dtype, const void* x, int64_t ldx,
                                              const void* packed, size_t packed_bytes, const float* s_gate,
@@ -420,8 +438,9 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   if (st != TP_OK) return st;
   if (act_dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "packed weights take bf16 activations");
   const int wb = weight_format(w_dtype);
-  if (M > tpmlp::forward_decode_max_m(wb))
-    return fail(TP_ERR_UNSUPPORTED, "packed weights serve the decode kernels: M <= %d (got %lld)",
+  const bool prefill = M > tpmlp::forward_decode_max_m(wb);
+  if (prefill && wb != tpmlp::kWeightWide)
+    return fail(TP_ERR_UNSUPPORTED, "packed one-byte weights serve the decode kernels: M <= %d (got %lld)",
                 tpmlp::forward_decode_max_m(wb), (long long)M);
   const int64_t pbytes = packed_need(h, I_full, t, w_dtype);
   if (pbytes == 0) return TP_ERR_UNSUPPORTED;
@@ -438,7 +457,7 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   if (ldx < h || ldp < h)
     return fail(TP_ERR_INVALID_ARG, "leading dimension smaller than the row length (ldx=%lld ldp=%lld)",
                 (long long)ldx, (long long)ldp);
-  const int64_t need = workspace_need(M, h, I_s, act_dtype, w_dtype);
+  const int64_t need = packed_workspace_need(M, h, I_s, w_dtype);
   if (!workspace || (int64_t)workspace_bytes < need)
     return fail(TP_ERR_WORKSPACE, "workspace of %lld bytes needed (got %llu)", (long long)need,
                 (unsigned long long)workspace_bytes);
@@ -478,6 +497,8 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   a.lda = I_s;
   a.sk = need > workspace_a_bytes(M, I_s, act_dtype)
              ? static_cast<uint8_t*>(workspace) + workspace_a_bytes(M, I_s, act_dtype) : nullptr;
+  if (prefill)
+    return from_hip(tpmlp::launch_forward_prefill(a, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
   return from_hip(tpmlp::launch_forward_decode(a, reinterpret_cast<hipStream_t>(stream)), "kernel launch");
 }
 

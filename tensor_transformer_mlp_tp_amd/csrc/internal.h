@@ -159,6 +159,8 @@ int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K);
 // Stream-K scratch of a prefill forward's two GEMMs (they run one after the
 // other and share it); a8: the fp8 x fp8 forward.
 int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8);
+// Stream-K scratch of the packed-weight prefill forward (bf16, 256-token tiles).
+int64_t forward_prefill_packed_sk_bytes(int M, int h, int I_s);
 // out = ordered sum of the nseg split sums in ws (nseg x M x N fp32), times
 // the row scales for one-byte weights (wb != 0), fp32 or bf16 (obf).
 hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,

@@ -171,9 +171,10 @@ struct SkTail {
 // d slots in k order into acc and returns true (it writes the tile), every
 // other piece returns false.  NT threads, each holding CB x TB 32x32 blocks;
 // `flag` is an int in LDS.
-template <int CB, int TB, int NT, int BM>
+template <int CB, int TB, int NT, int BM, int TBC = TB>
 __device__ __forceinline__ bool sk_handoff(f32x16 (&acc)[CB][TB], const SkTail sk, int tail, int piece, int tid,
                                            int* flag) {
+  static_assert(TB % TBC == 0, "token blocks per round trip");
   constexpr int SLOT = BM * BN * 4;     // bytes per slot
   static_assert(CB * TB * 16 * NT * 4 == SLOT, "a slot holds the tile");
   constexpr int kDeviceScope = 16;      // buffer cache policy: sc1
@@ -212,45 +213,48 @@ __device__ __forceinline__ bool sk_handoff(f32x16 (&acc)[CB][TB], const SkTail s
   if (tid == 0) *flag = __hip_atomic_fetch_add(sk.cnt + tail, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   if (*flag != sk.d - 1) return false;  // another piece writes the tile
-  // k-order sum, one weight-row block at a time: the block's 16 f32x4 of a
-  // slot are loaded together (one memory round trip per slot and block)
+  // k-order sum, TBC token blocks of one weight-row block at a time: their
+  // 4 TBC f32x4 of a slot are loaded together (one memory round trip per
+  // slot and chunk; a smaller TBC needs fewer registers)
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    f32x4 sum[TB * 4], v[TB * 4];
-    auto own = [&](f32x4 (&dst)[TB * 4]) {
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
+    for (int t0 = 0; t0 < TB; t0 += TBC) {
+      f32x4 sum[TBC * 4], v[TBC * 4];
+      auto own = [&](f32x4 (&dst)[TBC * 4]) {
+#pragma unroll
+        for (int tb = 0; tb < TBC; ++tb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][t0 + tb][4 * qd + i];
+      };
+      auto load = [&](int p, f32x4 (&dst)[TBC * 4]) {
+#pragma unroll
+        for (int tb = 0; tb < TBC; ++tb)
+#pragma unroll
+          for (int qd = 0; qd < 4; ++qd)
+            dst[tb * 4 + qd] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                           slots, p * SLOT + (((cb * TB + t0 + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
+      };
+      if (piece == 0) own(sum);
+      else load(0, sum);
+      for (int p = 1; p < sk.d; ++p) {
+        if (p == piece) own(v);
+        else load(p, v);
+#pragma unroll
+        for (int e = 0; e < TBC * 4; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
+      }
+#pragma unroll
+      for (int tb = 0; tb < TBC; ++tb)
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dst[tb * 4 + qd][i] = acc[cb][tb][4 * qd + i];
-    };
-    auto load = [&](int p, f32x4 (&dst)[TB * 4]) {
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-          dst[tb * 4 + qd] = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                         slots, p * SLOT + (((cb * TB + tb) * 4 + qd) * NT + tid) * 16, 0, kDeviceScope));
-    };
-    if (piece == 0) own(sum);
-    else load(0, sum);
-    for (int p = 1; p < sk.d; ++p) {
-      if (p == piece) own(v);
-      else load(p, v);
-#pragma unroll
-      for (int e = 0; e < TB * 4; ++e)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum[e][i] += v[e][i];
+          for (int i = 0; i < 4; ++i) acc[cb][t0 + tb][4 * qd + i] = sum[tb * 4 + qd][i];
     }
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[cb][tb][4 * qd + i] = sum[tb * 4 + qd][i];
-  }
   return true;
 }
 
@@ -833,6 +837,226 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
                                                      out, ld_out);
 }
 
+// Packed-weight GEMM (bf16 weights in the packed decode layout, bf16
+// activations, 256 x 256 tiles).  The packed array stores each 16-row block
+// of W as its run of 1 KB fragments, fragment f giving the 16 bytes at
+// 16 * L to lane L: row L % 16, k values 32 f + 8 (L / 16) + (0..7).  Two
+// consecutive blocks b, b + 1 then form the A operand of two 32x32x16 MFMAs
+// per fragment directly: for MFMA h (k values 32 f + 16 h + (0..15)), lane l
+// takes row l % 32 (block b + (l / 16) % 2, row l % 16) with k group l / 32,
+// i.e. the 16 bytes at 256 (2 h + l / 32) + 16 (l % 16) of that block's
+// fragment, and one 16-byte load per lane fetches two 512-byte contiguous
+// pieces.  The k order is the one the LDS-staged kernels use (chunk 2 kk + g
+// of a 64-k stage), so the activation side is unchanged.
+//
+// So the weights go from memory straight into registers, each wave loading
+// the fragments of its own 64 rows one stage ahead (64 VGPRs, two sets), and
+// only the activations pass through LDS: a ring of four 32 KB stages filled
+// by direct-to-LDS loads three stages ahead.  Per 64-k stage the LDS moves
+// 32 KB of writes and 128 KB of fragment reads (the two-operand kernels: 64 KB
+// and 192 KB).
+//
+// Eight waves, two per SIMD: wave q of group G (q = wave % 4, G = wave / 4)
+// owns the tile's blocks 4q .. 4q + 3 (64 weight rows) and tokens 128 G ..
+// 128 G + 127, 2 x 4 blocks of 32 x 32 (128 fp32 accumulators per lane).
+// Gate/up blocks hold 8 channels' gate rows then their up rows, so in a
+// 32-row MFMA block the lane's registers 0-3 / 4-7 are the gate / up sums of
+// channels 8 b + 4 g + (0..3) and registers 8-11 / 12-15 those of block b + 1,
+// and SiLU(G) * U needs no exchange between lanes.
+template <bool SWIGLU, bool OBF, bool SK>
+__global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, const uint8_t* __restrict__ xb,
+                                                         int64_t ldx, const uint8_t* wp, int nblk,
+                                                         void* __restrict__ out, int64_t ld_out, int tiles_m,
+                                                         int tiles_n, const SkTail sk) {
+  constexpr int BM = 256, BK = 64;
+  constexpr int CB = 2, TB = 4;               // 32-row weight blocks, 32-token blocks per wave
+  constexpr int ROWB = BK * 2;                // bytes per LDS row
+  constexpr int STAGE = BM * ROWB;            // 32 KB of activations per stage
+  constexpr int NS = 4;                       // stages in the ring
+  constexpr int KSUB = BK / 16;               // MFMA k-steps per stage
+  constexpr int BPT = 16;                     // 16-row blocks per tile
+  static_assert(NS * STAGE <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
+  const int q = wave & 3;
+  const int r32 = lane & 31, g = lane >> 5;
+
+  // ---- tile and k-range (as gemm_pp_kernel)
+  const int KT = K / BK;
+  const int blk = blockIdx.x;
+  int L, kt0 = 0, kt1 = KT, tail = -1, piece = 0;
+  if (SK && blk >= sk.nfull) {
+    const int rem = tiles_m * tiles_n - sk.nfull;
+    const int j = xcd_fold(blk - sk.nfull, rem * sk.d);
+    piece = j / rem;
+    tail = j - piece * rem;
+    kt0 = (int)((int64_t)piece * KT / sk.d);
+    kt1 = (int)((int64_t)(piece + 1) * KT / sk.d);
+    L = sk.nfull + tail;
+  } else {
+    L = xcd_fold(blk, SK ? sk.nfull : tiles_m * tiles_n);
+  }
+  const TileCoord tc = tile_coord(L, tiles_m, tiles_n);
+  const int m0 = tc.tm * BM;
+  const int b0 = tc.tn * BPT;
+
+  // ---- activation loads: this wave's 32 token rows of a stage, four 1 KB
+  // direct loads of 8 rows x 128 bytes, chunk-swizzled
+  const uint8_t* xsrc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wave * 32 + i * 8 + lane / 8;
+    const int c = (lane % 8) ^ swz<ROWB>(row);
+    xsrc[i] = xb + (int64_t)min(m0 + row, M - 1) * ldx * 2 + c * 16;
+  }
+  // stage kt (clamped to the k-range: every iteration issues the same loads)
+  auto load_x = [&](int kt, int buf) {
+    kt = min(kt, kt1 - 1);
+    uint8_t* dst = lds + buf * STAGE + wave * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_lds16(xsrc[i] + (int64_t)kt * ROWB, dst + i * 1024);
+  };
+
+  // ---- weight fragments: block pair (4q + 2cb, +1) of the tile; blocks past
+  // the end read the last block (their outputs are not stored)
+  const int64_t fpb = K / 32;                 // fragments per block
+  const uint8_t* wsrc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int b = min(b0 + 4 * q + 2 * cb + ((lane >> 4) & 1), nblk - 1);
+    wsrc[cb] = wp + (int64_t)b * fpb * 1024 + 256 * g + 16 * (lane & 15);
+  }
+  // one weight fragment (k-step kk, MFMA block cb) of stage kt
+  auto load_w = [&](int kt, int cb, int kk, u32x4& w) {
+    kt = min(kt, kt1 - 1);
+    w = *reinterpret_cast<const u32x4*>(wsrc[cb] + ((int64_t)kt * 2 + (kk >> 1)) * 1024 + 512 * (kk & 1));
+  };
+
+  int xrow[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) xrow[tb] = grp * 128 + tb * 32 + r32;
+
+  f32x16 acc[CB][TB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
+
+  // Order of the loads.  Iteration s (stage kt0 + s): wait for this wave's
+  // activation loads of stage s; barrier (every wave's loads of stage s have
+  // landed and every wave is done with stage s - 1); issue the activations of
+  // stage s + 3 into the buffer of stage s - 1 (four loads); compute stage s:
+  // for each k-step kk, wait for the weight fragments of kk (loaded during
+  // stage s - 1), issue the MFMAs of kk, then reload the same two registers
+  // with the fragments of kk for stage s + 1 (two loads).  So each weight
+  // fragment has one stage to arrive, the activations three, and the wave
+  // holds one set of weight registers (32 VGPRs).
+  // Loads issued after stage s's activations at the barrier wait: 32 (the
+  // weights of stages s - 2, s - 1 and s, the activations of s + 1 and
+  // s + 2); 16 at s = 0 (X1, X2, W0) and 24 at s = 1 (X2, W0, X3, W1).
+  // Loads issued after fragment kk of stage s at its wait: 2 (3 - kk) + 4.
+  // The waits are explicit: the direct-to-LDS loads are FLAT instructions,
+  // after which a wait that the compiler inserts itself for a register is
+  // widened to vmcnt(0), which would drain the prefetch.  The empty asm
+  // statements with a memory clobber keep the compiler from moving loads
+  // across those points.
+  typedef u32x4 WSet[CB][KSUB];
+  auto load_ws = [&](int kt, WSet& w) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) load_w(kt, cb, kk, w[cb][kk]);
+  };
+  auto compute = [&](int s, const WSet& w) {
+    const uint8_t* sx = lds + (s % NS) * STAGE;
+    bf16x8 xf[2][TB];
+    auto read = [&](int kk, bf16x8 (&x_)[TB]) {
+      const int c = 2 * kk + g;
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb)
+        x_[tb] = as_bf16x8(lds_read16(sx + xrow[tb] * ROWB + ((c ^ swz<ROWB>(xrow[tb])) * 16)));
+    };
+    read(0, xf[0]);
+#pragma unroll
+    for (int kk = 0; kk < KSUB; ++kk) {
+      if (kk + 1 < KSUB) read(kk + 1, xf[(kk + 1) & 1]);
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(as_bf16x8(w[cb][kk]), xf[kk & 1][tb], acc[cb][tb]);
+    }
+    constexpr int NMF = CB * TB;
+    __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
+    sched_substep<TB, NMF>();
+    sched_substep<TB, NMF>();
+    sched_substep<TB, NMF>();
+    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+  };
+  const int S = kt1 - kt0;
+  WSet wa, wb;
+  load_x(kt0, 0);
+  load_x(kt0 + 1, 1);
+  load_x(kt0 + 2, 2);
+  load_ws(kt0, wa);
+  asm volatile("" ::: "memory");
+  auto iter = [&](int s, const WSet& cur, WSet& nxt) {
+    load_ws(kt0 + s + 1, nxt);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (s == 0) wait_vmcnt<8>();
+    else wait_vmcnt<12>();
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(kt0 + s + 3, (s + 3) % NS);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s, cur);
+  };
+  int s = 0;
+  for (; s + 1 < S; s += 2) {
+    iter(s, wa, wb);
+    iter(s + 1, wb, wa);
+  }
+  if (s < S) iter(s, wa, wb);
+  __builtin_amdgcn_s_waitcnt(0);  // no load is left in flight at exit
+
+  if constexpr (SK) {
+    if (tail >= 0 && !sk_handoff<CB, TB, 512, BM, 1>(acc, sk, tail, piece, tid, reinterpret_cast<int*>(lds)))
+      return;
+  }
+  const int tok0 = m0 + grp * 128;
+  if constexpr (SWIGLU) {
+    uint16_t* a_out = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const int ch = (b0 + 4 * q + 2 * cb + hb) * 8 + 4 * g;  // channels ch .. ch+3
+        if (ch >= N) continue;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+          const int tok = tok0 + tb * 32 + r32;
+          if (tok >= M) continue;
+          float a[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[i] = silu(acc[cb][tb][8 * hb + i]) * acc[cb][tb][8 * hb + 4 + i];
+          const u32x2 pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
+          *reinterpret_cast<u32x2*>(a_out + (int64_t)tok * ld_out + ch) = pk;
+        }
+      }
+  } else {
+    store_tile<false, kWeightWide, false, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, r32, g, nullptr, nullptr,
+                                                       nullptr, out, ld_out);
+  }
+}
+
 // Stage shape: bf16 weights use two stages of BK = 64 (128 KB of LDS); fp8
 // weights, with 48 KB stages, fit three.
 constexpr int kBK = 64;
@@ -1010,6 +1234,31 @@ int64_t sk_bytes(bool swiglu, int M, int N, int K, int BK) {
   return sk_plan(gemm_tiles(swiglu, M, N, bm), K / BK, bm).bytes;
 }
 
+// Packed-weight GEMM launch (256-token tiles): N output channels (gate/up)
+// or rows (down) from nblk packed 16-row blocks; skws as in run_gemm_bm.
+template <bool SWIGLU>
+hipError_t run_gemm_pk(int kind, int M, int N, int K, const void* x, int64_t ldx, const void* wp, int nblk,
+                       void* out, int64_t ldo, void* skws, hipStream_t stream) {
+  constexpr int BM = 256;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles = gemm_tiles(SWIGLU, M, N, BM);
+  const SkPlan p = skws ? sk_plan(tiles, K / kBK, BM) : SkPlan{};
+  SkTail sk{};
+  if (p.d) {
+    sk.cnt = static_cast<int*>(skws);
+    sk.part = reinterpret_cast<float*>(static_cast<uint8_t*>(skws) + p.cnt_bytes);
+    sk.nfull = p.nfull;
+    sk.d = p.d;
+    const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
+    if (e != hipSuccess) return e;
+    return launch(kind, gemm_pk_kernel<SWIGLU, false, true>, dim3((unsigned)(p.nfull + p.rem * p.d)), dim3(512), 0,
+                  stream, M, N, K, (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, out, ldo, tiles_m,
+                  tiles / tiles_m, sk);
+  }
+  return launch(kind, gemm_pk_kernel<SWIGLU, false, false>, dim3((unsigned)tiles), dim3(512), 0, stream, M, N, K,
+                (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, out, ldo, tiles_m, tiles / tiles_m, sk);
+}
+
 }  // namespace
 
 int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K) { return sk_bytes(false, M, N, K, kBK); }
@@ -1017,6 +1266,11 @@ int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K) { return sk_bytes(f
 int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8) {
   const int bk = a8 ? 128 : kBK;
   return max(sk_bytes(true, M, I_s, h, bk), sk_bytes(false, M, h, I_s, bk));
+}
+
+int64_t forward_prefill_packed_sk_bytes(int M, int h, int I_s) {
+  return max(sk_plan(gemm_tiles(true, M, I_s, 256), h / kBK, 256).bytes,
+             sk_plan(gemm_tiles(false, M, h, 256), I_s / kBK, 256).bytes);
 }
 
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream) {
@@ -1043,7 +1297,18 @@ hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_
                                                   nullptr, a.ldw_down, a.sd, nullptr, b.sa, a.p, a.ldp, a.sk, stream);
 }
 
+// Packed bf16 weights (contiguous X: the packed forward has no row-block form).
+hipError_t launch_forward_prefill_packed(const ShardArgs& a, hipStream_t stream) {
+  if (a.x.nb != 1) return hipErrorInvalidValue;
+  hipError_t e = run_gemm_pk<true>(K_GATEUP_PREFILL, a.M, a.I_s, a.h, a.x.p[0], a.x.ld, a.wg, (a.I_s + 7) / 8, a.a,
+                                   a.lda, a.sk, stream);
+  if (e != hipSuccess) return e;
+  return run_gemm_pk<false>(K_DOWN_PREFILL, a.M, a.h, a.I_s, a.a, a.lda, a.wd, (a.h + 15) / 16, a.p, a.ldp, a.sk,
+                            stream);
+}
+
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {
+  if (a.packed) return launch_forward_prefill_packed(a, stream);
   hipError_t e;
   switch (a.wb) {
     case kWeightE4M3: e = run_gateup<kWeightE4M3>(a, stream); break;

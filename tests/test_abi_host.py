@@ -404,6 +404,23 @@ def test_quantize_rows_empty_is_noop():
     assert _lib.load().tp_quantize_rows_e4m3(0, 16, None, 16, None, 16, None, None) == _lib.TP_OK
 
 
+def test_packed_workspace_bytes():
+    lib = _lib.load()
+    pw = lib.tp_mlp_packed_workspace_bytes
+    # decode sizes: the same workspace as the row-major forward
+    for M, w in ((1, BF16), (8, BF16), (64, BF16), (32, FP8), (16, _lib.TP_INT8)):
+        assert pw(M, 8192, 28672, 8, w) == lib.tp_mlp_workspace_bytes(M, 8192, 28672, 8, BF16, w)
+    # above them (bf16 only) 256-token tiles: at 65 tokens of the 70B TP = 8 shard, 28 gate/up
+    # tiles of 128 k-tiles cut in 5 pieces (counters: 256 bytes) of 256 x 256 fp32 slots
+    assert pw(65, 8192, 28672, 8, BF16) == 65 * 3584 * 2 + 256 + 28 * 5 * SLOT
+    # 4096 tokens: 448 gate/up tiles (192 past the first round, kept whole), 512 down tiles
+    assert pw(4096, 8192, 28672, 8, BF16) == 4096 * 3584 * 2
+    assert pw(8192, 16384, 53248, 8, BF16) == lib.tp_mlp_workspace_bytes(8192, 16384, 53248, 8, BF16, BF16)
+    assert pw(33, 8192, 28672, 4, FP8) == 0            # one-byte weights: decode sizes only
+    assert pw(1, 320, 640, 2, BF16) == 0               # h % 128: not packable
+    assert pw(0, 512, 1024, 2, BF16) == 0
+
+
 def test_packed_weights_bytes_and_validation():
     lib = _lib.load()
     # the three matrices' bytes: 70B TP=8 bf16, TP=4 fp8
@@ -413,11 +430,15 @@ def test_packed_weights_bytes_and_validation():
     assert lib.tp_mlp_packed_weights_bytes(320, 512, 2, BF16) == 0          # h % 128
     assert lib.tp_mlp_packed_weights_bytes(512, 768, 2, FP8) == 0           # I_s = 384: % 256
     assert lib.tp_mlp_packed_weights_bytes(512, 1024, 2, F32) == 0          # fp32 weights
-    # forward: decode sizes and bf16 activations only; checked before any HIP call
-    def fwdp(M=1, h=512, I=1024, t=2, act=BF16, w=BF16, packed=P, nbytes=1 << 24, sc=None):
+    # forward: bf16 activations; one-byte weights at decode sizes only; checked before any HIP call
+    def fwdp(M=1, h=512, I=1024, t=2, act=BF16, w=BF16, packed=P, nbytes=1 << 24, sc=None, wsb=1 << 20):
         return lib.tp_mlp_shard_forward_packed(M, h, I, t, 0, act, w, P, h, packed, nbytes, sc, sc, sc, P * 8, h,
-                                               P * 16, 1 << 20, None)
-    assert fwdp(M=65) == _lib.TP_ERR_UNSUPPORTED
+                                               P * 16, wsb, None)
+    # bf16 weights above the decode sizes take the packed prefill kernels, which need the
+    # workspace of tp_mlp_packed_workspace_bytes (A and the stream-K scratch)
+    need = lib.tp_mlp_packed_workspace_bytes(65, 512, 1024, 2, BF16)
+    assert need >= 65 * 512 * 2
+    assert fwdp(M=65, wsb=need - 1) == _lib.TP_ERR_WORKSPACE
     assert fwdp(M=33, w=FP8, sc=P) == _lib.TP_ERR_UNSUPPORTED
     assert fwdp(act=F32, w=F32) == _lib.TP_ERR_UNSUPPORTED
     assert fwdp(packed=None) == _lib.TP_ERR_INVALID_ARG

@@ -1,5 +1,6 @@
-"""Packed decode weights: the layout, and the packed forward against the
-row-major forward (bit-identical) and the oracle."""
+"""Packed weights: the layout, and the packed forward (decode streams, and
+the packed-weight MFMA GEMMs above the decode sizes) against the row-major
+forward (bit-identical where both sum in the same order) and the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -96,14 +97,65 @@ def test_packed_forward_70b(M):
 
 
 def test_packed_rejects():
-    h, I_s, t = 256, 384, 2
-    x, ws = make_case(62, 65, h, I_s, "bf16", "bf16", 0.05, 0.05)
-    d = upload_case(x, ws, "bf16", "bf16")
+    h, I_s, t = 256, 512, 2
+    x, ws = make_case(62, 33, h, I_s, "bf16", "e4m3fn", 0.05, 0.05)
+    d = upload_case(x, ws, "bf16", "e4m3fn")
     pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
-    with pytest.raises(_lib.TPError, match="decode"):
-        tp.shard_forward_packed(d["x"], pk, k=0)          # 65 tokens: not a decode size
+    with pytest.raises(_lib.TPError, match="decode"):      # one-byte weights: 33 tokens is not a decode size
+        tp.shard_forward_packed(d["x"], pk, k=0, s_gate=d["s_gate"], s_up=d["s_up"], s_down=d["s_down"])
     small = tp.alloc_workspace(1024, "cuda")
     lib = _lib.load()
     st = lib.tp_mlp_pack_weights(h, I_s * t, t, _lib.TP_BF16, d["w_gate"].data_ptr(), d["w_up"].data_ptr(), h,
                                  d["w_down"].data_ptr(), I_s, small.data_ptr(), 1024, None)
     assert st == _lib.TP_ERR_INVALID_ARG                  # too small
+
+
+# Packed prefill (bf16 weights above 64 tokens): 256 x 256 tiles with the
+# weights read from the packed array straight into registers.  Shapes: ragged
+# token tiles (M not a multiple of 256), a down GEMM whose last tile has only
+# 8 of its 16 row blocks (h = 384), a single k-stage pair (h = 128), odd
+# stage counts, and stream-K tails.
+PREFILL_CASES = [(65, 256, 128), (300, 384, 256), (513, 512, 384), (257, 128, 128), (1024, 640, 640),
+                 (600, 1024, 1152)]
+
+
+@pytest.mark.parametrize("M,h,I_s", PREFILL_CASES)
+def test_packed_prefill_shapes(M, h, I_s):
+    t, k = 2, 1
+    print("packed prefill M=%d h=%d I_s=%d" % (M, h, I_s), flush=True)
+    x, ws = make_case(63, M, h, I_s, "bf16", "bf16", 0.05, 0.05, k=k, weight_set=M)
+    d = upload_case(x, ws, "bf16", "bf16")
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    p = tp.shard_forward_packed(d["x"], pk, k=k)
+    p2 = tp.shard_forward_packed(d["x"], pk, k=k)
+    torch.cuda.synchronize()
+    assert torch.equal(p.view(torch.int32), p2.view(torch.int32))       # deterministic
+    err = oracle.rms_normalised_max_error(p.cpu().numpy(), oracle_partial(x, ws, "bf16", "bf16"))
+    print("  err=%.3e" % err, flush=True)
+    assert err <= TOL_BF16
+
+
+@pytest.mark.parametrize("M,h,I_s", [(2304, 2048, 3712), (4096, 8192, 3584)])
+def test_packed_prefill_matches_row_major(M, h, I_s):
+    """Where both forwards use 256-token tiles and the same stream-K plan they
+    add the same products in the same order: the partials are bit-identical.
+    2304 x 2048 x 3712 has stream-K tails in both GEMMs (gate/up 261 tiles,
+    down 72 tiles in 3 pieces); 4096 x 8192 x 3584 is the 70B TP = 8 prefill.
+    Every element is also checked against the oracle on a third of the rows
+    of every 256-token tile."""
+    t = 8
+    print("packed prefill vs row-major M=%d h=%d I_s=%d" % (M, h, I_s), flush=True)
+    x, ws = make_case(3, M, h, I_s, "bf16", "bf16", 0.02, 0.02, weight_set=M)
+    d = upload_case(x, ws, "bf16", "bf16")
+    pk = tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)
+    nb = tp.packed_workspace_bytes(M, h, I_s * t, t)
+    wsp = tp.alloc_workspace(nb, "cuda")
+    wsp.fill_(0x7F)                                                     # a dirty workspace
+    p = tp.shard_forward_packed(d["x"], pk, k=0, workspace=wsp)
+    ref = tp.shard_forward(d["x"], d["w_gate"], d["w_up"], d["w_down"], t=t, k=0)
+    torch.cuda.synchronize()
+    assert torch.equal(p.view(torch.int32), ref.view(torch.int32))
+    rows = np.concatenate([np.arange(m0, min(m0 + 256, M), 3) for m0 in range(0, M, 256)])
+    err = oracle.rms_normalised_max_error(p.cpu().numpy()[rows], oracle_partial(x, ws, "bf16", "bf16", rows=rows))
+    print("  err=%.3e" % err, flush=True)
+    assert err <= TOL_BF16
