@@ -948,24 +948,23 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
 
-  // Order of the loads.  Iteration s (stage kt0 + s): wait for this wave's
-  // activation loads of stage s; barrier (every wave's loads of stage s have
-  // landed and every wave is done with stage s - 1); issue the activations of
-  // stage s + 3 into the buffer of stage s - 1 (four loads); compute stage s:
-  // for each k-step kk, wait for the weight fragments of kk (loaded during
-  // stage s - 1), issue the MFMAs of kk, then reload the same two registers
-  // with the fragments of kk for stage s + 1 (two loads).  So each weight
-  // fragment has one stage to arrive, the activations three, and the wave
-  // holds one set of weight registers (32 VGPRs).
-  // Loads issued after stage s's activations at the barrier wait: 32 (the
-  // weights of stages s - 2, s - 1 and s, the activations of s + 1 and
-  // s + 2); 16 at s = 0 (X1, X2, W0) and 24 at s = 1 (X2, W0, X3, W1).
-  // Loads issued after fragment kk of stage s at its wait: 2 (3 - kk) + 4.
-  // The waits are explicit: the direct-to-LDS loads are FLAT instructions,
-  // after which a wait that the compiler inserts itself for a register is
-  // widened to vmcnt(0), which would drain the prefetch.  The empty asm
-  // statements with a memory clobber keep the compiler from moving loads
-  // across those points.
+  // Order of the loads.  The wave holds two sets of weight registers (2 x
+  // 32 VGPRs).  Iteration s (stage kt0 + s): issue the weights of stage s + 1
+  // into the set last read by the MFMAs of stage s - 1 (eight loads); wait
+  // until the weights of stage s have arrived, and with them (issued
+  // earlier) this wave's activation loads of stage s; barrier (every wave's
+  // activations of stage s have landed and every wave is done with stage
+  // s - 1); issue the activations of stage s + 3 into the buffer of stage
+  // s - 1 (four loads); compute stage s.  So the weights have one stage to
+  // arrive and the activations three.  Loads issued after the weights of
+  // stage s at the wait: 8 at s = 0 (W1), else 12 (X of s + 2, W of s + 1).
+  // The wait is explicit because the direct-to-LDS loads are FLAT
+  // instructions, after which a wait that the compiler inserts itself for a
+  // register is widened to vmcnt(0) (it would also drain the prefetch); the
+  // empty asm statements with a memory clobber keep the compiler from moving
+  // the weight loads next to their first use.  Stage counts are even for
+  // whole tiles (K is a multiple of 128); a stream-K piece may end with one
+  // odd stage.
   typedef u32x4 WSet[CB][KSUB];
   auto load_ws = [&](int kt, WSet& w) {
 #pragma unroll
