@@ -926,12 +926,12 @@ def bench_attn_decode(tp, args):
     steps, warmup = args.steps or 402, args.warmup if args.warmup is not None else 42
     q_dur = []
     elapsed, prof = timed(tp, step, steps, warmup, [], "qkv_decode", q_dur)
-    prof_all, per_step = breakdown_rotating(tp, run_step, 3, ["qkv_decode", "oproj_decode", "splitk_finish",
+    prof_all, per_step = breakdown_rotating(tp, run_step, 3, ["qkv_decode", "oproj_decode", "sk_clear",
                                                               "partial_reduce"], steps, warmup + steps)
     step_bytes = sum(ph.bytes() for ph in phases)
     value = step_bytes * steps / elapsed / 1e9
     per = {"qkv_decode": sum(ph.qkv_bytes() for ph in phases), "oproj_decode": sum(ph.oproj_bytes() for ph in phases),
-           "partial_reduce": sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases), "splitk_finish": None}
+           "partial_reduce": sum(workloads.reduce_bytes(ph.M * h, t) for ph in phases), "sk_clear": None}
     kern = {}
     for name, b in per.items():
         if name not in prof_all:

@@ -149,7 +149,7 @@ thread_local bool g_no_alloc = false;
 const char* const kKindNames[tpmlp::K_NUM_KINDS] = {
     "gateup_decode", "down_decode", "gateup_prefill", "down_prefill",
     "partial_reduce", "gateup_f32", "down_f32", "qkv_decode", "qkv_prefill",
-    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "splitk_finish", "quant_rows",
+    "oproj_decode", "oproj_prefill", "qkv_f32", "oproj_f32", "quant_rows",
     "gateup_w8a8", "down_w8a8", "sk_clear"};
 
 // Appends one start/stop event pair to the timing pool.  The events only

@@ -34,8 +34,8 @@
 // The down kernels are generic row GEMMs, out = a * W^T with W in the
 // (out, in) layout (RowGemm): they also run the attention block's
 // projections, with fp32 or bf16 output, and for narrow outputs (too few row
-// blocks to cover the chip) split K over a second grid dimension, with an
-// ordered finishing sum.
+// blocks to cover the chip) split K over a second grid dimension, the range
+// that finishes a tile last adding its ranges in order.
 
 #include "common.h"
 #include "internal.h"
@@ -668,17 +668,20 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void gateup
   });
 }
 
-// Split K (gridDim.y = nseg > 1): workgroup (x, y) streams the y-th of nseg
-// contiguous ranges of the K slots and stores its unscaled fp32 sums to
-// seg_out[y] (M x h, dense); splitk_finish_kernel adds the nseg ranges in
-// order.  Skinny outputs (few 16-row blocks, long K) need it to keep enough
-// loads in flight across the chip.
+// Split K (SPLIT, gridDim.y = nseg > 1): workgroup (x, y) streams the y-th of
+// nseg contiguous ranges of the K slots, stores its unscaled fp32 sums in its
+// slot of `part` (RB x NT x 1 KB per tile and range) and counts itself in the
+// tile's arrival counter (zero at launch); the range that arrives last adds
+// the tile's nseg slots in range order (the same sum whichever range is
+// last), applies the row scales and writes the output.  No workgroup waits
+// for another.  Skinny outputs (few 16-row blocks, long K) need the split to
+// keep enough loads in flight across the chip.
 // PK: wd is the packed array of the N x K weights (ldw unused).
-template <int NT, int RB, int WB, bool XD, bool OBF, bool PK>
+template <int NT, int RB, int WB, bool XD, bool OBF, bool PK, bool SPLIT>
 __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_stream_kernel(
     int M, int h, int I_s, const uint16_t* __restrict__ a_in, int64_t lda,
     const uint8_t* __restrict__ wd, int64_t ldw, const float* __restrict__ sd,
-    void* __restrict__ p, int64_t ldp, int nseg, float* __restrict__ seg_out) {
+    void* __restrict__ p, int64_t ldp, int nseg, float* __restrict__ part, int* __restrict__ cnt) {
   using SS = StreamShape<NT, RB, WB, XD>;
   constexpr int EB = WB ? 1 : 2;
   constexpr int KS = WB ? 256 : 128;
@@ -723,52 +726,78 @@ __global__ __launch_bounds__((StreamShape<NT, RB, WB, XD>::WV * 64)) void down_s
     stream_rows<NT, RB, WB, SS::S, PK>(acc, ring, dsrc, xrow, xok, j_beg, nsl, jstep, lane);
   }
 
-  reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
-                                    [&](int rb, int b, f32x4 v) {
+  // the tile's slots (SPLIT): slot of range r at r * SLOT, position (rb, b)
+  // of lane l at ((rb * NT + b) * 64 + l) * 16
+  constexpr int SLOT = RB * NT * 1024;
+  constexpr int kDeviceScope = 16;   // buffer cache policy: sc1
+  const __amdgpu_buffer_rsrc_t slots = __builtin_amdgcn_make_buffer_rsrc(
+      SPLIT ? part + (int64_t)blockIdx.x * nseg * (SLOT / 4) : part, 0, SPLIT ? nseg * SLOT : 0, 0x00020000);
+  auto finish = [&](int rb, int b, f32x4 v) {
     const int f = n0 + 16 * rb + 4 * grp;
     const int tok = b * 16 + row16;
     if (tok < M && f < h) {
-      if (nseg > 1) {
-        store_out4<false>(seg_out, ((int64_t)seg * M + tok) * h + f, v);
-        return;
-      }
       if constexpr (WB) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= sd[f + i];
       }
       store_out4<OBF>(p, (int64_t)tok * ldp + f, v);
     }
+  };
+  reduce_waves_ring<NT, RB, SS::WV>(acc, reinterpret_cast<f32x4*>(ring_all), wave, lane,
+                                    [&](int rb, int b, f32x4 v) {
+    if constexpr (SPLIT)
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), slots,
+                                             seg * SLOT + ((rb * NT + b) * 64 + lane) * 16, 0, kDeviceScope);
+    else
+      finish(rb, b, v);
   });
-}
-
-// out = (((seg[0] + seg[1]) + ...) + seg[nseg-1]) (* row scale), four
-// outputs per thread (N % 4 == 0, so a group never crosses a row).
-template <int WB, bool OBF>
-__global__ __launch_bounds__(256) void splitk_finish_kernel(int M, int N, int nseg, const float* __restrict__ seg,
-                                                            const float* __restrict__ s, void* __restrict__ out,
-                                                            int64_t ldo) {
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)M * N;
-  const int64_t e = 4 * g;
-  if (e >= total) return;
-  const int tok = (int)(e / N), f = (int)(e % N);
-  auto at = [&](int q) { return *reinterpret_cast<const f32x4*>(seg + q * total + e); };
-  // the same left fold over the ranges, with eight loads in flight at a time
-  f32x4 v = at(0);
-  int q = 1;
-  for (; q + 8 <= nseg; q += 8) {
-    f32x4 t[8];
+  if constexpr (SPLIT) {
+    // The ordering argument is the prefill stream-K tail's: every slot store
+    // and load carries sc1 (they go to the point of coherence shared by the
+    // XCDs), vmcnt(0) completes this range's stores at agent scope, the
+    // barrier orders all lanes before the counter increment, and the last
+    // range's loads are issued only once the increment's result is known.
+    // The flag lives in the ring's memory (the cross-wave sums above are read
+    // before the barrier).
+    int* flag = reinterpret_cast<int*>(ring_all);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0)
+      *flag = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (*flag != nseg - 1) return;
+    if (threadIdx.x == 0) __hip_atomic_store(cnt + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // Wave w sums positions w, w + WV, ... (QPW of them), every range in
+    // order; the loads of all its positions for FB ranges are issued
+    // together (one memory round trip per FB ranges: the last range's sum
+    // is the tail of the launch).
+    constexpr int QPW = (RB * NT + SS::WV - 1) / SS::WV;
+    constexpr int FB = 8;
+    f32x4 sum[QPW];
+    for (int r0 = 0; r0 < nseg; r0 += FB) {
+      f32x4 t[FB][QPW];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) t[j] = at(q + j);
+      for (int j = 0; j < FB; ++j)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v = v + t[j];
+        for (int i = 0; i < QPW; ++i) {
+          const int q = wave + SS::WV * i;
+          if (r0 + j < nseg && q < RB * NT)
+            t[j][i] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(slots, (r0 + j) * SLOT + (q * 64 + lane) * 16, 0,
+                                                             kDeviceScope));
+        }
+#pragma unroll
+      for (int j = 0; j < FB; ++j)
+#pragma unroll
+        for (int i = 0; i < QPW; ++i)
+          if (r0 + j < nseg) sum[i] = r0 + j == 0 ? t[j][i] : sum[i] + t[j][i];
+    }
+#pragma unroll
+    for (int i = 0; i < QPW; ++i) {
+      const int q = wave + SS::WV * i;
+      if (q < RB * NT) finish(q / NT, q % NT, sum[i]);
+    }
   }
-  for (; q < nseg; ++q) v = v + at(q);
-  if constexpr (WB) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] *= s[f + i];
-  }
-  store_out4<OBF>(out, (int64_t)tok * ldo + f, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -1069,7 +1098,7 @@ __global__ __launch_bounds__(W * 64) void sk_stream_kernel(
 // streams.  Pipelines of 12 or 16 steps instead of 8 measured no faster.  For the same reason they lose on a narrow output
 // such as the attention block's QKV projection (1280 rows: 10 tiles, 22
 // ranges of 11-12 steps): 13.2 us plus a 2 us finishing kernel on the
-// rings against 26.3 us at 64 tokens.
+// rings (then a separate launch) against 26.3 us at 64 tokens.
 template <int NT, int WB>
 constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
 
@@ -1276,9 +1305,9 @@ constexpr int kRowRBSplit = kStreamXD<NT, WB> && !WB ? 3 : kRowRB<NT, WB>;
 // K split of a streaming row GEMM.  A narrow output (few 16-row blocks, e.g.
 // a rank's QKV projection: 80 blocks for 1280 rows) keeps too few loads in
 // flight across the chip; its K slots are then split into nseg contiguous
-// ranges over a second grid dimension (two launches: the split sums, then
-// their ordered sum), aiming at about four waves per CU, with each wave
-// keeping at least two slots.  (Sixteen waves per row block instead of a
+// ranges over a second grid dimension (the range that finishes a tile last
+// adds its ranges: a clear of the arrival counters, then one launch), aiming
+// at about four waves per CU, with each wave keeping at least two slots.  (Sixteen waves per row block instead of a
 // split was measured slower: per-CU streaming rate, not wave count, is the
 // limit.)
 constexpr int kSplitTargetWaves = 1024;
@@ -1292,15 +1321,34 @@ int stream_splits(int N, int K) {
   return max(1, min(want, cap));
 }
 
+// Split scratch of a streaming row GEMM with nseg > 1 ranges: one arrival
+// counter per tile (256-byte rounded), then RB x NT KB per tile and range.
+template <int NT, int RB>
+constexpr int64_t split_cnt_bytes(int tiles) { return ((int64_t)tiles * 4 + 255) / 256 * 256; }
+
 template <int NT, int RB, int WB, bool OBF>
 hipError_t rowgemm_stream_launch(const RowGemm& g, int nseg, hipStream_t stream) {
   constexpr bool XD = kStreamXD<NT, WB>;
-  const dim3 grid((g.N + 16 * RB - 1) / (16 * RB), nseg), block(StreamShape<NT, RB, WB, XD>::WV * 64);
+  const int tiles = (g.N + 16 * RB - 1) / (16 * RB);
+  const dim3 grid(tiles, nseg), block(StreamShape<NT, RB, WB, XD>::WV * 64);
+  const uint16_t* a = (const uint16_t*)g.a;
+  const uint8_t* w = (const uint8_t*)g.w;
+  if (nseg > 1) {
+    int* cnt = reinterpret_cast<int*>(g.ws);
+    float* part = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(g.ws) + split_cnt_bytes<NT, RB>(tiles));
+    const hipError_t e = launch_counter_clear(cnt, tiles, stream);
+    if (e != hipSuccess) return e;
+    if (g.packed)
+      return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, true, true>, grid, block, 0, stream, g.M,
+                    g.N, g.K, a, g.lda, w, g.ldw, g.s, g.out, g.ldo, nseg, part, cnt);
+    return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, false, true>, grid, block, 0, stream, g.M,
+                  g.N, g.K, a, g.lda, w, g.ldw, g.s, g.out, g.ldo, nseg, part, cnt);
+  }
   if (g.packed)
-    return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, true>, grid, block, 0, stream, g.M, g.N,
-                  g.K, (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
-  return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, false>, grid, block, 0, stream, g.M, g.N,
-                g.K, (const uint16_t*)g.a, g.lda, (const uint8_t*)g.w, g.ldw, g.s, g.out, g.ldo, nseg, g.ws);
+    return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, true, false>, grid, block, 0, stream, g.M,
+                  g.N, g.K, a, g.lda, w, g.ldw, g.s, g.out, g.ldo, 1, (float*)nullptr, (int*)nullptr);
+  return launch(g.kind_decode, down_stream_kernel<NT, RB, WB, XD, OBF, false, false>, grid, block, 0, stream, g.M,
+                g.N, g.K, a, g.lda, w, g.ldw, g.s, g.out, g.ldo, 1, (float*)nullptr, (int*)nullptr);
 }
 
 template <int NT, int WB, bool OBF>
@@ -1313,11 +1361,7 @@ hipError_t rowgemm_stream(const RowGemm& g, hipStream_t stream) {
     if (nseg == 1 && g.M >= kRb2MinMDown) return rowgemm_stream_launch<1, 2, WB, OBF>(g, 1, stream);
   }
   if (nseg == 1) return rowgemm_stream_launch<NT, kRowRB<NT, WB>, WB, OBF>(g, 1, stream);
-  hipError_t e = rowgemm_stream_launch<NT, kRowRBSplit<NT, WB>, WB, OBF>(g, nseg, stream);
-  if (e != hipSuccess) return e;
-  const int64_t groups = (int64_t)g.M * g.N / 4;
-  return launch(K_SPLITK_FINISH, splitk_finish_kernel<WB, OBF>, dim3((unsigned)((groups + 255) / 256)), dim3(256),
-                0, stream, g.M, g.N, nseg, (const float*)g.ws, g.s, g.out, g.ldo);
+  return rowgemm_stream_launch<NT, kRowRBSplit<NT, WB>, WB, OBF>(g, nseg, stream);
 }
 
 // The streaming kernels move whole 16-row x 256-byte slots along K: they need
@@ -1360,9 +1404,11 @@ namespace {
 
 template <int NT, int WB>
 int64_t workspace_bytes_nt(int M, int N, int K) {
+  constexpr int RB = kRowRBSplit<NT, WB>;
   const int nseg = stream_splits<NT, WB>(N, K);
   if (nseg == 1) return 0;
-  return (int64_t)nseg * M * N * 4;
+  const int tiles = (N + 16 * RB - 1) / (16 * RB);
+  return split_cnt_bytes<NT, RB>(tiles) + (int64_t)tiles * nseg * RB * NT * 1024;
 }
 
 template <int WB>
@@ -1383,23 +1429,9 @@ hipError_t rowgemm_wb(const RowGemm& g, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,
-                                int wb, bool obf, hipStream_t stream) {
-  const dim3 grid((unsigned)(((int64_t)M * N / 4 + 255) / 256));
-  if (wb)   // one-byte weights: the row scale is applied after the sum
-    return obf ? launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightE4M3, true>, grid, dim3(256), 0, stream, M, N,
-                        nseg, ws, s, out, ldo)
-               : launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightE4M3, false>, grid, dim3(256), 0, stream, M,
-                        N, nseg, ws, s, out, ldo);
-  return obf ? launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightWide, true>, grid, dim3(256), 0, stream, M, N,
-                      nseg, ws, s, out, ldo)
-             : launch(K_SPLITK_FINISH, splitk_finish_kernel<kWeightWide, false>, grid, dim3(256), 0, stream, M, N,
-                      nseg, ws, s, out, ldo);
-}
-
 // A narrow row GEMM that the matrix-core stream would split along K (the
 // QKV projection) goes, at up to kGemvMaxM tokens with bf16 weights, to the
-// row-streaming VALU kernel of gemv.hip: no split and no finishing kernel.
+// row-streaming VALU kernel of gemv.hip: no split and no arrival counters.
 static bool use_gemv(int M, int N, int K, int wb) {
   return gemv_supported(M, K, wb) && stream_splits<1, kWeightWide>(N, K) > 1;
 }

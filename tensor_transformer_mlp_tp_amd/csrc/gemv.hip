@@ -4,22 +4,25 @@
 //
 // The matrix-core streams (decode.hip) read 16 rows of W side by side and,
 // with so few row blocks for the chip, split K over extra workgroups whose
-// sums a second kernel adds.  At M <= 2 a row is 2*M FLOP per weight, so the
-// dot products fit on the VALU (v_dot2_f32_bf16: two bf16 products and their
-// sum into fp32 per instruction) and each wave can stream whole rows of W one
+// sums meet in memory.  At M <= 2 a row is 2*M FLOP per weight, so the dot
+// products fit on the VALU (v_dot2_f32_bf16: two bf16 products and their sum
+// into fp32 per instruction) and each wave can stream whole rows of W one
 // after the other, one kilobyte per load instruction (lane l holds eight
 // consecutive k of a 512-k chunk): with 1280 rows that is enough waves for
-// the chip without a split, and no finishing kernel.  Measured at M = 1 on
-// the 70B QKV shard: 7.0 us against 7.3 us + 4.2 us (split + finish).  (For
-// wide outputs and for the MLP the matrix-core streams are as fast or
-// faster; they stay there.)
+// the chip without a split.  Measured at M = 1 on the 70B QKV shard: 7.0 us
+// against 7.3 us + 4.2 us (split + a separate finishing kernel, the split's
+// form when this kernel was written).  Eight tokens measured slower than the
+// split streams (16.3 against about 10 us at 70B TP = 8): one wave per row
+// (1280 waves), eight times the VALU and LDS work per weight byte, and 128
+// KB of activations in LDS leave too little in flight.  (For wide outputs
+// and for the MLP the matrix-core streams are as fast or faster; they stay
+// there.)
 //
 // The activations of the M tokens (M x K bf16) are copied into LDS once per
 // workgroup; per chunk each lane reads its 16 bytes of every token from
-// there.  A row's sum is finished
-// with a butterfly over the wave's 64 lanes (every lane ends with the same
-// bits, the order fixed: the result is deterministic) and written by the
-// lanes of the tokens.
+// there.  A row's sum is finished with a butterfly over the wave's 64 lanes
+// (every lane ends with the same bits, the order fixed: the result is
+// deterministic) and written by the lanes of the tokens.
 #include "common.h"
 #include "internal.h"
 

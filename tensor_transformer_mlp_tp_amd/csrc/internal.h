@@ -21,12 +21,11 @@ enum KernelKind : int {
   K_OPROJ_PREFILL = 10,
   K_QKV_F32 = 11,
   K_OPROJ_F32 = 12,
-  K_SPLITK_FINISH = 13,
-  K_QUANT_ROWS = 14,
-  K_GATEUP_W8A8 = 15,
-  K_DOWN_W8A8 = 16,
-  K_SK_CLEAR = 17,
-  K_NUM_KINDS = 18
+  K_QUANT_ROWS = 13,
+  K_GATEUP_W8A8 = 14,
+  K_DOWN_W8A8 = 15,
+  K_SK_CLEAR = 16,
+  K_NUM_KINDS = 17
 };
 
 constexpr int kMaxPartials = 64;
@@ -161,10 +160,6 @@ int64_t rowgemm_prefill_workspace_bytes(int M, int N, int K);
 int64_t forward_prefill_sk_bytes(int M, int h, int I_s, bool a8);
 // Stream-K scratch of the packed-weight prefill forward (bf16, 256-token tiles).
 int64_t forward_prefill_packed_sk_bytes(int M, int h, int I_s);
-// out = ordered sum of the nseg split sums in ws (nseg x M x N fp32), times
-// the row scales for one-byte weights (wb != 0), fp32 or bf16 (obf).
-hipError_t launch_splitk_finish(int M, int N, int nseg, const float* ws, const float* s, void* out, int64_t ldo,
-                                int wb, bool obf, hipStream_t stream);
 hipError_t launch_rowgemm_prefill(const RowGemm& g, hipStream_t stream);
 // Row-streaming VALU row GEMM (M <= kGemvMaxM, bf16 weights, K a multiple of
 // 512 up to 16384): whether it can take this shape, and the launch.

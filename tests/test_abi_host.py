@@ -266,13 +266,19 @@ def qkv_call(M=1, h=128, nh=8, nkv=2, d=32, t=2, k=0, act=BF16, w=BF16, x=P, ldx
 
 def test_attn_qkv_workspace_bytes():
     lib = _lib.load()
-    # 70B TP=8 decode: at one or two tokens the row-streaming kernel needs no scratch; above,
-    # the 1280-wide output over h = 8192 is split along h
+    # 70B TP=8 decode: at one or two tokens the row-streaming kernel needs no scratch
     for M in (1, 2):
         assert lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16) == 0
-    for M in (3, 8, 32, 64):
+    # above, the 1280-wide output over h = 8192 is split along h: one arrival counter per tile
+    # of 16 RB rows (256-byte rounded), then a 1 KB fp32 fragment per 16-row block, 16-token
+    # block, tile and range
+    for M in (3, 8, 9, 16, 32, 64):
         b = lib.tp_attn_qkv_workspace_bytes(M, 8192, 64, 8, 128, 8, BF16, BF16)
-        assert b > 0 and b % 256 == 0 and b % (M * 1280 * 4) == 0
+        nt = (M + 15) // 16
+        assert b % 256 == 0
+        assert b >= 256 + 1280 // 16 * nt * 1024 * 2          # at least two ranges of every block
+    # M = 8: tiles of one 16-row block (80 tiles: 512 bytes of counters), 4 ranges of h
+    assert lib.tp_attn_qkv_workspace_bytes(8, 8192, 64, 8, 128, 8, BF16, BF16) == 512 + 80 * 4 * 1024
     # fp8 weights keep the split at M = 1
     assert lib.tp_attn_qkv_workspace_bytes(1, 8192, 64, 8, 128, 8, BF16, FP8) > 0
     # prefill: 80 tiles of 256 x 256 for 4096 tokens, fewer than the 256 CUs: every tile is cut

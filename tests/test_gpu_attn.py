@@ -87,7 +87,9 @@ QKV_CASES = [
     (3, 1024, 8, 2, 64, 2, "e4m3fn"),
     (40, 320, 8, 2, 64, 2, "e4m3fn"),     # fp8 register-batch path
     (257, 1024, 8, 2, 64, 2, "e4m3fn"),
-    (4, 4096, 8, 2, 64, 2, "bf16"),       # narrow output, long h: h split in 4 ranges
+    (4, 4096, 8, 2, 64, 2, "bf16"),       # narrow output, long h: h split in 4 ranges, the last one adds them
+    (9, 4096, 8, 2, 64, 2, "bf16"),
+    (12, 8192, 64, 8, 128, 8, "bf16"),    # 70B TP=8 QKV width at 12 tokens: split, one token block
     (2, 8192, 4, 4, 32, 4, "bf16"),       # n_loc = 96: h split in 8 ranges
     (40, 4096, 8, 2, 64, 2, "bf16"),      # activation-staged kernels, h split in 8 ranges
     (16, 4096, 8, 2, 64, 2, "e4m3fn"),    # fp8, h split in 2 ranges
@@ -95,6 +97,10 @@ QKV_CASES = [
     (1, 4096, 8, 2, 64, 2, "bf16"),       # one or two tokens, a narrow output the streams would split:
     (2, 16384, 32, 8, 128, 4, "bf16"),    # the row-streaming kernel (whole rows per wave, no split);
     (1, 2048, 16, 4, 64, 4, "bf16"),      # K = 16384 is its largest
+    (3, 8192, 64, 8, 128, 8, "bf16"),     # 3, 5, 8 tokens of the 70B TP=8 QKV: split streams
+    (5, 8192, 64, 8, 128, 8, "bf16"),
+    (8, 8192, 64, 8, 128, 8, "bf16"),
+    (8, 16384, 32, 8, 128, 4, "bf16"),
 ]
 
 
