@@ -872,7 +872,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
   constexpr int CB = 2, TB = 4;               // 32-row weight blocks, 32-token blocks per wave
   constexpr int ROWB = BK * 2;                // bytes per LDS row
   constexpr int STAGE = BM * ROWB;            // 32 KB of activations per stage
-  constexpr int NS = 4;                       // stages in the ring
+  constexpr int NS = 4;                       // stages in the ring (five measured slower)
   constexpr int KSUB = BK / 16;               // MFMA k-steps per stage
   constexpr int BPT = 16;                     // 16-row blocks per tile
   static_assert(NS * STAGE <= 160 * 1024, "LDS");
@@ -999,9 +999,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
   };
   const int S = kt1 - kt0;
   WSet wa, wb;
-  load_x(kt0, 0);
-  load_x(kt0 + 1, 1);
-  load_x(kt0 + 2, 2);
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) load_x(kt0 + i, i);
   load_ws(kt0, wa);
   asm volatile("" ::: "memory");
   auto iter = [&](int s, const WSet& cur, WSet& nxt) {
@@ -1013,7 +1012,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    load_x(kt0 + s + 3, (s + 3) % NS);
+    load_x(kt0 + s + NS - 1, (s + NS - 1) % NS);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     compute(s, cur);
