@@ -917,14 +917,20 @@ __global__ __launch_bounds__(W * 64) void sk_stream_kernel(
   // iterations then issues the same loads, so the compiler's wait counts
   // need no worst case over the range length.
   const uint8_t* spare = xsrc[0] + (int64_t)(n - 1) * (2 * KSTEP);
+  // (A wave whose share of the step's fragments runs past NF loads and
+  // stages nothing there: the CU's load bytes per step set the pace here, so
+  // the three idle fragment loads of a 7-wave gate/up tile at 64 tokens cost
+  // 5 % of its time.)
   auto issue_x = [&](int i, u32x4 (&dst)[AF]) {
 #pragma unroll
-    for (int a = 0; a < AF; ++a) dst[a] = ld16(i < n ? xsrc[a] + (int64_t)i * (2 * KSTEP) : spare);
+    for (int a = 0; a < AF; ++a)
+      if (wave + W * a < SS::NF) dst[a] = ld16(i < n ? xsrc[a] + (int64_t)i * (2 * KSTEP) : spare);
   };
   auto stage_x = [&](int stage, const u32x4 (&src)[AF]) {
 #pragma unroll
     for (int a = 0; a < AF; ++a)
-      *reinterpret_cast<u32x4*>(stage_buf[stage] + (wave + W * a) * 1024 + lane * 16) = src[a];
+      if (wave + W * a < SS::NF)
+        *reinterpret_cast<u32x4*>(stage_buf[stage] + (wave + W * a) * 1024 + lane * 16) = src[a];
   };
   auto issue_w = [&](int i, u32x4 (&dst)[RB]) {
 #pragma unroll
@@ -1105,7 +1111,11 @@ constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
 // Tiles: gate/up seven waves of one 16-row block (112 rows = 56 channels),
 // so the 70B shards' gate/up rows (7168 and 14336) make whole multiples of
 // 64 tiles and their ranges fill the 256 CUs; the down projection four
-// waves of two blocks (128 rows).
+// waves of two blocks (128 rows).  Wider tiles, so that each activation
+// fragment serves more rows, measured slower at 64 tokens (70B TP = 8, gate/up
+// 26.8 us: 14 waves 30.6, 7 waves of two blocks 31.2; down 14.0 us: 8 waves
+// of two blocks 17.8, 4 of four 18.1): the longer tiles need more, shorter
+// ranges.
 template <int NT, int WB, bool GU>
 struct SkPlan {
   static constexpr int W = GU ? 7 : 4;
