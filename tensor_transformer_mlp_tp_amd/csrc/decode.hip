@@ -379,6 +379,8 @@ __device__ __forceinline__ void stream_rows(f32x4 (&acc)[RB][NT], uint8_t* ring,
 #pragma unroll
       for (int i = 0; i < 4; ++i) dma16(dsrc[rb][i] + (int64_t)j * JS, dst + rb * 4096 + i * 1024);
   };
+  // (Loading only the lanes of real tokens, exec-masked, measured slower: 70B
+  // gate/up at one token 21.4 -> 22.0 us; the clamped rows are L1 hits.)
   auto load_x = [&](int j, u32x4 (&xf)[STEPS][NT]) {
 #pragma unroll
     for (int b = 0; b < NT; ++b)
