@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     ap.add_argument("--row-major", action="store_true",
                     help="decode70b: read the weights in the (out, in) layout instead of packed for the decode kernels")
+    ap.add_argument("--packed", action="store_true",
+                    help="prefill70b, prefill405b: run the prefill on the weights packed for the decode kernels "
+                         "(the packed-weight GEMMs) instead of the (out, in) layout")
     return ap.parse_args()
 
 
@@ -162,8 +165,10 @@ class Phase:
         self.x_host = workloads.make_x(cfg_id, M, h, act)
         self.x = to_dev(self.x_host, act)
         self.partial = torch.empty((M, h), dtype=torch.float32, device="cuda")
-        nbytes = tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16,
-                                    {"e4m3fn": torch.float8_e4m3fn, "int8": torch.int8}.get(w, torch.bfloat16))
+        wdt = {"e4m3fn": torch.float8_e4m3fn, "int8": torch.int8}.get(w, torch.bfloat16)
+        # the larger of the two forwards' workspaces (packed weights: 256-token tiles above the decode sizes)
+        nbytes = max(tp.workspace_bytes(M, h, I_s * t, t, torch.bfloat16, wdt),
+                     tp.packed_workspace_bytes(M, h, I_s * t, t, wdt) if act == "bf16" else 0)
         self.ws = tp.alloc_workspace(nbytes, "cuda")
         self.with_reduce = with_reduce
         # the t - 1 other ranks' partials: `other_sets` distinct sets, used in turn
@@ -490,6 +495,10 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
     n_sets = 1   # compute-bound: weight reuse across tokens dwarfs any cache effect
     log("generating the %s inputs" % c["name"])
     sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
+    if args.packed:
+        # the packed-weight GEMMs read the decode kernels' layout (packed once, outside the timing)
+        sets = [dict(d, packed=tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)) for d in sets]
+        label += ", weights packed for the decode kernels (packed-weight GEMMs)"
     ph = Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, c["reduce_n"] is not None)
 
     def step(i):
@@ -527,8 +536,8 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
                             "source": "HIP events on every reduce launch of a further pass of the same steps"}}
     roof = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
-            "traffic": recorded_traffic("gateup_prefill", args.workload if args.workload != "default" else
-                                        "prefill70b"),
+            "traffic": recorded_traffic("gateup_prefill", (args.workload if args.workload != "default" else
+                                                           "prefill70b") + ("_packed" if args.packed else "")),
             "kernel": "gateup_prefill", "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
             "launch_us": spread(gu_dur),
             "source": "HIP events on every gate/up launch of the timed steps, on the launch stream"}
