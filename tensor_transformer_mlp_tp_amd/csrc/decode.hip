@@ -1112,16 +1112,19 @@ constexpr bool kSkStream = WB ? NT == 2 : NT == 4;
 
 // Tiles: gate/up seven waves of one 16-row block (112 rows = 56 channels),
 // so the 70B shards' gate/up rows (7168 and 14336) make whole multiples of
-// 64 tiles and their ranges fill the 256 CUs; the down projection four
-// waves of two blocks (128 rows).  Wider tiles, so that each activation
-// fragment serves more rows, measured slower at 64 tokens (70B TP = 8, gate/up
-// 26.8 us: 14 waves 30.6, 7 waves of two blocks 31.2; down 14.0 us: 8 waves
-// of two blocks 17.8, 4 of four 18.1): the longer tiles need more, shorter
-// ranges.
+// 64 tiles and their ranges fill the 256 CUs; the down projection eight
+// waves of one block (128 rows; against four waves of two blocks the decode
+// step at 8192 x 3584 went 4.30 -> 4.33 TB/s, the fp8 down at 32 tokens
+// 16.8-17.2 -> 16.1-16.4 us).  Wider tiles, so that each activation fragment
+// serves more rows, measured slower at 64 tokens (70B TP = 8, gate/up 26.8
+// us: 14 waves 30.6, 7 waves of two blocks 31.2; down: 256-row tiles 17.8
+// and 18.1 against 18.1 us for the M = 64 launch), and so did 64-row down
+// tiles (two ranges of 56 steps): the longer tiles need more, shorter
+// ranges, the shorter ones reread the activations more often.
 template <int NT, int WB, bool GU>
 struct SkPlan {
-  static constexpr int W = GU ? 7 : 4;
-  static constexpr int RB = GU ? 1 : 2;
+  static constexpr int W = GU ? 7 : 8;
+  static constexpr int RB = 1;
   static constexpr int D = 8;
   static constexpr int ROWS = 16 * W * RB;
 };
