@@ -863,6 +863,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
 // 32-row MFMA block the lane's registers 0-3 / 4-7 are the gate / up sums of
 // channels 8 b + 4 g + (0..3) and registers 8-11 / 12-15 those of block b + 1,
 // and SiLU(G) * U needs no exchange between lanes.
+// (wp is deliberately not __restrict__: with it the compiler moved the
+// weight loads across the memory-clobbering asm statements that fix their
+// place in the schedule.)
 template <bool SWIGLU, bool OBF, bool SK>
 __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, const uint8_t* __restrict__ xb,
                                                          int64_t ldx, const uint8_t* wp, int nblk,
