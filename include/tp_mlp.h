@@ -483,11 +483,11 @@ tp_status tp_profile_durations(int32_t kind, float* ms, int64_t capacity, int64_
  * matrices from one array in the order the weight-streaming decode kernels
  * consume them: each workgroup then reads one contiguous range of memory
  * instead of 16 rows side by side (on MI355X the gate/up launches of the 70B
- * shard measured 5 to 14 % shorter).  With bf16 weights the same array also
- * serves every larger M: MFMA GEMMs on 256-token tiles that load each
- * packed 1 KB fragment straight into the matrix instruction's operand
- * registers, so a server keeps one copy of the weights for decode and
- * prefill.  Packing is a permutation of the weight bytes, done once per
+ * shard measured 5 to 14 % shorter).  The same array also serves every
+ * larger M: MFMA GEMMs on 256-token tiles that load the packed fragments
+ * straight into the matrix instruction's operand registers (one-byte codes
+ * widened to bf16 there), so a server keeps one copy of the weights for
+ * decode and prefill.  Packing is a permutation of the weight bytes, done once per
  * weight set on the GPU.  At decode sizes the packed forward's partial is
  * bit-identical to tp_mlp_shard_forward's on the same weights; above them
  * too when both add the products in the same order (256-token tiles with
@@ -530,16 +530,14 @@ tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32_t w_dt
  * activations): A (M x I_s bf16) plus the split scratch of the decode
  * streams or, above the decode sizes, the stream-K scratch of the packed
  * 256-token GEMMs (this can exceed tp_mlp_workspace_bytes for a few hundred
- * tokens).  0 if the shapes are invalid or the packed forward does not take
- * them (one-byte weights above 32 tokens).
+ * tokens).  0 if the shapes are invalid or not packable.
  */
 size_t tp_mlp_packed_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t w_dtype);
 
 /*
  * tp_mlp_shard_forward with the weights given as a packed array (above)
  * instead of w_gate, w_up, w_down and their leading dimensions; bf16
- * activations only.  Any M >= 1 with bf16 weights; with one-byte weights M
- * at most 32, else TP_ERR_UNSUPPORTED.  packed_bytes is the size of the
+ * activations only; any M >= 1.  packed_bytes is the size of the
  * caller's packed array; fewer than tp_mlp_packed_weights_bytes(h, I_full,
  * t, w_dtype) bytes (an array packed for other shapes) is
  * TP_ERR_INVALID_ARG.  The workspace needs tp_mlp_packed_workspace_bytes(...)

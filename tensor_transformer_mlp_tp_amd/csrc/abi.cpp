@@ -423,8 +423,6 @@ TP_API tp_status tp_mlp_pack_weights(int64_t h, int64_t I_full, int32_t t, int32
 
 TP_API size_t tp_mlp_packed_workspace_bytes(int64_t M, int64_t h, int64_t I_full, int32_t t, int32_t w_dtype) {
   if (check_shapes(M, h, I_full, t, 0, TP_BF16, w_dtype) != TP_OK) return 0;
-  const int wb = weight_format(w_dtype);
-  if (M > tpmlp::forward_decode_max_m(wb) && wb != tpmlp::kWeightWide) return 0;
   if (packed_need(h, I_full, t, w_dtype) == 0) return 0;
   return (size_t)packed_workspace_need(M, h, I_full / t, w_dtype);
 }
@@ -439,9 +437,6 @@ TP_API tp_status tp_mlp_shard_forward_packed(int64_t M, int64_t h, int64_t I_ful
   if (act_dtype != TP_BF16) return fail(TP_ERR_UNSUPPORTED, "packed weights take bf16 activations");
   const int wb = weight_format(w_dtype);
   const bool prefill = M > tpmlp::forward_decode_max_m(wb);
-  if (prefill && wb != tpmlp::kWeightWide)
-    return fail(TP_ERR_UNSUPPORTED, "packed one-byte weights serve the decode kernels: M <= %d (got %lld)",
-                tpmlp::forward_decode_max_m(wb), (long long)M);
   const int64_t pbytes = packed_need(h, I_full, t, w_dtype);
   if (pbytes == 0) return TP_ERR_UNSUPPORTED;
   const int64_t I_s = I_full / t;

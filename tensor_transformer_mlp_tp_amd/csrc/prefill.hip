@@ -863,12 +863,23 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
 // 32-row MFMA block the lane's registers 0-3 / 4-7 are the gate / up sums of
 // channels 8 b + 4 g + (0..3) and registers 8-11 / 12-15 those of block b + 1,
 // and SiLU(G) * U needs no exchange between lanes.
+// One-byte weights (WB: e4m3fn or int8 codes, packed the same way with 64
+// k-values per row in a fragment, 16 rows x 64 bytes): lane l loads the
+// chunks 2g and 2g + 1 of its row (g = l / 32), 16 codes each, which
+// widened to bf16 (exact) give MFMA kk the codes 8 (kk mod 2) .. +7 of chunk
+// 2g + kk / 2, i.e. k values 16 (2g + kk / 2) + 8 (kk mod 2) + (0..7) of the
+// 64-k stage; the activation side reads the same k values (LDS chunk
+// 4g + kk instead of 2kk + g).  Any k assignment shared by both operands
+// gives the same products; the row scales multiply the fp32 sums in the
+// epilogue, as in the other kernels.
 // (wp is deliberately not __restrict__: with it the compiler moved the
 // weight loads across the memory-clobbering asm statements that fix their
 // place in the schedule.)
-template <bool SWIGLU, bool OBF, bool SK>
+template <bool SWIGLU, int WB, bool OBF, bool SK>
 __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, const uint8_t* __restrict__ xb,
                                                          int64_t ldx, const uint8_t* wp, int nblk,
+                                                         const float* __restrict__ s0,
+                                                         const float* __restrict__ s1,
                                                          void* __restrict__ out, int64_t ld_out, int tiles_m,
                                                          int tiles_n, const SkTail sk) {
   constexpr int BM = 256, BK = 64;
@@ -926,17 +937,31 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
 
   // ---- weight fragments: block pair (4q + 2cb, +1) of the tile; blocks past
   // the end read the last block (their outputs are not stored)
-  const int64_t fpb = K / 32;                 // fragments per block
+  const int64_t fpb = K / (WB ? 64 : 32);     // fragments per block
   const uint8_t* wsrc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
     const int b = min(b0 + 4 * q + 2 * cb + ((lane >> 4) & 1), nblk - 1);
-    wsrc[cb] = wp + (int64_t)b * fpb * 1024 + 256 * g + 16 * (lane & 15);
+    wsrc[cb] = wp + (int64_t)b * fpb * 1024 + (WB ? 512 : 256) * g + 16 * (lane & 15);
   }
-  // one weight fragment (k-step kk, MFMA block cb) of stage kt
-  auto load_w = [&](int kt, int cb, int kk, u32x4& w) {
+  // 16-byte weight load i (bf16: k-step i; one-byte: chunk 2g + i, i < 2) of
+  // MFMA block cb at stage kt
+  constexpr int WL = WB ? 2 : KSUB;           // loads per block and stage
+  auto load_w = [&](int kt, int cb, int i, u32x4& w) {
     kt = min(kt, kt1 - 1);
-    w = *reinterpret_cast<const u32x4*>(wsrc[cb] + ((int64_t)kt * 2 + (kk >> 1)) * 1024 + 512 * (kk & 1));
+    if constexpr (WB)
+      w = *reinterpret_cast<const u32x4*>(wsrc[cb] + (int64_t)kt * 1024 + 256 * i);
+    else
+      w = *reinterpret_cast<const u32x4*>(wsrc[cb] + ((int64_t)kt * 2 + (i >> 1)) * 1024 + 512 * (i & 1));
+  };
+  // bf16 A operand of k-step kk from the stage's loads
+  auto wfrag = [&](const u32x4 (&w)[WL], int kk) -> bf16x8 {
+    if constexpr (WB) {
+      const u32x4 v = w[kk >> 1];
+      return (kk & 1) ? byte8_to_bf16x8<WB>(v[2], v[3]) : byte8_to_bf16x8<WB>(v[0], v[1]);
+    } else {
+      return as_bf16x8(w[kk]);
+    }
   };
 
   int xrow[TB];
@@ -952,15 +977,17 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
       for (int i = 0; i < 16; ++i) acc[cb][tb][i] = 0.f;
 
   // Order of the loads.  The wave holds two sets of weight registers (2 x
-  // 32 VGPRs).  Iteration s (stage kt0 + s): issue the weights of stage s + 1
-  // into the set last read by the MFMAs of stage s - 1 (eight loads); wait
+  // 32 VGPRs; one-byte weights 2 x 16).  Iteration s (stage kt0 + s): issue
+  // the weights of stage s + 1 into the set last read by the MFMAs of stage
+  // s - 1 (NWL = eight loads, one-byte weights four); wait
   // until the weights of stage s have arrived, and with them (issued
   // earlier) this wave's activation loads of stage s; barrier (every wave's
   // activations of stage s have landed and every wave is done with stage
   // s - 1); issue the activations of stage s + 3 into the buffer of stage
   // s - 1 (four loads); compute stage s.  So the weights have one stage to
   // arrive and the activations three.  Loads issued after the weights of
-  // stage s at the wait: 8 at s = 0 (W1), else 12 (X of s + 2, W of s + 1).
+  // stage s at the wait: NWL at s = 0 (W1), else NWL + 4 (X of s + 2, W of
+  // s + 1).
   // The wait is explicit because the direct-to-LDS loads are FLAT
   // instructions, after which a wait that the compiler inserts itself for a
   // register is widened to vmcnt(0) (it would also drain the prefetch); the
@@ -968,18 +995,18 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
   // the weight loads next to their first use.  Stage counts are even for
   // whole tiles (K is a multiple of 128); a stream-K piece may end with one
   // odd stage.
-  typedef u32x4 WSet[CB][KSUB];
+  typedef u32x4 WSet[CB][WL];
   auto load_ws = [&](int kt, WSet& w) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int kk = 0; kk < KSUB; ++kk) load_w(kt, cb, kk, w[cb][kk]);
+      for (int i = 0; i < WL; ++i) load_w(kt, cb, i, w[cb][i]);
   };
   auto compute = [&](int s, const WSet& w) {
     const uint8_t* sx = lds + (s % NS) * STAGE;
     bf16x8 xf[2][TB];
     auto read = [&](int kk, bf16x8 (&x_)[TB]) {
-      const int c = 2 * kk + g;
+      const int c = WB ? 4 * g + kk : 2 * kk + g;
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
         x_[tb] = as_bf16x8(lds_read16(sx + xrow[tb] * ROWB + ((c ^ swz<ROWB>(xrow[tb])) * 16)));
@@ -989,9 +1016,11 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
     for (int kk = 0; kk < KSUB; ++kk) {
       if (kk + 1 < KSUB) read(kk + 1, xf[(kk + 1) & 1]);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb) {
+        const bf16x8 a = wfrag(w[cb], kk);
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(as_bf16x8(w[cb][kk]), xf[kk & 1][tb], acc[cb][tb]);
+        for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(a, xf[kk & 1][tb], acc[cb][tb]);
+      }
     }
     constexpr int NMF = CB * TB;
     __builtin_amdgcn_sched_group_barrier(0x100, TB, 0);
@@ -1006,12 +1035,13 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
   for (int i = 0; i < NS - 1; ++i) load_x(kt0 + i, i);
   load_ws(kt0, wa);
   asm volatile("" ::: "memory");
+  constexpr int NWL = CB * WL;                // weight loads per stage (8; one-byte weights 4)
   auto iter = [&](int s, const WSet& cur, WSet& nxt) {
     load_ws(kt0 + s + 1, nxt);
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    if (s == 0) wait_vmcnt<8>();
-    else wait_vmcnt<12>();
+    if (s == 0) wait_vmcnt<NWL>();
+    else wait_vmcnt<NWL + 4>();
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -1041,20 +1071,29 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
       for (int hb = 0; hb < 2; ++hb) {
         const int ch = (b0 + 4 * q + 2 * cb + hb) * 8 + 4 * g;  // channels ch .. ch+3
         if (ch >= N) continue;
+        float sg[4] = {1.f, 1.f, 1.f, 1.f}, su[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (WB) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sg[i] = s0[ch + i];
+            su[i] = s1[ch + i];
+          }
+        }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
           const int tok = tok0 + tb * 32 + r32;
           if (tok >= M) continue;
           float a[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) a[i] = silu(acc[cb][tb][8 * hb + i]) * acc[cb][tb][8 * hb + 4 + i];
+          for (int i = 0; i < 4; ++i)
+            a[i] = silu(acc[cb][tb][8 * hb + i] * sg[i]) * (acc[cb][tb][8 * hb + 4 + i] * su[i]);
           const u32x2 pk = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3])};
           *reinterpret_cast<u32x2*>(a_out + (int64_t)tok * ld_out + ch) = pk;
         }
       }
   } else {
-    store_tile<false, kWeightWide, false, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, r32, g, nullptr, nullptr,
-                                                       nullptr, out, ld_out);
+    store_tile<false, WB, false, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, r32, g, s0, nullptr, nullptr, out,
+                                              ld_out);
   }
 }
 
@@ -1237,9 +1276,9 @@ int64_t sk_bytes(bool swiglu, int M, int N, int K, int BK) {
 
 // Packed-weight GEMM launch (256-token tiles): N output channels (gate/up)
 // or rows (down) from nblk packed 16-row blocks; skws as in run_gemm_bm.
-template <bool SWIGLU>
+template <bool SWIGLU, int WB>
 hipError_t run_gemm_pk(int kind, int M, int N, int K, const void* x, int64_t ldx, const void* wp, int nblk,
-                       void* out, int64_t ldo, void* skws, hipStream_t stream) {
+                       const float* s0, const float* s1, void* out, int64_t ldo, void* skws, hipStream_t stream) {
   constexpr int BM = 256;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles = gemm_tiles(SWIGLU, M, N, BM);
@@ -1252,12 +1291,12 @@ hipError_t run_gemm_pk(int kind, int M, int N, int K, const void* x, int64_t ldx
     sk.d = p.d;
     const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
     if (e != hipSuccess) return e;
-    return launch(kind, gemm_pk_kernel<SWIGLU, false, true>, dim3((unsigned)(p.nfull + p.rem * p.d)), dim3(512), 0,
-                  stream, M, N, K, (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, out, ldo, tiles_m,
+    return launch(kind, gemm_pk_kernel<SWIGLU, WB, false, true>, dim3((unsigned)(p.nfull + p.rem * p.d)), dim3(512),
+                  0, stream, M, N, K, (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, s0, s1, out, ldo, tiles_m,
                   tiles / tiles_m, sk);
   }
-  return launch(kind, gemm_pk_kernel<SWIGLU, false, false>, dim3((unsigned)tiles), dim3(512), 0, stream, M, N, K,
-                (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, out, ldo, tiles_m, tiles / tiles_m, sk);
+  return launch(kind, gemm_pk_kernel<SWIGLU, WB, false, false>, dim3((unsigned)tiles), dim3(512), 0, stream, M, N, K,
+                (const uint8_t*)x, ldx, (const uint8_t*)wp, nblk, s0, s1, out, ldo, tiles_m, tiles / tiles_m, sk);
 }
 
 }  // namespace
@@ -1298,14 +1337,23 @@ hipError_t launch_forward_w8a8(const ShardArgs& a, const W8A8Bufs& b, hipStream_
                                                   nullptr, a.ldw_down, a.sd, nullptr, b.sa, a.p, a.ldp, a.sk, stream);
 }
 
-// Packed bf16 weights (contiguous X: the packed forward has no row-block form).
+// Packed weights (contiguous X: the packed forward has no row-block form).
+template <int WB>
+hipError_t forward_prefill_packed_wb(const ShardArgs& a, hipStream_t stream) {
+  hipError_t e = run_gemm_pk<true, WB>(K_GATEUP_PREFILL, a.M, a.I_s, a.h, a.x.p[0], a.x.ld, a.wg, (a.I_s + 7) / 8,
+                                       a.sg, a.su, a.a, a.lda, a.sk, stream);
+  if (e != hipSuccess) return e;
+  return run_gemm_pk<false, WB>(K_DOWN_PREFILL, a.M, a.h, a.I_s, a.a, a.lda, a.wd, (a.h + 15) / 16, a.sd, nullptr,
+                                a.p, a.ldp, a.sk, stream);
+}
+
 hipError_t launch_forward_prefill_packed(const ShardArgs& a, hipStream_t stream) {
   if (a.x.nb != 1) return hipErrorInvalidValue;
-  hipError_t e = run_gemm_pk<true>(K_GATEUP_PREFILL, a.M, a.I_s, a.h, a.x.p[0], a.x.ld, a.wg, (a.I_s + 7) / 8, a.a,
-                                   a.lda, a.sk, stream);
-  if (e != hipSuccess) return e;
-  return run_gemm_pk<false>(K_DOWN_PREFILL, a.M, a.h, a.I_s, a.a, a.lda, a.wd, (a.h + 15) / 16, a.p, a.ldp, a.sk,
-                            stream);
+  switch (a.wb) {
+    case kWeightE4M3: return forward_prefill_packed_wb<kWeightE4M3>(a, stream);
+    case kWeightI8: return forward_prefill_packed_wb<kWeightI8>(a, stream);
+    default: return forward_prefill_packed_wb<kWeightWide>(a, stream);
+  }
 }
 
 hipError_t launch_forward_prefill(const ShardArgs& a, hipStream_t stream) {

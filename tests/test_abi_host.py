@@ -422,7 +422,10 @@ def test_packed_workspace_bytes():
     # 4096 tokens: 448 gate/up tiles (192 past the first round, kept whole), 512 down tiles
     assert pw(4096, 8192, 28672, 8, BF16) == 4096 * 3584 * 2
     assert pw(8192, 16384, 53248, 8, BF16) == lib.tp_mlp_workspace_bytes(8192, 16384, 53248, 8, BF16, BF16)
-    assert pw(33, 8192, 28672, 4, FP8) == 0            # one-byte weights: decode sizes only
+    # one-byte weights above 32 tokens: the packed-weight GEMMs (4096 x 7168 fp8: 448 gate/up tiles,
+    # 192 past the first round, kept whole; 256 down tiles)
+    assert pw(2048, 8192, 28672, 4, FP8) == 2048 * 7168 * 2
+    assert pw(33, 8192, 28672, 4, FP8) > pw(32, 8192, 28672, 4, FP8) > 0
     assert pw(1, 320, 640, 2, BF16) == 0               # h % 128: not packable
     assert pw(0, 512, 1024, 2, BF16) == 0
 
@@ -445,7 +448,8 @@ def test_packed_weights_bytes_and_validation():
     need = lib.tp_mlp_packed_workspace_bytes(65, 512, 1024, 2, BF16)
     assert need >= 65 * 512 * 2
     assert fwdp(M=65, wsb=need - 1) == _lib.TP_ERR_WORKSPACE
-    assert fwdp(M=33, w=FP8, sc=P) == _lib.TP_ERR_UNSUPPORTED
+    need8 = lib.tp_mlp_packed_workspace_bytes(33, 512, 1024, 2, FP8)
+    assert fwdp(M=33, w=FP8, sc=P, wsb=need8 - 1) == _lib.TP_ERR_WORKSPACE
     assert fwdp(act=F32, w=F32) == _lib.TP_ERR_UNSUPPORTED
     assert fwdp(packed=None) == _lib.TP_ERR_INVALID_ARG
     assert fwdp(w=FP8) == _lib.TP_ERR_INVALID_ARG                            # scales missing
