@@ -80,11 +80,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--weight-sets", type=int, default=N_WEIGHT_SETS)
     ap.add_argument("--row-major", action="store_true",
-                    help="decode70b, fp8_70b, int8_70b: read the weights in the (out, in) layout instead of packed "
-                         "for the decode kernels (the one-byte workloads' prefill too)")
-    ap.add_argument("--packed", action="store_true",
-                    help="prefill70b, prefill405b: run the prefill on the weights packed for the decode kernels "
-                         "(the packed-weight GEMMs) instead of the (out, in) layout")
+                    help="read the weights in the (out, in) layout instead of packed for the decode kernels "
+                         "(decode and prefill phases of the MLP workloads)")
     return ap.parse_args()
 
 
@@ -496,10 +493,11 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
     n_sets = 1   # compute-bound: weight reuse across tokens dwarfs any cache effect
     log("generating the %s inputs" % c["name"])
     sets, host0 = device_weights(cfg_id, h, I_s, w, c["std_gu"], c["std_down"], n_sets)
-    if args.packed:
-        # the packed-weight GEMMs read the decode kernels' layout (packed once, outside the timing)
+    if not args.row_major:
+        # the packed-weight GEMMs read the decode kernels' layout (packed once, outside the timing): the
+        # same single copy of the weights as the decode phases
         sets = [dict(d, packed=tp.pack_weights(d["w_gate"], d["w_up"], d["w_down"], t=t)) for d in sets]
-        label += ", weights packed for the decode kernels (packed-weight GEMMs)"
+        label += ", weights packed for the decode kernels"
     ph = Phase(tp, cfg_id, M, h, I_s, t, "bf16", w, c["reduce_n"] is not None)
 
     def step(i):
@@ -538,7 +536,7 @@ def bench_prefill(tp, args, cfg_id, M, label, step_ms):
     roof = {"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
             "traffic": recorded_traffic("gateup_prefill", (args.workload if args.workload != "default" else
-                                                           "prefill70b") + ("_packed" if args.packed else "")),
+                                                           "prefill70b") + ("_rowmajor" if args.row_major else "")),
             "kernel": "gateup_prefill", "per_launch_flop": 4 * M * h * I_s, "avg_us": round(1e3 * gu_ms / gu_n, 2),
             "launch_us": spread(gu_dur),
             "source": "HIP events on every gate/up launch of the timed steps, on the launch stream"}
