@@ -340,6 +340,56 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[CB][TB], int M, i
   }
 }
 
+// Epilogue of the down projection (fp32 or bf16 rows of out) through LDS, for
+// waves of 64 consecutive features (CB = 2) and TB 32-token blocks.  In the
+// MFMA layout a lane holds four consecutive features of one token, so a
+// direct store instruction writes 32-byte pieces of 32 rows; here each
+// wave writes its 32 x 64 block of one token block to LDS, reads it back
+// row-wise and stores four whole 64-feature row pieces per instruction
+// (256 bytes each in fp32).  LDS: 8.5 KB per wave (row pitch 68 floats);
+// every wave of the workgroup calls it (block barriers).
+template <int WB, bool OBF, int CB, int TB>
+__device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[CB][TB], int M, int N, int ch0, int tok0,
+                                                int lane, int wave, const float* __restrict__ s0,
+                                                void* __restrict__ out, int64_t ld_out, uint8_t* lds) {
+  static_assert(CB == 2, "64 features per wave");
+  constexpr int RP = 68;                      // LDS row pitch in floats (64 features + 4)
+  float* buf = reinterpret_cast<float*>(lds) + wave * 32 * RP;
+  const int r32 = lane & 31, g = lane >> 5;
+  const int c = lane & 15, t4 = lane >> 4;    // read side: features 4c .. 4c+3 of token t4 + 4 it
+  const int f = ch0 + 4 * c;
+  float sv[4] = {1.f, 1.f, 1.f, 1.f};
+  if constexpr (WB != 0) {
+    if (f < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[i] = s0[f + i];
+    }
+  }
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    asm volatile("" ::: "memory");
+    lds_barrier();                            // every wave is done with the buffer (k-loop stages, block tb-1)
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f32x4 v = {acc[cb][tb][4 * j], acc[cb][tb][4 * j + 1], acc[cb][tb][4 * j + 2], acc[cb][tb][4 * j + 3]};
+        *reinterpret_cast<f32x4*>(buf + r32 * RP + cb * 32 + 8 * j + 4 * g) = v;
+      }
+    asm volatile("" ::: "memory");
+    lds_barrier();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int t = 4 * it + t4;
+      const int tok = tok0 + tb * 32 + t;
+      f32x4 v = *reinterpret_cast<const f32x4*>(buf + t * RP + 4 * c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] *= sv[i];
+      if (tok < M && f < N) store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
+    }
+  }
+}
+
 // A8: the activations are e4m3fn codes too (W8A8): one byte per element in
 // LDS, 32x32x64 fp8 MFMAs (twice the bf16 rate), and the per-token scales sx
 // applied in the epilogue with the weight row scales.
@@ -832,9 +882,14 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
     if (tail >= 0 && !sk_handoff<CB, TB, WV * 64, BM>(acc, sk, tail, piece, tid, reinterpret_cast<int*>(lds)))
       return;
   }
-  store_tile<SWIGLU, kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + (SWIGLU ? q * 32 : q * 64),
-                                                     m0 + (grpB ? 128 : 0), r32, g, nullptr, nullptr, nullptr,
-                                                     out, ld_out);
+  if constexpr (SWIGLU) {
+    store_tile<true, kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + q * 32, m0 + (grpB ? 128 : 0), r32, g, nullptr,
+                                                      nullptr, nullptr, out, ld_out);
+  } else {
+    static_assert(8 * 32 * 68 * 4 <= NH * HALF, "LDS of the row-wise epilogue");
+    store_tile_rows<kWeightWide, OBF, CB, TB>(acc, M, N, n0 + q * 64, m0 + (grpB ? 128 : 0), lane, wave, nullptr, out,
+                                              ld_out, lds);
+  }
 }
 
 // Packed-weight GEMM (bf16 weights in the packed decode layout, bf16
@@ -1092,8 +1147,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
         }
       }
   } else {
-    store_tile<false, WB, false, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, r32, g, s0, nullptr, nullptr, out,
-                                              ld_out);
+    static_assert(8 * 32 * 68 * 4 <= NS * STAGE, "LDS of the row-wise epilogue");
+    store_tile_rows<WB, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, lane, wave, s0, out, ld_out, lds);
   }
 }
 
