@@ -341,22 +341,29 @@ __device__ __forceinline__ void store_tile(const f32x16 (&acc)[CB][TB], int M, i
 }
 
 // Epilogue of the down projection (fp32 or bf16 rows of out) through LDS, for
-// waves of 64 consecutive features (CB = 2) and TB 32-token blocks.  In the
-// MFMA layout a lane holds four consecutive features of one token, so a
-// direct store instruction writes 32-byte pieces of 32 rows; here each
-// wave writes its 32 x 64 block of one token block to LDS, reads it back
-// row-wise and stores four whole 64-feature row pieces per instruction
-// (256 bytes each in fp32).  LDS: 8.5 KB per wave (row pitch 68 floats);
-// every wave of the workgroup calls it (block barriers).
-template <int WB, bool OBF, int CB, int TB>
+// waves of 32 CB consecutive features and TB 32-token blocks.  In the MFMA
+// layout a lane holds four consecutive features of one token, so a direct
+// store instruction writes 32-byte pieces of 32 rows; here each wave writes
+// its 32-token x 32 CB-feature block of one token block to LDS, reads it
+// back row-wise and stores whole 32 CB-feature row pieces (64 / 2 CB rows
+// per instruction, 128 CB bytes each in fp32).  LDS: 32 x (32 CB + 4)
+// floats per wave; every wave of the workgroup calls it (block barriers).
+// One-byte weights scale by the row scales s0, fp8 activations by sx.
+template <int CB>
+constexpr int rows_epilogue_lds(int waves) { return waves * 32 * (32 * CB + 4) * 4; }
+
+template <int WB, bool A8, bool OBF, int CB, int TB>
 __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[CB][TB], int M, int N, int ch0, int tok0,
                                                 int lane, int wave, const float* __restrict__ s0,
-                                                void* __restrict__ out, int64_t ld_out, uint8_t* lds) {
-  static_assert(CB == 2, "64 features per wave");
-  constexpr int RP = 68;                      // LDS row pitch in floats (64 features + 4)
+                                                const float* __restrict__ sx, void* __restrict__ out,
+                                                int64_t ld_out, uint8_t* lds) {
+  static_assert(CB == 2 || CB == 4, "64 or 128 features per wave");
+  constexpr int RP = 32 * CB + 4;             // LDS row pitch in floats
+  constexpr int LPR = 8 * CB;                 // lanes per row on the read side
+  constexpr int RPI = 64 / LPR;               // rows per store instruction
   float* buf = reinterpret_cast<float*>(lds) + wave * 32 * RP;
   const int r32 = lane & 31, g = lane >> 5;
-  const int c = lane & 15, t4 = lane >> 4;    // read side: features 4c .. 4c+3 of token t4 + 4 it
+  const int c = lane % LPR, tr = lane / LPR;  // read side: features 4c .. 4c+3 of token tr + RPI it
   const int f = ch0 + 4 * c;
   float sv[4] = {1.f, 1.f, 1.f, 1.f};
   if constexpr (WB != 0) {
@@ -379,13 +386,20 @@ __device__ __forceinline__ void store_tile_rows(const f32x16 (&acc)[CB][TB], int
     asm volatile("" ::: "memory");
     lds_barrier();
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int t = 4 * it + t4;
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int t = RPI * it + tr;
       const int tok = tok0 + tb * 32 + t;
       f32x4 v = *reinterpret_cast<const f32x4*>(buf + t * RP + 4 * c);
+      if (tok < M && f < N) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] *= sv[i];
-      if (tok < M && f < N) store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
+        for (int i = 0; i < 4; ++i) v[i] *= sv[i];
+        if constexpr (A8) {
+          const float st = sx[tok];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] *= st;
+        }
+        store_out4<OBF>(out, (int64_t)tok * ld_out + f, v);
+      }
     }
   }
 }
@@ -674,8 +688,13 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
         !sk_handoff<CB, TB, WV * 64, BM>(acc, sk, tail, piece, tid, reinterpret_cast<int*>(lds + NS * SBYTES + WV * 512)))
       return;
   }
-  store_tile<SWIGLU, WB, A8, OBF, CB, TB>(acc, M, N, n0 + (SWIGLU ? wn * (BN / 2 / WN) : wn * (BN / WN)),
-                                          m0 + wm * (BM / WM), r32, g, s0, s1, sx, out, ld_out);
+  if constexpr (!SWIGLU && rows_epilogue_lds<CB>(WV) <= NS * SBYTES) {
+    store_tile_rows<WB, A8, OBF, CB, TB>(acc, M, N, n0 + wn * (BN / WN), m0 + wm * (BM / WM), lane, wave, s0, sx, out,
+                                         ld_out, lds);
+  } else {
+    store_tile<SWIGLU, WB, A8, OBF, CB, TB>(acc, M, N, n0 + (SWIGLU ? wn * (BN / 2 / WN) : wn * (BN / WN)),
+                                            m0 + wm * (BM / WM), r32, g, s0, s1, sx, out, ld_out);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -886,9 +905,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
     store_tile<true, kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + q * 32, m0 + (grpB ? 128 : 0), r32, g, nullptr,
                                                       nullptr, nullptr, out, ld_out);
   } else {
-    static_assert(8 * 32 * 68 * 4 <= NH * HALF, "LDS of the row-wise epilogue");
-    store_tile_rows<kWeightWide, OBF, CB, TB>(acc, M, N, n0 + q * 64, m0 + (grpB ? 128 : 0), lane, wave, nullptr, out,
-                                              ld_out, lds);
+    static_assert(rows_epilogue_lds<CB>(8) <= NH * HALF, "LDS of the row-wise epilogue");
+    store_tile_rows<kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + q * 64, m0 + (grpB ? 128 : 0), lane, wave,
+                                                     nullptr, nullptr, out, ld_out, lds);
   }
 }
 
@@ -1147,8 +1166,9 @@ __global__ __launch_bounds__(512, 1) void gemm_pk_kernel(int M, int N, int K, co
         }
       }
   } else {
-    static_assert(8 * 32 * 68 * 4 <= NS * STAGE, "LDS of the row-wise epilogue");
-    store_tile_rows<WB, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, lane, wave, s0, out, ld_out, lds);
+    static_assert(rows_epilogue_lds<CB>(8) <= NS * STAGE, "LDS of the row-wise epilogue");
+    store_tile_rows<WB, false, OBF, CB, TB>(acc, M, N, (b0 + 4 * q) * 16, tok0, lane, wave, s0, nullptr, out, ld_out,
+                                            lds);
   }
 }
 
