@@ -733,21 +733,29 @@ __global__ __launch_bounds__(WV * 64, 1) void gemm_kernel(
 // issued, X_s has two slots after its load slot to land and W_s one; each
 // wave waits for its own loads (vmcnt) before the barrier after which they
 // are read.
-template <bool SWIGLU, bool OBF, bool SK>
+template <bool SWIGLU, bool OBF, bool SK, bool A8>
 __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, const XRows xr,
                                                          const uint8_t* __restrict__ w0,
                                                          const uint8_t* __restrict__ w1, int64_t ldw,
+                                                         const float* __restrict__ s0,
+                                                         const float* __restrict__ s1,
+                                                         const float* __restrict__ sx,
                                                          void* __restrict__ out, int64_t ld_out, int tiles_m,
                                                          int tiles_n, const SkTail sk) {
-  constexpr int BM = 256, BK = 64, WV = 8;
+  // A8: e4m3fn activations and weights (one byte each, row scales s0 / s1,
+  // token scales sx): a stage holds 128 k in the same 128-byte rows, and
+  // each 64-k sub-step is one 32x32x64 fp8 MFMA per block pair
+  constexpr int BM = 256, BK = A8 ? 128 : 64, WV = 8;
+  constexpr int EB = A8 ? 1 : 2;              // bytes per element
+  constexpr int WBF = A8 ? kWeightE4M3 : kWeightWide;
   constexpr int CB = 2, TB = 4;               // 32-row weight blocks, 32-token blocks per wave
-  constexpr int ROWB = BK * 2;                // bytes per LDS row
+  constexpr int ROWB = BK * EB;               // bytes per LDS row
   constexpr int HALF = 256 * ROWB;            // one half-stage: 256 rows
   constexpr int NH = 5;                       // half-stages in the ring
   constexpr int LPH = HALF / 1024 / 4;        // 1 KB loads per wave per half-stage
   constexpr int RPI = 1024 / ROWB;            // rows per 1 KB load
   constexpr int CH = ROWB / 16;               // 16-byte chunks per row
-  constexpr int KSUB = BK / 16;               // MFMA sub-steps per stage
+  constexpr int KSUB = BK / (A8 ? 64 : 16);   // MFMA sub-steps per stage
   constexpr int TILE_N = SWIGLU ? BN / 2 : BN;
   static_assert(NH * HALF <= 160 * 1024, "LDS");
   // One LDS object (the stream-K flag reuses its first bytes once the ring
@@ -788,7 +796,8 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
     const int row = q * (256 / 4) + i * RPI + lane / CH;
     const int c = (lane % CH) ^ swz<ROWB>(row);
     if (!grpB) {
-      src[i] = reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, min(m0 + row, M - 1))) + c * 16;
+      src[i] = A8 ? x_row<uint8_t>(xr, min(m0 + row, M - 1)) + c * 16
+                  : reinterpret_cast<const uint8_t*>(x_row<uint16_t>(xr, min(m0 + row, M - 1))) + c * 16;
     } else {
       int ch;
       const uint8_t* base;
@@ -799,7 +808,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
         ch = n0 + row;
         base = w0;
       }
-      src[i] = base + (int64_t)min(ch, N - 1) * ldw * 2 + c * 16;
+      src[i] = base + (int64_t)min(ch, N - 1) * ldw * EB + c * 16;
     }
   }
   // half-stage of stage kt (clamped to the k-range: past its end the last
@@ -809,7 +818,7 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
     kt = min(kt, kt1 - 1);
     uint8_t* dst = lds + hb * HALF + q * (HALF / 4);
 #pragma unroll
-    for (int i = 0; i < LPH; ++i) load_lds16(src[i] + (int64_t)kt * BK * 2, dst + i * 1024);
+    for (int i = 0; i < LPH; ++i) load_lds16(src[i] + (int64_t)kt * ROWB, dst + i * 1024);
   };
 
   // ---- fragment rows
@@ -838,6 +847,40 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
   auto compute = [&](int s) {
     const uint8_t* sx = lds + ((2 * s) % NH) * HALF;
     const uint8_t* sw = lds + ((2 * s + 1) % NH) * HALF;
+    if constexpr (A8) {
+      // lane group g takes bytes [32g, 32g + 32) of the sub-step's 64 k of its
+      // weight row and of its token row (chunks 4kk + 2g, +1)
+      v8i wf[2][CB], xf[2][TB];
+      auto read8 = [&](const uint8_t* base, int r, int kk) {
+        const int c0 = 4 * kk + 2 * g;
+        const u32x4 lo = lds_read16(base + r * ROWB + ((c0 ^ swz<ROWB>(r)) * 16));
+        const u32x4 hi = lds_read16(base + r * ROWB + (((c0 + 1) ^ swz<ROWB>(r)) * 16));
+        return v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
+      auto read = [&](int kk, v8i (&w_)[CB], v8i (&x_)[TB]) {
+        w_[0] = read8(sw, wrow[0], kk);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) x_[tb] = read8(sx, xrow[tb], kk);
+#pragma unroll
+        for (int cb = 1; cb < CB; ++cb) w_[cb] = read8(sw, wrow[cb], kk);
+      };
+      __builtin_amdgcn_s_setprio(1);
+      read(0, wf[0], xf[0]);
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) {
+        if (kk + 1 < KSUB) read(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32x64_f8(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+      }
+      constexpr int NMF = CB * TB, NRD = 2 * (CB + TB);
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      sched_substep<NRD, NMF>();
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     bf16x8 wf[2][CB], xf[2][TB];
     auto read = [&](int kk, bf16x8 (&w_)[CB], bf16x8 (&x_)[TB]) {
       const int c = 2 * kk + g;
@@ -902,12 +945,12 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
       return;
   }
   if constexpr (SWIGLU) {
-    store_tile<true, kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + q * 32, m0 + (grpB ? 128 : 0), r32, g, nullptr,
-                                                      nullptr, nullptr, out, ld_out);
+    store_tile<true, WBF, A8, OBF, CB, TB>(acc, M, N, n0 + q * 32, m0 + (grpB ? 128 : 0), r32, g, s0, s1, sx, out,
+                                           ld_out);
   } else {
     static_assert(rows_epilogue_lds<CB>(8) <= NH * HALF, "LDS of the row-wise epilogue");
-    store_tile_rows<kWeightWide, false, OBF, CB, TB>(acc, M, N, n0 + q * 64, m0 + (grpB ? 128 : 0), lane, wave,
-                                                     nullptr, nullptr, out, ld_out, lds);
+    store_tile_rows<WBF, A8, OBF, CB, TB>(acc, M, N, n0 + q * 64, m0 + (grpB ? 128 : 0), lane, wave, s0, sx, out,
+                                          ld_out, lds);
   }
 }
 
@@ -1288,13 +1331,13 @@ hipError_t run_gemm_bm(int kind, int M, int N, int K, const XRows& xr, const voi
     const hipError_t e = launch(K_SK_CLEAR, sk_clear_kernel, dim3(1), dim3(256), 0, stream, sk.cnt, p.rem);
     if (e != hipSuccess) return e;
   }
-  if constexpr (BM == 256 && WB == kWeightWide && !A8) {
-    // bf16 x bf16 on 256 x 256 tiles: the eight-wave ping-pong kernel
+  if constexpr (BM == 256 && ((WB == kWeightWide && !A8) || (WB == kWeightE4M3 && A8 && BK == 128))) {
+    // bf16 x bf16 and fp8 x fp8 on 256 x 256 tiles: the eight-wave ping-pong kernel
     if (p.d)
-      return launch(kind, gemm_pp_kernel<SWIGLU, OBF, true>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
-                    (const uint8_t*)w0, (const uint8_t*)w1, ldw, out, ldo, tiles_m, tiles / tiles_m, sk);
-    return launch(kind, gemm_pp_kernel<SWIGLU, OBF, false>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
-                  (const uint8_t*)w0, (const uint8_t*)w1, ldw, out, ldo, tiles_m, tiles / tiles_m, sk);
+      return launch(kind, gemm_pp_kernel<SWIGLU, OBF, true, A8>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
+                    (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
+    return launch(kind, gemm_pp_kernel<SWIGLU, OBF, false, A8>, dim3(grid), dim3(512), 0, stream, M, N, K, xr,
+                  (const uint8_t*)w0, (const uint8_t*)w1, ldw, s0, s1, sx, out, ldo, tiles_m, tiles / tiles_m, sk);
   }
   if (p.d)
     return launch(kind, gemm_kernel<SWIGLU, WB, BK, NS, kWV, BM, OBF, A8, true>, dim3(grid), dim3(kWV * 64), 0, stream, M,
