@@ -179,6 +179,8 @@ def _w8a8_check(x, ws, M, h, I_s, t):
     (300, 4096, 2048),     # gate/up tiles cut along K in 2 stream-K pieces (32 k-tiles of 128)
     (2304, 7424, 4096),    # 256-token tiles (eight-wave kernel) with stream-K tails in both GEMMs:
                            # gate/up 288 tiles (32 in 3 pieces), down 261 tiles (5 in 2 pieces)
+    (2200, 4096, 4096),    # ... ragged: the last 256-token tile holds 152 tokens (gate/up 288 tiles,
+                           # 32 in 2 pieces)
 ])
 def test_w8a8_forward_shapes(M, h, I_s):
     x, ws = make_case(93, M, h, I_s, "bf16", "e4m3fn", 0.05, 0.05, weight_set=M)
