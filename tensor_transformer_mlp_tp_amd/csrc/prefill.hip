@@ -879,38 +879,38 @@ __global__ __launch_bounds__(512, 1) void gemm_pp_kernel(int M, int N, int K, co
       sched_substep<NRD, NMF>();
       __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
       __builtin_amdgcn_s_setprio(0);
-      return;
+    } else {
+      bf16x8 wf[2][CB], xf[2][TB];
+      auto read = [&](int kk, bf16x8 (&w_)[CB], bf16x8 (&x_)[TB]) {
+        const int c = 2 * kk + g;
+        w_[0] = as_bf16x8(lds_read16(sw + wrow[0] * ROWB + ((c ^ swz<ROWB>(wrow[0])) * 16)));
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+          x_[tb] = as_bf16x8(lds_read16(sx + xrow[tb] * ROWB + ((c ^ swz<ROWB>(xrow[tb])) * 16)));
+#pragma unroll
+        for (int cb = 1; cb < CB; ++cb)
+          w_[cb] = as_bf16x8(lds_read16(sw + wrow[cb] * ROWB + ((c ^ swz<ROWB>(wrow[cb])) * 16)));
+      };
+      __builtin_amdgcn_s_setprio(1);
+      read(0, wf[0], xf[0]);
+#pragma unroll
+      for (int kk = 0; kk < KSUB; ++kk) {
+        if (kk + 1 < KSUB) read(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
+      }
+      // reads of sub-step 0, then per sub-step its MFMAs with the next
+      // sub-step's reads threaded one after each of the first MFMAs
+      constexpr int NMF = CB * TB, NRD = CB + TB;
+      __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
+      sched_substep<NRD, NMF>();
+      sched_substep<NRD, NMF>();
+      sched_substep<NRD, NMF>();
+      __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
+      __builtin_amdgcn_s_setprio(0);
     }
-    bf16x8 wf[2][CB], xf[2][TB];
-    auto read = [&](int kk, bf16x8 (&w_)[CB], bf16x8 (&x_)[TB]) {
-      const int c = 2 * kk + g;
-      w_[0] = as_bf16x8(lds_read16(sw + wrow[0] * ROWB + ((c ^ swz<ROWB>(wrow[0])) * 16)));
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        x_[tb] = as_bf16x8(lds_read16(sx + xrow[tb] * ROWB + ((c ^ swz<ROWB>(xrow[tb])) * 16)));
-#pragma unroll
-      for (int cb = 1; cb < CB; ++cb)
-        w_[cb] = as_bf16x8(lds_read16(sw + wrow[cb] * ROWB + ((c ^ swz<ROWB>(wrow[cb])) * 16)));
-    };
-    __builtin_amdgcn_s_setprio(1);
-    read(0, wf[0], xf[0]);
-#pragma unroll
-    for (int kk = 0; kk < KSUB; ++kk) {
-      if (kk + 1 < KSUB) read(kk + 1, wf[(kk + 1) & 1], xf[(kk + 1) & 1]);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[cb][tb] = mfma32(wf[kk & 1][cb], xf[kk & 1][tb], acc[cb][tb]);
-    }
-    // reads of sub-step 0, then per sub-step its MFMAs with the next
-    // sub-step's reads threaded one after each of the first MFMAs
-    constexpr int NMF = CB * TB, NRD = CB + TB;
-    __builtin_amdgcn_sched_group_barrier(0x100, NRD, 0);
-    sched_substep<NRD, NMF>();
-    sched_substep<NRD, NMF>();
-    sched_substep<NRD, NMF>();
-    __builtin_amdgcn_sched_group_barrier(0x008, NMF, 0);
-    __builtin_amdgcn_s_setprio(0);
   };
 
   // ---- prologue (slot 0): A loads X_0 and X_1, B loads W_0
