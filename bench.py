@@ -814,7 +814,7 @@ def bench_sp_prefill(tp, args):
                                      "rows of the 8-way fp32 sum", "M": M, "h": h, "I_s": I_s, "t": t},
                  roofline={"bound": "mfma", "achieved": round(gu_tf, 1), "peak": BF16_PEAK_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(gu_tf / BF16_PEAK_TFLOPS, 4),
-                           "traffic": recorded_traffic("gateup_prefill", "prefill70b"), "kernel": "gateup_prefill"},
+                           "traffic": recorded_traffic("gateup_prefill", "sp_prefill70b"), "kernel": "gateup_prefill"},
                  kernels={k: {"launches": v[1], "avg_us": 1e3 * v[0] / v[1]} for k, v in prof.items()},
                  reduce_scatter={"GBps": round(rs_bytes * rs_n / (rs_ms * 1e-3) / 1e9, 1),
                                  "frac_hbm": round(rs_bytes * rs_n / (rs_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
