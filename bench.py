@@ -420,7 +420,8 @@ def bench_decode70b(tp, args):
     achieved = timed_bytes / (ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": recorded_traffic("gateup_decode", "decode70b"), "kernel": "gateup_decode",
+            "traffic": recorded_traffic("gateup_decode", "decode70b" + ("_rowmajor" if args.row_major else "")),
+            "kernel": "gateup_decode",
             "per_launch_bytes": {str(ph.M): workloads.gateup_bytes(ph.M, h, I_s) for ph in phases},
             "avg_us": round(1e3 * ms / cnt, 3),
             "per_M_launch_us": {str(ph.M): spread([d for j, d in enumerate(gu_dur) if (warmup + j) % nph == idx])
@@ -653,7 +654,9 @@ def bench_quant(tp, args, cfg_id):
                        "h": h, "I_s": I_s, "t": t, "weight_sets": len(sets)},
                roofline={"bound": "hbm", "achieved": round(gu_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-                         "traffic": recorded_traffic("gateup_decode", args.workload), "kernel": "gateup_decode",
+                         "traffic": recorded_traffic("gateup_decode",
+                                                     args.workload + ("_rowmajor" if args.row_major else "")),
+                         "kernel": "gateup_decode",
                          "avg_us": round(1e3 * gu_ms / gu_n, 3), "launch_us": spread(gu_dur),
                          "source": "HIP events on the gate/up launch of phase i mod %d on the timed steps i "
                                    "with i mod %d < %d" % (max(nph, 3), max(nph, 3), nph)},
